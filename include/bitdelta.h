@@ -1,0 +1,186 @@
+/*
+ * bitdelta.h -- C ABI of libbitdelta.so: BitDelta compression of fine-tune
+ * deltas and multi-tenant application of many users' 1-bit deltas on one
+ * shared base weight, on AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those described on the pages
+ *  [P1] "BitDelta (ZIP-7) - Per-User Personalization Without LoRA"
+ *       (hanzoskills.com/bitdelta), "How BitDelta Works" steps 1-5 and
+ *       "Safety Benefits / 1. Outlier Clipping";
+ *  [P2] "BitDelta Guide: 1-Bit Delta Quantization for LLM Serving"
+ *       (aifetchly blog), "1. Mathematical Formulation", "2. Optimal L2 Norm
+ *       Initialization", "Systems Mechanics: Fused 1-Bit GEMM and
+ *       Multi-Tenant Serving Runtimes" 1-2;
+ *  [P5] "Per-Axis Weight Deltas for Frequent Model Updates" (ai.info summary
+ *       of arXiv 2512.19720), "Key Contributions" 1 and the implementation
+ *       details under "Methodology in Plain English".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Weights use the nn.Linear layout W[d_out][d_in], row-major; activations
+ *    X[T][d_in]; outputs Y[T][d_out].
+ *  - Every pointer except the host-side `params` structs is a DEVICE pointer
+ *    owned by the caller.  The library never allocates, frees or keeps device
+ *    memory; scratch space is the caller's `workspace`, sized by the
+ *    *_workspace_bytes queries.
+ *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *    stream).  All work is enqueued on it; no entry point synchronises except
+ *    bd_device_status.  Calls are re-entrant: no global mutable state.
+ *  - Argument and shape errors are returned synchronously before anything is
+ *    enqueued.  Data-dependent errors (non-finite delta, out-of-range user id)
+ *    are recorded in a status word inside the workspace and read back with
+ *    bd_device_status after the call.
+ *  - Sign convention: bit 1 <-> +1, bit 0 <-> -1 ([P2] "1. Mathematical
+ *    Formulation"); a zero delta (+0 or -0) maps to +1, i.e. the bit is
+ *    !(delta < 0).
+ *  - Packed signs: uint64 signs[d_out][d_in/64]; bit k of word w of row o is
+ *    the sign of column 64*w + k (bits packed along the input axis, [P2]
+ *    "Systems Mechanics 2", [P5] implementation details).
+ */
+#ifndef BITDELTA_H
+#define BITDELTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BD_ABI_VERSION 1
+
+typedef enum {
+    BD_OK = 0,
+    BD_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum value */
+    BD_ERR_SHAPE = 2,       /* d_in % 64 != 0, d_in % group_size != 0, too few elements to clip */
+    BD_ERR_DTYPE = 3,       /* dtype not accepted for that argument */
+    BD_ERR_UNSUPPORTED = 4, /* bits != 1, group_size not a power of two in [8, 512] */
+    BD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the query returns */
+    BD_ERR_DEVICE = 6,      /* a HIP call or launch failed */
+    BD_ERR_NONFINITE = 7,   /* (async) a delta was NaN or Inf */
+    BD_ERR_USER_ID = 8      /* (async) a user id outside [-1, n_users) */
+} bd_status;
+
+typedef enum { BD_F32 = 0, BD_BF16 = 1, BD_F16 = 2 } bd_dtype;
+
+/* Scale unit of the absmean magnitude.
+ *  MATRIX: one value for the whole matrix ([P2] "2. Optimal L2 Norm
+ *          Initialization": alpha = mean |delta|).
+ *  GROUP:  one value per group of `group_size` consecutive elements along the
+ *          input axis, stored [d_out][d_in/group_size] ([P1] step 2 "Group
+ *          Quantization").
+ *  ROW:    one value per output row, [d_out] (the 1 x d_out vector of [P5]
+ *          "Key Contributions" 1).
+ *  COL:    one value per input column, [d_in] (the d_in x 1 vector). */
+typedef enum {
+    BD_SCALE_MATRIX = 0,
+    BD_SCALE_GROUP = 1,
+    BD_SCALE_ROW = 2,
+    BD_SCALE_COL = 3
+} bd_scale_mode;
+
+typedef struct {
+    int32_t bits;        /* must be 1 */
+    int32_t mode;        /* bd_scale_mode */
+    int32_t group_size;  /* GROUP only: power of two in [8, 512], divides d_in */
+    float clip_k;        /* 0: no clipping; > 0: clamp delta to mean +- clip_k * std first */
+    int32_t scale_dtype; /* BD_F32 or BD_F16 */
+} bd_compress_params;
+
+/* ---------------------------------------------------------------- queries */
+
+int bd_abi_version(void);
+const char* bd_status_string(bd_status s);
+
+/* Bytes of one matrix's packed signs: d_out * d_in / 8 (d_in % 64 == 0), or 0
+ * for invalid sizes. */
+size_t bd_signs_bytes(int64_t d_out, int64_t d_in);
+
+/* Number of scale values of one matrix for params p (MATRIX 1, GROUP
+ * d_out*d_in/group_size, ROW d_out, COL d_in); -1 if p is invalid. */
+int64_t bd_scales_count(const bd_compress_params* p, int64_t d_out, int64_t d_in);
+
+/* Workspace bytes bd_compress needs for this shape (0 if invalid). */
+size_t bd_compress_workspace_bytes(const bd_compress_params* p, int64_t d_out, int64_t d_in);
+
+/* Workspace bytes bd_apply needs (0 if invalid). */
+size_t bd_apply_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t n_users,
+                                int64_t d_out, int64_t d_in, bd_dtype x_dtype, bd_dtype y_dtype);
+
+/* ------------------------------------------------------------ compression */
+
+/* Compress one user's fine-tune delta of one matrix.
+ *
+ * Computes delta = W_fine - W_base ([P1] step 1, [P2] "1. Mathematical
+ * Formulation") as one binary32 subtraction of the widened inputs; when
+ * p->clip_k > 0 clamps it to [mu - k*sigma, mu + k*sigma] with the
+ * whole-matrix mean and unbiased standard deviation computed in binary64 in
+ * two passes ([P1] "Outlier Clipping"); writes the packed signs of the clamped
+ * delta ([P1] step 3, [P2] Sign) and the absmean of |clamped delta| over each
+ * scale unit, accumulated in binary64 and rounded once to p->scale_dtype
+ * ([P2] "2. Optimal L2 Norm Initialization", [P1] step 2, [P5] "Key
+ * Contributions" 1).
+ *
+ *  w_fine, w_base : [d_out][d_in] of w_dtype (BD_F32 or BD_BF16); w_base may
+ *                   be NULL, then w_fine already holds the delta.
+ *  signs_out      : bd_signs_bytes(d_out, d_in) bytes, layout above.
+ *  scales_out     : bd_scales_count(p, ...) values of p->scale_dtype.
+ *  workspace      : >= bd_compress_workspace_bytes(p, d_out, d_in) bytes,
+ *                   256-byte aligned; its status word is reset by the call.
+ * Requires d_in % 64 == 0, d_out >= 1; with clipping d_out*d_in >= 2.
+ * A NaN/Inf delta sets BD_ERR_NONFINITE in the status word (outputs are then
+ * unspecified). */
+bd_status bd_compress(const void* w_fine, const void* w_base, bd_dtype w_dtype, int64_t d_out,
+                      int64_t d_in, const bd_compress_params* p, uint64_t* signs_out,
+                      void* scales_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* -------------------------------------------------------- reconstruction */
+
+/* Dense reconstruction ([P1] step 4 "Reconstruction", step 5 "Serving"):
+ * out[o][i] = (w_base ? w_base[o][i] : 0) + sign(o,i) * scale(o,i), summed in
+ * fp32 and rounded once to out_dtype (BD_F32 or BD_BF16).  w_base (of
+ * w_dtype, BD_F32 or BD_BF16) may be NULL.  Not on the serving hot path: the
+ * apply below never materialises this. */
+bd_status bd_reconstruct(const uint64_t* signs, const void* scales, const bd_compress_params* p,
+                         int64_t d_out, int64_t d_in, const void* w_base, bd_dtype w_dtype,
+                         void* out, bd_dtype out_dtype, void* stream);
+
+/* ------------------------------------------------------------------ apply */
+
+/* Multi-tenant forward of one linear layer ([P2] "Systems Mechanics" 1-2):
+ *     y[t] = X[t] . W_base^T + scale_u (.) (X[t] . S_u^T),   u = user_ids[t],
+ * with the base product computed once for the whole batch and each user's
+ * packed signs streamed from HBM and expanded on chip, never materialising a
+ * dense per-user weight.  The scale enters per mode: MATRIX/ROW multiply the
+ * signed sum, GROUP multiplies each group's partial sum, COL scales X before
+ * the signed sum.
+ *
+ *  x           : [T][d_in] of x_dtype (BD_BF16, or BD_F32 with fp32 w_base).
+ *  w_base      : [d_out][d_in], same dtype as x.
+ *  signs_bank  : [n_users][d_out][d_in/64] uint64, one bd_compress output per
+ *                user, back to back.
+ *  scales_bank : [n_users][bd_scales_count(p, d_out, d_in)] of p->scale_dtype.
+ *  user_ids    : device int32[T]; -1 = base model only; any other id outside
+ *                [0, n_users) also gets the base term only and sets
+ *                BD_ERR_USER_ID in the status word.
+ *  y           : [T][d_out] of y_dtype (BD_F32, or BD_BF16 rounded once from
+ *                the fp32 result).
+ *  workspace   : >= bd_apply_workspace_bytes(...) bytes, 256-byte aligned.
+ * Accumulation is fp32.  T == 0 is a no-op. */
+bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const void* w_base,
+                   int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
+                   const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
+                   bd_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------- status read-back */
+
+/* Synchronises `stream`, then returns the status recorded in the workspace of
+ * the last bd_compress / bd_apply that used it (BD_OK, BD_ERR_NONFINITE or
+ * BD_ERR_USER_ID), or BD_ERR_DEVICE if the copy fails. */
+bd_status bd_device_status(const void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITDELTA_H */

@@ -1,0 +1,114 @@
+// bd_internal.h -- internals shared by the translation units of libbitdelta.so.
+//
+// Workspace layouts, launch plans and small device helpers.  Every size a
+// kernel assumes is computed here once and used both by the workspace queries
+// and by the launches, so a plan that validates is a plan that fits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bitdelta.h"
+
+namespace bd {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Status word bits (first 4 bytes of every workspace).
+enum : uint32_t { ST_NONFINITE = 1u, ST_USER_ID = 2u };
+
+// ---------------------------------------------------------------- compress
+// Stream tiling: a wave covers one row segment of kSegCols columns per row
+// (8 consecutive elements per lane, 16-byte loads for bf16), a block of 4
+// waves covers `rows_per_block` rows of one segment.
+constexpr int kSegCols = 512;
+constexpr int kCompressThreads = 256;
+
+struct CompressPlan {
+    int64_t d_out = 0, d_in = 0, n = 0;
+    int64_t n_seg = 0, rows_per_block = 0, n_rchunk = 0, n_blocks = 0;
+    int mode = 0, group = 0, sdtype = 0;
+    bool clip = false;
+    double clip_k = 0.0;
+    // workspace offsets (bytes)
+    size_t off_status = 0, off_stats = 0, off_part_sum = 0, off_part_m2 = 0, off_part_abs = 0;
+    size_t total = 0;
+};
+
+// Returns BD_OK and fills `plan`, or the synchronous error for these params.
+bd_status make_compress_plan(const bd_compress_params* p, int64_t d_out, int64_t d_in,
+                             CompressPlan* plan);
+hipError_t launch_compress(const CompressPlan& pl, const void* wf, const void* wb, int wdtype,
+                           uint64_t* signs, void* scales, char* ws, hipStream_t s);
+
+// ------------------------------------------------------------------- apply
+constexpr int kItemTokens = 64;   // max tokens of one (user, chunk) work item
+constexpr int kMaxGroupT = 8192;  // tokens the one-block grouping kernel sorts in LDS
+constexpr int kMaxUsers = (1 << 17) - 1;
+
+struct ApplyPlan {
+    int64_t T = 0, d_in = 0, d_out = 0;
+    int32_t U = 0;
+    int mode = 0, group = 0, sdtype = 0;
+    int xdtype = 0, ydtype = 0;
+    int64_t max_items = 0;
+    size_t off_status = 0, off_perm = 0, off_items = 0, off_xp = 0, off_yf = 0;
+    size_t total = 0;
+};
+
+bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int64_t d_out,
+                          int64_t d_in, int xdtype, int ydtype, ApplyPlan* plan);
+hipError_t launch_apply(const ApplyPlan& pl, const void* x, const void* wb, const uint64_t* signs,
+                        const void* scales, const int32_t* ids, void* y, char* ws, hipStream_t s);
+
+hipError_t launch_reconstruct(const uint64_t* signs, const void* scales, int mode, int group,
+                              int sdtype, int64_t d_out, int64_t d_in, const void* wb, int wdtype,
+                              void* out, int odtype, hipStream_t s);
+
+// Zero `n` 32-bit words with a kernel (no memset node, so capture-safe).
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// binary64 -> binary16, round to nearest even, from the bit fields.
+__device__ __forceinline__ uint16_t f64_to_f16(double x) {
+    uint64_t b = (uint64_t)__double_as_longlong(x);
+    uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+    uint64_t a = b & 0x7FFFFFFFFFFFFFFFull;
+    if (a > 0x7FF0000000000000ull) return 0x7E00u;
+    if (a == 0x7FF0000000000000ull) return sign | 0x7C00u;
+    int e = (int)(a >> 52) - 1023;
+    if (e < -25) return sign;  // below half the smallest subnormal (also double subnormals)
+    uint64_t mant = (a & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;  // 53 bits
+    if (e >= -14) {
+        uint64_t q = mant >> 42, rem = mant & ((1ull << 42) - 1), half = 1ull << 41;
+        if (rem > half || (rem == half && (q & 1))) ++q;
+        uint64_t r = ((uint64_t)(e + 15) << 10) + q - 1024;  // carry into the exponent is right
+        if (r >= 0x7C00u) return sign | 0x7C00u;
+        return sign | (uint16_t)r;
+    }
+    int sh = 28 - e;  // value / 2^-24 = mant * 2^(e-28); 43 <= sh <= 53
+    uint64_t q = mant >> sh, rem = mant & ((1ull << sh) - 1), half = 1ull << (sh - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+    return sign | (uint16_t)q;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    _Float16 v;
+    __builtin_memcpy(&v, &h, 2);
+    return (float)v;
+}
+
+}  // namespace bd

@@ -1,0 +1,70 @@
+// bd_reconstruct.hip -- dense reconstruction of a packed delta.
+//
+// out[o][i] = (W_base[o][i] if given) + sign(o,i) * scale(o,i) ([P1] "How
+// BitDelta Works" step 4 "Reconstruction" and step 5 "Serving"), added in
+// fp32 and rounded once to the output dtype.  Off the serving hot path (the
+// apply never builds this); used for checks and for merging a hot user's
+// weight.  Each thread writes 8 consecutive columns.
+#include "bd_internal.h"
+
+namespace bd {
+namespace {
+
+__device__ __forceinline__ float scale_at(const void* s, int sdtype, int mode, int group,
+                                          int64_t d_in, int64_t o, int64_t i) {
+    int64_t idx = 0;
+    if (mode == BD_SCALE_GROUP) idx = o * (d_in / group) + i / group;
+    else if (mode == BD_SCALE_ROW) idx = o;
+    else if (mode == BD_SCALE_COL) idx = i;
+    return sdtype == BD_F16 ? f16_to_f32(((const uint16_t*)s)[idx]) : ((const float*)s)[idx];
+}
+
+__global__ void __launch_bounds__(256)
+k_reconstruct(const uint64_t* __restrict__ signs, const void* __restrict__ scales, int mode,
+              int group, int sdtype, int64_t d_out, int64_t d_in, const void* __restrict__ wb,
+              int wdtype, void* __restrict__ out, int odtype) {
+    const int64_t per_row = d_in / 8;
+    const int64_t total = d_out * per_row;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t o = idx / per_row, i0 = (idx % per_row) * 8;
+        const uint32_t byte = (uint32_t)(signs[o * (d_in / 64) + i0 / 64] >> (i0 % 64)) & 0xFFu;
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float s = scale_at(scales, sdtype, mode, group, d_in, o, i0 + j);
+            float d = ((byte >> j) & 1u) ? s : -s;
+            if (wb) {
+                const int64_t e = o * d_in + i0 + j;
+                const float b = wdtype == BD_BF16 ? __uint_as_float((uint32_t)((const uint16_t*)wb)[e] << 16)
+                                                  : ((const float*)wb)[e];
+                d = b + d;
+            }
+            v[j] = d;
+        }
+        if (odtype == BD_BF16) {
+            uint16_t* dst = (uint16_t*)out + o * d_in + i0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = f32_to_bf16(v[j]);
+        } else {
+            float* dst = (float*)out + o * d_in + i0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = v[j];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_reconstruct(const uint64_t* signs, const void* scales, int mode, int group,
+                              int sdtype, int64_t d_out, int64_t d_in, const void* wb, int wdtype,
+                              void* out, int odtype, hipStream_t s) {
+    const int64_t total = d_out * (d_in / 8);
+    int64_t nb = (total + 255) / 256;
+    if (nb > 65535) nb = 65535;
+    hipLaunchKernelGGL(k_reconstruct, dim3((unsigned)nb), dim3(256), 0, s, signs, scales, mode,
+                       group, sdtype, d_out, d_in, wb, wdtype, out, odtype);
+    return hipGetLastError();
+}
+
+}  // namespace bd

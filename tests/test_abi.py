@@ -1,0 +1,104 @@
+"""Host-only checks of the C ABI library: it loads, exports what the header
+declares, answers size queries, and rejects bad arguments before enqueueing
+anything (every call below fails validation, so no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+torch = pytest.importorskip("torch")  # loads the HIP runtime the library binds to
+
+from tenant_serving_amd import bitdelta as B  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "bitdelta.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bd_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.lib()
+    names = header_functions()
+    assert "bd_compress" in names and "bd_apply" in names and "bd_reconstruct" in names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    assert lib.bd_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(9):
+        assert B.status_string(s) and B.status_string(s) != "unknown status"
+
+
+def test_size_queries():
+    assert B.bd_signs_bytes(4096, 4096) == 4096 * 4096 // 8
+    assert B.bd_signs_bytes(4096, 100) == 0
+    p = B.params("group", 128)
+    assert B.bd_scales_count(p, 256, 512) == 256 * 4
+    assert B.bd_scales_count(B.params("row"), 17408, 5120) == 17408
+    assert B.bd_scales_count(B.params("col"), 5120, 17408) == 17408
+    assert B.bd_scales_count(B.params("matrix"), 7, 64) == 1
+    assert B.bd_scales_count(B.params("group", 100), 8, 512) == -1
+    assert B.bd_compress_workspace_bytes(p, 256, 512) >= 256
+    assert B.bd_apply_workspace_bytes(p, 16, 4, 256, 512, B.BD_BF16, B.BD_F32) > 0
+
+
+def test_llama8b_stack_signs_bytes():
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096),
+              (14336, 4096), (4096, 14336)]
+    assert 32 * sum(B.bd_signs_bytes(o, i) for o, i in shapes) == 872_415_232
+
+
+def _compress_raw(p, d_out=64, d_in=128, wf=1, ws=1, ws_bytes=1 << 20, dtype=B.BD_BF16,
+                  signs=1, scales=1):
+    L = B.lib()
+    vp = ctypes.c_void_p
+    return L.bd_compress(vp(wf) if wf else None, None, dtype, d_out, d_in,
+                         ctypes.byref(p) if p is not None else None, vp(signs) if signs else None,
+                         vp(scales) if scales else None, vp(ws) if ws else None, ws_bytes, None)
+
+
+def test_compress_rejects_bad_arguments_synchronously():
+    ok = B.params("matrix")
+    assert _compress_raw(None) == B.BD_ERR_INVALID_ARG
+    assert _compress_raw(ok, wf=0) == B.BD_ERR_INVALID_ARG
+    assert _compress_raw(ok, signs=0) == B.BD_ERR_INVALID_ARG
+    assert _compress_raw(ok, d_in=100) == B.BD_ERR_SHAPE
+    assert _compress_raw(ok, d_out=0) == B.BD_ERR_SHAPE
+    assert _compress_raw(ok, dtype=B.BD_F16) == B.BD_ERR_DTYPE
+    assert _compress_raw(B.params("matrix", bits=2)) == B.BD_ERR_UNSUPPORTED
+    assert _compress_raw(B.params("group", 100)) == B.BD_ERR_UNSUPPORTED
+    assert _compress_raw(B.params("group", 256), d_in=192) == B.BD_ERR_SHAPE
+    assert _compress_raw(B.params("matrix", scale_dtype=B.BD_BF16)) == B.BD_ERR_DTYPE
+    assert _compress_raw(B.params("matrix", clip_k=float("nan"))) == B.BD_ERR_INVALID_ARG
+    assert _compress_raw(ok, ws=0) == B.BD_ERR_WORKSPACE
+    assert _compress_raw(ok, ws_bytes=8) == B.BD_ERR_WORKSPACE
+    assert _compress_raw(ok, ws=256 + 8) == B.BD_ERR_WORKSPACE      # misaligned workspace
+    assert _compress_raw(ok, wf=256 + 8, ws=1 << 12) == B.BD_ERR_INVALID_ARG  # misaligned input
+
+
+def test_apply_rejects_bad_arguments_synchronously():
+    L = B.lib()
+    vp = ctypes.c_void_p
+
+    def call(p=B.params("matrix"), T=16, d_in=128, d_out=64, U=4, xd=B.BD_BF16, yd=B.BD_F32,
+             ws=1 << 12, ws_bytes=1 << 30, x=1 << 12):
+        return L.bd_apply(vp(x) if x else None, xd, T, d_in, vp(1 << 12), d_out, vp(1 << 12),
+                          vp(1 << 12), ctypes.byref(p), U, vp(1 << 12), vp(1 << 12), yd,
+                          vp(ws) if ws else None, ws_bytes, None)
+
+    assert call(d_in=96) == B.BD_ERR_SHAPE
+    assert call(xd=B.BD_F16) == B.BD_ERR_DTYPE
+    assert call(yd=B.BD_F16) == B.BD_ERR_DTYPE
+    assert call(T=-1) == B.BD_ERR_INVALID_ARG
+    assert call(U=-2) == B.BD_ERR_INVALID_ARG
+    assert call(p=B.params("group", 64)) == B.BD_ERR_UNSUPPORTED  # bf16 MFMA path needs g >= 128
+    assert call(T=9000) == B.BD_ERR_UNSUPPORTED
+    assert call(ws=0) == B.BD_ERR_WORKSPACE
+    assert call(ws_bytes=16) == B.BD_ERR_WORKSPACE
+    assert call(x=0) == B.BD_ERR_INVALID_ARG
+    assert call(x=(1 << 12) + 2) == B.BD_ERR_INVALID_ARG
