@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-user BitDelta decode apply on one MI355X.
+
+Workload (default): the Llama-3.1-8B-shaped q_proj, W_base 4096x4096 bf16,
+16 users' packed 1-bit deltas with one fp32 scale per matrix, a decode batch
+of 16 tokens (one per user, in a seeded shuffled order), fp32 output.  A step
+is one apply of that layer: group the batch by user, the shared base product
+on the matrix cores, the per-user delta product (bd_batch_prepare +
+bd_base_gemm + bd_delta_apply, the phases of bd_apply).  Steps rotate over R
+independent input sets (weights, banks, activations) so consecutive steps do
+not hit the 256 MB last-level cache; all inputs are resident in HBM before the
+timed region starts.
+
+Printed: one JSON line with the apply throughput in algorithmic HBM GB/s
+(value), tokens/s, per-kernel HIP-event timings, the roofline of the dominant
+kernel, the compress leg (bd_compress on the same matrix shape), and the CPU
+oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+METRIC = ("multi-user BitDelta decode apply: achieved HBM GB/s (% peak) and tokens/s per GPU")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--sets", type=int, default=16, help="rotating input sets")
+    ap.add_argument("--compress-steps", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="output rows of the oracle's sampled apply")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("bd_apply.hip", "bd_compress.hip", "bd_internal.h"):
+        with open(os.path.join(ROOT, "tenant_serving_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(workload, {}).get(kernel)
+    if not e or e.get("source_digest") != kernel_source_digest():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from tenant_serving_amd import bitdelta as B
+    from tenant_serving_amd import synth as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R = max(1, args.sets)
+    w0 = S.workload(2)
+    mat = w0.matrices[0]
+    d_out, d_in, U, T = mat.d_out, mat.d_in, w0.n_users, w0.T
+    w = dataclasses.replace(w0, matrices=[mat] * R, xgroups=[d_in] * R)
+    p = B.params("matrix")
+
+    # ---------------------------------------------------------- resident inputs
+    ids_np = S.user_ids(w0)
+    ids = torch.from_numpy(ids_np).to(dev)
+    sets = []
+    wf = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)
+    cws = B.workspace(B.bd_compress_workspace_bytes(p, d_out, d_in), dev)
+    for s in range(R):
+        wb = S.dev_wbase(w, s)
+        signs = torch.empty((U, d_out, d_in // 64), dtype=torch.int64, device=dev)
+        scales = torch.empty((U, 1), dtype=torch.float32, device=dev)
+        for u in range(U):
+            S.dev_wfine(w, s, u, wb, out=wf)
+            B.compress(wf, wb, p, signs_out=signs[u], scales_out=scales[u], ws=cws)
+        x = S.dev_x(w, s)
+        y = torch.empty((T, d_out), dtype=torch.float32, device=dev)
+        sets.append((wb, signs, scales, x, y))
+    batch_bytes = B.bd_batch_workspace_bytes(T, U, d_in, B.BD_BF16)
+    batch = B.workspace(batch_bytes, dev)
+    torch.cuda.synchronize()
+    assert B.bd_device_status(cws) == B.BD_OK
+
+    def step(k, ev=None):
+        wb, signs, scales, x, y = sets[k % R]
+        if ev is not None:
+            ev[0].record()
+        st = B.bd_batch_prepare(x, ids, U, batch)
+        if ev is not None:
+            ev[1].record()
+        st |= B.bd_base_gemm(x, wb, y)
+        if ev is not None:
+            ev[2].record()
+        st |= B.bd_delta_apply(batch, x, U, signs, scales, p, y)
+        if ev is not None:
+            ev[3].record()
+        return st
+
+    for k in range(args.warmup):
+        assert step(k) == B.BD_OK
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------- timed steps
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert B.bd_device_status(batch) == B.BD_OK
+    ms_per_step = (t1 - t0) * 1e3 / K
+    prep_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    gemm_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    delta_us = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
+    gpu_step_us = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) * 1e3
+
+    # algorithmic bytes (each byte the math must touch once)
+    n_active = len(set(int(u) for u in ids_np if 0 <= u < U))
+    bytes_w = d_out * d_in * 2
+    bytes_bits = n_active * (d_out * d_in // 8 + 4)
+    bytes_x, bytes_y = T * d_in * 2, T * d_out * 4
+    bytes_step = bytes_w + bytes_bits + bytes_x + bytes_y + 4 * T
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+    kernels = {"k_base_gemm": (gemm_us, bytes_w + bytes_x + bytes_y),
+               "k_delta": (delta_us, bytes_bits)}
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    dom_us, dom_bytes = kernels[dom]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, w0.name),
+                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)}
+
+    # ------------------------------------------------------------ compress leg
+    n_c = min(8, U)
+    wfs = []
+    for u in range(n_c):
+        t = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)
+        S.dev_wfine(w, u % R, u, sets[u % R][0], out=t)
+        wfs.append((t, sets[u % R][0]))
+    c_signs = torch.empty((d_out, d_in // 64), dtype=torch.int64, device=dev)
+    c_scales = torch.empty(1, dtype=torch.float32, device=dev)
+    for k in range(4):
+        B.bd_compress(wfs[k % n_c][0], wfs[k % n_c][1], p, c_signs, c_scales, cws)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.compress_steps)]
+    torch.cuda.synchronize()
+    for k in range(args.compress_steps):
+        cev[k][0].record()
+        B.bd_compress(wfs[k % n_c][0], wfs[k % n_c][1], p, c_signs, c_scales, cws)
+        cev[k][1].record()
+    torch.cuda.synchronize()
+    comp_us = float(np.mean([e[0].elapsed_time(e[1]) for e in cev])) * 1e3
+    comp_bytes = 2 * d_out * d_in * 2 + d_out * d_in // 8 + 4
+    comp_gbs = comp_bytes / (comp_us * 1e-6) / 1e9
+    compress = {"call_us": round(comp_us, 3), "algorithmic_bytes": comp_bytes,
+                "achieved": round(comp_gbs, 1), "unit": "GB/s",
+                "frac": round(comp_gbs / HBM_PEAK_GBS, 4)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w0.name, "d_out": d_out, "d_in": d_in, "n_users": U,
+                   "active_users": n_active, "tokens": T, "scale": "matrix fp32",
+                   "y_dtype": "fp32", "rotating_sets": R, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": bytes_step,
+        "gpu_step_us_events": round(gpu_step_us, 3),
+        "kernels_us": {"batch_prepare": round(prep_us, 3), "k_base_gemm": round(gemm_us, 3),
+                       "k_delta": round(delta_us, 3)},
+        "roofline": roofline,
+        "compress": compress,
+        "kernel_source_digest": kernel_source_digest(),
+    }
+
+    # --------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, ids_np, args.cpu_rows, bytes_step)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, ids_np, rows, bytes_step):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    the apply of all tokens on `rows` output rows of input set 0 (its bank is
+    compressed by the oracle first, not timed in the rate)."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "oracle"))
+    import oracle as O
+
+    from tenant_serving_amd import synth as S
+
+    mat = w.matrices[0]
+    d_out, d_in, U = mat.d_out, mat.d_in, w.n_users
+    rows = max(1, min(rows, d_out))
+    t0 = time.perf_counter()
+    wb = S.host_wbase(w, 0)
+    words, scs = [], []
+    for u in range(U):
+        wf = S.host_wfine(w, 0, u, wbase=wb)
+        ww, ss, _, _ = O.compress(wf, wb, O.MATRIX, dtype=O.BF16)
+        words.append(ww[:rows])
+        scs.append(ss)
+    t1 = time.perf_counter()
+    x = S.host_x(w, 0)
+    t2 = time.perf_counter()
+    O.apply(x, wb[:rows], np.stack(words), np.stack(scs), O.MATRIX, ids_np)
+    t3 = time.perf_counter()
+    sample_bytes = bytes_step * rows / d_out
+    return {"value": round(sample_bytes / (t3 - t2) / 1e9, 4), "unit": "GB/s",
+            "cores": min(O.num_threads(), w.T), "kind": "oracle",
+            "sample": f"apply of all {w.T} tokens on {rows} of {d_out} output rows of one "
+                      f"input set (fp64 plain loops, OpenMP over tokens); rate = that share of "
+                      f"the step's algorithmic bytes / oracle time",
+            "apply_s": round(t3 - t2, 3), "compress_16_users_s": round(t1 - t0, 3),
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -166,17 +166,54 @@ bd_status bd_reconstruct(const uint64_t* signs, const void* scales, const bd_com
  *  y           : [T][d_out] of y_dtype (BD_F32, or BD_BF16 rounded once from
  *                the fp32 result).
  *  workspace   : >= bd_apply_workspace_bytes(...) bytes, 256-byte aligned.
- * Accumulation is fp32.  T == 0 is a no-op. */
+ * Accumulation is fp32.  T == 0 is a no-op.  bf16 inputs: T <= 8192 tokens
+ * per call and GROUP group_size >= 128 (BD_ERR_UNSUPPORTED otherwise).
+ * Equivalent to bd_batch_prepare + bd_base_gemm + bd_delta_apply (+ a cast
+ * for bf16 y) on one workspace. */
 bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const void* w_base,
                    int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
                    const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
                    bd_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
 
+/* The three phases of bd_apply, for callers that apply many matrices to one
+ * batch (e.g. q, k and v read the same X and the same user ids): prepare the
+ * batch once, then run the shared base product and the per-user delta product
+ * of each matrix ([P2] "Systems Mechanics" 1: Y = Y_base + Y_delta). */
+
+/* Workspace of a prepared batch: the grouping of the tokens by user. */
+size_t bd_batch_workspace_bytes(int64_t T, int32_t n_users, int64_t d_in, bd_dtype x_dtype);
+
+/* Groups the T tokens by user id (tokens of one user contiguous, in token
+ * order, cut into work items of at most 32 tokens) into `batch` (caller-owned
+ * device memory of >= bd_batch_workspace_bytes, 256-byte aligned).  Its first
+ * word is the status word (BD_ERR_USER_ID for an id outside [-1, n_users)).
+ * x is not read for bf16 inputs (it may be NULL); the grouping depends only on
+ * the ids. */
+bd_status bd_batch_prepare(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                           const int32_t* user_ids, int32_t n_users, void* batch,
+                           size_t batch_bytes, void* stream);
+
+/* Shared base product y[T][d_out] = X . W_base^T in fp32 (overwrites y); bf16
+ * inputs run on the matrix cores, fp32 inputs on the vector ALUs. */
+bd_status bd_base_gemm(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                       const void* w_base, int64_t d_out, float* y, void* stream);
+
+/* Per-user delta product added into y: y[t] += scale_u (.) (X[t] . S_u^T) for
+ * every token of the prepared batch whose user is valid.  `batch` must come
+ * from bd_batch_prepare with the same user ids, x_dtype, T, d_in and n_users;
+ * x is [T][d_in] (any activation tensor of that batch, e.g. the input of q, k
+ * or v); y is fp32 [T][d_out]. */
+bd_status bd_delta_apply(const void* batch, const void* x, bd_dtype x_dtype, int64_t T,
+                         int64_t d_in, int32_t n_users, int64_t d_out, const uint64_t* signs_bank,
+                         const void* scales_bank, const bd_compress_params* p, float* y,
+                         void* stream);
+
 /* ------------------------------------------------------- status read-back */
 
-/* Synchronises `stream`, then returns the status recorded in the workspace of
- * the last bd_compress / bd_apply that used it (BD_OK, BD_ERR_NONFINITE or
- * BD_ERR_USER_ID), or BD_ERR_DEVICE if the copy fails. */
+/* Synchronises `stream`, then returns the status recorded in the workspace (or
+ * prepared batch) of the last bd_compress / bd_apply / bd_batch_prepare that
+ * used it (BD_OK, BD_ERR_NONFINITE or BD_ERR_USER_ID), or BD_ERR_DEVICE if the
+ * copy fails. */
 bd_status bd_device_status(const void* workspace, void* stream);
 
 #ifdef __cplusplus

@@ -41,8 +41,20 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { O_F32 = 0, O_BF16 = 1, O_F16 = 2 };
+
+/* Threads the parallel loops of orc_apply may use. */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 enum { O_MATRIX = 0, O_GROUP = 1, O_ROW = 2, O_COL = 3 };
 
 /* ------------------------------------------------------------ conversions */

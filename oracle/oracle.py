@@ -40,6 +40,8 @@ def lib():
             build()
         L = ctypes.CDLL(LIB)
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = ctypes.c_int
         L.orc_f64_to_f16.argtypes = [dbl]
         L.orc_f64_to_f16.restype = ctypes.c_uint16
         L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -83,6 +85,10 @@ def _dtype_of(a: np.ndarray, dtype=None) -> int:
     if a.dtype == np.uint16:
         return BF16
     raise TypeError(f"unsupported array dtype {a.dtype}")
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
 
 
 def f64_to_f16(x: float) -> int:

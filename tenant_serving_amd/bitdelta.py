@@ -73,6 +73,14 @@ def lib() -> ctypes.CDLL:
                                ctypes.c_int, vp, sz, vp]
         L.bd_device_status.restype = ctypes.c_int
         L.bd_device_status.argtypes = [vp, vp]
+        L.bd_batch_workspace_bytes.restype = sz
+        L.bd_batch_workspace_bytes.argtypes = [i64, i32, i64, ctypes.c_int]
+        L.bd_batch_prepare.restype = ctypes.c_int
+        L.bd_batch_prepare.argtypes = [vp, ctypes.c_int, i64, i64, vp, i32, vp, sz, vp]
+        L.bd_base_gemm.restype = ctypes.c_int
+        L.bd_base_gemm.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp]
+        L.bd_delta_apply.restype = ctypes.c_int
+        L.bd_delta_apply.argtypes = [vp, vp, ctypes.c_int, i64, i64, i32, i64, vp, vp, P, vp, vp]
         _lib = L
     return _lib
 
@@ -165,6 +173,31 @@ def bd_apply(x, w_base, signs_bank, scales_bank, p, n_users, user_ids, y, worksp
 
 def bd_device_status(workspace, stream=None) -> int:
     return int(lib().bd_device_status(_ptr(workspace), _stream(workspace, stream)))
+
+
+def bd_batch_workspace_bytes(T: int, n_users: int, d_in: int, x_dtype: int) -> int:
+    return int(lib().bd_batch_workspace_bytes(T, n_users, d_in, x_dtype))
+
+
+def bd_batch_prepare(x, user_ids, n_users, batch, stream=None) -> int:
+    T, d_in = x.shape
+    return int(lib().bd_batch_prepare(_ptr(x), _dtype_code(x), T, d_in, _ptr(user_ids),
+                                      int(n_users), _ptr(batch),
+                                      batch.numel() * batch.element_size(), _stream(x, stream)))
+
+
+def bd_base_gemm(x, w_base, y, stream=None) -> int:
+    T, d_in = x.shape
+    return int(lib().bd_base_gemm(_ptr(x), _dtype_code(x), T, d_in, _ptr(w_base),
+                                  w_base.shape[0], _ptr(y), _stream(x, stream)))
+
+
+def bd_delta_apply(batch, x, n_users, signs_bank, scales_bank, p, y, stream=None) -> int:
+    T, d_in = x.shape
+    d_out = y.shape[1]
+    return int(lib().bd_delta_apply(_ptr(batch), _ptr(x), _dtype_code(x), T, d_in, int(n_users),
+                                    d_out, _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p),
+                                    _ptr(y), _stream(y, stream)))
 
 
 # ------------------------------------------------------- allocating helpers

@@ -62,6 +62,12 @@ size_t bd_apply_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t 
     return pl.total;
 }
 
+size_t bd_batch_workspace_bytes(int64_t T, int32_t n_users, int64_t d_in, bd_dtype x_dtype) {
+    BatchPlan pl;
+    if (make_batch_plan(T, n_users, d_in, x_dtype, &pl) != BD_OK) return 0;
+    return pl.total;
+}
+
 bd_status bd_compress(const void* w_fine, const void* w_base, bd_dtype w_dtype, int64_t d_out,
                       int64_t d_in, const bd_compress_params* p, uint64_t* signs_out,
                       void* scales_out, void* workspace, size_t ws_bytes, void* stream) {
@@ -93,6 +99,55 @@ bd_status bd_reconstruct(const uint64_t* signs, const void* scales, const bd_com
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
+bd_status bd_batch_prepare(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                           const int32_t* user_ids, int32_t n_users, void* batch,
+                           size_t batch_bytes, void* stream) {
+    BatchPlan bp;
+    bd_status st = make_batch_plan(T, n_users, d_in, x_dtype, &bp);
+    if (st != BD_OK) return st;
+    if (!batch || batch_bytes < bp.total || !aligned(batch, kAlign)) return BD_ERR_WORKSPACE;
+    if (T > 0 && (!x || !user_ids)) return BD_ERR_INVALID_ARG;
+    if (T > 0 && (!aligned(x, 16) || !aligned(user_ids, 4))) return BD_ERR_INVALID_ARG;
+    hipError_t e = launch_batch_prepare(bp, x, user_ids, (char*)batch, (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_base_gemm(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                       const void* w_base, int64_t d_out, float* y, void* stream) {
+    if (!valid_wdtype(x_dtype)) return BD_ERR_DTYPE;
+    if (T < 0) return BD_ERR_INVALID_ARG;
+    if (d_in <= 0 || d_in % 64 != 0 || d_out <= 0) return BD_ERR_SHAPE;
+    if (x_dtype == BD_BF16 && (d_out * d_in * 2 >= ((int64_t)1 << 31) ||
+                               T * d_in * 2 >= ((int64_t)1 << 31)))
+        return BD_ERR_UNSUPPORTED;  // 32-bit buffer offsets
+    if (T == 0) return BD_OK;
+    if (!x || !w_base || !y) return BD_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w_base, 16) || !aligned(y, 16)) return BD_ERR_INVALID_ARG;
+    hipError_t e = launch_base_gemm(x, x_dtype, T, d_in, w_base, d_out, y, (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_delta_apply(const void* batch, const void* x, bd_dtype x_dtype, int64_t T,
+                         int64_t d_in, int32_t n_users, int64_t d_out, const uint64_t* signs_bank,
+                         const void* scales_bank, const bd_compress_params* p, float* y,
+                         void* stream) {
+    BatchPlan bp;
+    DeltaPlan dp;
+    bd_status st = make_batch_plan(T, n_users, d_in, x_dtype, &bp);
+    if (st != BD_OK) return st;
+    st = make_delta_plan(p, bp, d_out, &dp);
+    if (st != BD_OK) return st;
+    if (!batch || !aligned(batch, kAlign)) return BD_ERR_INVALID_ARG;
+    if (T == 0) return BD_OK;
+    if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return BD_ERR_INVALID_ARG;
+    if (n_users > 0 && (!signs_bank || !scales_bank || !aligned(signs_bank, 16) ||
+                        !aligned(scales_bank, 16)))
+        return BD_ERR_INVALID_ARG;
+    hipError_t e = launch_delta(bp, dp, (const char*)batch, x, signs_bank, scales_bank, y,
+                                (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
 bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const void* w_base,
                    int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
                    const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
@@ -102,17 +157,23 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
     bd_status st = make_apply_plan(p, T, n_users, d_out, d_in, x_dtype, y_dtype, &pl);
     if (st != BD_OK) return st;
     if (!workspace || ws_bytes < pl.total || !aligned(workspace, kAlign)) return BD_ERR_WORKSPACE;
-    if (T == 0) {
-        hipError_t e = launch_zero_u32((uint32_t*)workspace, (int64_t)(kAlign / 4), (hipStream_t)stream);
-        return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+    if (T > 0) {
+        if (!x || !w_base || !y || !user_ids) return BD_ERR_INVALID_ARG;
+        if (n_users > 0 && (!signs_bank || !scales_bank)) return BD_ERR_INVALID_ARG;
+        if (!aligned(x, 16) || !aligned(w_base, 16) || !aligned(y, 16) || !aligned(user_ids, 4) ||
+            (signs_bank && !aligned(signs_bank, 16)) || (scales_bank && !aligned(scales_bank, 16)))
+            return BD_ERR_INVALID_ARG;
     }
-    if (!x || !w_base || !y || !user_ids) return BD_ERR_INVALID_ARG;
-    if (n_users > 0 && (!signs_bank || !scales_bank)) return BD_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(w_base, 16) || !aligned(y, 16) || !aligned(user_ids, 4) ||
-        (signs_bank && !aligned(signs_bank, 16)))
-        return BD_ERR_INVALID_ARG;
-    hipError_t e = launch_apply(pl, x, w_base, signs_bank, scales_bank, user_ids, y,
-                                (char*)workspace, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    hipError_t e = launch_batch_prepare(pl.batch, x, user_ids, ws, s);
+    if (e != hipSuccess || T == 0) return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+    float* yacc = y_dtype == BD_F32 ? (float*)y : (float*)(ws + pl.off_yf);
+    e = launch_base_gemm(x, x_dtype, T, d_in, w_base, d_out, yacc, s);
+    if (e == hipSuccess)
+        e = launch_delta(pl.batch, pl.delta, ws, x, signs_bank, scales_bank, yacc, s);
+    if (e == hipSuccess && y_dtype == BD_BF16)
+        e = launch_cast_bf16(yacc, (uint16_t*)y, T * d_out, s);
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 

@@ -9,14 +9,14 @@
 //   k_group      one block: sorts (user, token) keys with a bitonic network in
 //                LDS, so tokens of a user are contiguous and in token order;
 //                emits work items of <= kItemTokens tokens of one user.
-//   k_prep_x     gathers X rows in that order into a workspace copy whose
-//                32-column blocks are permuted to the order in which the delta
-//                kernel unpacks bit pairs (COL scales are applied here).
 //   k_base_gemm  Y = X W_base^T with v_mfma_f32_16x16x32_bf16, fp32 out.
-//   k_delta      per (64-row tile, work item): streams the user's packed
-//                rows once, turns bits into +-1 bf16 MFMA operands in
-//                registers, accumulates X S^T in fp32 and adds scale * sum
-//                into Y.  Each Y element belongs to one item: no atomics.
+//   k_delta      per (64-row tile, work item): gathers the item's X rows into
+//                LDS with every 32-column block permuted to the order in which
+//                bit pairs are unpacked (COL scales applied there), streams the
+//                user's packed rows once, turns bits into +-1 bf16 MFMA
+//                operands in registers, accumulates X S^T in fp32 and adds
+//                scale * sum into Y.  Each Y element belongs to one item: no
+//                atomics.
 // fp32 inputs take plain VALU kernels (reference-grade, fp32 FMA).
 #include "bd_internal.h"
 
@@ -61,9 +61,9 @@ k_group(const int32_t* __restrict__ ids, int T, int U, int P, int32_t* __restric
         }
         keys[i] = k;
     }
-    if (badid) atomicOr(&meta[0], ST_USER_ID);
     if (tid == 0) nvalid_sh = T;
-    __syncthreads();
+    const int anybad = __syncthreads_or((int)badid);
+    if (tid == 0) meta[0] = anybad ? ST_USER_ID : 0u;  // the status word is owned by this kernel
     for (int k = 2; k <= P; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = tid; i < P; i += kGroupThreads) {
@@ -129,68 +129,102 @@ k_group(const int32_t* __restrict__ ids, int T, int U, int P, int32_t* __restric
     }
 }
 
-// ----------------------------------------------------------------- prep X
-// Xp[i][32c + 8q + 2j + h] = X[perm[i]][32c + 4q + j + 16h] (times the user's
-// column scale in COL mode), for the nv tokens that have a user.
-template <bool COL>
-__global__ void __launch_bounds__(256)
-k_prep_x(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-         const int4* __restrict__ items, const uint32_t* __restrict__ meta, int64_t T, int64_t d_in,
-         const void* __restrict__ scales, int sdtype, int64_t per_user, const int32_t* __restrict__ ids,
-         uint16_t* __restrict__ xp) {
-    const int64_t nv = meta[2];
-    const int64_t per_row = d_in / 8;  // 8 output elements per thread
-    const int64_t total = nv * per_row;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = idx / per_row, r = idx % per_row;
-        const int64_t blk = r / 4, q = r % 4;
-        const int64_t t = perm[i];
-        const uint16_t* src = x + t * d_in + blk * 32 + 4 * q;
-        const u32x2 a = *(const u32x2*)src;          // k = 4q .. 4q+3
-        const u32x2 b = *(const u32x2*)(src + 16);   // k = 4q+16 .. 4q+19
-        u32x4 o;
-        if (!COL) {
-            o.x = (a.x & 0xFFFFu) | (b.x << 16);
-            o.y = (a.x >> 16) | (b.x & 0xFFFF0000u);
-            o.z = (a.y & 0xFFFFu) | (b.y << 16);
-            o.w = (a.y >> 16) | (b.y & 0xFFFF0000u);
-        } else {
-            const int u = ids[t];
-            const int64_t k0 = blk * 32 + 4 * q;
-            float s[8];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int64_t s0 = (int64_t)u * per_user + k0 + jj, s1 = s0 + 16;
-                if (sdtype == BD_F16) {
-                    s[2 * jj] = f16_to_f32(((const uint16_t*)scales)[s0]);
-                    s[2 * jj + 1] = f16_to_f32(((const uint16_t*)scales)[s1]);
-                } else {
-                    s[2 * jj] = ((const float*)scales)[s0];
-                    s[2 * jj + 1] = ((const float*)scales)[s1];
-                }
-            }
-            const float xa[4] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y)};
-            const float xb[4] = {bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y)};
-            uint32_t w[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                w[jj] = (uint32_t)f32_to_bf16(xa[jj] * s[2 * jj]) |
-                        ((uint32_t)f32_to_bf16(xb[jj] * s[2 * jj + 1]) << 16);
-            o = u32x4{w[0], w[1], w[2], w[3]};
-        }
-        *(u32x4*)(xp + i * d_in + blk * 32 + 8 * q) = o;
+// Batches of at most 64 tokens: one wave, no barriers.  Lane l holds key l;
+// a 64-lane bitonic network of shuffles sorts them, ballots find the segment
+// starts and prefix counts place the items.  Same outputs as k_group.
+__global__ void __launch_bounds__(64)
+k_group_wave(const int32_t* __restrict__ ids, int T, int U, int32_t* __restrict__ perm,
+             int4* __restrict__ items, uint32_t* __restrict__ meta) {
+    const int l = threadIdx.x;
+    uint32_t key = 0xFFFFFFFFu;
+    bool bad = false;
+    if (l < T) {
+        const int u = ids[l];
+        const bool ok = u >= 0 && u < U;
+        bad = !ok && u != -1;
+        key = ((ok ? (uint32_t)u : (uint32_t)U) << 14) | (uint32_t)l;
     }
-    (void)items;
-    (void)T;
+    for (int k = 2; k <= 64; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t other = __shfl_xor(key, j);
+            const bool lower = (l & j) == 0;          // this lane keeps the smaller if ascending
+            const bool asc = (l & k) == 0;
+            const uint32_t mn = key < other ? key : other, mx = key < other ? other : key;
+            key = (lower == asc) ? mn : mx;
+        }
+    }
+    const uint32_t user = key >> 14;
+    const bool valid = user < (uint32_t)U;
+    const uint64_t vmask = __ballot(valid);
+    const int nv = __popcll(vmask);  // valid keys sort first
+    if (valid) perm[l] = (int32_t)(key & 0x3FFFu);
+    const uint32_t prev = __shfl_up(user, 1);
+    const bool start = valid && (l == 0 || prev != user);
+    const uint64_t smask = __ballot(start);
+    const uint64_t above = l == 63 ? 0ull : (smask >> (l + 1)) << (l + 1);
+    const int next = above ? __ffsll((unsigned long long)above) - 1 : nv;
+    const int len = start ? next - l : 0;
+    const int nit = (len + kItemTokens - 1) / kItemTokens;  // 0, 1 or 2
+    const uint64_t below = (1ull << l) - 1ull;
+    const int base = __popcll(__ballot(nit >= 1) & below) + __popcll(__ballot(nit >= 2) & below);
+    for (int q = 0; q < nit; ++q) {
+        const int b = l + q * kItemTokens;
+        items[base + q] = make_int4((int)user, b, min(kItemTokens, next - b), 0);
+    }
+    const int total = __popcll(__ballot(nit >= 1)) + __popcll(__ballot(nit >= 2));
+    const bool anybad = __ballot(bad) != 0ull;
+    if (l == 0) {
+        meta[0] = anybad ? ST_USER_ID : 0u;
+        meta[1] = (uint32_t)total;
+        meta[2] = (uint32_t)nv;
+    }
+}
+
+constexpr int kDeltaWaves = 4;           // 64 output rows per block
+constexpr int kChunk = 512;               // columns per bit-word load of a lane (non-GROUP)
+constexpr int kStageBytes = 40 * 1024;    // LDS for the staged activations of one item (4 blocks/CU)
+static_assert((kItemTokens + 1) * (kChunk / 8 + kChunk / 128 + 1) * 16 <= kStageBytes,
+              "a full item (plus its zero row) must fit one chunk-wide LDS stage");
+constexpr uint32_t kOOB = 0x80000000u;    // buffer offset past num_records: the load returns 0
+
+// Columns of one LDS stage for an item of n tokens: the largest multiple of 4
+// chunks whose n+1 padded rows fit kStageBytes, else of one chunk; capped at
+// d_in rounded up to a chunk.
+// A staged row of KC columns takes KC/8 16-byte units plus one pad unit per
+// 16 units (so the 4 lane groups, 256 bytes apart, start in different banks)
+// plus one (an odd pitch spreads consecutive rows over the banks).
+__device__ __forceinline__ int stage_pitch16(int64_t KC) { return (int)(KC / 8 + KC / 128 + 1); }
+__device__ __forceinline__ int stage_phys16(int c16) { return c16 + (c16 >> 4); }
+__device__ __forceinline__ int64_t stage_cols(int n, int64_t d_in) {
+    const int64_t dpad = (d_in + kChunk - 1) / kChunk * kChunk;
+    const int64_t fit16 = (int64_t)kStageBytes / 16 / (n + 1) - 1;  // units per row
+    const int64_t fit = fit16 * 128 / 17;                            // columns
+    int64_t kc = fit / (4 * kChunk) * (4 * kChunk);
+    if (kc == 0) kc = fit / kChunk * kChunk;
+    return kc < dpad ? kc : dpad;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+    const int nrec = bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
 // -------------------------------------------------------------- base GEMM
 // Block = 8 waves on one 16-row tile of W and NT 16-token tiles of X; wave w
 // takes the 32-wide K steps w, w+8, ... and the 8 partial tiles are summed in
-// LDS in wave order.
+// LDS in wave order.  Operands stream through a ring of 4 register slots, each
+// reloaded in place after its MFMAs, so 3 steps of loads stay in flight; loads
+// of absent tokens or steps past d_in are buffer loads out of range (zero).
 constexpr int kGemmWaves = 8;
-constexpr int kGemmUnroll = 4;
 
 template <int NT>
 __global__ void __launch_bounds__(64 * kGemmWaves)
@@ -201,34 +235,54 @@ k_base_gemm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, floa
     const int m = lane & 15, g = lane >> 4;
     const int64_t r0 = (int64_t)blockIdx.x * 16, t0 = (int64_t)blockIdx.y * 16 * NT;
     const int64_t rowA = r0 + m < d_out ? r0 + m : d_out - 1;
-    const uint16_t* wrow = w + rowA * d_in + 8 * g;
-    const uint16_t* xrow[NT];
-    bool tok_ok[NT];
+    // descriptors stay uniform (SGPRs); the lane's row lives in its 32-bit offset
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint64_t)d_out * d_in * 2);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)T * d_in * 2);
+    const uint32_t woff = (uint32_t)((rowA * d_in + 8 * g) * 2);
+    const int64_t nsteps = d_in / 32;
+    uint32_t xoff[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int64_t t = t0 + 16 * nt + m;
-        tok_ok[nt] = t < T;
-        xrow[nt] = x + (tok_ok[nt] ? t : 0) * d_in + 8 * g;
+        xoff[nt] = t < T ? (uint32_t)((t * d_in + 8 * g) * 2) : kOOB;
     }
+    struct Slot {
+        u32x4 a, b[NT];
+    };
+    auto load = [&](int64_t st) {
+        Slot sl;
+        const bool ok = st < nsteps;
+        sl.a = buf_load16(wr, ok ? woff + (uint32_t)(st * 64) : kOOB);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            sl.b[nt] = buf_load16(xr, (ok && xoff[nt] != kOOB) ? xoff[nt] + (uint32_t)(st * 64) : kOOB);
+        return sl;
+    };
     f32x4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int64_t nsteps = d_in / 32;
-    for (int64_t s = wv; s < nsteps; s += kGemmWaves * kGemmUnroll) {
-        u32x4 A[kGemmUnroll], B[kGemmUnroll][NT];
+    auto use = [&](const Slot& sl) {
 #pragma unroll
-        for (int u = 0; u < kGemmUnroll; ++u) {
-            const int64_t st = s + (int64_t)u * kGemmWaves;
-            const bool ok = st < nsteps;
-            A[u] = ok ? __builtin_nontemporal_load((const u32x4*)(wrow + st * 32)) : u32x4{0, 0, 0, 0};
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(sl.a, sl.b[nt], acc[nt]);
+    };
+    constexpr int W = kGemmWaves;
+    constexpr int R = NT <= 2 ? 8 : 4;  // ring depth: slots whose loads are in flight
+    Slot ring[R];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                B[u][nt] = (ok && tok_ok[nt]) ? *(const u32x4*)(xrow[nt] + st * 32) : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < R; ++r) {
+        ring[r] = load(wv + r * W);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // steps past d_in load zeros, so the MFMAs run unconditionally (straight-line
+    // code keeps the wait counters exact); scheduling barriers keep each slot's
+    // reload after its MFMAs
+    for (int64_t st = wv; st < nsteps; st += R * W) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            use(ring[r]);
+            ring[r] = load(st + (R + r) * W);
+            __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int u = 0; u < kGemmUnroll; ++u)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(A[u], B[u][nt], acc[nt]);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) red[wv][nt][lane] = acc[nt];
@@ -256,12 +310,12 @@ k_base_gemm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, floa
 // j of step q takes bits (4q + j) and (4q + j + 16) into the two bf16 sign
 // positions.  Bit 1 (+1) gives -1.0 and bit 0 gives +1.0, so the accumulator
 // holds -(X S^T); the epilogue multiplies by -scale.
-__device__ __forceinline__ u32x4 expand_pairs(uint32_t d, int q) {
+__device__ __forceinline__ u32x4 expand_pairs(uint32_t d, int q, uint32_t mask, uint32_t one) {
     u32x4 a;
-    a.x = ((d << (15 - 4 * q)) & 0x80008000u) | 0x3F803F80u;
-    a.y = ((d << (14 - 4 * q)) & 0x80008000u) | 0x3F803F80u;
-    a.z = ((d << (13 - 4 * q)) & 0x80008000u) | 0x3F803F80u;
-    a.w = ((d << (12 - 4 * q)) & 0x80008000u) | 0x3F803F80u;
+    a.x = ((d << (15 - 4 * q)) & mask) | one;
+    a.y = ((d << (14 - 4 * q)) & mask) | one;
+    a.z = ((d << (13 - 4 * q)) & mask) | one;
+    a.w = ((d << (12 - 4 * q)) & mask) | one;
     return a;
 }
 
@@ -269,106 +323,188 @@ __device__ __forceinline__ float load_scale(const void* s, int sdtype, int64_t i
     return sdtype == BD_F16 ? f16_to_f32(((const uint16_t*)s)[i]) : ((const float*)s)[i];
 }
 
-constexpr int kDeltaWaves = 4;  // 64 output rows per block
 
-template <int MODE>
-__global__ void __launch_bounds__(64 * kDeltaWaves)
-k_delta(const uint16_t* __restrict__ xp, const uint64_t* __restrict__ signs,
-        const void* __restrict__ scales, int sdtype, int64_t per_user, int group,
-        const int4* __restrict__ items, const uint32_t* __restrict__ meta,
-        const int32_t* __restrict__ perm, float* __restrict__ y, int64_t d_in, int64_t d_out) {
-    const int item = blockIdx.y;
-    if (item >= (int)meta[1]) return;
-    const int4 it = items[item];
-    const int u = it.x, b = it.y, n = it.z;
+// One block = 64 output rows (4 waves x 16) of one work item (one user, <= 32
+// of its tokens).  The item's reordered activations are staged in LDS, as many
+// columns per stage as fit (the whole row for decode-sized items), with one
+// all-zero row that lanes of absent tokens read.  Every lane streams its row's
+// packed bits through a ring of 4 register slots (16 bytes = 512 columns per
+// slot), each reloaded in place right after use, so 4 KB per wave stay in
+// flight from HBM while the MFMAs run.  Each 512-column chunk is 16 MFMA steps
+// per 16-token tile:
+//  non-GROUP: lane group g owns columns [128g, 128g+128) of the chunk;
+//  GROUP:     128-column block c of the chunk is one MFMA step set, lane group
+//             g takes its 32-column quarter g, so every step stays in one group.
+// NTL (token tiles) is a template parameter so accumulators stay in registers.
+template <int MODE, int NTL, bool BIG>
+__device__ __forceinline__ void delta_item(
+    const uint16_t* __restrict__ x, int64_t T, const uint64_t* __restrict__ signs,
+    const void* __restrict__ scales, int sdtype, int64_t per_user, int group, int u, int b, int n,
+    const int32_t* __restrict__ perm, float* __restrict__ y, int64_t d_in, int64_t d_out) {
+    extern __shared__ u32x4 xs_raw[];  // kStageBytes, dynamic
+    __shared__ int32_t tok[kItemTokens];
+    if (threadIdx.x < n) tok[threadIdx.x] = perm[b + threadIdx.x];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t r0 = (int64_t)blockIdx.x * (16 * kDeltaWaves) + 16 * wv;
-    if (r0 >= d_out) return;
-    const int64_t wpr32 = d_in / 32;
+    const bool wave_active = r0 < d_out;
     const int64_t rowA = r0 + m < d_out ? r0 + m : d_out - 1;
-    const uint32_t* bits = (const uint32_t*)(signs + (int64_t)u * d_out * (d_in / 64)) + rowA * wpr32;
+
+    // stage geometry (in 16-byte units): rows 0..n-1 hold tokens, row n is zero.
+    // BIG: KC is a multiple of 4 chunks (or covers d_in), so stages start only at
+    // ring-group boundaries.
+    const int64_t KC = stage_cols(n, d_in);
+    const int pitch16 = stage_pitch16(KC);  // 16-byte units per staged row (padded)
+    const int pieces_row = (int)(KC / 8);
+
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)T * d_in * 2);
+    const __amdgpu_buffer_rsrc_t br =
+        make_rsrc(signs + (int64_t)u * d_out * (d_in / 64), (uint64_t)d_out * (d_in / 8));
+    const uint32_t row_byte = (uint32_t)(rowA * (d_in / 8));
     const void* su = (const char*)scales + (size_t)u * per_user * (sdtype == BD_F16 ? 2 : 4);
-    const int ntl = (n + 15) >> 4;
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(su, (uint64_t)per_user * (sdtype == BD_F16 ? 2 : 4));
+    // operand constants kept in registers: gfx9 VOP3 encodings take no literals,
+    // so this lets the expansion use v_and_or_b32
+    uint32_t kmask, kone;
+    asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(kmask));
+    asm volatile("s_mov_b32 %0, 0x3f803f80" : "=s"(kone));
 
-    const uint16_t* xr[4];
-    bool tok_ok[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int slot = 16 * nt + m;
-        tok_ok[nt] = slot < n;
-        xr[nt] = xp + (int64_t)(b + (tok_ok[nt] ? slot : 0)) * d_in;
-    }
-    f32x4 acc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (MODE != BD_SCALE_GROUP) {
-        // super-step of 512 columns: lane group g owns columns [kb+128g, kb+128g+128)
-        for (int64_t kb = 0; kb < d_in; kb += 512) {
-            const int64_t kg = kb + 128 * g;
-            u32x4 D;
-            if (kg + 128 <= d_in) {
-                D = __builtin_nontemporal_load((const u32x4*)(bits + kg / 32));
-            } else {
-                D = u32x4{0, 0, 0, 0};
-                for (int c = 0; c < 4; ++c)
-                    if (kg + 32 * c < d_in) D[c] = bits[kg / 32 + c];
-            }
+    auto bload = [&](int64_t kb) {
+        u32x4 D;
+        if (MODE == BD_SCALE_GROUP) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int64_t k0 = kg + 32 * c;
-                const bool kok = k0 < d_in;
+                const int64_t col = kb + 128 * c + 32 * g;
+                D[c] = buf_load4(br, col < d_in ? row_byte + (uint32_t)(col / 8) : kOOB);
+            }
+        } else {
+            // columns past d_in in the last word read the next row's bits (or 0 past
+            // the bank): they meet zero activations, so they add nothing
+            const int64_t col = kb + 128 * g;
+            D = buf_load16(br, col < d_in ? row_byte + (uint32_t)(col / 8) : kOOB);
+        }
+        return D;
+    };
+    u32x4 D0 = bload(0), D1 = bload(kChunk), D2 = bload(2 * kChunk), D3 = bload(3 * kChunk);
+
+    for (int p = threadIdx.x; p < pieces_row; p += 64 * kDeltaWaves)
+        xs_raw[n * pitch16 + stage_phys16(p)] = u32x4{0, 0, 0, 0};
+
+    f32x4 acc[NTL], accp[NTL];
+    int xrow16[NTL];  // staged row of this lane's token, in 16-byte units
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const u32x4 A = expand_pairs(D[c], q);
+    for (int nt = 0; nt < NTL; ++nt) {
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accp[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int slot = 16 * nt + m;
+        xrow16[nt] = (slot < n ? slot : n) * pitch16;
+    }
+    const int64_t gpr = MODE == BD_SCALE_GROUP ? d_in / group : 1;
+    const int bpg = MODE == BD_SCALE_GROUP ? group / 128 : 1;
+
+    // Stage KC columns of the item's activations starting at column s0 (whole
+    // block).  Piece (row, c16) is LDS columns 8*c16 .. +7 of the stage, i.e.
+    // positions 8q..8q+7 of a 32-column block, which hold the natural columns
+    // 4q..4q+3 and 4q+16..4q+19 interleaved (the bit-pair order of expand_pairs).
+    auto stage = [&](int64_t s0) {
+        __syncthreads();  // readers of the previous stage are done (and tok[] is set)
+        const int total = n * pieces_row;
+        for (int p0 = threadIdx.x; p0 < total; p0 += 2 * 64 * kDeltaWaves) {
+            u32x2 va[2], vb[2];
+            int64_t kcol[2];
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) {
-                        if (nt < ntl) {
-                            const u32x4 B = (kok && tok_ok[nt])
-                                                ? *(const u32x4*)(xr[nt] + k0 + 8 * q)
-                                                : u32x4{0, 0, 0, 0};
-                            acc[nt] = mfma_bf16(A, B, acc[nt]);
+            for (int j = 0; j < 2; ++j) {
+                const int p = p0 + j * 64 * kDeltaWaves;
+                const int row = p < total ? p / pieces_row : 0, c16 = p - row * pieces_row;
+                const int64_t k0 = s0 + 32 * (c16 >> 2) + 4 * (c16 & 3);
+                kcol[j] = k0;
+                const bool ok = p < total && k0 < d_in;
+                const uint32_t off = ok ? (uint32_t)((tok[row] * d_in + k0) * 2) : kOOB;
+                va[j] = buf_load8(xr, off);
+                vb[j] = buf_load8(xr, ok ? off + 32 : kOOB);
+            }
+            // every load is consumed (pieces past the item store their zeros into the
+            // zero row), so no load stays pending on a register the loop reuses
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int p = p0 + j * 64 * kDeltaWaves;
+                const int row = p < total ? p / pieces_row : 0, c16 = p - row * pieces_row;
+                u32x4 o;
+                if (MODE == BD_SCALE_COL) {
+                    // column scales of this user: natural columns k0..k0+3, k0+16..k0+19
+                    const int64_t k0 = kcol[j] < d_in ? kcol[j] : 0;
+                    float sa[4], sb[4];
+                    if (sdtype == BD_F16) {
+                        const u32x2 ha = buf_load8(sr, (uint32_t)(k0 * 2));
+                        const u32x2 hb = buf_load8(sr, (uint32_t)((k0 + 16) * 2));
+                        sa[0] = f16_to_f32((uint16_t)ha.x); sa[1] = f16_to_f32((uint16_t)(ha.x >> 16));
+                        sa[2] = f16_to_f32((uint16_t)ha.y); sa[3] = f16_to_f32((uint16_t)(ha.y >> 16));
+                        sb[0] = f16_to_f32((uint16_t)hb.x); sb[1] = f16_to_f32((uint16_t)(hb.x >> 16));
+                        sb[2] = f16_to_f32((uint16_t)hb.y); sb[3] = f16_to_f32((uint16_t)(hb.y >> 16));
+                    } else {
+                        const u32x4 fa = buf_load16(sr, (uint32_t)(k0 * 4));
+                        const u32x4 fb = buf_load16(sr, (uint32_t)((k0 + 16) * 4));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            sa[e] = __uint_as_float(fa[e]);
+                            sb[e] = __uint_as_float(fb[e]);
                         }
                     }
+                    const float xa[4] = {bf16_lo(va[j].x), bf16_hi(va[j].x), bf16_lo(va[j].y), bf16_hi(va[j].y)};
+                    const float xb[4] = {bf16_lo(vb[j].x), bf16_hi(vb[j].x), bf16_lo(vb[j].y), bf16_hi(vb[j].y)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = (uint32_t)f32_to_bf16(xa[e] * sa[e]) | ((uint32_t)f32_to_bf16(xb[e] * sb[e]) << 16);
+                } else {
+                    o.x = (va[j].x & 0xFFFFu) | (vb[j].x << 16);
+                    o.y = (va[j].x >> 16) | (vb[j].x & 0xFFFF0000u);
+                    o.z = (va[j].y & 0xFFFFu) | (vb[j].y << 16);
+                    o.w = (va[j].y >> 16) | (vb[j].y & 0xFFFF0000u);
                 }
+                xs_raw[p < total ? row * pitch16 + stage_phys16(c16)
+                                 : n * pitch16 + stage_phys16(p % pieces_row)] =
+                    p < total ? o : u32x4{0, 0, 0, 0};
             }
         }
-    } else {
-        // GROUP (group = 128 * 2^a): every MFMA step stays inside one 128-column
-        // block; partial sums are scaled when a group is complete.
-        f32x4 accp[4];
+        __syncthreads();
+    };
+    // One 512-column chunk: 16 MFMA steps per token tile with the bit words D.
+    auto chunk = [&](int64_t kb, const u32x4 D) {
+        if (!BIG && kb % KC == 0) stage(kb);  // uniform over the block
+        if (!wave_active) return;
+        const int lc16 = (int)((kb % KC) / 8);  // chunk start inside the stage, 16-byte units
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) accp[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int64_t gpr = d_in / group;
-        const int blocks_per_group = group / 128;
-        const int64_t nblk = d_in / 128;
-        for (int64_t G = 0; G < nblk; ++G) {
-            const uint32_t dw = bits[G * 4 + g];
-            const int64_t k0 = G * 128 + 32 * g;
+        for (int c = 0; c < 4; ++c) {
+            // 16-byte unit of this MFMA step set (4 consecutive units, one per q); the
+            // 4 units never cross a 16-unit boundary, so one pad offset serves them
+            const int col16 = stage_phys16(lc16 + (MODE == BD_SCALE_GROUP ? 16 * c + 4 * g : 16 * g + 4 * c));
+            u32x4 A[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 A = expand_pairs(dw, q);
+            for (int q = 0; q < 4; ++q) A[q] = expand_pairs(D[c], q, kmask, kone);
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    if (nt < ntl) {
-                        const u32x4 B = tok_ok[nt] ? *(const u32x4*)(xr[nt] + k0 + 8 * q) : u32x4{0, 0, 0, 0};
-                        accp[nt] = mfma_bf16(A, B, accp[nt]);
-                    }
+            for (int nt = 0; nt < NTL; ++nt) {
+                u32x4 Bv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Bv[q] = xs_raw[xrow16[nt] + col16 + q];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (MODE == BD_SCALE_GROUP) accp[nt] = mfma_bf16(A[q], Bv[q], accp[nt]);
+                    else acc[nt] = mfma_bf16(A[q], Bv[q], acc[nt]);
                 }
             }
-            if ((G + 1) % blocks_per_group == 0) {
-                const int64_t gi = G / blocks_per_group;
-                float sc[4];
+            if (MODE == BD_SCALE_GROUP) {
+                const int64_t G = kb / 128 + c;  // global 128-column block
+                if (G * 128 < d_in && (G + 1) % bpg == 0) {
+                    const int64_t gi = G / bpg;
+                    float sc[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    int64_t o = r0 + 4 * g + e;
-                    o = o < d_out ? o : d_out - 1;
-                    sc[e] = -load_scale(su, sdtype, o * gpr + gi);
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        int64_t o = r0 + 4 * g + e;
+                        o = o < d_out ? o : d_out - 1;
+                        sc[e] = -load_scale(su, sdtype, o * gpr + gi);
+                    }
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    if (nt < ntl) {
+                    for (int nt = 0; nt < NTL; ++nt) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) acc[nt][e] += accp[nt][e] * sc[e];
                         accp[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -376,9 +512,21 @@ k_delta(const uint16_t* __restrict__ xp, const uint64_t* __restrict__ signs,
                 }
             }
         }
+    };
+    for (int64_t kb = 0; kb < d_in; kb += 4 * kChunk) {
+        if (BIG && kb % KC == 0) stage(kb);
+        chunk(kb, D0);
+        D0 = bload(kb + 4 * kChunk);
+        if (kb + kChunk < d_in) chunk(kb + kChunk, D1);
+        D1 = bload(kb + 5 * kChunk);
+        if (kb + 2 * kChunk < d_in) chunk(kb + 2 * kChunk, D2);
+        D2 = bload(kb + 6 * kChunk);
+        if (kb + 3 * kChunk < d_in) chunk(kb + 3 * kChunk, D3);
+        D3 = bload(kb + 7 * kChunk);
     }
+    if (!wave_active) return;
 
-    // epilogue: Y[t][o] += factor * acc
+    // epilogue: Y[t][o] += factor * acc (one 16-byte read-modify-write per lane and tile)
     float f[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -390,8 +538,7 @@ k_delta(const uint16_t* __restrict__ xp, const uint64_t* __restrict__ signs,
         else f[e] = 1.0f;
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        if (nt >= ntl) break;
+    for (int nt = 0; nt < NTL; ++nt) {
         const int slot = 16 * nt + m;
         if (slot >= n) continue;
         const int64_t t = perm[b + slot];
@@ -407,6 +554,29 @@ k_delta(const uint16_t* __restrict__ xp, const uint64_t* __restrict__ signs,
                 if (o + e < d_out) dst[e] += acc[nt][e] * f[e];
         }
     }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(64 * kDeltaWaves)
+k_delta(const uint16_t* __restrict__ x, int64_t T, const uint64_t* __restrict__ signs,
+        const void* __restrict__ scales, int sdtype, int64_t per_user, int group,
+        const int4* __restrict__ items, const uint32_t* __restrict__ meta,
+        const int32_t* __restrict__ perm, float* __restrict__ y, int64_t d_in, int64_t d_out) {
+    const int item = blockIdx.y;
+    if (item >= (int)meta[1]) return;  // uniform over the block
+    const int4 it = items[item];
+    const bool big = stage_cols(it.z, d_in) % (4 * kChunk) == 0 || stage_cols(it.z, d_in) >= d_in;
+#define BD_ITEM(NTL, BIG)                                                                          \
+    delta_item<MODE, NTL, BIG>(x, T, signs, scales, sdtype, per_user, group, it.x, it.y, it.z, perm, \
+                               y, d_in, d_out)
+    if (it.z <= 16) {
+        if (big) BD_ITEM(1, true);
+        else BD_ITEM(1, false);
+    } else {
+        if (big) BD_ITEM(2, true);
+        else BD_ITEM(2, false);
+    }
+#undef BD_ITEM
 }
 
 __global__ void __launch_bounds__(256) k_cast_bf16(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
@@ -482,17 +652,12 @@ int pow2_at_least(int64_t n) {
 
 }  // namespace
 
-bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int64_t d_out,
-                          int64_t d_in, int xdtype, int ydtype, ApplyPlan* pl) {
-    if (!p || !pl) return BD_ERR_INVALID_ARG;
+bd_status check_params(const bd_compress_params* p, int64_t d_out, int64_t d_in, int xdtype) {
+    if (!p) return BD_ERR_INVALID_ARG;
     if (p->bits != 1) return BD_ERR_UNSUPPORTED;
     if (p->mode < BD_SCALE_MATRIX || p->mode > BD_SCALE_COL) return BD_ERR_INVALID_ARG;
     if (p->scale_dtype != BD_F32 && p->scale_dtype != BD_F16) return BD_ERR_DTYPE;
-    if (xdtype != BD_BF16 && xdtype != BD_F32) return BD_ERR_DTYPE;
-    if (ydtype != BD_F32 && ydtype != BD_BF16) return BD_ERR_DTYPE;
-    if (T < 0 || U < 0 || U > kMaxUsers) return BD_ERR_INVALID_ARG;
-    if (d_out <= 0 || d_in <= 0 || d_in % 64 != 0) return BD_ERR_SHAPE;
-    if (d_out > (int64_t)1 << 31 || d_in > (int64_t)1 << 31) return BD_ERR_SHAPE;
+    if (d_out <= 0 || d_out > (int64_t)1 << 31) return BD_ERR_SHAPE;
     if (p->mode == BD_SCALE_GROUP) {
         const int g = p->group_size;
         if (g < 8 || g > kSegCols || (g & (g - 1)) != 0) return BD_ERR_UNSUPPORTED;
@@ -500,28 +665,70 @@ bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int
         // the MFMA path keeps each step inside one 128-column block
         if (xdtype == BD_BF16 && g < 128) return BD_ERR_UNSUPPORTED;
     }
+    return BD_OK;
+}
+
+bd_status make_batch_plan(int64_t T, int32_t U, int64_t d_in, int xdtype, BatchPlan* pl) {
+    if (!pl) return BD_ERR_INVALID_ARG;
+    if (xdtype != BD_BF16 && xdtype != BD_F32) return BD_ERR_DTYPE;
+    if (T < 0 || U < 0 || U > kMaxUsers) return BD_ERR_INVALID_ARG;
+    if (d_in <= 0 || d_in % 64 != 0 || d_in > (int64_t)1 << 31) return BD_ERR_SHAPE;
     if (xdtype == BD_BF16 && T > kMaxGroupT) return BD_ERR_UNSUPPORTED;
-    ApplyPlan q;
+    // the delta kernel addresses X with 32-bit buffer offsets
+    if (T * d_in * 2 >= ((int64_t)1 << 31)) return BD_ERR_UNSUPPORTED;
+    BatchPlan q;
     q.T = T;
     q.U = U;
     q.d_in = d_in;
+    q.xdtype = xdtype;
+    const int64_t act = T < U ? T : U;
+    q.max_items = act + T / kItemTokens + 1;
+    const size_t Tn = (size_t)(T > 0 ? T : 1);
+    size_t off = 0;
+    q.off_meta = off;
+    off += kAlign;
+    q.off_perm = off;
+    off += align_up(sizeof(int32_t) * Tn);
+    q.off_user = off;
+    off += align_up(sizeof(int32_t) * Tn);
+    q.off_items = off;
+    off += align_up(sizeof(int4) * (size_t)q.max_items);
+    q.total = off;
+    *pl = q;
+    return BD_OK;
+}
+
+bd_status make_delta_plan(const bd_compress_params* p, const BatchPlan& b, int64_t d_out,
+                          DeltaPlan* pl) {
+    bd_status st = check_params(p, d_out, b.d_in, b.xdtype);
+    if (st != BD_OK) return st;
+    // the kernels address one user's bits and the base weight with 32-bit buffer offsets
+    if (d_out * (b.d_in / 8) >= ((int64_t)1 << 31)) return BD_ERR_UNSUPPORTED;
+    if (b.xdtype == BD_BF16 && d_out * b.d_in * 2 >= ((int64_t)1 << 31)) return BD_ERR_UNSUPPORTED;
+    DeltaPlan q;
     q.d_out = d_out;
     q.mode = p->mode;
     q.group = p->mode == BD_SCALE_GROUP ? p->group_size : 0;
     q.sdtype = p->scale_dtype;
-    q.xdtype = xdtype;
+    q.per_user = q.mode == BD_SCALE_MATRIX ? 1
+                 : q.mode == BD_SCALE_GROUP ? d_out * (b.d_in / q.group)
+                 : q.mode == BD_SCALE_ROW ? d_out
+                                          : b.d_in;
+    *pl = q;
+    return BD_OK;
+}
+
+bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int64_t d_out,
+                          int64_t d_in, int xdtype, int ydtype, ApplyPlan* pl) {
+    if (!p || !pl) return BD_ERR_INVALID_ARG;
+    if (ydtype != BD_F32 && ydtype != BD_BF16) return BD_ERR_DTYPE;
+    ApplyPlan q;
+    bd_status st = make_batch_plan(T, U, d_in, xdtype, &q.batch);
+    if (st != BD_OK) return st;
+    st = make_delta_plan(p, q.batch, d_out, &q.delta);
+    if (st != BD_OK) return st;
     q.ydtype = ydtype;
-    const int64_t act = T < U ? T : U;
-    q.max_items = act + T / kItemTokens + 1;
-    size_t off = 0;
-    q.off_status = off;
-    off += kAlign;
-    q.off_perm = off;
-    off += align_up(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
-    q.off_items = off;
-    off += align_up(sizeof(int4) * (size_t)q.max_items);
-    q.off_xp = off;
-    if (xdtype == BD_BF16) off += align_up(2 * (size_t)T * (size_t)d_in);
+    size_t off = q.batch.total;
     q.off_yf = off;
     if (ydtype == BD_BF16) off += align_up(4 * (size_t)T * (size_t)d_out);
     q.total = off;
@@ -529,70 +736,88 @@ bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int
     return BD_OK;
 }
 
-hipError_t launch_apply(const ApplyPlan& pl, const void* x, const void* wb, const uint64_t* signs,
-                        const void* scales, const int32_t* ids, void* y, char* ws, hipStream_t s) {
-    uint32_t* meta = (uint32_t*)(ws + pl.off_status);
-    hipError_t err = launch_zero_u32(meta, (int64_t)(kAlign / 4), s);
+hipError_t launch_batch_prepare(const BatchPlan& pl, const void* x, const int32_t* ids,
+                                char* batch, hipStream_t s) {
+    (void)x;
+    uint32_t* meta = (uint32_t*)(batch + pl.off_meta);
+    hipError_t err = hipSuccess;
+    if (pl.T == 0 || pl.xdtype == BD_F32) err = launch_zero_u32(meta, (int64_t)(kAlign / 4), s);
     if (err != hipSuccess || pl.T == 0) return err;
-    const int64_t per_user =
-        pl.mode == BD_SCALE_MATRIX ? 1
-        : pl.mode == BD_SCALE_GROUP ? pl.d_out * (pl.d_in / pl.group)
-        : pl.mode == BD_SCALE_ROW ? pl.d_out
-                                  : pl.d_in;
-    float* yacc = pl.ydtype == BD_F32 ? (float*)y : (float*)(ws + pl.off_yf);
-    const int64_t n_out = pl.T * pl.d_out;
-
-    if (pl.xdtype == BD_F32) {
+    if (pl.xdtype == BD_F32) {  // fp32 path: no grouping, the delta kernel reads the ids
         hipLaunchKernelGGL(k_check_ids, dim3(grid_1d(pl.T, 256, 1024)), dim3(256), 0, s, ids, pl.T,
                            pl.U, meta);
-        hipLaunchKernelGGL(k_base_f32, dim3(grid_1d(n_out, 256, 1ll << 30)), dim3(256), 0, s,
-                           (const float*)x, (const float*)wb, yacc, pl.T, pl.d_in, pl.d_out);
-        hipLaunchKernelGGL(k_delta_f32, dim3(grid_1d(n_out, 256, 1ll << 30)), dim3(256), 0, s,
-                           (const float*)x, ids, pl.U, signs, scales, pl.sdtype, per_user, pl.mode,
-                           pl.group, yacc, pl.T, pl.d_in, pl.d_out);
-    } else {
-        int32_t* perm = (int32_t*)(ws + pl.off_perm);
-        int4* items = (int4*)(ws + pl.off_items);
-        uint16_t* xp = (uint16_t*)(ws + pl.off_xp);
-        const int P = pow2_at_least(pl.T);
-        hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), sizeof(uint32_t) * P, s, ids,
-                           (int)pl.T, pl.U, P, perm, items, meta);
-        const unsigned gp = grid_1d(pl.T * (pl.d_in / 8), 256, 8192);
-        if (pl.mode == BD_SCALE_COL)
-            hipLaunchKernelGGL(k_prep_x<true>, dim3(gp), dim3(256), 0, s, (const uint16_t*)x, perm,
-                               items, meta, pl.T, pl.d_in, scales, pl.sdtype, per_user, ids, xp);
-        else
-            hipLaunchKernelGGL(k_prep_x<false>, dim3(gp), dim3(256), 0, s, (const uint16_t*)x, perm,
-                               items, meta, pl.T, pl.d_in, scales, pl.sdtype, per_user, ids, xp);
-        // base GEMM: tokens in tiles of 16 * NT
-        const dim3 gb((unsigned)((pl.d_out + 15) / 16), 1);
-        if (pl.T <= 16) {
-            hipLaunchKernelGGL(k_base_gemm<1>, gb, dim3(64 * kGemmWaves), 0, s, (const uint16_t*)x,
-                               (const uint16_t*)wb, yacc, pl.T, pl.d_in, pl.d_out);
-        } else if (pl.T <= 32) {
-            hipLaunchKernelGGL(k_base_gemm<2>, gb, dim3(64 * kGemmWaves), 0, s, (const uint16_t*)x,
-                               (const uint16_t*)wb, yacc, pl.T, pl.d_in, pl.d_out);
-        } else {
-            const dim3 g4((unsigned)((pl.d_out + 15) / 16), (unsigned)((pl.T + 63) / 64));
-            hipLaunchKernelGGL(k_base_gemm<4>, g4, dim3(64 * kGemmWaves), 0, s, (const uint16_t*)x,
-                               (const uint16_t*)wb, yacc, pl.T, pl.d_in, pl.d_out);
-        }
-        const dim3 gd((unsigned)((pl.d_out + 16 * kDeltaWaves - 1) / (16 * kDeltaWaves)),
-                      (unsigned)pl.max_items);
-#define BD_DELTA(MODE)                                                                              \
-    hipLaunchKernelGGL(k_delta<MODE>, gd, dim3(64 * kDeltaWaves), 0, s, xp, signs, scales,         \
-                       pl.sdtype, per_user, pl.group, items, meta, perm, yacc, pl.d_in, pl.d_out)
-        switch (pl.mode) {
-            case BD_SCALE_MATRIX: BD_DELTA(BD_SCALE_MATRIX); break;
-            case BD_SCALE_GROUP: BD_DELTA(BD_SCALE_GROUP); break;
-            case BD_SCALE_ROW: BD_DELTA(BD_SCALE_ROW); break;
-            default: BD_DELTA(BD_SCALE_COL); break;
-        }
-#undef BD_DELTA
+        err = hipMemcpyAsync(batch + pl.off_user, ids, sizeof(int32_t) * pl.T,
+                             hipMemcpyDeviceToDevice, s);
+        return err != hipSuccess ? err : hipGetLastError();
     }
-    if (pl.ydtype == BD_BF16)
-        hipLaunchKernelGGL(k_cast_bf16, dim3(grid_1d(n_out, 256, 16384)), dim3(256), 0, s, yacc,
-                           (uint16_t*)y, n_out);
+    if (pl.T <= 64) {
+        hipLaunchKernelGGL(k_group_wave, dim3(1), dim3(64), 0, s, ids, (int)pl.T, pl.U,
+                           (int32_t*)(batch + pl.off_perm), (int4*)(batch + pl.off_items), meta);
+        return hipGetLastError();
+    }
+    const int P = pow2_at_least(pl.T);
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), sizeof(uint32_t) * P, s, ids,
+                       (int)pl.T, pl.U, P, (int32_t*)(batch + pl.off_perm),
+                       (int4*)(batch + pl.off_items), meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_base_gemm(const void* x, int xdtype, int64_t T, int64_t d_in, const void* wb,
+                            int64_t d_out, float* y, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (xdtype == BD_F32) {
+        hipLaunchKernelGGL(k_base_f32, dim3(grid_1d(T * d_out, 256, 1ll << 30)), dim3(256), 0, s,
+                           (const float*)x, (const float*)wb, y, T, d_in, d_out);
+        return hipGetLastError();
+    }
+    const dim3 gb((unsigned)((d_out + 15) / 16), 1);
+    if (T <= 16) {
+        hipLaunchKernelGGL(k_base_gemm<1>, gb, dim3(64 * kGemmWaves), 0, s, (const uint16_t*)x,
+                           (const uint16_t*)wb, y, T, d_in, d_out);
+    } else if (T <= 32) {
+        hipLaunchKernelGGL(k_base_gemm<2>, gb, dim3(64 * kGemmWaves), 0, s, (const uint16_t*)x,
+                           (const uint16_t*)wb, y, T, d_in, d_out);
+    } else {
+        const dim3 g4((unsigned)((d_out + 15) / 16), (unsigned)((T + 63) / 64));
+        hipLaunchKernelGGL(k_base_gemm<4>, g4, dim3(64 * kGemmWaves), 0, s, (const uint16_t*)x,
+                           (const uint16_t*)wb, y, T, d_in, d_out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, const char* batch,
+                        const void* x, const uint64_t* signs, const void* scales, float* y,
+                        hipStream_t s) {
+    if (bp.T == 0) return hipSuccess;
+    const uint32_t* meta = (const uint32_t*)(batch + bp.off_meta);
+    const int32_t* perm = (const int32_t*)(batch + bp.off_perm);
+    const int32_t* row_user = (const int32_t*)(batch + bp.off_user);
+    const int4* items = (const int4*)(batch + bp.off_items);
+    if (bp.xdtype == BD_F32) {
+        hipLaunchKernelGGL(k_delta_f32, dim3(grid_1d(bp.T * dp.d_out, 256, 1ll << 30)), dim3(256), 0,
+                           s, (const float*)x, row_user, bp.U, signs, scales, dp.sdtype, dp.per_user,
+                           dp.mode, dp.group, y, bp.T, bp.d_in, dp.d_out);
+        return hipGetLastError();
+    }
+    const dim3 gd((unsigned)((dp.d_out + 16 * kDeltaWaves - 1) / (16 * kDeltaWaves)),
+                  (unsigned)bp.max_items);
+#define BD_DELTA(MODE)                                                                              \
+    hipLaunchKernelGGL(k_delta<MODE>, gd, dim3(64 * kDeltaWaves), kStageBytes, s,                  \
+                       (const uint16_t*)x, bp.T, signs, scales, dp.sdtype, dp.per_user, dp.group,  \
+                       items, meta, perm, y, bp.d_in, dp.d_out)
+    switch (dp.mode) {
+        case BD_SCALE_MATRIX: BD_DELTA(BD_SCALE_MATRIX); break;
+        case BD_SCALE_GROUP: BD_DELTA(BD_SCALE_GROUP); break;
+        case BD_SCALE_ROW: BD_DELTA(BD_SCALE_ROW); break;
+        default: BD_DELTA(BD_SCALE_COL); break;
+    }
+#undef BD_DELTA
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_cast_bf16, dim3(grid_1d(n, 256, 16384)), dim3(256), 0, s, src, dst, n);
     return hipGetLastError();
 }
 

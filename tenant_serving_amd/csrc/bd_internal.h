@@ -44,24 +44,48 @@ hipError_t launch_compress(const CompressPlan& pl, const void* wf, const void* w
                            uint64_t* signs, void* scales, char* ws, hipStream_t s);
 
 // ------------------------------------------------------------------- apply
-constexpr int kItemTokens = 64;   // max tokens of one (user, chunk) work item
+constexpr int kItemTokens = 32;   // max tokens of one (user, chunk) work item (<= 2 MFMA tiles)
 constexpr int kMaxGroupT = 8192;  // tokens the one-block grouping kernel sorts in LDS
 constexpr int kMaxUsers = (1 << 17) - 1;
 
-struct ApplyPlan {
-    int64_t T = 0, d_in = 0, d_out = 0;
+// Prepared batch (bd_batch_prepare): tokens grouped by user into work items.
+struct BatchPlan {
+    int64_t T = 0, d_in = 0;
     int32_t U = 0;
-    int mode = 0, group = 0, sdtype = 0;
-    int xdtype = 0, ydtype = 0;
+    int xdtype = 0;
     int64_t max_items = 0;
-    size_t off_status = 0, off_perm = 0, off_items = 0, off_xp = 0, off_yf = 0;
+    size_t off_meta = 0, off_perm = 0, off_user = 0, off_items = 0;
     size_t total = 0;
 };
 
+// One matrix's delta application on a prepared batch.
+struct DeltaPlan {
+    int64_t d_out = 0, per_user = 0;
+    int mode = 0, group = 0, sdtype = 0;
+};
+
+// bd_apply workspace = batch | fp32 Y (bf16 output only).
+struct ApplyPlan {
+    BatchPlan batch;
+    DeltaPlan delta;
+    int ydtype = 0;
+    size_t off_yf = 0, total = 0;
+};
+
+bd_status check_params(const bd_compress_params* p, int64_t d_out, int64_t d_in, int xdtype);
+bd_status make_batch_plan(int64_t T, int32_t U, int64_t d_in, int xdtype, BatchPlan* plan);
+bd_status make_delta_plan(const bd_compress_params* p, const BatchPlan& b, int64_t d_out,
+                          DeltaPlan* plan);
 bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int64_t d_out,
                           int64_t d_in, int xdtype, int ydtype, ApplyPlan* plan);
-hipError_t launch_apply(const ApplyPlan& pl, const void* x, const void* wb, const uint64_t* signs,
-                        const void* scales, const int32_t* ids, void* y, char* ws, hipStream_t s);
+hipError_t launch_batch_prepare(const BatchPlan& pl, const void* x, const int32_t* ids,
+                                char* batch, hipStream_t s);
+hipError_t launch_base_gemm(const void* x, int xdtype, int64_t T, int64_t d_in, const void* wb,
+                            int64_t d_out, float* y, hipStream_t s);
+hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, const char* batch,
+                        const void* x, const uint64_t* signs, const void* scales, float* y,
+                        hipStream_t s);
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 
 hipError_t launch_reconstruct(const uint64_t* signs, const void* scales, int mode, int group,
                               int sdtype, int64_t d_out, int64_t d_in, const void* wb, int wdtype,

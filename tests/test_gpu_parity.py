@@ -162,6 +162,53 @@ def test_apply_parity(case):
     assert np.all(y0.cpu().numpy()[ids < 0] == 0)
 
 
+@pytest.mark.parametrize("mode", ["matrix", "group"])
+def test_apply_parity_large_batch(mode):
+    # T * d_in above the single-block reorder threshold: separate prep kernel,
+    # users with 0, 1, 31, 32, 33 and 150 tokens (item splits at 32)
+    ids = _ids_mixed(T_users=(150, 0, 1, 31, 32, 33, 5), extra_none=7, seed=11)
+    T, U = len(ids), 7
+    d_out, d_in = 136, 1024
+    w = custom(d_out, d_in, S.BF16, n_users=U, T=T, b=5e-3, cid=1350)
+    p = B.params(mode, 128)
+    wb_dev = S.dev_wbase(w, 0)
+    x_dev = S.dev_x(w, 0)
+    signs, scales = gpu_bank(w, 0, wb_dev, p, range(U))
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    y = B.apply(x_dev, wb_dev, signs, scales, p, ids_dev, check=True)
+    wb = S.host_wbase(w, 0)
+    words, osc = oracle_bank(w, 0, wb, p, range(U))
+    yr, yb, yd = O.apply(S.host_x(w, 0), wb, words, osc, p.mode, ids, g=128)
+    err, rms = max_err_vs_rms(y.cpu().numpy(), yr)
+    assert err <= TOL_BF16 * rms, (err, rms)
+    y0 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
+    err0, rms0 = max_err_vs_rms(y0.cpu().numpy(), yd)
+    assert err0 <= TOL_BF16 * rms0, (err0, rms0)
+
+
+@pytest.mark.parametrize("mode", ["matrix", "col"])
+def test_apply_parity_single_wave_grouping(mode):
+    # T <= 64 takes the one-wave grouping kernel; a 40-token user spans two items
+    ids = _ids_mixed(T_users=(40, 15, 0, 5), extra_none=3, seed=13)
+    T, U = len(ids), 4
+    d_out, d_in = 100, 1536
+    w = custom(d_out, d_in, S.BF16, n_users=U, T=T, b=5e-3, cid=1360)
+    p = B.params(mode, 128, 0.0, B.BD_F16 if mode == "col" else B.BD_F32)
+    wb_dev = S.dev_wbase(w, 0)
+    x_dev = S.dev_x(w, 0)
+    signs, scales = gpu_bank(w, 0, wb_dev, p, range(U))
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    y = B.apply(x_dev, wb_dev, signs, scales, p, ids_dev, check=True)
+    wb = S.host_wbase(w, 0)
+    words, osc = oracle_bank(w, 0, wb, p, range(U))
+    yr, yb, yd = O.apply(S.host_x(w, 0), wb, words, osc, p.mode, ids, g=128, sdtype=o_sdtype(p))
+    err, rms = max_err_vs_rms(y.cpu().numpy(), yr)
+    assert err <= TOL_BF16 * rms, (err, rms)
+    y0 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
+    err0, rms0 = max_err_vs_rms(y0.cpu().numpy(), yd)
+    assert err0 <= TOL_BF16 * rms0, (err0, rms0)
+
+
 def test_apply_out_of_range_user_gets_base_and_status():
     w = custom(64, 512, S.BF16, n_users=2, T=4, cid=1400)
     p = B.params("matrix")
