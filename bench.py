@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="output rows of the oracle's sampled apply")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the run, copy this many MiB device-to-device 3 times (a plain "
+                         "copy kernel of known size, to calibrate HBM byte counters)")
     return ap.parse_args()
 
 
@@ -206,6 +209,16 @@ def main():
         "compress": compress,
         "kernel_source_digest": kernel_source_digest(),
     }
+
+    if args.calib_copy_mib > 0:
+        nb = args.calib_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = nb
 
     # --------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
