@@ -168,8 +168,10 @@ bd_status bd_reconstruct(const uint64_t* signs, const void* scales, const bd_com
  *  workspace   : >= bd_apply_workspace_bytes(...) bytes, 256-byte aligned.
  * Accumulation is fp32.  T == 0 is a no-op.  bf16 inputs: T <= 8192 tokens
  * per call and GROUP group_size >= 128 (BD_ERR_UNSUPPORTED otherwise).
- * Equivalent to bd_batch_prepare + bd_base_gemm + bd_delta_apply (+ a cast
- * for bf16 y) on one workspace. */
+ * bf16 batches of 1..16 tokens with MATRIX, ROW or COL scales take a one-pass
+ * path, equivalent to bd_decode_prepare + bd_decode_apply on the workspace;
+ * every other batch is equivalent to bd_batch_prepare + bd_base_gemm +
+ * bd_delta_apply (+ a cast for bf16 y) on one workspace. */
 bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const void* w_base,
                    int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
                    const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
@@ -207,6 +209,34 @@ bd_status bd_delta_apply(const void* batch, const void* x, bd_dtype x_dtype, int
                          int64_t d_in, int32_t n_users, int64_t d_out, const uint64_t* signs_bank,
                          const void* scales_bank, const bd_compress_params* p, float* y,
                          void* stream);
+
+/* The two launches of bd_apply's one-pass path for decode batches: bf16 x and
+ * w_base, 1 <= T <= 16, MATRIX, ROW or COL scales (BD_ERR_UNSUPPORTED for any
+ * other batch).  Same formula as bd_apply ([P2] "Systems Mechanics" 1-2).
+ *
+ * bd_decode_prepare sorts the tokens by user and encodes x for the delta
+ * products (per 32-column block a power-of-two scale and two fp8 e4m3 parts,
+ * about 8 significant bits, the precision of bf16) into `workspace`:
+ * caller-owned device memory of >= bd_apply_workspace_bytes(p, T, n_users,
+ * d_out, d_in, BD_BF16, y_dtype) bytes, 256-byte aligned, whose first word is
+ * the status word (BD_ERR_USER_ID for an id outside [-1, n_users)).  For COL
+ * scales the users' column scales (scales_bank) are folded into the encoding;
+ * other modes do not read scales_bank here (it may be NULL).
+ *
+ * bd_decode_apply computes y[T][d_out] (y_dtype BD_F32 or BD_BF16, written,
+ * not accumulated) for one matrix from a prepared workspace.  One prepared
+ * workspace serves every matrix that reads the same x and user ids with the
+ * same p->mode (for COL, the same column scales), e.g. q, k and v; the
+ * workspace size does not depend on d_out.  Arguments as for bd_apply. */
+bd_status bd_decode_prepare(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                            const int32_t* user_ids, int32_t n_users, const void* scales_bank,
+                            const bd_compress_params* p, void* workspace, size_t ws_bytes,
+                            void* stream);
+bd_status bd_decode_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                          const void* w_base, int64_t d_out, const uint64_t* signs_bank,
+                          const void* scales_bank, const bd_compress_params* p, int32_t n_users,
+                          void* y, bd_dtype y_dtype, const void* workspace, size_t ws_bytes,
+                          void* stream);
 
 /* ------------------------------------------------------- status read-back */
 

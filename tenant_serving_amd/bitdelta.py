@@ -81,6 +81,11 @@ def lib() -> ctypes.CDLL:
         L.bd_base_gemm.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp]
         L.bd_delta_apply.restype = ctypes.c_int
         L.bd_delta_apply.argtypes = [vp, vp, ctypes.c_int, i64, i64, i32, i64, vp, vp, P, vp, vp]
+        L.bd_decode_prepare.restype = ctypes.c_int
+        L.bd_decode_prepare.argtypes = [vp, ctypes.c_int, i64, i64, vp, i32, vp, P, vp, sz, vp]
+        L.bd_decode_apply.restype = ctypes.c_int
+        L.bd_decode_apply.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp, P, i32, vp,
+                                      ctypes.c_int, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -198,6 +203,24 @@ def bd_delta_apply(batch, x, n_users, signs_bank, scales_bank, p, y, stream=None
     return int(lib().bd_delta_apply(_ptr(batch), _ptr(x), _dtype_code(x), T, d_in, int(n_users),
                                     d_out, _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p),
                                     _ptr(y), _stream(y, stream)))
+
+
+def bd_decode_prepare(x, user_ids, n_users, scales_bank, p, workspace, stream=None) -> int:
+    T, d_in = x.shape
+    return int(lib().bd_decode_prepare(_ptr(x), _dtype_code(x), T, d_in, _ptr(user_ids),
+                                       int(n_users), _ptr(scales_bank), ctypes.byref(p),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(x, stream)))
+
+
+def bd_decode_apply(x, w_base, signs_bank, scales_bank, p, n_users, y, workspace,
+                    stream=None) -> int:
+    T, d_in = x.shape
+    return int(lib().bd_decode_apply(_ptr(x), _dtype_code(x), T, d_in, _ptr(w_base),
+                                     w_base.shape[0], _ptr(signs_bank), _ptr(scales_bank),
+                                     ctypes.byref(p), int(n_users), _ptr(y), _dtype_code(y),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(x, stream)))
 
 
 # ------------------------------------------------------- allocating helpers

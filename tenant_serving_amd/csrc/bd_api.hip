@@ -166,6 +166,13 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
     }
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
+    if (pl.decode) {
+        hipError_t e = launch_decode_prep(pl.dec, n_users, pl.delta, x, user_ids, scales_bank, ws, s);
+        if (e == hipSuccess)
+            e = launch_decode_main(pl.dec, pl.delta, x, w_base, signs_bank, scales_bank, y,
+                                   y_dtype, ws, s);
+        return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+    }
     hipError_t e = launch_batch_prepare(pl.batch, x, user_ids, ws, s);
     if (e != hipSuccess || T == 0) return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
     float* yacc = y_dtype == BD_F32 ? (float*)y : (float*)(ws + pl.off_yf);
@@ -174,6 +181,54 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
         e = launch_delta(pl.batch, pl.delta, ws, x, signs_bank, scales_bank, yacc, s);
     if (e == hipSuccess && y_dtype == BD_BF16)
         e = launch_cast_bf16(yacc, (uint16_t*)y, T * d_out, s);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+// Shared validation of the two decode-path entry points.
+static bd_status decode_plans(const bd_compress_params* p, int64_t T, int32_t n_users,
+                              int64_t d_out, int64_t d_in, bd_dtype x_dtype, ApplyPlan* pl) {
+    if (!p) return BD_ERR_INVALID_ARG;
+    bd_status st = make_apply_plan(p, T, n_users, d_out, d_in, x_dtype, BD_F32, pl);
+    if (st != BD_OK) return st;
+    return pl->decode ? BD_OK : BD_ERR_UNSUPPORTED;
+}
+
+bd_status bd_decode_prepare(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                            const int32_t* user_ids, int32_t n_users, const void* scales_bank,
+                            const bd_compress_params* p, void* workspace, size_t ws_bytes,
+                            void* stream) {
+    ApplyPlan pl;
+    bd_status st = decode_plans(p, T, n_users, 1, d_in, x_dtype, &pl);
+    if (st != BD_OK) return st;
+    if (!workspace || ws_bytes < pl.dec.total || !aligned(workspace, kAlign))
+        return BD_ERR_WORKSPACE;
+    if (!x || !user_ids || !aligned(x, 16) || !aligned(user_ids, 4)) return BD_ERR_INVALID_ARG;
+    if (p->mode == BD_SCALE_COL && n_users > 0 && (!scales_bank || !aligned(scales_bank, 16)))
+        return BD_ERR_INVALID_ARG;
+    pl.delta.per_user = d_in;  // COL: one scale per input column
+    hipError_t e = launch_decode_prep(pl.dec, n_users, pl.delta, x, user_ids, scales_bank,
+                                      (char*)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_decode_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                          const void* w_base, int64_t d_out, const uint64_t* signs_bank,
+                          const void* scales_bank, const bd_compress_params* p, int32_t n_users,
+                          void* y, bd_dtype y_dtype, const void* workspace, size_t ws_bytes,
+                          void* stream) {
+    ApplyPlan pl;
+    bd_status st = decode_plans(p, T, n_users, d_out, d_in, x_dtype, &pl);
+    if (st != BD_OK) return st;
+    if (y_dtype != BD_F32 && y_dtype != BD_BF16) return BD_ERR_DTYPE;
+    if (!workspace || ws_bytes < pl.dec.total || !aligned(workspace, kAlign))
+        return BD_ERR_WORKSPACE;
+    if (!x || !w_base || !y || !aligned(x, 16) || !aligned(w_base, 16) || !aligned(y, 16))
+        return BD_ERR_INVALID_ARG;
+    if (n_users > 0 && (!signs_bank || !scales_bank || !aligned(signs_bank, 16) ||
+                        !aligned(scales_bank, 16)))
+        return BD_ERR_INVALID_ARG;
+    hipError_t e = launch_decode_main(pl.dec, pl.delta, x, w_base, signs_bank, scales_bank, y,
+                                      y_dtype, (const char*)workspace, (hipStream_t)stream);
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 

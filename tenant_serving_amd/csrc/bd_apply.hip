@@ -728,6 +728,13 @@ bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int
     st = make_delta_plan(p, q.batch, d_out, &q.delta);
     if (st != BD_OK) return st;
     q.ydtype = ydtype;
+    q.decode = decode_path_supported(xdtype, T, p->mode);
+    if (q.decode) {
+        make_decode_plan(T, d_in, &q.dec);
+        q.total = q.dec.total;
+        *pl = q;
+        return BD_OK;
+    }
     size_t off = q.batch.total;
     q.off_yf = off;
     if (ydtype == BD_BF16) off += align_up(4 * (size_t)T * (size_t)d_out);

@@ -1,0 +1,521 @@
+// bd_decode.hip -- one-pass multi-tenant apply for decode-sized batches (T <= 16).
+//
+// y[t] = X[t] W_base^T + scale_u (.) (X[t] S_u^T) for every token of the batch
+// in one kernel over the output rows ([P2] "Systems Mechanics" 1-2: one shared
+// base product per batch, each request adds its user's 1-bit delta product,
+// the bits cross HBM packed and are expanded on chip).
+//
+// Two launches:
+//   k_decode_prep  sorts the (<= 16) tokens by user in one wave and encodes X
+//                  for the delta products: every 32-column block of a token is
+//                  scaled by a power of two (an MX block scale) and split into
+//                  two OCP fp8 e4m3 parts, hi = fp8(x') and lo = fp8(x' - hi),
+//                  which keeps about 8 significant bits, the precision of the
+//                  bf16 input.
+//   k_decode       one block per 16 output rows, 8 waves.  Base waves stream
+//                  W_base rows (bf16 MFMA 16x16x32 against the bf16 tokens);
+//                  delta waves stream the users' packed sign rows and run the
+//                  gfx950 block-scaled MFMA 16x16x128 with the signs as fp4
+//                  e2m1 +-1 operands and the encoded tokens as fp8 operands.
+//                  The 16 tokens form one MFMA tile; for user u the tile's
+//                  other tokens enter with block scale 2^-127 (E8M0 code 0),
+//                  so one accumulator collects every user's product in its own
+//                  token columns.  Partial tiles are summed in LDS in wave order
+//                  and written once: no atomics, no read-modify-write of y.
+//
+// Sign bits to fp4: nibble = 0x2 | (bit << 3), i.e. +1.0 for a negative delta
+// and -1.0 for a non-negative one, so the accumulator holds -(X S^T) and the
+// epilogue multiplies by -scale.  Dword d of the A operand of a 32-bit sign
+// word w is ((w << (3 - d)) & 0x88888888) | 0x22222222: its nibble n carries
+// bit 4n + d.  The token encoding places column 4n + d of every 32-column
+// block at MFMA k position 8d + n to match.
+#include "bd_internal.h"
+
+namespace bd {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kDecodeWaves = 16;
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past num_records: the load returns 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+    const int nrec = bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D += A(fp4, 16 x 128) * B(fp8 e4m3, 128 x 16) * 2^(scale_b - 127), scale_b = byte SEL of sc.
+template <int SEL>
+__device__ __forceinline__ f32x4 mfma_f4f8(u32x4 a, i32x8 b, f32x4 c, uint32_t sc) {
+    const i32x8 a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 0, 0, 127, SEL, (int)sc);
+}
+
+__device__ __forceinline__ float load_scale(const void* s, int sdtype, int64_t i) {
+    return sdtype == BD_F16 ? f16_to_f32(((const uint16_t*)s)[i]) : ((const float*)s)[i];
+}
+
+// ------------------------------------------------------------------- prep
+// Every block, wave 0: bitonic sort of (user, token) keys over 64 lanes.  Tokens
+// with a valid user come first, grouped by user in token order; the others (id
+// -1 or out of range) follow.  Block 0 stores perm[p] = token at sorted position
+// p, suser[p] = its user (or -1), seg[i] = {user, first position, count, 0} and
+// the counts.  Then every thread encodes one (sorted position, 32-column block).
+//
+// Both operand buffers are stored in MFMA lane order, so every load of the apply
+// kernel reads 1 KB contiguous (all blocks of that kernel read these buffers):
+//  xs : bf16 B operand of the base product.  Step s (columns 32s .. 32s+31):
+//       1 KB at s*1024, lane (m, g) = m + 16g holds columns 32s + 8g .. +7 of
+//       the token at sorted position m (zero for m >= T).
+//  x8 : fp8 B operands of the delta products, per chunk q (columns 128q ..
+//       128q+127), part p (0 hi, 1 lo) and half h: 1 KB at ((q*2 + p)*2 + h)*1024,
+//       lane (m, G) = m + 16G holding bytes 16h .. 16h+15 of that lane's 32-byte
+//       operand.  The 32-column block kb of the chunk fills lane groups
+//       G = 2 (kb % 2) + e, e = 0, 1, half h = kb / 2; byte b' of each 16-byte run
+//       holds column 4 (b' % 8) + 2e + b' / 8 of the block: the column whose sign
+//       bit the A operand puts at that k position.  Zero for positions without a
+//       valid user and past d_in.
+//  e8 : the blocks' scale codes, one dword per lane and 512-column unit u at
+//       u*256 + 4 (m + 16 kb), byte q % 4 for chunk q = 4u + q % 4.
+__global__ void __launch_bounds__(256)
+k_decode_prep(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int T, int U,
+              int64_t d_in, int64_t dpad, int col_mode, const void* __restrict__ scales, int sdtype,
+              int64_t per_user, uint32_t* __restrict__ meta, int32_t* __restrict__ perm,
+              int32_t* __restrict__ suser, int4* __restrict__ seg, uint16_t* __restrict__ xs,
+              uint8_t* __restrict__ x8, uint8_t* __restrict__ e8) {
+    __shared__ int32_t ptok[kDecodeMaxT], puser[kDecodeMaxT];
+    if (threadIdx.x < 64) {
+        const int l = threadIdx.x;
+        uint32_t key = 0xFFFFFFFFu;
+        bool bad = false;
+        if (l < T) {
+            const int u = ids[l];
+            const bool ok = u >= 0 && u < U;
+            bad = !ok && u != -1;
+            key = ((ok ? (uint32_t)u : (uint32_t)U) << 6) | (uint32_t)l;
+        }
+        for (int k = 2; k <= 64; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                const uint32_t other = __shfl_xor(key, j);
+                const bool lower = (l & j) == 0;
+                const bool asc = (l & k) == 0;
+                const uint32_t mn = key < other ? key : other, mx = key < other ? other : key;
+                key = (lower == asc) ? mn : mx;
+            }
+        }
+        const uint32_t user = key >> 6;
+        const bool valid = l < T && user < (uint32_t)U;
+        const int nv = __popcll(__ballot(valid));
+        if (l < kDecodeMaxT) {
+            ptok[l] = l < T ? (int32_t)(key & 63u) : -1;
+            puser[l] = valid ? (int32_t)user : -1;
+        }
+        if (blockIdx.x == 0) {
+            if (l < T) {
+                perm[l] = (int32_t)(key & 63u);
+                suser[l] = valid ? (int32_t)user : -1;
+            }
+            const uint32_t prev = __shfl_up(user, 1);
+            const bool start = valid && (l == 0 || prev != user);
+            const uint64_t smask = __ballot(start);
+            const uint64_t above = l == 63 ? 0ull : (smask >> (l + 1)) << (l + 1);
+            const int next = above ? __ffsll((unsigned long long)above) - 1 : nv;
+            if (start) {
+                const int idx = __popcll(smask & ((1ull << l) - 1ull));
+                seg[idx] = make_int4((int)user, l, next - l, 0);
+            }
+            const bool anybad = __ballot(bad) != 0ull;
+            if (l == 0) {
+                meta[0] = anybad ? ST_USER_ID : 0u;
+                meta[1] = (uint32_t)__popcll(smask);
+                meta[2] = (uint32_t)nv;
+            }
+        }
+    }
+    __syncthreads();
+    const int64_t nblk = dpad / 32;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < kDecodeMaxT * nblk;
+         idx += (int64_t)gridDim.x * 256) {
+        const int m = (int)(idx % kDecodeMaxT);
+        const int64_t b = idx / kDecodeMaxT;
+        const int64_t c0 = b * 32;
+        const int tok = ptok[m], usr = puser[m];
+        u32x4 raw[4] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u},
+                        u32x4{0u, 0u, 0u, 0u}};
+        if (tok >= 0 && c0 < d_in) {
+            const u32x4* src = (const u32x4*)(x + tok * d_in + c0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) raw[q] = src[q];
+        }
+        if (c0 < d_in) {  // base operand, step b: lane group g takes columns 8g .. 8g+7
+#pragma unroll
+            for (int g = 0; g < 4; ++g) *(u32x4*)(xs + (b * 64 + m + 16 * g) * 8) = raw[g];
+        }
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[8 * q + 2 * e] = usr >= 0 ? bf16_lo(raw[q][e]) : 0.f;
+                v[8 * q + 2 * e + 1] = usr >= 0 ? bf16_hi(raw[q][e]) : 0.f;
+            }
+        }
+        if (col_mode && usr >= 0 && c0 < d_in) {  // the user's column scales, folded into X
+            const int64_t s0 = (int64_t)usr * per_user + c0;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) v[c] *= load_scale(scales, sdtype, s0 + c);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(v[c]));
+        // amax in [2^(E-1), 2^E): x' = x * 2^(8-E) puts the block maximum in [128, 256),
+        // inside e4m3's range (448); the MFMA scale code 127 - (8-E) undoes it
+        int code = 127, sh = 0;
+        if (amax > 0.f) {
+            int E;
+            (void)frexpf(amax, &E);
+            code = 119 + E;
+            if (code < 0) code = 0;
+            sh = 127 - code;
+        }
+        float hi[32], lo[32];
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            const float xsc = ldexpf(v[c], sh);
+            const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(xsc, 0.f, 0, false);
+            hi[c] = xsc;
+            lo[c] = xsc - __builtin_amdgcn_cvt_f32_fp8(pk, 0);
+        }
+        const int64_t q = b / 4;
+        const int kb = (int)(b % 4);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            u32x4 ph, pl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // bytes 4i .. 4i+3 of the run: b' = 4i + j, column 4 (b' % 8) + 2e + b' / 8
+                const int base = 16 * (i & 1) + 2 * e + (i >> 1);
+                int wh = __builtin_amdgcn_cvt_pk_fp8_f32(hi[base], hi[base + 4], 0, false);
+                wh = __builtin_amdgcn_cvt_pk_fp8_f32(hi[base + 8], hi[base + 12], wh, true);
+                int wl = __builtin_amdgcn_cvt_pk_fp8_f32(lo[base], lo[base + 4], 0, false);
+                wl = __builtin_amdgcn_cvt_pk_fp8_f32(lo[base + 8], lo[base + 12], wl, true);
+                ph[i] = (uint32_t)wh;
+                pl[i] = (uint32_t)wl;
+            }
+            const int lane = m + 16 * (2 * (kb & 1) + e), h = kb >> 1;
+            *(u32x4*)(x8 + (((q * 2 + 0) * 2 + h) * 64 + lane) * 16) = ph;
+            *(u32x4*)(x8 + (((q * 2 + 1) * 2 + h) * 64 + lane) * 16) = pl;
+        }
+        e8[(q / 4) * 256 + 4 * (m + 16 * kb) + (q % 4)] = (uint8_t)code;
+    }
+}
+
+// ------------------------------------------------------------------ apply
+// Encoded tokens of one 512-column unit (4 chunks) for this lane.
+struct Unit {
+    i32x8 hi[4], lo[4];
+    uint32_t e;
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(64 * kDecodeWaves)
+k_decode(const uint16_t* __restrict__ x, int T, int64_t d_in, int64_t dpad,
+         const uint16_t* __restrict__ w, int64_t d_out, const uint64_t* __restrict__ signs,
+         const void* __restrict__ scales, int sdtype, int64_t per_user,
+         const uint32_t* __restrict__ meta, const int32_t* __restrict__ perm,
+         const int32_t* __restrict__ suser, const int4* __restrict__ seg,
+         const uint16_t* __restrict__ xs, const uint8_t* __restrict__ x8,
+         const uint8_t* __restrict__ e8, void* __restrict__ y, int ydtype) {
+    __shared__ f32x4 red_base[kDecodeWaves][64];   // per K slice of the base product
+    __shared__ f32x4 red_delta[kDecodeWaves][64];  // per delta wave
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+    const int m = lane & 15, g = lane >> 4;
+    const int nseg = (int)meta[1], nv = (int)meta[2];
+    // waves split by HBM bytes per row: 2 d_in (base) against nseg d_in / 8 (delta)
+    int nwb = kDecodeWaves;
+    if (nseg > 0) {
+        nwb = (16 * kDecodeWaves + (16 + nseg) / 2) / (16 + nseg);
+        nwb = nwb < 1 ? 1 : (nwb > kDecodeWaves - 1 ? kDecodeWaves - 1 : nwb);
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * 16;
+    const int64_t rowA = r0 + m < d_out ? r0 + m : d_out - 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+    if (wv < nwb) {
+        // ---- base: the K steps of 32 columns form kDecodeWaves fixed slices (slice s =
+        // steps s, s + kDecodeWaves, ...), each summed in step order and stored to LDS;
+        // wave wv takes slices wv, wv + nwb, ...  The partition, and so the rounding, does
+        // not depend on the batch's users.  Ring of 8 slots over the wave's steps.
+        const int nsteps = (int)(d_in / 32);
+        const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint64_t)d_out * d_in * 2);
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(xs, (uint64_t)nsteps * 1024);
+        const uint32_t woff = (uint32_t)((rowA * d_in + 8 * g) * 2);
+        const uint32_t xoff = (uint32_t)(lane * 16);
+        const int spp = (nsteps + kDecodeWaves - 1) / kDecodeWaves;  // steps per slice
+        const int nown = (kDecodeWaves - wv + nwb - 1) / nwb;          // slices of this wave
+        const int total = nown * spp;
+        struct Slot {
+            u32x4 a, b;
+        };
+        // item i of the wave is step st(i) = wv + nwb * (i / spp) + kDecodeWaves * (i % spp);
+        // the load stream (8 items ahead) and the compute stream each keep (slice, k)
+        int ls = wv, lk = 0;   // next item to load
+        auto load = [&](int i) {
+            Slot sl;
+            const int st = ls + kDecodeWaves * lk;
+            const bool ok = i < total && st < nsteps;
+            sl.a = buf_load16(wr, ok ? woff + (uint32_t)(st * 64) : kOOB);
+            sl.b = buf_load16(xr, ok ? xoff + (uint32_t)(st * 1024) : kOOB);
+            if (++lk == spp) {
+                lk = 0;
+                ls += nwb;
+            }
+            return sl;
+        };
+        constexpr int R = 8;
+        Slot ring[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ring[r] = load(r);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int cs = wv, ck = 0;  // slice and step of the item being summed
+        for (int i0 = 0; i0 < total; i0 += R) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int i = i0 + r;
+                acc = mfma_bf16(ring[r].a, ring[r].b, acc);
+                ring[r] = load(i + R);
+                if (++ck == spp) {  // uniform: the slice is complete
+                    if (i < total) red_base[cs][lane] = acc;
+                    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                    ck = 0;
+                    cs += nwb;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+        // ---- delta: 512-column units u = wd, wd + nwd, ...; every user of the batch
+        const int wd = wv - nwb, nwd = kDecodeWaves - nwb;
+        const int nunit = (int)(dpad / 512);
+        constexpr int RB = 8;  // bits ring depth (16 bytes per lane per slot)
+        const int nsegR = (nseg + RB - 1) / RB * RB;
+        const int64_t bank_row = d_in / 8;  // bytes of one packed row
+        const uint64_t user_bytes = (uint64_t)d_out * (uint64_t)bank_row;
+        const int lane_user = m < nv ? suser[m] : -1;    // user of this lane's token column
+        const int utab = lane < nseg ? seg[lane].x : 0;  // lane j: user of segment j
+        const __amdgpu_buffer_rsrc_t xr8 = make_rsrc(x8, (uint64_t)(dpad / 128) * 4096);
+        const __amdgpu_buffer_rsrc_t er = make_rsrc(e8, (uint64_t)(dpad / 512) * 256);
+        const uint32_t brow = (uint32_t)(rowA * bank_row + 16 * g);
+        uint32_t kmask, kone;  // operand constants in registers (gfx9 VOP3 takes no literal)
+        asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
+        asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
+
+        auto load_unit = [&](int u) {
+            Unit X;
+            const bool ok = u < nunit;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t o = (uint32_t)(((4 * u + i) * 4) * 1024 + lane * 16);
+                const u32x4 h0 = buf_load16(xr8, ok ? o : kOOB);
+                const u32x4 h1 = buf_load16(xr8, ok ? o + 1024 : kOOB);
+                const u32x4 l0 = buf_load16(xr8, ok ? o + 2048 : kOOB);
+                const u32x4 l1 = buf_load16(xr8, ok ? o + 3072 : kOOB);
+                X.hi[i] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w,
+                                (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+                X.lo[i] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w,
+                                (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+            }
+            X.e = buf_load4(er, ok ? (uint32_t)(u * 256 + lane * 4) : kOOB);
+            return X;
+        };
+        // 16 bytes of user j's row: columns [512u + 128g, +128) (4 words, one per chunk).
+        // Always issued (out of range: a zero load), so the loads of the ring retire in
+        // issue order on straight-line code and every wait is exact.
+        auto load_bits = [&](int u, int j) {
+            const bool ok = j < nseg && u < nunit;  // uniform
+            const int usr = __builtin_amdgcn_readlane(utab, ok ? j : 0);
+            const __amdgpu_buffer_rsrc_t br =
+                make_rsrc((const char*)signs + (uint64_t)(uint32_t)usr * user_bytes, user_bytes);
+            const bool in = ok && (int64_t)u * 512 + 128 * g < d_in;
+            return buf_load16(br, in ? brow + (uint32_t)(u * 64) : kOOB);
+        };
+        auto item = [&](const Unit& X, int u, int j, u32x4 D) {
+            // 4x4 transpose over the lane groups: lane group g gets word g of every chunk.
+            // Done for every slot, so each slot's load is consumed at the same point on
+            // every path and the waits stay exact; only the products are skipped.
+            auto s32a = __builtin_amdgcn_permlane32_swap(D.x, D.z, false, false);
+            auto s32b = __builtin_amdgcn_permlane32_swap(D.y, D.w, false, false);
+            auto s16a = __builtin_amdgcn_permlane16_swap(s32a[0], s32b[0], false, false);
+            auto s16b = __builtin_amdgcn_permlane16_swap(s32a[1], s32b[1], false, false);
+            const uint32_t wd4[4] = {s16a[0], s16a[1], s16b[0], s16b[1]};
+            if (j >= nseg || u >= nunit) return;  // uniform; no loads inside
+            const int usr = __builtin_amdgcn_readlane(utab, j);
+            const uint32_t sc = lane_user == usr ? X.e : 0u;
+#define BD_CHUNK(I)                                                                   \
+    {                                                                                 \
+        const uint32_t wq = wd4[I];                                                   \
+        u32x4 A;                                                                      \
+        A.x = ((wq << 3) & kmask) | kone;                                             \
+        A.y = ((wq << 2) & kmask) | kone;                                             \
+        A.z = ((wq << 1) & kmask) | kone;                                             \
+        A.w = (wq & kmask) | kone;                                                    \
+        acc = mfma_f4f8<I>(A, X.hi[I], acc, sc);                                      \
+        acc = mfma_f4f8<I>(A, X.lo[I], acc, sc);                                      \
+    }
+            BD_CHUNK(0) BD_CHUNK(1) BD_CHUNK(2) BD_CHUNK(3)
+#undef BD_CHUNK
+        };
+        // Per unit: the encoded tokens first, then a ring of RB bit loads over the users
+        // (slot r holds user j = r mod RB), so every wait in the user loop is exact.
+        if (nseg > 0) {
+            for (int u = wd; u < nunit; u += nwd) {
+                const Unit X = load_unit(u);
+                __builtin_amdgcn_sched_barrier(0);
+                u32x4 ring[RB];
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {  // in slot order: slot r retires before r + 1
+                    ring[r] = load_bits(u, r);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                for (int j = 0; j < nsegR; j += RB) {
+#pragma unroll
+                    for (int r = 0; r < RB; ++r) {
+                        item(X, u, j + r, ring[r]);
+                        ring[r] = load_bits(u, j + r + RB);  // past the last user: a zero load
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        }
+    }
+    if (wv >= nwb) red_delta[wv - nwb][lane] = acc;
+    __syncthreads();
+    if (wv != 0) return;
+
+    // ---- epilogue: base slices + factor * delta partials, each in a fixed order
+    f32x4 vb = {0.f, 0.f, 0.f, 0.f}, vd = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < kDecodeWaves; ++q) vb += red_base[q][lane];
+    for (int q = 0; q < kDecodeWaves - nwb; ++q) vd += red_delta[q][lane];
+    if (m >= T) return;
+    const int64_t o = r0 + 4 * g;
+    float f[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m < nv) {
+        const int64_t u = suser[m];
+        const void* su = (const char*)scales + (size_t)u * per_user * (sdtype == BD_F16 ? 2 : 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t oe = o + e < d_out ? o + e : d_out - 1;
+            if (MODE == BD_SCALE_MATRIX) f[e] = -load_scale(su, sdtype, 0);
+            else if (MODE == BD_SCALE_ROW) f[e] = -load_scale(su, sdtype, oe);
+            else f[e] = -1.0f;  // COL: the scales are folded into the encoded tokens
+        }
+    }
+    f32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = vb[e] + f[e] * vd[e];
+    const int64_t t = perm[m];
+    if (ydtype == BD_F32) {
+        float* dst = (float*)y + t * d_out + o;
+        if (o + 3 < d_out && (d_out & 3) == 0) {
+            *(f32x4*)dst = out;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (o + e < d_out) dst[e] = out[e];
+        }
+    } else {
+        uint16_t* dst = (uint16_t*)y + t * d_out + o;
+        if (o + 3 < d_out && (d_out & 3) == 0) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16);
+            *(uint2*)dst = pk;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (o + e < d_out) dst[e] = f32_to_bf16(out[e]);
+        }
+    }
+}
+
+}  // namespace
+
+bool decode_path_supported(int xdtype, int64_t T, int mode) {
+    return xdtype == BD_BF16 && T >= 1 && T <= kDecodeMaxT && mode != BD_SCALE_GROUP;
+}
+
+void make_decode_plan(int64_t T, int64_t d_in, DecodePlan* pl) {
+    DecodePlan q;
+    q.T = T;
+    q.d_in = d_in;
+    q.dpad = (d_in + 511) / 512 * 512;
+    size_t off = 0;
+    q.off_meta = off;
+    off += kAlign;
+    q.off_perm = off;
+    off += align_up(sizeof(int32_t) * kDecodeMaxT);
+    q.off_suser = off;
+    off += align_up(sizeof(int32_t) * kDecodeMaxT);
+    q.off_seg = off;
+    off += align_up(sizeof(int4) * kDecodeMaxT);
+    q.off_xs = off;
+    off += align_up((size_t)(d_in / 32) * 1024);
+    q.off_x8 = off;
+    off += align_up((size_t)(q.dpad / 128) * 4096);
+    q.off_e8 = off;
+    off += align_up((size_t)(q.dpad / 512) * 256);
+    q.total = off;
+    *pl = q;
+}
+
+hipError_t launch_decode_prep(const DecodePlan& pl, int U, const DeltaPlan& dp, const void* x,
+                              const int32_t* ids, const void* scales, char* ws, hipStream_t s) {
+    const int64_t work = kDecodeMaxT * (pl.dpad / 32);
+    int64_t gp = (work + 255) / 256;
+    gp = gp < 1 ? 1 : (gp > 1024 ? 1024 : gp);
+    hipLaunchKernelGGL(k_decode_prep, dim3((unsigned)gp), dim3(256), 0, s, (const uint16_t*)x, ids,
+                       (int)pl.T, U, pl.d_in, pl.dpad, dp.mode == BD_SCALE_COL ? 1 : 0, scales,
+                       dp.sdtype, dp.per_user, (uint32_t*)(ws + pl.off_meta),
+                       (int32_t*)(ws + pl.off_perm), (int32_t*)(ws + pl.off_suser),
+                       (int4*)(ws + pl.off_seg), (uint16_t*)(ws + pl.off_xs),
+                       (uint8_t*)(ws + pl.off_x8), (uint8_t*)(ws + pl.off_e8));
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_main(const DecodePlan& pl, const DeltaPlan& dp, const void* x,
+                              const void* wb, const uint64_t* signs, const void* scales, void* y,
+                              int ydtype, const char* ws, hipStream_t s) {
+    const dim3 grid((unsigned)((dp.d_out + 15) / 16));
+#define BD_DECODE(MODE)                                                                           \
+    hipLaunchKernelGGL(k_decode<MODE>, grid, dim3(64 * kDecodeWaves), 0, s, (const uint16_t*)x,   \
+                       (int)pl.T, pl.d_in, pl.dpad, (const uint16_t*)wb, dp.d_out, signs, scales,  \
+                       dp.sdtype, dp.per_user, (const uint32_t*)(ws + pl.off_meta),                \
+                       (const int32_t*)(ws + pl.off_perm), (const int32_t*)(ws + pl.off_suser),    \
+                       (const int4*)(ws + pl.off_seg), (const uint16_t*)(ws + pl.off_xs),          \
+                       (const uint8_t*)(ws + pl.off_x8), (const uint8_t*)(ws + pl.off_e8), y,      \
+                       ydtype)
+    switch (dp.mode) {
+        case BD_SCALE_MATRIX: BD_DECODE(BD_SCALE_MATRIX); break;
+        case BD_SCALE_ROW: BD_DECODE(BD_SCALE_ROW); break;
+        default: BD_DECODE(BD_SCALE_COL); break;
+    }
+#undef BD_DECODE
+    return hipGetLastError();
+}
+
+}  // namespace bd

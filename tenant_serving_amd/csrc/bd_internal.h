@@ -64,11 +64,22 @@ struct DeltaPlan {
     int mode = 0, group = 0, sdtype = 0;
 };
 
-// bd_apply workspace = batch | fp32 Y (bf16 output only).
+// One-pass path for decode batches of at most kDecodeMaxT bf16 tokens: the
+// prepared batch (sorted tokens, user segments) and the fp8 encoding of X.
+constexpr int kDecodeMaxT = 16;
+struct DecodePlan {
+    int64_t T = 0, d_in = 0, dpad = 0;
+    size_t off_meta = 0, off_perm = 0, off_suser = 0, off_seg = 0;
+    size_t off_xs = 0, off_x8 = 0, off_e8 = 0, total = 0;
+};
+
+// bd_apply workspace = batch | fp32 Y (bf16 output only), or the decode plan's.
 struct ApplyPlan {
     BatchPlan batch;
     DeltaPlan delta;
     int ydtype = 0;
+    bool decode = false;
+    DecodePlan dec;
     size_t off_yf = 0, total = 0;
 };
 
@@ -86,6 +97,14 @@ hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, const char* ba
                         const void* x, const uint64_t* signs, const void* scales, float* y,
                         hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
+
+bool decode_path_supported(int xdtype, int64_t T, int mode);
+void make_decode_plan(int64_t T, int64_t d_in, DecodePlan* plan);
+hipError_t launch_decode_prep(const DecodePlan& pl, int U, const DeltaPlan& dp, const void* x,
+                              const int32_t* ids, const void* scales, char* ws, hipStream_t s);
+hipError_t launch_decode_main(const DecodePlan& pl, const DeltaPlan& dp, const void* x,
+                              const void* wb, const uint64_t* signs, const void* scales, void* y,
+                              int ydtype, const char* ws, hipStream_t s);
 
 hipError_t launch_reconstruct(const uint64_t* signs, const void* scales, int mode, int group,
                               int sdtype, int64_t d_out, int64_t d_in, const void* wb, int wdtype,
