@@ -311,7 +311,10 @@ k_decode(const uint16_t* __restrict__ x, int T, int64_t d_in, int64_t dpad,
             }
         }
     } else {
-        // ---- delta: 512-column units u = wd, wd + nwd, ...; every user of the batch
+        // ---- delta: 512-column units u = wd, wd + nwd, ...; every user of the batch.
+        // Delta waves issue first: their operands gate the matrix-core work, while the
+        // base waves only stream, so the delta loads should not queue behind them.
+        __builtin_amdgcn_s_setprio(3);
         const int wd = wv - nwb, nwd = kDecodeWaves - nwb;
         const int nunit = (int)(dpad / 512);
         constexpr int RB = 8;  // bits ring depth (16 bytes per lane per slot)
