@@ -98,6 +98,13 @@ hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, const char* ba
                         hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 
+// Tiled matrix-core GEMM for the base product of batches of more than kGemmMinT
+// bf16 tokens (smaller batches take the streaming kernel of bd_apply.hip).
+constexpr int64_t kGemmMinT = 64;
+bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out);
+hipError_t launch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb, int64_t d_out,
+                       float* y, hipStream_t s);
+
 bool decode_path_supported(int xdtype, int64_t T, int mode);
 void make_decode_plan(int64_t T, int64_t d_in, DecodePlan* plan);
 hipError_t launch_decode_prep(const DecodePlan& pl, int U, const DeltaPlan& dp, const void* x,
