@@ -166,6 +166,11 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
     }
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
+    if (pl.fused) {
+        hipError_t e = launch_decode_fused(T, n_users, d_in, pl.delta, x, user_ids, w_base,
+                                           signs_bank, scales_bank, y, y_dtype, ws, s);
+        return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+    }
     if (pl.decode) {
         hipError_t e = launch_decode_prep(pl.dec, n_users, pl.delta, x, user_ids, scales_bank, ws, s);
         if (e == hipSuccess)

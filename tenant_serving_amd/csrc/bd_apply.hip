@@ -729,6 +729,7 @@ bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int
     if (st != BD_OK) return st;
     q.ydtype = ydtype;
     q.decode = decode_path_supported(xdtype, T, p->mode);
+    q.fused = fused_path_supported(xdtype, T, p->mode, d_in);
     if (q.decode) {
         make_decode_plan(T, d_in, &q.dec);
         q.total = q.dec.total;

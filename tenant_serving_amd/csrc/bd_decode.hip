@@ -456,7 +456,370 @@ k_decode(const uint16_t* __restrict__ x, int T, int64_t d_in, int64_t dpad,
     }
 }
 
+// ------------------------------------------------------------ fused apply
+// One launch for a whole decode batch (bf16 X, at most 16 tokens, MATRIX or ROW
+// scales, d_in padded to 512 at most kFusedMaxDpad): every block stages the batch's
+// tokens in LDS and encodes them for the delta products itself, so nothing has to
+// run before it.  12 waves: 4 base waves stream W_base (bf16 MFMA against the
+// tokens read from LDS), 8 delta waves stream the users' packed rows (fp4 x fp8
+// block-scaled MFMA as in k_decode).
+//
+// LDS: token row t (zeros past T and past d_in) at t * 2 dpad bytes; its 16-byte
+// chunk c sits at slot (c & ~15) | ((c ^ t) & 15), so the 16 tokens read at one
+// chunk index hit 16 distinct bank groups.  After the products the same memory
+// holds the partial tiles for the reduction.
+constexpr int kFusedBaseWaves = 4, kFusedDeltaWaves = 8;
+constexpr int kFusedWaves = kFusedBaseWaves + kFusedDeltaWaves;
+constexpr int kFusedSlices = 16;  // fixed K slices of the base product
+constexpr int kFusedRedBytes = (kFusedSlices + kFusedDeltaWaves) * 64 * 16;
+static_assert(kFusedBaseWaves * 4 == kDecodeMaxT, "each base wave stages four token rows");
+static_assert(kFusedSlices % kFusedBaseWaves == 0, "whole slices per base wave");
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t xslot(int t, int c, uint32_t rowb) {
+    return (uint32_t)t * rowb + 16u * (uint32_t)((c & ~15) | ((c ^ t) & 15));
+}
+
+// s_waitcnt with only the vector-memory count: vmcnt <= n (expcnt, lgkmcnt untouched).
+#define BD_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
+
 }  // namespace
+
+// Encodes the tokens' columns [512 u, 512 u + 512) from LDS into this lane's delta
+// operands (the layout k_decode_prep writes to x8 / e8): lane (m, G) takes, for chunk
+// q, the 16 columns 4n + 2(G & 1) + {0, 1} of 32-column blocks G / 2 and 2 + G / 2.
+__device__ __forceinline__ void fused_encode(const char* smem, uint32_t rowb, int u, int lane,
+                                             Unit& X) {
+    const int m = lane & 15, G = lane >> 4, hh = G & 1;
+    uint32_t codes[2] = {0u, 0u};  // byte q: code of this lane's block in half p of chunk q
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        int hq[8], lq[8];  // the chunk's two 32-byte operands
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c0 = 64 * u + 16 * q + 4 * ((G >> 1) + 2 * p);  // the block's first chunk
+            uint32_t raw[8];  // raw[n]: columns 4n + 2hh (low half) and 4n + 2hh + 1 (high half)
+#pragma unroll
+            for (int n2 = 0; n2 < 4; ++n2) {
+                const char* a = smem + xslot(m, c0 + n2, rowb) + 4 * hh;
+                raw[2 * n2] = *(const uint32_t*)a;
+                raw[2 * n2 + 1] = *(const uint32_t*)(a + 8);
+            }
+            float v[16];  // v[b]: the value for byte b of the 16-byte run
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                v[n] = bf16_lo(raw[n]);
+                v[8 + n] = bf16_hi(raw[n]);
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[c]));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));  // the other half of the block
+            // amax in [2^(E-1), 2^E): x' = x 2^(8-E) puts the block maximum in [128, 256)
+            int code = 127, sh = 0;
+            if (amax > 0.f) {
+                int E;
+                (void)frexpf(amax, &E);
+                code = 119 + E;
+                if (code < 0) code = 0;
+                sh = 127 - code;
+            }
+            const float mul = __uint_as_float((uint32_t)(sh + 127) << 23);  // 2^sh, a normal
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                float s[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] = v[4 * d + i] * mul;
+                int h = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
+                h = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], h, true);
+                const float r0 = s[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0);
+                const float r1 = s[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1);
+                const float r2 = s[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2);
+                const float r3 = s[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3);
+                int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+                l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
+                asm volatile("" : "+v"(h), "+v"(l));  // converted here, not next to the MFMAs
+                hq[4 * p + d] = h;
+                lq[4 * p + d] = l;
+            }
+            codes[p] |= (uint32_t)code << (8 * q);
+            __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded register use
+        }
+        X.hi[q] = i32x8{hq[0], hq[1], hq[2], hq[3], hq[4], hq[5], hq[6], hq[7]};
+        X.lo[q] = i32x8{lq[0], lq[1], lq[2], lq[3], lq[4], lq[5], lq[6], lq[7]};
+    }
+    // scale lane (m, kb) takes block kb of token m: computed by lane m + 32 (kb & 1), half kb / 2
+    const int src = m + 32 * (G & 1);
+    const uint32_t c0 = (uint32_t)__shfl((int)codes[0], src);
+    const uint32_t c1 = (uint32_t)__shfl((int)codes[1], src);
+    X.e = (G >> 1) ? c1 : c0;
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(64 * kFusedWaves)
+k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int T, int U,
+               int64_t d_in, int dpad, const uint16_t* __restrict__ w, int64_t d_out,
+               const uint64_t* __restrict__ signs, const void* __restrict__ scales, int sdtype,
+               int64_t per_user, void* __restrict__ y, int ydtype, uint32_t* __restrict__ status) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+    const int m = lane & 15, g = lane >> 4;
+    const uint32_t rowb = 2u * (uint32_t)dpad;
+    const int64_t r0 = (int64_t)blockIdx.x * 16;
+    const int64_t rowA = r0 + m < d_out ? r0 + m : d_out - 1;
+    if (wv < kFusedBaseWaves) {
+        // ---- base: step pairs (64 columns, one 128-byte line of each row) form 16 fixed
+        // slices (slice s = pairs s, s + 16, ...), each summed in order; wave wv takes slices
+        // wv, wv + 4, wv + 8, wv + 12.  The partition, and so the rounding, does not depend
+        // on the batch's users.  Ring of 16 W loads; the tokens come from LDS.
+        constexpr int NSL = kFusedSlices / kFusedBaseWaves;
+        f32x4 acc[NSL];  // one per slice of this wave
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int nsteps = (int)(d_in / 32);  // even
+        const int ipsl = 2 * ((nsteps / 2 + kFusedSlices - 1) / kFusedSlices);  // items per slice
+        const int total = NSL * ipsl;
+        const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint64_t)d_out * (uint64_t)d_in * 2);
+        const uint32_t woff = (uint32_t)((rowA * d_in + 8 * g) * 2);
+        constexpr int R = 16;
+        int ls = wv, lk = 0;  // slice and item of the next load
+        auto load = [&](int i) {
+            const int st = 2 * (ls + kFusedSlices * (lk >> 1)) + (lk & 1);
+            const bool ok = i < total && st < nsteps;
+            const u32x4 a = buf_load16(wr, ok ? woff + (uint32_t)(st * 64) : kOOB);
+            if (++lk == ipsl) {
+                lk = 0;
+                ls += kFusedBaseWaves;
+            }
+            return a;
+        };
+        u32x4 ring[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ring[r] = load(r);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- stage token rows 4 wv .. 4 wv + 3 in LDS (1 KB of a row per copy), behind
+        // the ring's first loads of W
+        {
+            const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)T * (uint64_t)d_in * 2);
+            const int npc = dpad / 512;  // 1 KB pieces per row
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * wv + r;
+                const int cl = (lane & 48) | ((lane & 15) ^ t);
+#pragma unroll
+                for (int j = 0; j < (int)(kFusedMaxDpad / 512); ++j) {
+                    if (j < npc) {  // uniform
+                        const int c = 64 * j + cl;
+                        const bool ok = t < T && (int64_t)c * 8 < d_in;
+                        lds_copy16(xr, smem + t * rowb + 1024 * j,
+                                   ok ? (uint32_t)(((int64_t)t * d_in + 8 * c) * 2) : kOOB);
+                    }
+                }
+            }
+        }
+        BD_WAIT_VMCNT(0);  // this wave's token copies have landed (and the ring's first loads)
+        __builtin_amdgcn_s_barrier();
+        int cs = 0, ck = 0;  // slice index (0 .. NSL-1) and item of the product being summed
+        f32x4 cur = {0.f, 0.f, 0.f, 0.f};
+        int i0 = 0;
+        do {  // total > 0 (d_in >= 64): the ring is always consumed, so its loads stay above
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int i = i0 + r;
+                const int st = 2 * (wv + kFusedBaseWaves * cs + kFusedSlices * (ck >> 1)) + (ck & 1);
+                u32x4 b = {0u, 0u, 0u, 0u};
+                if (i < total && st < nsteps)  // uniform
+                    b = *(const u32x4*)(smem + xslot(m, 4 * st + g, rowb));
+                cur = mfma_bf16(ring[r], b, cur);
+                ring[r] = load(i + R);
+                if (++ck == ipsl) {  // uniform: the slice is complete
+#pragma unroll
+                    for (int s = 0; s < NSL; ++s)
+                        if (s == cs) acc[s] = cur;
+                    cur = f32x4{0.f, 0.f, 0.f, 0.f};
+                    ck = 0;
+                    ++cs;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            i0 += R;
+        } while (i0 < total);
+        // the token rows are no longer read: the slices' partial tiles go to LDS
+        __syncthreads();
+        f32x4* red = (f32x4*)smem;  // [16 base slices][64], then [8 delta waves][64]
+#pragma unroll
+        for (int s = 0; s < NSL; ++s) red[(wv + kFusedBaseWaves * s) * 64 + lane] = acc[s];
+        __syncthreads();
+        return;
+    }
+
+    // ---- delta: 512-column units u = wd, wd + 8, ...; every user of the batch
+    __builtin_amdgcn_s_setprio(3);
+    const int wd = wv - kFusedBaseWaves;
+    // the batch's users, in order of first appearance (lane j of utab: the j-th)
+    const int uid = lane < T ? ids[lane] : -1;
+    const bool valid = lane < T && uid >= 0 && uid < U;
+    bool dup = false;
+#pragma unroll
+    for (int j = 0; j < kDecodeMaxT; ++j)
+        dup |= (j < lane) & (__builtin_amdgcn_readlane(uid, j) == uid);
+    const uint64_t fmask = __ballot(valid && !dup);
+    const int nseg = __popcll(fmask);
+    int utab = 0;
+    {
+        uint64_t mk = fmask;
+        for (int j = 0; j < nseg; ++j) {
+            const int src = __ffsll((unsigned long long)mk) - 1;
+            mk &= mk - 1;
+            const int us = __builtin_amdgcn_readlane(uid, src);
+            if (lane == j) utab = us;
+        }
+    }
+    const int tok_user = __shfl(valid ? uid : -1, m);  // user of this lane's token column
+    uint32_t sraw[4] = {0u, 0u, 0u, 0u};  // epilogue wave: the scales of its outputs (bits)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (wd == 0) {
+        if (blockIdx.x == 0) {
+            const bool bad = lane < T && !valid && uid != -1;
+            const bool anybad = __ballot(bad) != 0ull;
+            if (lane == 0) status[0] = anybad ? ST_USER_ID : 0u;
+        }
+        if (tok_user >= 0 && m < T) {  // the epilogue's scales, loaded early, used at the end
+            const int64_t o = r0 + 4 * g;
+            const int64_t s0 = (int64_t)tok_user * per_user;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t i = s0 + (MODE == BD_SCALE_MATRIX ? 0 : (o + e < d_out ? o + e : d_out - 1));
+                sraw[e] = sdtype == BD_F16 ? (uint32_t)((const uint16_t*)scales)[i]
+                                           : ((const uint32_t*)scales)[i];
+            }
+        }
+    }
+    const int nunit = dpad / 512;
+    const int nuw = wd < nunit ? (nunit - wd + kFusedDeltaWaves - 1) / kFusedDeltaWaves : 0;
+    constexpr int RB = 8;
+    const int nsegR = (nseg + RB - 1) / RB * RB;  // users padded: item (k, j) sits in slot j % RB
+    const int64_t bank_row = d_in / 8;
+    const uint64_t user_bytes = (uint64_t)d_out * (uint64_t)bank_row;
+    const uint32_t brow = (uint32_t)(rowA * bank_row + 16 * g);
+    uint32_t kmask, kone;  // operand constants in registers (gfx9 VOP3 takes no literal)
+    asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
+    asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
+    int lk = 0, lj = 0;  // unit (of this wave) and user slot of the next load
+    // 16 bytes of user lj's row: columns [512u + 128g, +128) (4 words, one per chunk);
+    // always issued (a zero load for padding and past the end) so every wait is exact
+    auto load_bits = [&]() {
+        const bool ok = lk < nuw && lj < nseg;  // uniform
+        const int usr = __builtin_amdgcn_readlane(utab, ok ? lj : 0);
+        const int u = wd + kFusedDeltaWaves * lk;
+        const __amdgpu_buffer_rsrc_t br =
+            make_rsrc((const char*)signs + (uint64_t)(uint32_t)usr * user_bytes, user_bytes);
+        const bool in = ok && (int64_t)u * 512 + 128 * g < d_in;
+        const u32x4 v = buf_load16(br, in ? brow + (uint32_t)(u * 64) : kOOB);
+        if (++lj == nsegR) {
+            lj = 0;
+            ++lk;
+        }
+        return v;
+    };
+    u32x4 ring[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        ring[r] = load_bits();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    BD_WAIT_VMCNT(RB);  // ids and scales (older than the ring) have landed
+    __builtin_amdgcn_s_barrier();  // the tokens are in LDS
+    Unit X;
+    for (int k = 0; k < nuw && nseg > 0; ++k) {
+        // encode this unit's tokens while its first users' rows are in flight
+        fused_encode(smem, rowb, wd + kFusedDeltaWaves * k, lane, X);
+        for (int j0 = 0; j0 < nsegR; j0 += RB) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int j = j0 + r;
+                const u32x4 D = ring[r];
+                // 4x4 transpose over the lane groups: lane group g gets word g of every
+                // chunk (done for every slot so each load is consumed at the same point)
+                auto s32a = __builtin_amdgcn_permlane32_swap(D.x, D.z, false, false);
+                auto s32b = __builtin_amdgcn_permlane32_swap(D.y, D.w, false, false);
+                auto s16a = __builtin_amdgcn_permlane16_swap(s32a[0], s32b[0], false, false);
+                auto s16b = __builtin_amdgcn_permlane16_swap(s32a[1], s32b[1], false, false);
+                const uint32_t wd4[4] = {s16a[0], s16a[1], s16b[0], s16b[1]};
+                if (j < nseg) {  // uniform
+                    const int usr = __builtin_amdgcn_readlane(utab, j);
+                    const uint32_t sc = tok_user == usr ? X.e : 0u;
+#define BD_CHUNK(I)                                                                   \
+    {                                                                                 \
+        const uint32_t wq = wd4[I];                                                   \
+        u32x4 A;                                                                      \
+        A.x = ((wq << 3) & kmask) | kone;                                             \
+        A.y = ((wq << 2) & kmask) | kone;                                             \
+        A.z = ((wq << 1) & kmask) | kone;                                             \
+        A.w = (wq & kmask) | kone;                                                    \
+        acc = mfma_f4f8<I>(A, X.hi[I], acc, sc);                                      \
+        acc = mfma_f4f8<I>(A, X.lo[I], acc, sc);                                      \
+    }
+                    BD_CHUNK(0) BD_CHUNK(1) BD_CHUNK(2) BD_CHUNK(3)
+#undef BD_CHUNK
+                }
+                ring[r] = load_bits();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+
+    // ---- reduction: the token rows are no longer read; partial tiles go to LDS
+    __syncthreads();
+    f32x4* red = (f32x4*)smem;
+    red[(kFusedSlices + wd) * 64 + lane] = acc;
+    __syncthreads();
+    if (wv != kFusedBaseWaves) return;  // the first delta wave holds the factors
+    f32x4 vb = {0.f, 0.f, 0.f, 0.f}, vd = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < kFusedSlices; ++q) vb += red[q * 64 + lane];
+    for (int q = 0; q < kFusedDeltaWaves; ++q) vd += red[(kFusedSlices + q) * 64 + lane];
+    if (m >= T) return;
+    const int64_t o = r0 + 4 * g;
+    f32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // -scale (the fp4 operands carry -sign); 0 for tokens without a valid user
+        const float f = tok_user < 0 ? 0.f
+                        : sdtype == BD_F16 ? -f16_to_f32((uint16_t)sraw[e])
+                                           : -__uint_as_float(sraw[e]);
+        out[e] = vb[e] + f * vd[e];
+    }
+    if (ydtype == BD_F32) {
+        float* dst = (float*)y + (int64_t)m * d_out + o;
+        if (o + 3 < d_out && (d_out & 3) == 0) {
+            *(f32x4*)dst = out;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (o + e < d_out) dst[e] = out[e];
+        }
+    } else {
+        uint16_t* dst = (uint16_t*)y + (int64_t)m * d_out + o;
+        if (o + 3 < d_out && (d_out & 3) == 0) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16);
+            *(uint2*)dst = pk;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (o + e < d_out) dst[e] = f32_to_bf16(out[e]);
+        }
+    }
+}
 
 bool decode_path_supported(int xdtype, int64_t T, int mode) {
     return xdtype == BD_BF16 && T >= 1 && T <= kDecodeMaxT && mode != BD_SCALE_GROUP;
@@ -518,6 +881,29 @@ hipError_t launch_decode_main(const DecodePlan& pl, const DeltaPlan& dp, const v
         default: BD_DECODE(BD_SCALE_COL); break;
     }
 #undef BD_DECODE
+    return hipGetLastError();
+}
+
+bool fused_path_supported(int xdtype, int64_t T, int mode, int64_t d_in) {
+    return xdtype == BD_BF16 && T >= 1 && T <= kDecodeMaxT &&
+           (mode == BD_SCALE_MATRIX || mode == BD_SCALE_ROW) &&
+           (d_in + 511) / 512 * 512 <= kFusedMaxDpad;
+}
+
+hipError_t launch_decode_fused(int64_t T, int U, int64_t d_in, const DeltaPlan& dp, const void* x,
+                               const int32_t* ids, const void* wb, const uint64_t* signs,
+                               const void* scales, void* y, int ydtype, char* ws, hipStream_t s) {
+    const int dpad = (int)((d_in + 511) / 512 * 512);
+    const size_t lds = (size_t)32 * dpad > (size_t)kFusedRedBytes ? (size_t)32 * dpad
+                                                                  : (size_t)kFusedRedBytes;
+    const dim3 grid((unsigned)((dp.d_out + 15) / 16));
+#define BD_FUSED(MODE)                                                                          \
+    k_decode_fused<MODE><<<grid, dim3(64 * kFusedWaves), lds, s>>>(                             \
+        (const uint16_t*)x, ids, (int)T, U, d_in, dpad, (const uint16_t*)wb, dp.d_out, signs,   \
+        scales, dp.sdtype, dp.per_user, y, ydtype, (uint32_t*)ws)
+    if (dp.mode == BD_SCALE_MATRIX) BD_FUSED(BD_SCALE_MATRIX);
+    else BD_FUSED(BD_SCALE_ROW);
+#undef BD_FUSED
     return hipGetLastError();
 }
 

@@ -73,12 +73,16 @@ struct DecodePlan {
     size_t off_xs = 0, off_x8 = 0, off_e8 = 0, total = 0;
 };
 
+// Single-launch decode path (MATRIX or ROW scales): the tokens of the batch, d_in
+// padded to 512 columns, are staged in LDS, 32 bytes per padded column.
+constexpr int64_t kFusedMaxDpad = 5120;
+
 // bd_apply workspace = batch | fp32 Y (bf16 output only), or the decode plan's.
 struct ApplyPlan {
     BatchPlan batch;
     DeltaPlan delta;
     int ydtype = 0;
-    bool decode = false;
+    bool decode = false, fused = false;
     DecodePlan dec;
     size_t off_yf = 0, total = 0;
 };
@@ -112,6 +116,11 @@ hipError_t launch_decode_prep(const DecodePlan& pl, int U, const DeltaPlan& dp, 
 hipError_t launch_decode_main(const DecodePlan& pl, const DeltaPlan& dp, const void* x,
                               const void* wb, const uint64_t* signs, const void* scales, void* y,
                               int ydtype, const char* ws, hipStream_t s);
+bool fused_path_supported(int xdtype, int64_t T, int mode, int64_t d_in);
+// Writes the status word at ws (bad user ids) and y; reads nothing else of ws.
+hipError_t launch_decode_fused(int64_t T, int U, int64_t d_in, const DeltaPlan& dp, const void* x,
+                               const int32_t* ids, const void* wb, const uint64_t* signs,
+                               const void* scales, void* y, int ydtype, char* ws, hipStream_t s);
 
 hipError_t launch_reconstruct(const uint64_t* signs, const void* scales, int mode, int group,
                               int sdtype, int64_t d_out, int64_t d_in, const void* wb, int wdtype,

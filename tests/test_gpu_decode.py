@@ -1,9 +1,11 @@
-"""GPU parity of the one-pass decode path (bf16, at most 16 tokens, MATRIX/ROW/COL
-scales): bd_apply against the CPU oracle on the same seeded inputs, for the whole
-output and for the delta term alone, over ragged shapes (d_in not a multiple of
-128 or 512, d_out not a multiple of 16), repeated users, invalid ids, a batch
-without any valid user, one token, and unit counts that do not divide evenly
-over the kernel's waves."""
+"""GPU parity of the decode paths (bf16, at most 16 tokens): the single-launch
+kernel (MATRIX/ROW scales, d_in up to 5120) and the two-launch one (prepare +
+apply; also COL scales and wider rows).  bd_apply against the CPU oracle on the
+same seeded inputs, for the whole output and for the delta term alone, over
+ragged shapes (d_in not a multiple of 128 or 512, d_out not a multiple of 16),
+repeated users, invalid ids, a batch without any valid user, one token, unit
+counts that do not divide evenly over the kernels' waves, the widest rows the
+single-launch kernel stages and the first width past it."""
 import numpy as np
 import pytest
 import torch
@@ -37,6 +39,9 @@ CASES = [
     ("odd-units", "matrix", B.BD_F32, 48, 2560, _shuffled([(u, 1) for u in range(12)], n_invalid=2, seed=4), 12, torch.float32),
     ("d_in-64", "row", B.BD_F32, 40, 64, np.array([0, 1, 1, 0, 2], np.int32), 3, torch.float32),
     ("nine-users", "col", B.BD_F32, 33, 1152, _shuffled([(u, 1 + u % 2) for u in range(9)], seed=5), 9, torch.bfloat16),
+    ("widest-staged", "matrix", B.BD_F32, 48, 5120, np.random.default_rng(6).permutation(16).astype(np.int32), 16, torch.float32),
+    ("past-staged", "row", B.BD_F16, 40, 5632, _shuffled([(0, 4), (2, 5), (1, 3)], n_invalid=1, seed=8), 3, torch.float32),
+    ("nine-units", "row", B.BD_F16, 64, 4608, _shuffled([(u, 1) for u in range(14)], n_invalid=2, seed=9), 14, torch.bfloat16),
 ]
 
 
@@ -142,3 +147,39 @@ def test_decode_under_graph_capture_replays_match_eager():
         assert torch.equal(y, y_eager), f"replay {rep} differs from the eager result"
         B.apply(x_other, wb_dev, signs, scales, p, ids_dev, ws=ws_other)  # eager work between
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode,sd", [("matrix", B.BD_F32), ("row", B.BD_F16)])
+def test_single_launch_matches_two_launch_path(mode, sd):
+    """The single-launch kernel (bd_apply) and the two-launch decode calls
+    (bd_decode_prepare + bd_decode_apply) compute the same product with different
+    partitions of the sums: both within the bf16 tolerance of each other, and the
+    single-launch result repeats bit for bit."""
+    ids = _shuffled([(0, 2), (3, 5), (1, 1), (5, 4), (2, 3)], n_invalid=1, seed=11)
+    T, U, d_out, d_in = len(ids), 6, 208, 4096
+    w = custom(d_out, d_in, S.BF16, n_users=U, T=T, b=5e-3, cid=1799)
+    p = B.params(mode, 128, 0.0, sd)
+    wb_dev = S.dev_wbase(w, 0)
+    x_dev = S.dev_x(w, 0)
+    signs, scales = gpu_bank(w, 0, wb_dev, p, range(U))
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    y1 = B.apply(x_dev, wb_dev, signs, scales, p, ids_dev, check=True)
+    y2 = B.apply(x_dev, wb_dev, signs, scales, p, ids_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ws = B.workspace(B.bd_apply_workspace_bytes(p, T, U, d_out, d_in, B.BD_BF16, B.BD_F32), DEV)
+    assert B.bd_decode_prepare(x_dev, ids_dev, U, scales, p, ws) == B.BD_OK
+    yt = torch.empty((T, d_out), dtype=torch.float32, device=DEV)
+    assert B.bd_decode_apply(x_dev, wb_dev, signs, scales, p, U, yt, ws) == B.BD_OK
+    torch.cuda.synchronize()
+    assert B.bd_device_status(ws) == B.BD_OK
+    err, rms = max_err_vs_rms(y1.cpu().numpy(), yt.cpu().numpy().astype(np.float64))
+    assert err <= TOL_BF16 * rms, (err, rms)
+    # and both against the oracle's delta term alone (W_base = 0)
+    z = torch.zeros_like(wb_dev)
+    d1 = B.apply(x_dev, z, signs, scales, p, ids_dev, check=True)
+    wb = S.host_wbase(w, 0)
+    words, osc = oracle_bank(w, 0, wb, p, range(U))
+    _, _, yd = O.apply(S.host_x(w, 0), wb, words, osc, p.mode, ids, g=128, sdtype=o_sdtype(p))
+    err, rms = max_err_vs_rms(d1.cpu().numpy(), yd)
+    assert err <= TOL_BF16 * rms, ("delta only", err, rms)
