@@ -461,19 +461,19 @@ k_decode(const uint16_t* __restrict__ x, int T, int64_t d_in, int64_t dpad,
 // scales, d_in padded to 512 at most kFusedMaxDpad): every block stages the batch's
 // tokens in LDS and encodes them for the delta products itself, so nothing has to
 // run before it.  12 waves: 4 base waves stream W_base (bf16 MFMA against the
-// tokens read from LDS), 8 delta waves stream the users' packed rows (fp4 x fp8
-// block-scaled MFMA as in k_decode).
+// tokens read from LDS), each over a quarter of the columns; 8 delta waves stream
+// the users' packed rows (fp4 x fp8 block-scaled MFMA as in k_decode), each over
+// its 512-column units.  The delta waves first copy the tokens into LDS (each its
+// own units); one barrier then starts every wave's weight or sign-row stream.
 //
 // LDS: token row t (zeros past T and past d_in) at t * 2 dpad bytes; its 16-byte
 // chunk c sits at slot (c & ~15) | ((c ^ t) & 15), so the 16 tokens read at one
 // chunk index hit 16 distinct bank groups.  After the products the same memory
-// holds the partial tiles for the reduction.
+// holds the waves' partial tiles for the reduction.
 constexpr int kFusedBaseWaves = 4, kFusedDeltaWaves = 8;
 constexpr int kFusedWaves = kFusedBaseWaves + kFusedDeltaWaves;
-constexpr int kFusedSlices = 16;  // fixed K slices of the base product
-constexpr int kFusedRedBytes = (kFusedSlices + kFusedDeltaWaves) * 64 * 16;
-static_assert(kFusedBaseWaves * 4 == kDecodeMaxT, "each base wave stages four token rows");
-static_assert(kFusedSlices % kFusedBaseWaves == 0, "whole slices per base wave");
+constexpr int kFusedRedBytes = kFusedWaves * 64 * 16;
+constexpr int kFusedMaxPieces = (int)(kFusedMaxDpad / 512);  // 1 KB pieces of a token row
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -493,18 +493,29 @@ __device__ __forceinline__ uint32_t xslot(int t, int c, uint32_t rowb) {
 }  // namespace
 
 // Encodes the tokens' columns [512 u, 512 u + 512) from LDS into this lane's delta
-// operands (the layout k_decode_prep writes to x8 / e8): lane (m, G) takes, for chunk
-// q, the 16 columns 4n + 2(G & 1) + {0, 1} of 32-column blocks G / 2 and 2 + G / 2.
+// operands.  Product q of the unit takes, at k-group kb (32 k positions), the 32
+// columns 512 u + 128 kb + 32 q: the word of the sign rows that lane group kb loads
+// as its q-th word, so the sign operands need no exchange between lanes.  Lane (m, G)
+// encodes, for each product, the blocks at k-groups G / 2 and 2 + G / 2 (its two
+// 16-byte runs), taking the 16 columns 4 n + 2 (G & 1) + {0, 1} of each: byte b of a
+// run holds column 4 (b % 8) + 2 (G & 1) + b / 8, the column whose sign bit the fp4
+// operand puts at that k position.  Each block gets a power-of-two scale that puts
+// its largest |x| in [128, 256) (code 119 + E for a maximum in [2^(E-1), 2^E)),
+// hi = fp8(x') and lo = fp8(x' - hi) (both rounded to nearest even; x' - hi is exact).
 __device__ __forceinline__ void fused_encode(const char* smem, uint32_t rowb, int u, int lane,
                                              Unit& X) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef short i16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     const int m = lane & 15, G = lane >> 4, hh = G & 1;
-    uint32_t codes[2] = {0u, 0u};  // byte q: code of this lane's block in half p of chunk q
+    uint32_t codes[2] = {0u, 0u};  // byte q: code of this lane's block in half p of product q
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        int hq[8], lq[8];  // the chunk's two 32-byte operands
+        int hq[8], lq[8];  // the product's two 32-byte operands
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int c0 = 64 * u + 16 * q + 4 * ((G >> 1) + 2 * p);  // the block's first chunk
+            const int c0 = 64 * u + 16 * ((G >> 1) + 2 * p) + 4 * q;  // the block's first chunk
             uint32_t raw[8];  // raw[n]: columns 4n + 2hh (low half) and 4n + 2hh + 1 (high half)
 #pragma unroll
             for (int n2 = 0; n2 < 4; ++n2) {
@@ -512,54 +523,100 @@ __device__ __forceinline__ void fused_encode(const char* smem, uint32_t rowb, in
                 raw[2 * n2] = *(const uint32_t*)a;
                 raw[2 * n2 + 1] = *(const uint32_t*)(a + 8);
             }
-            float v[16];  // v[b]: the value for byte b of the 16-byte run
+            // the values as fp32 (exact): xf[2n] the low half of raw[n], xf[2n+1] the high
+            float xf[16];
 #pragma unroll
             for (int n = 0; n < 8; ++n) {
-                v[n] = bf16_lo(raw[n]);
-                v[8 + n] = bf16_hi(raw[n]);
+                xf[2 * n] = __uint_as_float(raw[n] << 16);
+                xf[2 * n + 1] = __uint_as_float(raw[n] & 0xFFFF0000u);
             }
-            float amax = 0.f;
+            // block maximum of |x|: on the bf16 bits of non-negative values the integer
+            // order is the numeric order
+            u16x2 mx2 = {0, 0};
 #pragma unroll
-            for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[c]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16));  // the other half of the block
-            // amax in [2^(E-1), 2^E): x' = x 2^(8-E) puts the block maximum in [128, 256)
-            int code = 127, sh = 0;
-            if (amax > 0.f) {
-                int E;
-                (void)frexpf(amax, &E);
-                code = 119 + E;
-                if (code < 0) code = 0;
-                sh = 127 - code;
+            for (int n = 0; n < 8; ++n)
+                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, raw[n] & 0x7FFF7FFFu));
+            uint32_t mx = mx2.x > mx2.y ? mx2.x : mx2.y;
+            const uint32_t mo = (uint32_t)__shfl_xor((int)mx, 16);  // the other half of the block
+            mx = mx > mo ? mx : mo;
+            const int eb = (int)(mx >> 7);  // biased exponent of the maximum
+            const int code = eb == 0 ? 127 : (eb > 8 ? eb - 7 : 1);
+            // the conversions divide by 2^(code - 127), i.e. multiply by 2^(127 - code)
+            const float sc = __uint_as_float((uint32_t)code << 23);
+            uint32_t P[4], L[4];  // P[i]: bytes (A_2i, B_2i, A_2i+1, B_2i+1) of hi, L[i] of lo
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // raw[2i] into the low word, raw[2i+1] into the high word (constant selectors;
+                // the first conversion's other word is overwritten by the second)
+                const uint32_t r0 = raw[2 * i], r1 = raw[2 * i + 1];
+                i16x2 ph = __builtin_bit_cast(i16x2, r0);  // (its dead registers as the
+                                                            // conversions' untouched halves)
+                ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(ph, __builtin_bit_cast(bf16x2, r0),
+                                                               sc, false);
+                ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(ph, __builtin_bit_cast(bf16x2, r1),
+                                                               sc, true);
+                // hi back in the input's scale (exact), then the exact residuals
+                const f32x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(
+                    __builtin_bit_cast(uint32_t, ph), sc, false);
+                const f32x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(
+                    __builtin_bit_cast(uint32_t, ph), sc, true);
+                i16x2 pl = __builtin_bit_cast(i16x2, r1);
+                pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, xf[4 * i] - h0.x,
+                                                              xf[4 * i + 1] - h0.y, sc, false);
+                pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, xf[4 * i + 2] - h1.x,
+                                                              xf[4 * i + 3] - h1.y, sc, true);
+                P[i] = __builtin_bit_cast(uint32_t, ph);
+                L[i] = __builtin_bit_cast(uint32_t, pl);
             }
-            const float mul = __uint_as_float((uint32_t)(sh + 127) << 23);  // 2^sh, a normal
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                float s[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[i] = v[4 * d + i] * mul;
-                int h = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
-                h = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], h, true);
-                const float r0 = s[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0);
-                const float r1 = s[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1);
-                const float r2 = s[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2);
-                const float r3 = s[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3);
-                int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-                l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
-                asm volatile("" : "+v"(h), "+v"(l));  // converted here, not next to the MFMAs
-                hq[4 * p + d] = h;
-                lq[4 * p + d] = l;
-            }
+            // bytes 0..7 of the run: the low halves (A), bytes 8..15: the high halves (B)
+            hq[4 * p + 0] = (int)__builtin_amdgcn_perm(P[1], P[0], 0x06040200u);
+            hq[4 * p + 1] = (int)__builtin_amdgcn_perm(P[3], P[2], 0x06040200u);
+            hq[4 * p + 2] = (int)__builtin_amdgcn_perm(P[1], P[0], 0x07050301u);
+            hq[4 * p + 3] = (int)__builtin_amdgcn_perm(P[3], P[2], 0x07050301u);
+            lq[4 * p + 0] = (int)__builtin_amdgcn_perm(L[1], L[0], 0x06040200u);
+            lq[4 * p + 1] = (int)__builtin_amdgcn_perm(L[3], L[2], 0x06040200u);
+            lq[4 * p + 2] = (int)__builtin_amdgcn_perm(L[1], L[0], 0x07050301u);
+            lq[4 * p + 3] = (int)__builtin_amdgcn_perm(L[3], L[2], 0x07050301u);
+            asm volatile("" : "+v"(hq[4 * p]), "+v"(hq[4 * p + 1]), "+v"(hq[4 * p + 2]),
+                              "+v"(hq[4 * p + 3]), "+v"(lq[4 * p]), "+v"(lq[4 * p + 1]),
+                              "+v"(lq[4 * p + 2]), "+v"(lq[4 * p + 3]));
             codes[p] |= (uint32_t)code << (8 * q);
             __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded register use
         }
         X.hi[q] = i32x8{hq[0], hq[1], hq[2], hq[3], hq[4], hq[5], hq[6], hq[7]};
         X.lo[q] = i32x8{lq[0], lq[1], lq[2], lq[3], lq[4], lq[5], lq[6], lq[7]};
     }
-    // scale lane (m, kb) takes block kb of token m: computed by lane m + 32 (kb & 1), half kb / 2
+    // scale lane (m, kb) takes block kb of token m: encoded by lane m + 32 (kb & 1), half kb / 2
     const int src = m + 32 * (G & 1);
     const uint32_t c0 = (uint32_t)__shfl((int)codes[0], src);
     const uint32_t c1 = (uint32_t)__shfl((int)codes[1], src);
     X.e = (G >> 1) ? c1 : c0;
+}
+
+// Copies 1 KB pieces j0, j0 + step, ... (n of them, n <= NMAX) of every token row
+// (piece j: columns [512 j, +512)) into LDS; all arguments wave-uniform.  The rows are
+// taken in an order rotated by the block's place on its XCD, so the blocks of one XCD,
+// which all copy the same activations, do not queue on the same lines at once.
+template <int NMAX>
+__device__ __forceinline__ void fused_stage(char* smem, uint32_t rowb, __amdgpu_buffer_rsrc_t xr,
+                                            int T, int64_t d_in, int j0, int n, int step,
+                                            int lane) {
+    const int rot = (int)((blockIdx.x >> 3) & 15);
+#pragma unroll
+    for (int tt = 0; tt < kDecodeMaxT; ++tt) {
+        const int t = (tt + rot) & 15;
+        const int cl = (lane & 48) | ((lane & 15) ^ t);
+#pragma unroll
+        for (int k = 0; k < NMAX; ++k) {
+            if (k < n) {  // uniform
+                const int j = j0 + step * k;
+                const int c = 64 * j + cl;
+                const bool ok = t < T && (int64_t)c * 8 < d_in;
+                lds_copy16(xr, smem + t * rowb + 1024 * j,
+                           ok ? (uint32_t)(((int64_t)t * d_in + 8 * c) * 2) : kOOB);
+            }
+        }
+    }
 }
 
 template <int MODE>
@@ -575,31 +632,23 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
     const uint32_t rowb = 2u * (uint32_t)dpad;
     const int64_t r0 = (int64_t)blockIdx.x * 16;
     const int64_t rowA = r0 + m < d_out ? r0 + m : d_out - 1;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)T * (uint64_t)d_in * 2);
+    f32x4* red = (f32x4*)smem;  // after the products: [12 waves][64] partial tiles
+
     if (wv < kFusedBaseWaves) {
-        // ---- base: step pairs (64 columns, one 128-byte line of each row) form 16 fixed
-        // slices (slice s = pairs s, s + 16, ...), each summed in order; wave wv takes slices
-        // wv, wv + 4, wv + 8, wv + 12.  The partition, and so the rounding, does not depend
-        // on the batch's users.  Ring of 16 W loads; the tokens come from LDS.
-        constexpr int NSL = kFusedSlices / kFusedBaseWaves;
-        f32x4 acc[NSL];  // one per slice of this wave
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int nsteps = (int)(d_in / 32);  // even
-        const int ipsl = 2 * ((nsteps / 2 + kFusedSlices - 1) / kFusedSlices);  // items per slice
-        const int total = NSL * ipsl;
+        // ---- base: wave wv takes the steps (32 columns) of columns [wv Kb, (wv+1) Kb),
+        // Kb = dpad / 4, in order, into one accumulator; the partition does not depend on
+        // the batch's users.  Ring of 16 W loads; the tokens come from LDS.
+        const int spw = dpad / 128;  // steps per base wave (a multiple of 4)
+        const int st0 = wv * spw;
+        const int nsteps = (int)(d_in / 32);
         const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint64_t)d_out * (uint64_t)d_in * 2);
         const uint32_t woff = (uint32_t)((rowA * d_in + 8 * g) * 2);
         constexpr int R = 16;
-        int ls = wv, lk = 0;  // slice and item of the next load
         auto load = [&](int i) {
-            const int st = 2 * (ls + kFusedSlices * (lk >> 1)) + (lk & 1);
-            const bool ok = i < total && st < nsteps;
-            const u32x4 a = buf_load16(wr, ok ? woff + (uint32_t)(st * 64) : kOOB);
-            if (++lk == ipsl) {
-                lk = 0;
-                ls += kFusedBaseWaves;
-            }
-            return a;
+            const int st = st0 + i;
+            const bool ok = i < spw && st < nsteps;
+            return buf_load16(wr, ok ? woff + (uint32_t)(st * 64) : kOOB);
         };
         u32x4 ring[R];
 #pragma unroll
@@ -607,58 +656,32 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
             ring[r] = load(r);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // ---- stage token rows 4 wv .. 4 wv + 3 in LDS (1 KB of a row per copy), behind
-        // the ring's first loads of W
-        {
-            const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)T * (uint64_t)d_in * 2);
-            const int npc = dpad / 512;  // 1 KB pieces per row
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * wv + r;
-                const int cl = (lane & 48) | ((lane & 15) ^ t);
-#pragma unroll
-                for (int j = 0; j < (int)(kFusedMaxDpad / 512); ++j) {
-                    if (j < npc) {  // uniform
-                        const int c = 64 * j + cl;
-                        const bool ok = t < T && (int64_t)c * 8 < d_in;
-                        lds_copy16(xr, smem + t * rowb + 1024 * j,
-                                   ok ? (uint32_t)(((int64_t)t * d_in + 8 * c) * 2) : kOOB);
-                    }
-                }
-            }
-        }
-        BD_WAIT_VMCNT(0);  // this wave's token copies have landed (and the ring's first loads)
-        __builtin_amdgcn_s_barrier();
-        int cs = 0, ck = 0;  // slice index (0 .. NSL-1) and item of the product being summed
-        f32x4 cur = {0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_s_barrier();  // the tokens are in LDS
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // token operand of step i (zero past the wave's steps), read one step ahead
+        auto tok = [&](int i) {
+            u32x4 b = {0u, 0u, 0u, 0u};
+            if (i < spw)  // uniform
+                b = *(const u32x4*)(smem + xslot(m, 4 * (st0 + i) + g, rowb));
+            return b;
+        };
+        u32x4 bnext = tok(0);
         int i0 = 0;
-        do {  // total > 0 (d_in >= 64): the ring is always consumed, so its loads stay above
+        do {  // spw > 0: the ring is always consumed, so its loads stay above the barrier
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int i = i0 + r;
-                const int st = 2 * (wv + kFusedBaseWaves * cs + kFusedSlices * (ck >> 1)) + (ck & 1);
-                u32x4 b = {0u, 0u, 0u, 0u};
-                if (i < total && st < nsteps)  // uniform
-                    b = *(const u32x4*)(smem + xslot(m, 4 * st + g, rowb));
-                cur = mfma_bf16(ring[r], b, cur);
+                const u32x4 b = bnext;
+                bnext = tok(i + 1);
+                acc = mfma_bf16(ring[r], b, acc);
                 ring[r] = load(i + R);
-                if (++ck == ipsl) {  // uniform: the slice is complete
-#pragma unroll
-                    for (int s = 0; s < NSL; ++s)
-                        if (s == cs) acc[s] = cur;
-                    cur = f32x4{0.f, 0.f, 0.f, 0.f};
-                    ck = 0;
-                    ++cs;
-                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             i0 += R;
-        } while (i0 < total);
-        // the token rows are no longer read: the slices' partial tiles go to LDS
+        } while (i0 < spw);
+        // the token rows are no longer read: the partial tiles go to LDS
         __syncthreads();
-        f32x4* red = (f32x4*)smem;  // [16 base slices][64], then [8 delta waves][64]
-#pragma unroll
-        for (int s = 0; s < NSL; ++s) red[(wv + kFusedBaseWaves * s) * 64 + lane] = acc[s];
+        red[wv * 64 + lane] = acc;
         __syncthreads();
         return;
     }
@@ -666,8 +689,19 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
     // ---- delta: 512-column units u = wd, wd + 8, ...; every user of the batch
     __builtin_amdgcn_s_setprio(3);
     const int wd = wv - kFusedBaseWaves;
-    // the batch's users, in order of first appearance (lane j of utab: the j-th)
-    const int uid = lane < T ? ids[lane] : -1;
+    const int nunit = dpad / 512;
+    const int nuw = wd < nunit ? (nunit - wd + kFusedDeltaWaves - 1) / kFusedDeltaWaves : 0;
+    // the batch's user ids (scalar loads: their wait does not wait for the copies below)
+    int sid[kDecodeMaxT];
+#pragma unroll
+    for (int j = 0; j < kDecodeMaxT; ++j) sid[j] = ids[j < T ? j : T - 1];  // in bounds
+    fused_stage<(kFusedMaxPieces + kFusedDeltaWaves - 1) / kFusedDeltaWaves>(
+        smem, rowb, xr, T, d_in, wd, nuw, kFusedDeltaWaves, lane);
+
+    int uid = -1;
+#pragma unroll
+    for (int j = 0; j < kDecodeMaxT; ++j) uid = lane == j && j < T ? sid[j] : uid;
+    // the users in order of first appearance (lane j of utab: the j-th)
     const bool valid = lane < T && uid >= 0 && uid < U;
     bool dup = false;
 #pragma unroll
@@ -687,26 +721,13 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
     }
     const int tok_user = __shfl(valid ? uid : -1, m);  // user of this lane's token column
     uint32_t sraw[4] = {0u, 0u, 0u, 0u};  // epilogue wave: the scales of its outputs (bits)
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (wd == 0) {
         if (blockIdx.x == 0) {
             const bool bad = lane < T && !valid && uid != -1;
             const bool anybad = __ballot(bad) != 0ull;
             if (lane == 0) status[0] = anybad ? ST_USER_ID : 0u;
         }
-        if (tok_user >= 0 && m < T) {  // the epilogue's scales, loaded early, used at the end
-            const int64_t o = r0 + 4 * g;
-            const int64_t s0 = (int64_t)tok_user * per_user;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t i = s0 + (MODE == BD_SCALE_MATRIX ? 0 : (o + e < d_out ? o + e : d_out - 1));
-                sraw[e] = sdtype == BD_F16 ? (uint32_t)((const uint16_t*)scales)[i]
-                                           : ((const uint32_t*)scales)[i];
-            }
-        }
     }
-    const int nunit = dpad / 512;
-    const int nuw = wd < nunit ? (nunit - wd + kFusedDeltaWaves - 1) / kFusedDeltaWaves : 0;
     constexpr int RB = 8;
     const int nsegR = (nseg + RB - 1) / RB * RB;  // users padded: item (k, j) sits in slot j % RB
     const int64_t bank_row = d_in / 8;
@@ -715,17 +736,23 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
     uint32_t kmask, kone;  // operand constants in registers (gfx9 VOP3 takes no literal)
     asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
     asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
+    // this lane's offset in a user's bank for the wave's units (two at most)
+    uint32_t uoff[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = wd + kFusedDeltaWaves * k;
+        uoff[k] = (int64_t)u * 512 + 128 * g < d_in ? brow + (uint32_t)(u * 64) : kOOB;
+    }
     int lk = 0, lj = 0;  // unit (of this wave) and user slot of the next load
-    // 16 bytes of user lj's row: columns [512u + 128g, +128) (4 words, one per chunk);
-    // always issued (a zero load for padding and past the end) so every wait is exact
+    // 16 bytes of user lj's row: columns [512u + 128g, +128) (a word for each of the unit's
+    // four products); always issued (a zero load for padding and past the end) so every
+    // wait is exact
     auto load_bits = [&]() {
         const bool ok = lk < nuw && lj < nseg;  // uniform
         const int usr = __builtin_amdgcn_readlane(utab, ok ? lj : 0);
-        const int u = wd + kFusedDeltaWaves * lk;
         const __amdgpu_buffer_rsrc_t br =
             make_rsrc((const char*)signs + (uint64_t)(uint32_t)usr * user_bytes, user_bytes);
-        const bool in = ok && (int64_t)u * 512 + 128 * g < d_in;
-        const u32x4 v = buf_load16(br, in ? brow + (uint32_t)(u * 64) : kOOB);
+        const u32x4 v = buf_load16(br, ok ? (lk == 0 ? uoff[0] : uoff[1]) : kOOB);
         if (++lj == nsegR) {
             lj = 0;
             ++lk;
@@ -738,56 +765,77 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
         ring[r] = load_bits();
         __builtin_amdgcn_sched_barrier(0);
     }
-    BD_WAIT_VMCNT(RB);  // ids and scales (older than the ring) have landed
-    __builtin_amdgcn_s_barrier();  // the tokens are in LDS
+    BD_WAIT_VMCNT(RB);  // this wave's token copies have landed (the ring loads are younger)
+    __builtin_amdgcn_s_barrier();  // and every delta wave's
+    if (wd == 0 && tok_user >= 0 && m < T) {  // the epilogue's scales, used at the end
+        const int64_t o = r0 + 4 * g;
+        const int64_t s0 = (int64_t)tok_user * per_user;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i =
+                s0 + (MODE == BD_SCALE_MATRIX ? 0 : (o + e < d_out ? o + e : d_out - 1));
+            sraw[e] = sdtype == BD_F16 ? (uint32_t)((const uint16_t*)scales)[i]
+                                       : ((const uint32_t*)scales)[i];
+        }
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     Unit X;
-    for (int k = 0; k < nuw && nseg > 0; ++k) {
+    // do-while loops: the ring is consumed on every path (its loads are never sunk
+    // below the wait above, whatever nuw and nseg are)
+    int k = 0;
+    do {
         // encode this unit's tokens while its first users' rows are in flight
-        fused_encode(smem, rowb, wd + kFusedDeltaWaves * k, lane, X);
-        for (int j0 = 0; j0 < nsegR; j0 += RB) {
+        if (k < nuw && nseg > 0) fused_encode(smem, rowb, wd + kFusedDeltaWaves * k, lane, X);
+        int j0 = 0;
+        do {
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 const int j = j0 + r;
                 const u32x4 D = ring[r];
-                // 4x4 transpose over the lane groups: lane group g gets word g of every
-                // chunk (done for every slot so each load is consumed at the same point)
-                auto s32a = __builtin_amdgcn_permlane32_swap(D.x, D.z, false, false);
-                auto s32b = __builtin_amdgcn_permlane32_swap(D.y, D.w, false, false);
-                auto s16a = __builtin_amdgcn_permlane16_swap(s32a[0], s32b[0], false, false);
-                auto s16b = __builtin_amdgcn_permlane16_swap(s32a[1], s32b[1], false, false);
-                const uint32_t wd4[4] = {s16a[0], s16a[1], s16b[0], s16b[1]};
-                if (j < nseg) {  // uniform
+                // the fp4 operands of the unit's four products: word q of this lane's
+                // load is k-group g of product q.  Built on every path, so each load is
+                // consumed at the same point; only the products are skipped.
+                u32x4 A[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = D[q];
+                    A[q].x = ((wq << 3) & kmask) | kone;
+                    A[q].y = ((wq << 2) & kmask) | kone;
+                    A[q].z = ((wq << 1) & kmask) | kone;
+                    A[q].w = (wq & kmask) | kone;
+                }
+                if (k < nuw && j < nseg) {  // uniform
                     const int usr = __builtin_amdgcn_readlane(utab, j);
                     const uint32_t sc = tok_user == usr ? X.e : 0u;
-#define BD_CHUNK(I)                                                                   \
-    {                                                                                 \
-        const uint32_t wq = wd4[I];                                                   \
-        u32x4 A;                                                                      \
-        A.x = ((wq << 3) & kmask) | kone;                                             \
-        A.y = ((wq << 2) & kmask) | kone;                                             \
-        A.z = ((wq << 1) & kmask) | kone;                                             \
-        A.w = (wq & kmask) | kone;                                                    \
-        acc = mfma_f4f8<I>(A, X.hi[I], acc, sc);                                      \
-        acc = mfma_f4f8<I>(A, X.lo[I], acc, sc);                                      \
-    }
-                    BD_CHUNK(0) BD_CHUNK(1) BD_CHUNK(2) BD_CHUNK(3)
-#undef BD_CHUNK
+                    acc = mfma_f4f8<0>(A[0], X.hi[0], acc, sc);
+                    acc = mfma_f4f8<0>(A[0], X.lo[0], acc, sc);
+                    acc = mfma_f4f8<1>(A[1], X.hi[1], acc, sc);
+                    acc = mfma_f4f8<1>(A[1], X.lo[1], acc, sc);
+                    acc = mfma_f4f8<2>(A[2], X.hi[2], acc, sc);
+                    acc = mfma_f4f8<2>(A[2], X.lo[2], acc, sc);
+                    acc = mfma_f4f8<3>(A[3], X.hi[3], acc, sc);
+                    acc = mfma_f4f8<3>(A[3], X.lo[3], acc, sc);
                 }
                 ring[r] = load_bits();
                 __builtin_amdgcn_sched_barrier(0);
             }
-        }
-    }
+            j0 += RB;
+        } while (j0 < nsegR);
+        ++k;
+    } while (k < nuw);
+    // the ring's last loads (past the end) land: no load of this wave stays in flight,
+    // so the base waves' code, which the compiler may lay out after a join with this
+    // path, starts without waits for it
+    BD_WAIT_VMCNT(0);
 
     // ---- reduction: the token rows are no longer read; partial tiles go to LDS
     __syncthreads();
-    f32x4* red = (f32x4*)smem;
-    red[(kFusedSlices + wd) * 64 + lane] = acc;
+    red[wv * 64 + lane] = acc;
     __syncthreads();
-    if (wv != kFusedBaseWaves) return;  // the first delta wave holds the factors
+    if (wd != 0) return;  // the first delta wave holds the factors
     f32x4 vb = {0.f, 0.f, 0.f, 0.f}, vd = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < kFusedSlices; ++q) vb += red[q * 64 + lane];
-    for (int q = 0; q < kFusedDeltaWaves; ++q) vd += red[(kFusedSlices + q) * 64 + lane];
+    for (int q = 0; q < kFusedBaseWaves; ++q) vb += red[q * 64 + lane];
+    for (int q = kFusedBaseWaves; q < kFusedWaves; ++q) vd += red[q * 64 + lane];
     if (m >= T) return;
     const int64_t o = r0 + 4 * g;
     f32x4 out;
