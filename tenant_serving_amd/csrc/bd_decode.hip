@@ -5,7 +5,12 @@
 // base product per batch, each request adds its user's 1-bit delta product,
 // the bits cross HBM packed and are expanded on chip).
 //
-// Two launches:
+// One launch (k_decode_fused, MATRIX and ROW scales, rows of up to 5120 columns):
+//   every block stages the batch's tokens in LDS and encodes them itself, as two
+//   fp6 e2m3 parts per 32-column block (below); the delta products run the
+//   block-scaled MFMA with fp4 signs and fp6 tokens.
+//
+// Two launches (any row width, and COL scales):
 //   k_decode_prep  sorts the (<= 16) tokens by user in one wave and encodes X
 //                  for the delta products: every 32-column block of a token is
 //                  scaled by a power of two (an MX block scale) and split into
@@ -38,6 +43,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
 
 constexpr int kDecodeWaves = 16;
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past num_records: the load returns 0
@@ -462,8 +468,10 @@ k_decode(const uint16_t* __restrict__ x, int T, int64_t d_in, int64_t dpad,
 // tokens in LDS and encodes them for the delta products itself, so nothing has to
 // run before it.  12 waves: 4 base waves stream W_base (bf16 MFMA against the
 // tokens read from LDS), each over a quarter of the columns; 8 delta waves stream
-// the users' packed rows (fp4 x fp8 block-scaled MFMA as in k_decode), each over
-// its 512-column units.  The delta waves first copy the tokens into LDS (each its
+// the users' packed rows (block-scaled MFMA, fp4 signs x fp6 e2m3 tokens: the fp6
+// operand runs at 20 cycles per 16x16x128 product against 32 for fp8, and its
+// 32-wide conversions take one instruction per block), each over its 512-column
+// units.  The delta waves first copy the tokens into LDS (each its
 // own units); one barrier then starts every wave's weight or sign-row stream.
 //
 // LDS: token row t (zeros past T and past d_in) at t * 2 dpad bytes; its 16-byte
@@ -492,105 +500,104 @@ __device__ __forceinline__ uint32_t xslot(int t, int c, uint32_t rowb) {
 
 }  // namespace
 
-// Encodes the tokens' columns [512 u, 512 u + 512) from LDS into this lane's delta
-// operands.  Product q of the unit takes, at k-group kb (32 k positions), the 32
-// columns 512 u + 128 kb + 32 q: the word of the sign rows that lane group kb loads
-// as its q-th word, so the sign operands need no exchange between lanes.  Lane (m, G)
-// encodes, for each product, the blocks at k-groups G / 2 and 2 + G / 2 (its two
-// 16-byte runs), taking the 16 columns 4 n + 2 (G & 1) + {0, 1} of each: byte b of a
-// run holds column 4 (b % 8) + 2 (G & 1) + b / 8, the column whose sign bit the fp4
-// operand puts at that k position.  Each block gets a power-of-two scale that puts
-// its largest |x| in [128, 256) (code 119 + E for a maximum in [2^(E-1), 2^E)),
-// hi = fp8(x') and lo = fp8(x' - hi) (both rounded to nearest even; x' - hi is exact).
-__device__ __forceinline__ void fused_encode(const char* smem, uint32_t rowb, int u, int lane,
-                                             Unit& X) {
+// The tokens' delta operands for one 512-column unit, as fp6 e2m3 B operands: in
+// the block-scaled 16x16x128 MFMA with 6-bit B values, lane (n, kb) supplies the 32
+// k positions of k-block kb for token column n, packed in 6 dwords, and the scale of
+// that block.
+struct Unit6 {
+    i32x6 hi[4], lo[4];
+    uint32_t ehi, elo;  // byte q: scale codes of product q's hi and lo operands
+};
+
+// D += A(fp4, 16 x 128) * B(fp6 e2m3, 128 x 16) * 2^(scale_b - 127), scale_b = byte SEL of sc.
+template <int SEL>
+__device__ __forceinline__ f32x4 mfma_f4f6(u32x4 a, i32x6 b, f32x4 c, uint32_t sc) {
+    const i32x8 a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const i32x8 b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, 4, 5, -1, -1);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 2, 0, 127, SEL, (int)sc);
+}
+
+// Encodes, for lane (m, G), product q of unit u: the 32 columns 512 u + 128 G + 32 q
+// of token m (the LDS chunks c0 .. c0 + 3, c0 = 64 u + 16 G + 4 q), k position
+// j = 8 d + n holding column 4 n + d, the column whose sign bit the fp4 operand puts
+// there.  With E the exponent of the block's largest |x| (in [2^E, 2^(E+1))) and
+// s = 2^(E-1): hi = fp6(x / s) and lo = fp6((x - hi) / (s / 32)), both rounded to
+// nearest even; hi + lo equals x for every |x| >= s and is within 2^-10 of the block
+// maximum otherwise.  kone_lo / kone_hi: the bf16 pairs (1, 0) and (0, 1).
+__device__ __forceinline__ void encode6(const char* smem, uint32_t rowb, int c0, int m,
+                                        uint32_t kone_lo, uint32_t kone_hi, i32x6& h, i32x6& l,
+                                        uint32_t& code_hi, uint32_t& code_lo) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    typedef short i16x2 __attribute__((ext_vector_type(2)));
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
+    typedef float f32x32 __attribute__((ext_vector_type(32)));
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    const int m = lane & 15, G = lane >> 4, hh = G & 1;
-    uint32_t codes[2] = {0u, 0u};  // byte q: code of this lane's block in half p of product q
+    typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
+    uint32_t R[16];  // R[p]: columns 2p (low half) and 2p + 1 (high half)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 v = *(const u32x4*)(smem + xslot(m, c0 + i, rowb));
+        R[4 * i] = v.x;
+        R[4 * i + 1] = v.y;
+        R[4 * i + 2] = v.z;
+        R[4 * i + 3] = v.w;
+    }
+    // block maximum of |x|: on the bf16 bits of non-negative values the integer
+    // order is the numeric order
+    u16x2 mx2 = {0, 0};
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, R[p] & 0x7FFF7FFFu));
+    const uint32_t eb = (uint32_t)(mx2.x > mx2.y ? mx2.x : mx2.y) >> 7;  // biased exponent
+    // s = 2^(eb - 128): code eb - 1; blocks below 2^-120 (zeros) take s = 1
+    code_hi = eb >= 7u && eb <= 255u ? eb - 1u : 127u;
+    code_lo = code_hi - 5u;
+    const float sh = __uint_as_float(code_hi << 23), sl = __uint_as_float(code_lo << 23);
+    // the values in k order: pair i = (column c, column c + 4), c = 8 (i % 4) + i / 4
+    // (kept as scalars: each pair also feeds a dot product below)
+    uint32_t V[16];
+    u32x16 Vv;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int a = i & 3, d = i >> 2;
+        const uint32_t r0 = R[4 * a + (d >> 1)], r1 = R[4 * a + (d >> 1) + 2];
+        V[i] = __builtin_amdgcn_perm(r1, r0, (d & 1) ? 0x07060302u : 0x05040100u);
+        Vv[i] = V[i];
+    }
+    h = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32, Vv), sh);
+    // -hi, exact: the 32 fields with their sign bits (bit 6j + 5) flipped, widened
+    const i32x6 sgn = {(int)0x20820820u, (int)0x08208208u, (int)0x82082082u,
+                       (int)0x20820820u, (int)0x08208208u, (int)0x82082082u};
+    f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(h ^ sgn, sh);
+    // the exact residuals x - hi (the bf16 dot product picks one half of the pair),
+    // accumulated onto -hi in place; each has at most 4 significant bits, so its bf16
+    // form (the upper half of the fp32 word) is exact
+    u32x16 W;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const bf16x2 pr = __builtin_bit_cast(bf16x2, V[i]);
+        r[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, kone_lo),
+                                                   r[2 * i], false);
+        r[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, kone_hi),
+                                                       r[2 * i + 1], false);
+        W[i] = __builtin_amdgcn_perm(__float_as_uint(r[2 * i + 1]), __float_as_uint(r[2 * i]),
+                                     0x07060302u);
+    }
+    l = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32, W), sl);
+}
+
+__device__ __forceinline__ void fused_encode6(const char* smem, uint32_t rowb, int u, int lane,
+                                              uint32_t kone_lo, uint32_t kone_hi, Unit6& X) {
+    const int m = lane & 15, G = lane >> 4;
+    X.ehi = 0u;
+    X.elo = 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        int hq[8], lq[8];  // the product's two 32-byte operands
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int c0 = 64 * u + 16 * ((G >> 1) + 2 * p) + 4 * q;  // the block's first chunk
-            uint32_t raw[8];  // raw[n]: columns 4n + 2hh (low half) and 4n + 2hh + 1 (high half)
-#pragma unroll
-            for (int n2 = 0; n2 < 4; ++n2) {
-                const char* a = smem + xslot(m, c0 + n2, rowb) + 4 * hh;
-                raw[2 * n2] = *(const uint32_t*)a;
-                raw[2 * n2 + 1] = *(const uint32_t*)(a + 8);
-            }
-            // the values as fp32 (exact): xf[2n] the low half of raw[n], xf[2n+1] the high
-            float xf[16];
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                xf[2 * n] = __uint_as_float(raw[n] << 16);
-                xf[2 * n + 1] = __uint_as_float(raw[n] & 0xFFFF0000u);
-            }
-            // block maximum of |x|: on the bf16 bits of non-negative values the integer
-            // order is the numeric order
-            u16x2 mx2 = {0, 0};
-#pragma unroll
-            for (int n = 0; n < 8; ++n)
-                mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, raw[n] & 0x7FFF7FFFu));
-            uint32_t mx = mx2.x > mx2.y ? mx2.x : mx2.y;
-            const uint32_t mo = (uint32_t)__shfl_xor((int)mx, 16);  // the other half of the block
-            mx = mx > mo ? mx : mo;
-            const int eb = (int)(mx >> 7);  // biased exponent of the maximum
-            const int code = eb == 0 ? 127 : (eb > 8 ? eb - 7 : 1);
-            // the conversions divide by 2^(code - 127), i.e. multiply by 2^(127 - code)
-            const float sc = __uint_as_float((uint32_t)code << 23);
-            uint32_t P[4], L[4];  // P[i]: bytes (A_2i, B_2i, A_2i+1, B_2i+1) of hi, L[i] of lo
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // raw[2i] into the low word, raw[2i+1] into the high word (constant selectors;
-                // the first conversion's other word is overwritten by the second)
-                const uint32_t r0 = raw[2 * i], r1 = raw[2 * i + 1];
-                i16x2 ph = __builtin_bit_cast(i16x2, r0);  // (its dead registers as the
-                                                            // conversions' untouched halves)
-                ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(ph, __builtin_bit_cast(bf16x2, r0),
-                                                               sc, false);
-                ph = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(ph, __builtin_bit_cast(bf16x2, r1),
-                                                               sc, true);
-                // hi back in the input's scale (exact), then the exact residuals
-                const f32x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(
-                    __builtin_bit_cast(uint32_t, ph), sc, false);
-                const f32x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(
-                    __builtin_bit_cast(uint32_t, ph), sc, true);
-                i16x2 pl = __builtin_bit_cast(i16x2, r1);
-                pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, xf[4 * i] - h0.x,
-                                                              xf[4 * i + 1] - h0.y, sc, false);
-                pl = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pl, xf[4 * i + 2] - h1.x,
-                                                              xf[4 * i + 3] - h1.y, sc, true);
-                P[i] = __builtin_bit_cast(uint32_t, ph);
-                L[i] = __builtin_bit_cast(uint32_t, pl);
-            }
-            // bytes 0..7 of the run: the low halves (A), bytes 8..15: the high halves (B)
-            hq[4 * p + 0] = (int)__builtin_amdgcn_perm(P[1], P[0], 0x06040200u);
-            hq[4 * p + 1] = (int)__builtin_amdgcn_perm(P[3], P[2], 0x06040200u);
-            hq[4 * p + 2] = (int)__builtin_amdgcn_perm(P[1], P[0], 0x07050301u);
-            hq[4 * p + 3] = (int)__builtin_amdgcn_perm(P[3], P[2], 0x07050301u);
-            lq[4 * p + 0] = (int)__builtin_amdgcn_perm(L[1], L[0], 0x06040200u);
-            lq[4 * p + 1] = (int)__builtin_amdgcn_perm(L[3], L[2], 0x06040200u);
-            lq[4 * p + 2] = (int)__builtin_amdgcn_perm(L[1], L[0], 0x07050301u);
-            lq[4 * p + 3] = (int)__builtin_amdgcn_perm(L[3], L[2], 0x07050301u);
-            asm volatile("" : "+v"(hq[4 * p]), "+v"(hq[4 * p + 1]), "+v"(hq[4 * p + 2]),
-                              "+v"(hq[4 * p + 3]), "+v"(lq[4 * p]), "+v"(lq[4 * p + 1]),
-                              "+v"(lq[4 * p + 2]), "+v"(lq[4 * p + 3]));
-            codes[p] |= (uint32_t)code << (8 * q);
-            __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded register use
-        }
-        X.hi[q] = i32x8{hq[0], hq[1], hq[2], hq[3], hq[4], hq[5], hq[6], hq[7]};
-        X.lo[q] = i32x8{lq[0], lq[1], lq[2], lq[3], lq[4], lq[5], lq[6], lq[7]};
+        uint32_t ch, cl;
+        encode6(smem, rowb, 64 * u + 16 * G + 4 * q, m, kone_lo, kone_hi, X.hi[q], X.lo[q], ch, cl);
+        X.ehi |= ch << (8 * q);
+        X.elo |= cl << (8 * q);
+        __builtin_amdgcn_sched_barrier(0);  // one product at a time: bounded register use
     }
-    // scale lane (m, kb) takes block kb of token m: encoded by lane m + 32 (kb & 1), half kb / 2
-    const int src = m + 32 * (G & 1);
-    const uint32_t c0 = (uint32_t)__shfl((int)codes[0], src);
-    const uint32_t c1 = (uint32_t)__shfl((int)codes[1], src);
-    X.e = (G >> 1) ? c1 : c0;
 }
 
 // Copies 1 KB pieces j0, j0 + step, ... (n of them, n <= NMAX) of every token row
@@ -736,6 +743,9 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
     uint32_t kmask, kone;  // operand constants in registers (gfx9 VOP3 takes no literal)
     asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
     asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
+    uint32_t kb_lo, kb_hi;  // the bf16 pairs (1, 0) and (0, 1), in registers as well
+    asm volatile("v_mov_b32 %0, 0x3f80" : "=v"(kb_lo));
+    asm volatile("v_mov_b32 %0, 0x3f800000" : "=v"(kb_hi));
     // this lane's offset in a user's bank for the wave's units (two at most)
     uint32_t uoff[2];
 #pragma unroll
@@ -779,13 +789,14 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
         }
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    Unit X;
+    Unit6 X;
     // do-while loops: the ring is consumed on every path (its loads are never sunk
     // below the wait above, whatever nuw and nseg are)
     int k = 0;
     do {
         // encode this unit's tokens while its first users' rows are in flight
-        if (k < nuw && nseg > 0) fused_encode(smem, rowb, wd + kFusedDeltaWaves * k, lane, X);
+        if (k < nuw && nseg > 0)
+            fused_encode6(smem, rowb, wd + kFusedDeltaWaves * k, lane, kb_lo, kb_hi, X);
         int j0 = 0;
         do {
 #pragma unroll
@@ -806,15 +817,16 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
                 }
                 if (k < nuw && j < nseg) {  // uniform
                     const int usr = __builtin_amdgcn_readlane(utab, j);
-                    const uint32_t sc = tok_user == usr ? X.e : 0u;
-                    acc = mfma_f4f8<0>(A[0], X.hi[0], acc, sc);
-                    acc = mfma_f4f8<0>(A[0], X.lo[0], acc, sc);
-                    acc = mfma_f4f8<1>(A[1], X.hi[1], acc, sc);
-                    acc = mfma_f4f8<1>(A[1], X.lo[1], acc, sc);
-                    acc = mfma_f4f8<2>(A[2], X.hi[2], acc, sc);
-                    acc = mfma_f4f8<2>(A[2], X.lo[2], acc, sc);
-                    acc = mfma_f4f8<3>(A[3], X.hi[3], acc, sc);
-                    acc = mfma_f4f8<3>(A[3], X.lo[3], acc, sc);
+                    const bool mine = tok_user == usr;
+                    const uint32_t sh = mine ? X.ehi : 0u, sl = mine ? X.elo : 0u;
+                    acc = mfma_f4f6<0>(A[0], X.hi[0], acc, sh);
+                    acc = mfma_f4f6<0>(A[0], X.lo[0], acc, sl);
+                    acc = mfma_f4f6<1>(A[1], X.hi[1], acc, sh);
+                    acc = mfma_f4f6<1>(A[1], X.lo[1], acc, sl);
+                    acc = mfma_f4f6<2>(A[2], X.hi[2], acc, sh);
+                    acc = mfma_f4f6<2>(A[2], X.lo[2], acc, sl);
+                    acc = mfma_f4f6<3>(A[3], X.hi[3], acc, sh);
+                    acc = mfma_f4f6<3>(A[3], X.lo[3], acc, sl);
                 }
                 ring[r] = load_bits();
                 __builtin_amdgcn_sched_barrier(0);
