@@ -790,51 +790,90 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     Unit6 X;
-    // do-while loops: the ring is consumed on every path (its loads are never sunk
-    // below the wait above, whatever nuw and nseg are)
-    int k = 0;
+    // The fp4 operand of product q from word wq of a ring slot (word q of this lane's
+    // load is k-group g of product q).  `one` is 0x22222222 (the magnitude 1.0) for a
+    // user of the batch and 0 for a padding slot, whose load reads zeros: its operands
+    // are then +0.0 and its products exactly 0.
+    auto expand = [&](uint32_t wq, uint32_t one) {
+        u32x4 a;
+        a.x = ((wq << 3) & kmask) | one;
+        a.y = ((wq << 2) & kmask) | one;
+        a.z = ((wq << 1) & kmask) | one;
+        a.w = (wq & kmask) | one;
+        return a;
+    };
+    // Software pipeline: while the eight products of user j run (from Ac), the operands
+    // of user j + 1 are expanded from the next ring slot into the other buffer (An),
+    // which no product in flight reads, and that slot is refilled.  The buffers
+    // alternate between users.  Products alternate between two accumulators, so two
+    // consecutive ones never wait for each other.  At a unit's last user the next slot
+    // (the next unit's first user) waits for the next unit.
+    u32x4 A0[4], A1[4];
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+    int k_cur = 0;
+    auto step = [&](int j, int r, bool next, u32x4* Ac, u32x4* An) {
+        const int usr = __builtin_amdgcn_readlane(utab, j < nseg ? j : 0);
+        const bool mine = k_cur < nuw && j < nseg && tok_user == usr;
+        const uint32_t sh = mine ? X.ehi : 0u, sl = mine ? X.elo : 0u;
+        const uint32_t onen = k_cur < nuw && j + 1 < nseg ? kone : 0u;
+        const u32x4 Dn = ring[(r + 1) % RB];
+        // (sched_barrier pins the order: two products, then one operand of the next
+        // user, four times)
+        acc = mfma_f4f6<0>(Ac[0], X.hi[0], acc, sh);
+        acc2 = mfma_f4f6<0>(Ac[0], X.lo[0], acc2, sl);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) An[0] = expand(Dn[0], onen);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_f4f6<1>(Ac[1], X.hi[1], acc, sh);
+        acc2 = mfma_f4f6<1>(Ac[1], X.lo[1], acc2, sl);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) An[1] = expand(Dn[1], onen);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_f4f6<2>(Ac[2], X.hi[2], acc, sh);
+        acc2 = mfma_f4f6<2>(Ac[2], X.lo[2], acc2, sl);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) An[2] = expand(Dn[2], onen);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_f4f6<3>(Ac[3], X.hi[3], acc, sh);
+        acc2 = mfma_f4f6<3>(Ac[3], X.lo[3], acc2, sl);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) {
+            An[3] = expand(Dn[3], onen);
+            ring[(r + 1) % RB] = load_bits();
+        }
+        // Ac stays allocated to the end of the step, so An never reuses the registers of
+        // an operand that a product in flight still reads (that would stall the expansion)
+        asm volatile("" ::"v"(Ac[0]), "v"(Ac[1]), "v"(Ac[2]), "v"(Ac[3]));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // do-while loops: every ring slot is consumed on every path, so no load is sunk
+    // below a wait
     do {
         // encode this unit's tokens while its first users' rows are in flight
-        if (k < nuw && nseg > 0)
-            fused_encode6(smem, rowb, wd + kFusedDeltaWaves * k, lane, kb_lo, kb_hi, X);
+        if (k_cur < nuw && nseg > 0)
+            fused_encode6(smem, rowb, wd + kFusedDeltaWaves * k_cur, lane, kb_lo, kb_hi, X);
+        // the unit's first user: ring slot 0 (each unit takes nsegR slots, a multiple of RB)
+        {
+            const uint32_t one0 = k_cur < nuw && nseg > 0 ? kone : 0u;
+            const u32x4 D0 = ring[0];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) A0[q] = expand(D0[q], one0);
+            ring[0] = load_bits();
+        }
         int j0 = 0;
         do {
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int j = j0 + r;
-                const u32x4 D = ring[r];
-                // the fp4 operands of the unit's four products: word q of this lane's
-                // load is k-group g of product q.  Built on every path, so each load is
-                // consumed at the same point; only the products are skipped.
-                u32x4 A[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t wq = D[q];
-                    A[q].x = ((wq << 3) & kmask) | kone;
-                    A[q].y = ((wq << 2) & kmask) | kone;
-                    A[q].z = ((wq << 1) & kmask) | kone;
-                    A[q].w = (wq & kmask) | kone;
-                }
-                if (k < nuw && j < nseg) {  // uniform
-                    const int usr = __builtin_amdgcn_readlane(utab, j);
-                    const bool mine = tok_user == usr;
-                    const uint32_t sh = mine ? X.ehi : 0u, sl = mine ? X.elo : 0u;
-                    acc = mfma_f4f6<0>(A[0], X.hi[0], acc, sh);
-                    acc = mfma_f4f6<0>(A[0], X.lo[0], acc, sl);
-                    acc = mfma_f4f6<1>(A[1], X.hi[1], acc, sh);
-                    acc = mfma_f4f6<1>(A[1], X.lo[1], acc, sl);
-                    acc = mfma_f4f6<2>(A[2], X.hi[2], acc, sh);
-                    acc = mfma_f4f6<2>(A[2], X.lo[2], acc, sl);
-                    acc = mfma_f4f6<3>(A[3], X.hi[3], acc, sh);
-                    acc = mfma_f4f6<3>(A[3], X.lo[3], acc, sl);
-                }
-                ring[r] = load_bits();
-                __builtin_amdgcn_sched_barrier(0);
+            for (int r = 0; r + 1 < RB; ++r) {  // RB is even: user r reads A0 for even r
+                if (r & 1) step(j0 + r, r, true, A1, A0);
+                else step(j0 + r, r, true, A0, A1);
             }
+            if (j0 + RB < nsegR) step(j0 + RB - 1, RB - 1, true, A1, A0);  // uniform
+            else step(j0 + RB - 1, RB - 1, false, A1, A0);
             j0 += RB;
         } while (j0 < nsegR);
-        ++k;
-    } while (k < nuw);
+        ++k_cur;
+    } while (k_cur < nuw);
+    acc += acc2;
     // the ring's last loads (past the end) land: no load of this wave stays in flight,
     // so the base waves' code, which the compiler may lay out after a join with this
     // path, starts without waits for it
