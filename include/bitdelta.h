@@ -182,7 +182,8 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
  * batch once, then run the shared base product and the per-user delta product
  * of each matrix ([P2] "Systems Mechanics" 1: Y = Y_base + Y_delta). */
 
-/* Workspace of a prepared batch: the grouping of the tokens by user. */
+/* Workspace of a prepared batch: the grouping of the tokens by user and, for
+ * bf16 inputs, room for the tokens encoded as delta-product operands. */
 size_t bd_batch_workspace_bytes(int64_t T, int32_t n_users, int64_t d_in, bd_dtype x_dtype);
 
 /* Groups the T tokens by user id (tokens of one user contiguous, in token
@@ -204,8 +205,11 @@ bd_status bd_base_gemm(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
  * every token of the prepared batch whose user is valid.  `batch` must come
  * from bd_batch_prepare with the same user ids, x_dtype, T, d_in and n_users;
  * x is [T][d_in] (any activation tensor of that batch, e.g. the input of q, k
- * or v); y is fp32 [T][d_out]. */
-bd_status bd_delta_apply(const void* batch, const void* x, bd_dtype x_dtype, int64_t T,
+ * or v); y is fp32 [T][d_out].  For bf16 inputs the call first writes this x
+ * (times the column scales, for COL) into `batch` as tiles of 16 user-sorted
+ * tokens encoded as fp6 e2m3 operands, so calls on one batch must not overlap;
+ * the grouping itself is left unchanged. */
+bd_status bd_delta_apply(void* batch, const void* x, bd_dtype x_dtype, int64_t T,
                          int64_t d_in, int32_t n_users, int64_t d_out, const uint64_t* signs_bank,
                          const void* scales_bank, const bd_compress_params* p, float* y,
                          void* stream);

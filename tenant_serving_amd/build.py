@@ -27,7 +27,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I" + INCLUDE, "-I" + CSRC]
 
-BITDELTA_SOURCES = ["bd_api.hip", "bd_compress.hip", "bd_apply.hip", "bd_decode.hip", "bd_gemm.hip",
+BITDELTA_SOURCES = ["bd_api.hip", "bd_compress.hip", "bd_apply.hip", "bd_decode.hip", "bd_delta.hip", "bd_gemm.hip",
                     "bd_reconstruct.hip"]
 
 

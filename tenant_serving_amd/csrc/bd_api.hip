@@ -127,7 +127,7 @@ bd_status bd_base_gemm(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
-bd_status bd_delta_apply(const void* batch, const void* x, bd_dtype x_dtype, int64_t T,
+bd_status bd_delta_apply(void* batch, const void* x, bd_dtype x_dtype, int64_t T,
                          int64_t d_in, int32_t n_users, int64_t d_out, const uint64_t* signs_bank,
                          const void* scales_bank, const bd_compress_params* p, float* y,
                          void* stream) {
@@ -143,7 +143,7 @@ bd_status bd_delta_apply(const void* batch, const void* x, bd_dtype x_dtype, int
     if (n_users > 0 && (!signs_bank || !scales_bank || !aligned(signs_bank, 16) ||
                         !aligned(scales_bank, 16)))
         return BD_ERR_INVALID_ARG;
-    hipError_t e = launch_delta(bp, dp, (const char*)batch, x, signs_bank, scales_bank, y,
+    hipError_t e = launch_delta(bp, dp, (char*)batch, x, signs_bank, scales_bank, y,
                                 (hipStream_t)stream);
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }

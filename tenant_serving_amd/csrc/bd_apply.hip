@@ -37,10 +37,11 @@ constexpr int kGroupThreads = 1024;
 
 // ------------------------------------------------------------------ group
 // meta[0] status bits, meta[1] number of items, meta[2] number of tokens with
-// a valid user.  items[i] = {user, first sorted position, token count, 0}.
+// a valid user.  items[i] = {user, first sorted position, token count, 0};
+// suser[p] = user of sorted position p (p < meta[2]).
 __global__ void __launch_bounds__(kGroupThreads)
 k_group(const int32_t* __restrict__ ids, int T, int U, int P, int32_t* __restrict__ perm,
-        int4* __restrict__ items, uint32_t* __restrict__ meta) {
+        int32_t* __restrict__ suser, int4* __restrict__ items, uint32_t* __restrict__ meta) {
     extern __shared__ uint32_t keys[];  // P entries
     __shared__ int32_t sc[kGroupThreads];
     __shared__ int nvalid_sh;
@@ -84,7 +85,10 @@ k_group(const int32_t* __restrict__ ids, int T, int U, int P, int32_t* __restric
         const bool v = (keys[i] >> 14) < (uint32_t)U;
         const bool vprev = i == 0 || (keys[i - 1] >> 14) < (uint32_t)U;
         if (!v && vprev) nvalid_sh = i;
-        if (v) perm[i] = (int32_t)(keys[i] & 0x3FFFu);
+        if (v) {
+            perm[i] = (int32_t)(keys[i] & 0x3FFFu);
+            suser[i] = (int32_t)(keys[i] >> 14);
+        }
     }
     __syncthreads();
     const int nv = nvalid_sh;
@@ -134,7 +138,7 @@ k_group(const int32_t* __restrict__ ids, int T, int U, int P, int32_t* __restric
 // starts and prefix counts place the items.  Same outputs as k_group.
 __global__ void __launch_bounds__(64)
 k_group_wave(const int32_t* __restrict__ ids, int T, int U, int32_t* __restrict__ perm,
-             int4* __restrict__ items, uint32_t* __restrict__ meta) {
+             int32_t* __restrict__ suser, int4* __restrict__ items, uint32_t* __restrict__ meta) {
     const int l = threadIdx.x;
     uint32_t key = 0xFFFFFFFFu;
     bool bad = false;
@@ -157,7 +161,10 @@ k_group_wave(const int32_t* __restrict__ ids, int T, int U, int32_t* __restrict_
     const bool valid = user < (uint32_t)U;
     const uint64_t vmask = __ballot(valid);
     const int nv = __popcll(vmask);  // valid keys sort first
-    if (valid) perm[l] = (int32_t)(key & 0x3FFFu);
+    if (valid) {
+        perm[l] = (int32_t)(key & 0x3FFFu);
+        suser[l] = (int32_t)user;
+    }
     const uint32_t prev = __shfl_up(user, 1);
     const bool start = valid && (l == 0 || prev != user);
     const uint64_t smask = __ballot(start);
@@ -693,6 +700,14 @@ bd_status make_batch_plan(int64_t T, int32_t U, int64_t d_in, int xdtype, BatchP
     off += align_up(sizeof(int32_t) * Tn);
     q.off_items = off;
     off += align_up(sizeof(int4) * (size_t)q.max_items);
+    if (xdtype == BD_BF16) {
+        q.ntiles = (int64_t)((Tn + 15) / 16);
+        q.nunit = (d_in + 511) / 512;
+        q.off_tmeta = off;
+        off += align_up(sizeof(int32_t) * kTileMetaInts * (size_t)q.ntiles);
+        q.off_enc = off;
+        off += align_up((size_t)kEncUnitBytes * (size_t)q.ntiles * (size_t)q.nunit);
+    }
     q.total = off;
     *pl = q;
     return BD_OK;
@@ -760,13 +775,14 @@ hipError_t launch_batch_prepare(const BatchPlan& pl, const void* x, const int32_
     }
     if (pl.T <= 64) {
         hipLaunchKernelGGL(k_group_wave, dim3(1), dim3(64), 0, s, ids, (int)pl.T, pl.U,
-                           (int32_t*)(batch + pl.off_perm), (int4*)(batch + pl.off_items), meta);
+                           (int32_t*)(batch + pl.off_perm), (int32_t*)(batch + pl.off_user),
+                           (int4*)(batch + pl.off_items), meta);
         return hipGetLastError();
     }
     const int P = pow2_at_least(pl.T);
     hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), sizeof(uint32_t) * P, s, ids,
                        (int)pl.T, pl.U, P, (int32_t*)(batch + pl.off_perm),
-                       (int4*)(batch + pl.off_items), meta);
+                       (int32_t*)(batch + pl.off_user), (int4*)(batch + pl.off_items), meta);
     return hipGetLastError();
 }
 
@@ -794,10 +810,11 @@ hipError_t launch_base_gemm(const void* x, int xdtype, int64_t T, int64_t d_in, 
     return hipGetLastError();
 }
 
-hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, const char* batch,
+hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                         const void* x, const uint64_t* signs, const void* scales, float* y,
                         hipStream_t s) {
     if (bp.T == 0) return hipSuccess;
+    if (bp.xdtype == BD_BF16) return launch_delta6(bp, dp, batch, x, signs, scales, y, s);
     const uint32_t* meta = (const uint32_t*)(batch + bp.off_meta);
     const int32_t* perm = (const int32_t*)(batch + bp.off_perm);
     const int32_t* row_user = (const int32_t*)(batch + bp.off_user);

@@ -518,20 +518,11 @@ __device__ __forceinline__ f32x4 mfma_f4f6(u32x4 a, i32x6 b, f32x4 c, uint32_t s
 }
 
 // Encodes, for lane (m, G), product q of unit u: the 32 columns 512 u + 128 G + 32 q
-// of token m (the LDS chunks c0 .. c0 + 3, c0 = 64 u + 16 G + 4 q), k position
-// j = 8 d + n holding column 4 n + d, the column whose sign bit the fp4 operand puts
-// there.  With E the exponent of the block's largest |x| (in [2^E, 2^(E+1))) and
-// s = 2^(E-1): hi = fp6(x / s) and lo = fp6((x - hi) / (s / 32)), both rounded to
-// nearest even; hi + lo equals x for every |x| >= s and is within 2^-10 of the block
-// maximum otherwise.  kone_lo / kone_hi: the bf16 pairs (1, 0) and (0, 1).
+// of token m (the LDS chunks c0 .. c0 + 3, c0 = 64 u + 16 G + 4 q); see
+// encode_fp6_block for the encoding.
 __device__ __forceinline__ void encode6(const char* smem, uint32_t rowb, int c0, int m,
                                         uint32_t kone_lo, uint32_t kone_hi, i32x6& h, i32x6& l,
                                         uint32_t& code_hi, uint32_t& code_lo) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
-    typedef float f32x32 __attribute__((ext_vector_type(32)));
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
     uint32_t R[16];  // R[p]: columns 2p (low half) and 2p + 1 (high half)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -541,48 +532,7 @@ __device__ __forceinline__ void encode6(const char* smem, uint32_t rowb, int c0,
         R[4 * i + 2] = v.z;
         R[4 * i + 3] = v.w;
     }
-    // block maximum of |x|: on the bf16 bits of non-negative values the integer
-    // order is the numeric order
-    u16x2 mx2 = {0, 0};
-#pragma unroll
-    for (int p = 0; p < 16; ++p)
-        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, R[p] & 0x7FFF7FFFu));
-    const uint32_t eb = (uint32_t)(mx2.x > mx2.y ? mx2.x : mx2.y) >> 7;  // biased exponent
-    // s = 2^(eb - 128): code eb - 1; blocks below 2^-120 (zeros) take s = 1
-    code_hi = eb >= 7u && eb <= 255u ? eb - 1u : 127u;
-    code_lo = code_hi - 5u;
-    const float sh = __uint_as_float(code_hi << 23), sl = __uint_as_float(code_lo << 23);
-    // the values in k order: pair i = (column c, column c + 4), c = 8 (i % 4) + i / 4
-    // (kept as scalars: each pair also feeds a dot product below)
-    uint32_t V[16];
-    u32x16 Vv;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int a = i & 3, d = i >> 2;
-        const uint32_t r0 = R[4 * a + (d >> 1)], r1 = R[4 * a + (d >> 1) + 2];
-        V[i] = __builtin_amdgcn_perm(r1, r0, (d & 1) ? 0x07060302u : 0x05040100u);
-        Vv[i] = V[i];
-    }
-    h = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32, Vv), sh);
-    // -hi, exact: the 32 fields with their sign bits (bit 6j + 5) flipped, widened
-    const i32x6 sgn = {(int)0x20820820u, (int)0x08208208u, (int)0x82082082u,
-                       (int)0x20820820u, (int)0x08208208u, (int)0x82082082u};
-    f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(h ^ sgn, sh);
-    // the exact residuals x - hi (the bf16 dot product picks one half of the pair),
-    // accumulated onto -hi in place; each has at most 4 significant bits, so its bf16
-    // form (the upper half of the fp32 word) is exact
-    u32x16 W;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const bf16x2 pr = __builtin_bit_cast(bf16x2, V[i]);
-        r[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, kone_lo),
-                                                   r[2 * i], false);
-        r[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, kone_hi),
-                                                       r[2 * i + 1], false);
-        W[i] = __builtin_amdgcn_perm(__float_as_uint(r[2 * i + 1]), __float_as_uint(r[2 * i]),
-                                     0x07060302u);
-    }
-    l = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32, W), sl);
+    encode_fp6_block(R, kone_lo, kone_hi, h, l, code_hi, code_lo);
 }
 
 __device__ __forceinline__ void fused_encode6(const char* smem, uint32_t rowb, int u, int lane,

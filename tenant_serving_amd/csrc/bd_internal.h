@@ -48,13 +48,18 @@ constexpr int kItemTokens = 32;   // max tokens of one (user, chunk) work item (
 constexpr int kMaxGroupT = 8192;  // tokens the one-block grouping kernel sorts in LDS
 constexpr int kMaxUsers = (1 << 17) - 1;
 
-// Prepared batch (bd_batch_prepare): tokens grouped by user into work items.
+// Prepared batch (bd_batch_prepare): tokens grouped by user into work items; for
+// bf16 inputs also the tiles of the delta products (bd_delta.hip): per tile of 16
+// sorted positions kTileMetaInts ints of meta, per (tile, 512-column unit)
+// kEncUnitBytes of encoded token operands.
+constexpr int kTileMetaInts = 64;
+constexpr int kEncUnitBytes = 13 * 1024;
 struct BatchPlan {
     int64_t T = 0, d_in = 0;
     int32_t U = 0;
     int xdtype = 0;
-    int64_t max_items = 0;
-    size_t off_meta = 0, off_perm = 0, off_user = 0, off_items = 0;
+    int64_t max_items = 0, ntiles = 0, nunit = 0;
+    size_t off_meta = 0, off_perm = 0, off_user = 0, off_items = 0, off_tmeta = 0, off_enc = 0;
     size_t total = 0;
 };
 
@@ -97,10 +102,14 @@ hipError_t launch_batch_prepare(const BatchPlan& pl, const void* x, const int32_
                                 char* batch, hipStream_t s);
 hipError_t launch_base_gemm(const void* x, int xdtype, int64_t T, int64_t d_in, const void* wb,
                             int64_t d_out, float* y, hipStream_t s);
-hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, const char* batch,
+hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                         const void* x, const uint64_t* signs, const void* scales, float* y,
                         hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
+// bf16 delta products of a prepared batch (writes the batch's tile meta and encoded
+// tokens, then adds into y).
+hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, const void* x,
+                         const uint64_t* signs, const void* scales, float* y, hipStream_t s);
 
 // Tiled matrix-core GEMM for the base product of batches of more than kGemmMinT
 // bf16 tokens (smaller batches take the streaming kernel of bd_apply.hip).
@@ -168,6 +177,71 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     _Float16 v;
     __builtin_memcpy(&v, &h, 2);
     return (float)v;
+}
+
+
+// The fp6 e2m3 B operands of the block-scaled MFMA 16x16x128 for one lane's 32
+// values (one 32-column block of one token): R[p] holds the bf16 values of
+// columns 2p (low half) and 2p + 1 (high half).  k position j = 8 d + n carries
+// column 4 n + d, the column whose sign bit the fp4 sign operand puts there.
+// With E the exponent of the block's largest |x| (in [2^E, 2^(E+1))) and
+// s = 2^(E-1): hi = fp6(x / s) and lo = fp6((x - hi) / (s / 32)), both rounded to
+// nearest even; hi + lo equals x for every |x| >= s and is within 2^-10 of the
+// block maximum otherwise.  code_hi / code_lo: the E8M0 scale codes of hi and lo.
+// kone_lo / kone_hi: the bf16 pairs (1, 0) and (0, 1), passed in registers.
+__device__ __forceinline__ void encode_fp6_block(const uint32_t* R, uint32_t kone_lo,
+                                                 uint32_t kone_hi,
+                                                 int __attribute__((ext_vector_type(6)))& h,
+                                                 int __attribute__((ext_vector_type(6)))& l,
+                                                 uint32_t& code_hi, uint32_t& code_lo) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
+    typedef float f32x32 __attribute__((ext_vector_type(32)));
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
+    typedef int i32x6 __attribute__((ext_vector_type(6)));
+    // block maximum of |x|: on the bf16 bits of non-negative values the integer
+    // order is the numeric order
+    u16x2 mx2 = {0, 0};
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, R[p] & 0x7FFF7FFFu));
+    const uint32_t eb = (uint32_t)(mx2.x > mx2.y ? mx2.x : mx2.y) >> 7;  // biased exponent
+    // s = 2^(eb - 128): code eb - 1; blocks below 2^-120 (zeros) take s = 1
+    code_hi = eb >= 7u && eb <= 255u ? eb - 1u : 127u;
+    code_lo = code_hi - 5u;
+    const float sh = __uint_as_float(code_hi << 23), sl = __uint_as_float(code_lo << 23);
+    // the values in k order: pair i = (column c, column c + 4), c = 8 (i % 4) + i / 4
+    // (kept as scalars: each pair also feeds a dot product below)
+    uint32_t V[16];
+    u32x16 Vv;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int a = i & 3, d = i >> 2;
+        const uint32_t r0 = R[4 * a + (d >> 1)], r1 = R[4 * a + (d >> 1) + 2];
+        V[i] = __builtin_amdgcn_perm(r1, r0, (d & 1) ? 0x07060302u : 0x05040100u);
+        Vv[i] = V[i];
+    }
+    h = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32, Vv), sh);
+    // -hi, exact: the 32 fields with their sign bits (bit 6j + 5) flipped, widened
+    const i32x6 sgn = {(int)0x20820820u, (int)0x08208208u, (int)0x82082082u,
+                       (int)0x20820820u, (int)0x08208208u, (int)0x82082082u};
+    f32x32 r = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(h ^ sgn, sh);
+    // the exact residuals x - hi (the bf16 dot product picks one half of the pair),
+    // accumulated onto -hi in place; each has at most 4 significant bits, so its bf16
+    // form (the upper half of the fp32 word) is exact
+    u32x16 W;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const bf16x2 pr = __builtin_bit_cast(bf16x2, V[i]);
+        r[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, kone_lo),
+                                                   r[2 * i], false);
+        r[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, __builtin_bit_cast(bf16x2, kone_hi),
+                                                       r[2 * i + 1], false);
+        W[i] = __builtin_amdgcn_perm(__float_as_uint(r[2 * i + 1]), __float_as_uint(r[2 * i]),
+                                     0x07060302u);
+    }
+    l = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32, W), sl);
 }
 
 }  // namespace bd
