@@ -701,8 +701,10 @@ bd_status make_batch_plan(int64_t T, int32_t U, int64_t d_in, int xdtype, BatchP
     q.off_items = off;
     off += align_up(sizeof(int4) * (size_t)q.max_items);
     if (xdtype == BD_BF16) {
-        q.ntiles = (int64_t)((Tn + 15) / 16);
+        q.ntiles = 2 * (int64_t)((Tn + 15) / 16) + 1;  // bound of the packed tiles
         q.nunit = (d_in + 511) / 512;
+        q.off_tiles = off;
+        off += align_up(sizeof(int32_t) * ((size_t)q.ntiles + 1));
         q.off_tmeta = off;
         off += align_up(sizeof(int32_t) * kTileMetaInts * (size_t)q.ntiles);
         q.off_enc = off;
@@ -777,13 +779,15 @@ hipError_t launch_batch_prepare(const BatchPlan& pl, const void* x, const int32_
         hipLaunchKernelGGL(k_group_wave, dim3(1), dim3(64), 0, s, ids, (int)pl.T, pl.U,
                            (int32_t*)(batch + pl.off_perm), (int32_t*)(batch + pl.off_user),
                            (int4*)(batch + pl.off_items), meta);
-        return hipGetLastError();
+    } else {
+        const int P = pow2_at_least(pl.T);
+        hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), sizeof(uint32_t) * P, s, ids,
+                           (int)pl.T, pl.U, P, (int32_t*)(batch + pl.off_perm),
+                           (int32_t*)(batch + pl.off_user), (int4*)(batch + pl.off_items), meta);
     }
-    const int P = pow2_at_least(pl.T);
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), sizeof(uint32_t) * P, s, ids,
-                       (int)pl.T, pl.U, P, (int32_t*)(batch + pl.off_perm),
-                       (int32_t*)(batch + pl.off_user), (int4*)(batch + pl.off_items), meta);
-    return hipGetLastError();
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_tile_plan(pl, batch, s);
 }
 
 hipError_t launch_base_gemm(const void* x, int xdtype, int64_t T, int64_t d_in, const void* wb,

@@ -3,27 +3,29 @@
 // 1-2: each request adds its own 1-bit delta product; the bits cross HBM packed
 // and are expanded on chip).
 //
-// The batch, sorted by user (k_group), is cut into tiles of 16 consecutive
-// positions; a tile may hold tokens of several users and a user's tokens may span
-// tiles.  Two kernels:
+// The batch, sorted by user (k_group), is cut into tiles of at most 16 consecutive
+// positions (k_tile_plan): users of at most 16 tokens are packed whole, so their
+// sign rows are read once per tile range; a tile may hold several users.  Kernels:
+//   k_tile_plan    one wave: greedy packing of the work items into tiles.
 //   k_tile_encode  per (tile, 512-column unit): the tile's 16 tokens as the fp6
-//                  e2m3 B operands of the gfx950 block-scaled MFMA 16x16x128, two
+//                  e2m3 A operands of the gfx950 block-scaled MFMA 16x16x128, two
 //                  parts per value (hi, lo) under one power-of-two scale per 32
 //                  columns (the encoding of the decode path; COL scales are folded
 //                  into the values first), and the tile's token and user lists.
 //   k_delta6       per (64 output rows, range of tiles): for each tile and unit the
-//                  tile's operands come into LDS (double-buffered copies shared by
-//                  the block's four waves); every user of the tile then loads its
-//                  16 B of sign bits per lane (a register ring keeps the next rows
-//                  in flight), expands them to fp4 e2m1 +-1 A operands (two VALU
-//                  ops per eight signs) and runs the four products twice (hi, lo).
+//                  tile's operands come into LDS (three buffers, copied two steps
+//                  ahead, shared by the block's four waves); every user of the tile
+//                  then loads its sign bits (16 B per lane) and scales, kept eight
+//                  slots ahead in a register ring that runs across the block's
+//                  tiles, expands the bits to fp4 e2m1 +-1 B operands (two VALU ops
+//                  per eight signs) and runs the four products twice (hi, lo).
 //                  Other users' tokens of the tile enter with block scale 2^-127,
 //                  so one accumulator per wave and tile collects every user's
-//                  product in its own token columns.  GROUP: each product covers
-//                  one 128-column group (the unit's group c at lane group g's
-//                  32 columns), and its result is scaled by the group scale of
-//                  each row before it is added.  The epilogue adds the tile's
-//                  result into Y (each Y element belongs to exactly one tile).
+//                  product in its own token rows.  MATRIX / ROW: each user's sum is
+//                  scaled when it is added; GROUP: each product covers one
+//                  128-column group and is scaled by the row's group scale.  The
+//                  tile's result is added into Y with one no-return atomic add per
+//                  element (each Y element belongs to exactly one tile).
 #include "bd_internal.h"
 
 namespace bd {
@@ -52,12 +54,12 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, char* lds, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
 }
 
-// D += A(fp4, 16 x 128) * B(fp6 e2m3, 128 x 16) * 2^(scale_b - 127), scale_b = byte SEL of sc.
+// D += A(fp6 e2m3, 16 x 128) * 2^(scale_a - 127) * B(fp4, 128 x 16), scale_a = byte SEL of sc.
 template <int SEL>
-__device__ __forceinline__ f32x4 mfma_f4f6(u32x4 a, i32x6 b, f32x4 c, uint32_t sc) {
-    const i32x8 a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-    const i32x8 b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, 4, 5, -1, -1);
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 2, 0, 127, SEL, (int)sc);
+__device__ __forceinline__ f32x4 mfma_f6f4(i32x6 a, u32x4 b, f32x4 c, uint32_t sc) {
+    const i32x8 a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, 4, 5, -1, -1);
+    const i32x8 b8 = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 2, 4, SEL, (int)sc, 0, 127);
 }
 
 // s_waitcnt with only the vector-memory count: vmcnt <= n (expcnt, lgkmcnt untouched).
@@ -65,6 +67,51 @@ __device__ __forceinline__ f32x4 mfma_f4f6(u32x4 a, i32x6 b, f32x4 c, uint32_t s
     __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
 
 }  // namespace
+
+// ------------------------------------------------------------ tile packing
+// The work items of k_group (runs of <= 32 positions of one user, in position
+// order) are packed into tiles of <= 16 positions: an item of c <= 16 positions
+// joins the open tile if it fits and otherwise starts a new one (so a user of at
+// most 16 tokens is never split); an item of 17..32 starts a tile of 16 and opens
+// one with the rest.  Every tile but the last, together with the next, holds more
+// than 16 positions: at most 2 ceil(T / 16) + 1 tiles.  One wave: the open tile's
+// length is a short serial recurrence over the items (scalar, 64 per round); the
+// tile starts are then written by the items' lanes.  tiles[t] = first position of
+// tile t, tiles[ntiles] = number of valid positions, meta[3] = ntiles.
+__global__ void __launch_bounds__(64)
+k_tile_plan(const int4* __restrict__ items, uint32_t* __restrict__ meta, int32_t* __restrict__ tiles,
+            int maxt) {
+    const int lane = threadIdx.x;
+    const int nit = (int)meta[1];
+    int cl = 0, nt = 0;  // open tile length, tiles started (uniform)
+    for (int b = 0; b < nit; b += 64) {
+        const int4 it = b + lane < nit ? items[b + lane] : make_int4(0, 0, 0, 0);
+        const int m = nit - b < 64 ? nit - b : 64;
+        uint64_t smask = 0;  // item k starts a tile
+        for (int k = 0; k < m; ++k) {
+            const int c = __builtin_amdgcn_readlane(it.z, k);
+            const int c0 = c > 16 ? 16 : c;
+            const bool st = cl == 0 || cl + c0 > 16;
+            smask |= (uint64_t)st << k;
+            cl = c > 16 ? c - 16 : (st ? c : cl + c);
+        }
+        const bool st = (smask >> lane) & 1ull;
+        const bool big = lane < m && it.z > 16;
+        const uint64_t bmask = __ballot(big);
+        const uint64_t below = (1ull << lane) - 1ull;
+        const int idx = nt + __popcll(smask & below) + __popcll(bmask & below);
+        if (lane < m) {
+            if (st && idx < maxt) tiles[idx] = it.y;
+            if (big && idx + (int)st < maxt) tiles[idx + (int)st] = it.y + 16;
+        }
+        nt += __popcll(smask) + __popcll(bmask);
+    }
+    nt = nt < maxt ? nt : maxt;
+    if (lane == 0) {
+        tiles[nt] = (int)meta[2];
+        meta[3] = (uint32_t)nt;
+    }
+}
 
 // ------------------------------------------------------------ tile encoding
 // Block (tile t, unit u), 4 waves: wave q encodes product q.  Lane (m, G) takes
@@ -78,16 +125,19 @@ template <bool GRP, bool COL>
 __global__ void __launch_bounds__(256)
 k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
               const int32_t* __restrict__ perm, const int32_t* __restrict__ suser,
-              const uint32_t* __restrict__ meta, const void* __restrict__ scales, int sdtype,
-              int64_t per_user, int32_t* __restrict__ tmeta, char* __restrict__ enc) {
+              const uint32_t* __restrict__ meta, const int32_t* __restrict__ tiles,
+              const void* __restrict__ scales, int sdtype, int64_t per_user,
+              int32_t* __restrict__ tmeta, char* __restrict__ enc) {
     const int t = blockIdx.x, u = blockIdx.y, nunit = gridDim.y;
     const int lane = threadIdx.x & 63;
     const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15, G = lane >> 4;
-    const int nv = (int)meta[2];
-    const int p = 16 * t + m;
-    const int tok = p < nv ? perm[p] : -1;
-    const int usr = p < nv ? suser[p] : -1;
+    const int ntv = (int)meta[3];
+    if (t >= ntv) return;  // uniform: no such tile in this batch
+    const int ts = tiles[t], tl = tiles[t + 1] - ts;  // start, length
+    const int p = ts + m;
+    const int tok = m < tl ? perm[p] : -1;
+    const int usr = m < tl ? suser[p] : -1;
     if (u == 0 && q == 0) {
         // tile meta: tokens, their users, the distinct users in order, their number
         int32_t* tm = tmeta + (size_t)t * kTileMetaInts;
@@ -102,7 +152,6 @@ k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
         if (start) tm[32 + j] = usr;
         if (lane == 0) tm[48] = __popcll(smask);
     }
-    if (16 * t >= nv) return;  // uniform: a tile past the valid tokens is skipped later
 
     const int64_t c0 = GRP ? 512 * (int64_t)u + 128 * q + 32 * G : 512 * (int64_t)u + 128 * G + 32 * q;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)T * (uint64_t)d_in * 2);
@@ -119,27 +168,29 @@ k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
     }
     if (COL) {
         // x * (column scale of the token's user), rounded to bf16; zero for no user
+        // (per-lane user: plain global loads, columns past d_in take scale 0)
         const size_t sb = sdtype == BD_F16 ? 2 : 4;
-        const __amdgpu_buffer_rsrc_t sr =
-            make_rsrc((const char*)scales + (usr >= 0 ? (size_t)usr * per_user * sb : 0),
-                      usr >= 0 ? (uint64_t)per_user * sb : 0);
+        const char* sp = (const char*)scales + (usr >= 0 ? (size_t)usr * per_user * sb : 0);
         float sc[32];
-        if (sdtype == BD_F16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 h = buf_load16(sr, (uint32_t)((c0 + 8 * i) * 2));
+        for (int i = 0; i < 4; ++i) {
+            const int64_t col = c0 + 8 * i;
+            const bool ok = usr >= 0 && col < d_in;
+            if (sdtype == BD_F16) {
+                const u32x4 h = ok ? *(const u32x4*)(sp + col * 2) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     sc[8 * i + 2 * e] = f16_to_f32((uint16_t)h[e]);
                     sc[8 * i + 2 * e + 1] = f16_to_f32((uint16_t)(h[e] >> 16));
                 }
-            }
-        } else {
+            } else {
+                const u32x4 f0 = ok ? *(const u32x4*)(sp + col * 4) : u32x4{0u, 0u, 0u, 0u};
+                const u32x4 f1 = ok ? *(const u32x4*)(sp + col * 4 + 16) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const u32x4 f = buf_load16(sr, (uint32_t)((c0 + 4 * i) * 4));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sc[4 * i + e] = __uint_as_float(f[e]);
+                for (int e = 0; e < 4; ++e) {
+                    sc[8 * i + e] = __uint_as_float(f0[e]);
+                    sc[8 * i + 4 + e] = __uint_as_float(f1[e]);
+                }
             }
         }
 #pragma unroll
@@ -165,57 +216,83 @@ k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
 }
 
 // ------------------------------------------------------------ delta products
-// Block (64 output rows, tiles [tpb y, tpb y + tpb)), 4 waves of 16 rows.  Per
-// tile: for each unit u the block copies the tile's operands into LDS buffer u & 1
-// (chunk i by wave i % 4) while the previous unit runs; a barrier per unit makes
-// the copy visible and frees the other buffer.  The users of the tile form a ring
-// sequence k = u * nusR + j (j < nusR, padded to a multiple of RB with zero
-// loads), each slot holding L loads (the sign word(s), and for GROUP the row's
-// group scales), issued RB slots ahead.  nusR >= RB keeps the copies of unit u + 1
-// older than the last RB slots, so the wait vmcnt <= RB * L before each unit's
-// barrier covers them.
-template <int MODE, bool SF16>
-__global__ void __launch_bounds__(256)
+// Block (64 RT output rows, tiles [t0, t0 + ntb)), 4 waves of RT row tiles of 16
+// rows.  The block's work is one sequence of slots: tile by tile, unit by unit (a
+// step), one slot per user of the tile.  Each wave keeps the loads of its next
+// kRing slots in flight in a ring of registers: a slot's sign words are expanded
+// first, and only then are its registers reloaded, in place, with the slot kRing
+// ahead (its scales likewise after their last use), so no register copy on a loop
+// edge ever waits for a load in flight.  The tile operands of step s are in LDS
+// buffer s % 3; their copy is issued right after the barrier that opens step s - 2,
+// and the opening of step s waits until at most as many loads are in flight as
+// were issued after that copy (at most kRing - 1 slots' worth).  RT row tiles share
+// each copy of the tile operands: the copies, which also pass through the L1 of the
+// CU, cost 13 KB per step against 4 KB of sign rows per user and row tile.  MFMA:
+// A = the tile's 16 tokens (fp6 hi and lo; tokens of other users take block code 0,
+// i.e. scale 2^-127), B = 16 sign rows (fp4 +-1); lane (j, g) of D holds tokens
+// 4 g .. 4 g + 3 of output row j of the row tile.
+constexpr int kNBuf = 3;     // LDS buffers of tile operands
+constexpr int kMaxTpb = 64;  // tiles per block, at most (their meta is held in LDS)
+
+template <int MODE, bool SF16, int RT>
+__global__ void __launch_bounds__(256, 2)
 k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, int64_t per_user,
-         int bpg, const int32_t* __restrict__ tmeta, const char* __restrict__ enc,
+         int bsh, const int32_t* __restrict__ tmeta, const char* __restrict__ enc,
          const uint32_t* __restrict__ meta, float* __restrict__ y, int64_t d_in, int64_t d_out,
          int nunit, int tpb) {
+    // bsh: log2 of the group size / 128 (GROUP sizes are powers of two >= 128)
     constexpr bool GRP = MODE == BD_SCALE_GROUP;
-    constexpr int RB = GRP ? 2 : 4;  // ring slots
-    constexpr int L = GRP ? 8 : 1;   // loads per slot
-    constexpr uint32_t SB = SF16 ? 2 : 4;  // bytes per scale
-    __shared__ __attribute__((aligned(16))) char sbuf[2 * kEncUnitBytes];
+    constexpr bool COL = MODE == BD_SCALE_COL;
+    constexpr int kRing = RT == 1 ? 8 : (RT == 2 ? 6 : 4);  // slots in flight per wave
+    constexpr int NS = COL ? 0 : (MODE == BD_SCALE_MATRIX ? 1 : RT);  // scale loads per slot
+    constexpr int L = RT + NS;                                // loads per slot
+    constexpr uint32_t SB = SF16 ? 2 : 4;                     // bytes per scale
+    static_assert((kRing - 1) * L <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) char sbuf[kNBuf * kEncUnitBytes];
+    __shared__ int32_t smeta[kMaxTpb * kTileMetaInts];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int m = lane & 15, G = lane >> 4;
-    const int64_t r0 = (int64_t)blockIdx.x * 64 + 16 * wv;
-    const int64_t rowA = r0 + m < d_out ? r0 + m : d_out - 1;  // A operand row of this lane
-    const int nv = (int)meta[2];
-    const int ntv = (nv + 15) / 16;
-    const int t0 = (int)blockIdx.y * tpb;
-    const int t1 = t0 + tpb < ntv ? t0 + tpb : ntv;
-    if (t0 >= t1) return;  // uniform over the block
+    const int n = lane & 15, G = lane >> 4;
+    const int64_t rw0 = (int64_t)blockIdx.x * (64 * RT) + 16 * RT * wv;  // the wave's first row
+    // this block's share of the batch's tiles (at most kMaxTpb)
+    const int ntv = (int)meta[3];
+    const int t0 = (int)(((int64_t)blockIdx.y * ntv) / gridDim.y);
+    const int ntb = (int)(((int64_t)(blockIdx.y + 1) * ntv) / gridDim.y) - t0;
+    if (ntb <= 0) return;  // uniform over the block
+    (void)tpb;
 
-    const int64_t bank_row = d_in / 8;
-    const uint64_t user_bytes = (uint64_t)d_out * (uint64_t)bank_row;
+    for (int i = threadIdx.x; i < ntb * kTileMetaInts; i += 256)
+        smeta[i] = tmeta[(size_t)t0 * kTileMetaInts + i];
+    __syncthreads();
+    int total = 0;  // slots of the block
+    for (int t = 0; t < ntb; ++t) {
+        const int c = __builtin_amdgcn_readfirstlane(smeta[t * kTileMetaInts + 48]);
+        total += c;
+    }
+    total *= nunit;
+    total = (total + kRing - 1) / kRing * kRing;  // padded with empty slots past the last tile
+    const int S = ntb * nunit;  // steps
+
+    const uint32_t bank_row = (uint32_t)(d_in / 8);
+    const uint64_t user_bytes = (uint64_t)d_out * bank_row;
     const int nrec_bits = user_bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)user_bytes;
     const uint64_t sc_bytes = (uint64_t)per_user * SB;
     const int nrec_sc = sc_bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)sc_bytes;
-    const uint32_t brow = (uint32_t)(rowA * bank_row);
-    const int64_t gpr = GRP ? d_in / (128 * (int64_t)bpg) : 1;  // groups per row
-    // GROUP: this lane's scale rows 4G + e (clamped), as byte offsets of group 0
-    uint32_t srow[4];
+    const uint32_t gpr = GRP ? (uint32_t)((d_in / 128) >> bsh) : 1u;  // groups per row
+    uint32_t brow[RT], srow[RT];  // byte offsets of this lane's sign row and scale(s), per row tile
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t ro = r0 + 4 * G + e < d_out ? r0 + 4 * G + e : d_out - 1;
-        srow[e] = (uint32_t)(ro * gpr * SB);
+    for (int t = 0; t < RT; ++t) {
+        const int64_t r = rw0 + 16 * t + n;
+        const uint32_t rowB = (uint32_t)(r < d_out ? r : d_out - 1);  // output row of B column n
+        brow[t] = rowB * bank_row;
+        srow[t] = GRP ? rowB * gpr * SB : (MODE == BD_SCALE_ROW ? rowB * SB : 0u);
     }
     const __amdgpu_buffer_rsrc_t er =
-        make_rsrc(enc, (uint64_t)(t1 > 0 ? t1 : 1) * (uint64_t)nunit * kEncUnitBytes);
+        make_rsrc(enc + (size_t)t0 * nunit * kEncUnitBytes, (uint64_t)S * kEncUnitBytes);
     uint32_t kmask, kone;  // operand constants in registers (gfx9 VOP3 takes no literal)
     asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
     asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
-    auto expand = [&](uint32_t wq) {
+    auto expand = [&](uint32_t wq) __attribute__((always_inline)) {
         u32x4 a;
         a.x = ((wq << 3) & kmask) | kone;
         a.y = ((wq << 2) & kmask) | kone;
@@ -223,9 +300,9 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
         a.w = (wq & kmask) | kone;
         return a;
     };
-    // copies of the tile's operands for unit u into LDS buffer b (chunk i by wave i % 4)
-    auto issue_enc = [&](int t, int u, int b) {
-        const uint32_t src = (uint32_t)(((int64_t)t * nunit + u) * kEncUnitBytes) + 16 * lane;
+    // the tile operands of step st into LDS buffer b (1 KB chunk i by wave i % 4)
+    auto issue_enc = [&](int st, int b) __attribute__((always_inline)) {
+        const uint32_t src = (uint32_t)st * kEncUnitBytes + 16 * lane;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = wv + 4 * i;
@@ -233,173 +310,315 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                 lds_copy16(er, sbuf + b * kEncUnitBytes + c * 1024, src + (uint32_t)c * 1024);
         }
     };
-    struct Slot {
-        uint32_t w[4];  // sign words (GROUP: one per group of the unit)
-        u32x4 s[4];     // GROUP: the group scales of rows 4G + e, 4 (fp32) or 8 (fp16) from g0
+    // GROUP: per unit and row tile, each lane loads a 16-byte window of its row's
+    // scales, starting at the unit's first group and moved back (never out of the
+    // user's scales) so that it holds the groups of all four products
+    const uint32_t swmax = sc_bytes >= 16 ? (uint32_t)sc_bytes - 16u : 0u;
+    auto swin = [&](int u, int t) __attribute__((always_inline)) {
+        uint32_t g0 = (4u * (uint32_t)u) >> bsh;
+        g0 = g0 < gpr ? g0 : gpr - 1u;
+        const uint32_t o = srow[t] + g0 * SB;
+        return o < swmax ? o : swmax;
     };
 
-    for (int t = t0; t < t1; ++t) {
-        const int32_t* tm = tmeta + (size_t)t * kTileMetaInts;
-        const int nus = tm[48];  // >= 1 for a tile of valid tokens
-        const int nusR = (nus + RB - 1) / RB * RB;
-        const int tok = tm[m];            // token of this lane's column (or -1)
-        const int tok_user = tm[16 + m];  // its user (or -1)
-        const int tusers = tm[32 + (lane & 15)];  // lane j < nus: the tile's j-th user
-        // lane j: base addresses of user j's bank and scales (read back with readlane)
-        const uint64_t ub = (uint64_t)(const char*)signs +
-                            (uint64_t)(uint32_t)(lane < nus ? tusers : 0) * user_bytes;
-        const uint64_t sbp = (uint64_t)(const char*)scales +
-                             (uint64_t)(uint32_t)(lane < nus ? tusers : 0) * sc_bytes;
-        const uint32_t ub_lo = (uint32_t)ub, ub_hi = (uint32_t)(ub >> 32);
-        const uint32_t sb_lo = (uint32_t)sbp, sb_hi = (uint32_t)(sbp >> 32);
-        // slot sequence: unit lu, user lj (padded to nusR with zero loads), then zeros
-        int lu = 0, lj = 0;
-        uint32_t g0b = 0;  // GROUP: byte offset of the first group of unit lu
-        auto load_slot = [&]() {
-            Slot sl;
-            const bool ok = lu < nunit && lj < nus;  // uniform
-            const int jj = ok ? lj : 0;
-            // (readlane returns int: widen through uint32_t, no sign extension)
-            const uint64_t bb =
-                ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ub_hi, jj) << 32) |
-                (uint64_t)(uint32_t)__builtin_amdgcn_readlane(ub_lo, jj);
-            const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)bb, (short)0, nrec_bits, 0x00020000);
+    // ---- loading side: slot (lt, lu, lj), the users of tile lt
+    int lt = 0, lu = 0, lj = 0, l_nus = 0, l_nusP = 0;
+    uint32_t ub_lo = 0, ub_hi = 0, sb_lo = 0, sb_hi = 0;
+    auto l_tile = [&]() __attribute__((always_inline)) {
+        const int32_t* tm = smeta + lt * kTileMetaInts;
+        l_nus = __builtin_amdgcn_readfirstlane(tm[48]);
+        l_nusP = l_nus;
+        const int uj = tm[32 + n];
+        const uint64_t usr = n < l_nus ? (uint64_t)(uint32_t)uj : 0ull;
+        const uint64_t ub = (uint64_t)(const char*)signs + usr * user_bytes;
+        const uint64_t sbp = (uint64_t)(const char*)scales + usr * sc_bytes;
+        ub_lo = (uint32_t)ub;
+        ub_hi = (uint32_t)(ub >> 32);
+        sb_lo = (uint32_t)sbp;
+        sb_hi = (uint32_t)(sbp >> 32);
+    };
+    l_tile();
+    uint32_t lwin[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) lwin[t] = GRP ? swin(0, t) : 0u;
+    struct Slot {
+        u32x4 w[RT];                // per row tile 16 bytes of sign words: 4 products
+                                    // (GROUP: group G's 4 k-blocks)
+        u32x4 s4[GRP ? RT : 1];     // GROUP: per row tile the scale window
+        uint32_t s1[GRP ? 1 : RT];  // MATRIX: s1[0]; ROW: per row tile the row's scale
+    };
+    // (readlane returns int: widen through uint32_t, no sign extension)
+    auto lbase = [&](uint32_t lo, uint32_t hi, int jj) __attribute__((always_inline)) {
+        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, jj) << 32) |
+               (uint64_t)(uint32_t)__builtin_amdgcn_readlane(lo, jj);
+    };
+    auto issue_w = [&](Slot& sl, int t) __attribute__((always_inline)) {
+        const bool ok = lt < ntb && lj < l_nus;  // uniform
+        const uint32_t oob = ok ? 0u : kOOB;     // (offsets stay below 2^31)
+        const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)lbase(ub_lo, ub_hi, ok ? lj : 0), (short)0, nrec_bits, 0x00020000);
+        sl.w[t] = buf_load16(br, (brow[t] + (uint32_t)(64 * lu + 16 * G)) | oob);
+    };
+    auto issue_s = [&](Slot& sl) __attribute__((always_inline)) {
+        if (NS == 0) return;
+        const bool ok = lt < ntb && lj < l_nus;  // uniform
+        const uint32_t oob = ok ? 0u : kOOB;     // (offsets stay below 2^31)
+        const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)lbase(sb_lo, sb_hi, ok ? lj : 0), (short)0, nrec_sc, 0x00020000);
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
             if (GRP) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    sl.w[c] = buf_load4(br, ok ? brow + (uint32_t)(64 * lu + 16 * c + 4 * G) : kOOB);
-                const uint64_t sp =
-                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(sb_hi, jj) << 32) |
-                    (uint64_t)(uint32_t)__builtin_amdgcn_readlane(sb_lo, jj);
-                const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)sp, (short)0, nrec_sc, 0x00020000);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sl.s[e] = buf_load16(sr, ok ? srow[e] + g0b : kOOB);
+                sl.s4[t] = buf_load16(sr, lwin[t] | oob);
             } else {
-                const u32x4 v = buf_load16(br, ok ? brow + (uint32_t)(64 * lu + 16 * G) : kOOB);
-                sl.w[0] = v.x;
-                sl.w[1] = v.y;
-                sl.w[2] = v.z;
-                sl.w[3] = v.w;
+                sl.s1[t] = SF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(sr, (int)(srow[t] | oob), 0, 0)
+                                : buf_load4(sr, srow[t] | oob);
             }
-            if (++lj == nusR) {
-                lj = 0;
-                ++lu;
-                if (GRP) g0b = (uint32_t)((4 * (int64_t)lu) / bpg) * SB;
-            }
-            return sl;
-        };
-        // the previous tile's readers of both buffers are done before new copies land
-        __builtin_amdgcn_s_barrier();
-        issue_enc(t, 0, 0);
-        Slot ring[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            ring[r] = load_slot();
-            __builtin_amdgcn_sched_barrier(0);
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-        int u = 0;
-        do {
-            BD_WAIT_VMCNT(RB * L);  // this wave's copies of unit u have landed
-            __builtin_amdgcn_s_barrier();  // and every wave's; buffer (u + 1) & 1 is free
-            if (u + 1 < nunit) issue_enc(t, u + 1, (u + 1) & 1);
-            const char* sb = sbuf + (u & 1) * kEncUnitBytes;
-            i32x6 hi[4], lo[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 c0 = *(const u32x4*)(sb + (3 * q + 0) * 1024 + 16 * lane);
-                const u32x4 c1 = *(const u32x4*)(sb + (3 * q + 1) * 1024 + 16 * lane);
-                const u32x4 c2 = *(const u32x4*)(sb + (3 * q + 2) * 1024 + 16 * lane);
-                hi[q] = i32x6{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y};
-                lo[q] = i32x6{(int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
+    };
+    auto l_advance = [&]() __attribute__((always_inline)) {
+        if (++lj == l_nusP) {
+            lj = 0;
+            if (++lu == nunit) {
+                lu = 0;
+                if (++lt < ntb) l_tile();
             }
-            const u32x4 cd = *(const u32x4*)(sb + 12 * 1024 + 16 * lane);
-            // GROUP: the slot element of product c's group (relative to the unit's first)
-            int gi[4];
             if (GRP) {
-                const int64_t g0 = (4 * (int64_t)u) / bpg;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) gi[c] = (int)((4 * (int64_t)u + c) / bpg - g0);
+                for (int t = 0; t < RT; ++t) lwin[t] = swin(lu, t);
             }
-            int j0 = 0;
-            do {
+        }
+    };
+
+    // ---- consumption side: step s (tile ct, unit cu), user cj
+    int s = 0, cu = 0, cj = 0, ct = 0, c_nus = 0, c_nusP = 0, bufc = 0, bufe = 2;
+    int c_tuser = -1, c_users = 0;  // lane n: user of token n; lane j: user j
+    auto c_tile = [&]() __attribute__((always_inline)) {
+        // past the last tile: no users and no step ends (empty slots to the end)
+        const bool in = ct < ntb;
+        const int32_t* tm = smeta + (in ? ct : 0) * kTileMetaInts;
+        const int nus = __builtin_amdgcn_readfirstlane(tm[48]);
+        c_nus = in ? nus : 0;
+        c_nusP = in ? nus : 0x40000000;
+        c_tuser = tm[16 + n];
+        c_users = tm[32 + n];
+    };
+    c_tile();
+
+    issue_enc(0, 0);
+    if (S > 1) issue_enc(1, 1);
+    // slots whose loads were issued; at that count the copies of steps s and s + 1 were issued
+    int nslot = kRing, mark0 = 0, mark1 = 0;
+    Slot ring[kRing];
 #pragma unroll
-                for (int r = 0; r < RB; ++r) {
-                    const int j = j0 + r;
-                    const Slot sl = ring[r];
-                    ring[r] = load_slot();
-                    if (j < nus) {  // uniform
-                        const int usr = __builtin_amdgcn_readlane(tusers, j);
-                        const bool mine = tok_user == usr;
-                        const uint32_t sh = mine ? cd.x : 0u, sl_ = mine ? cd.y : 0u;
-                        if (GRP) {
-#define BD_G(C)                                                                      \
-    {                                                                                \
-        const u32x4 a = expand(sl.w[C]);                                             \
-        f32x4 tmp = {0.f, 0.f, 0.f, 0.f};                                            \
-        tmp = mfma_f4f6<C>(a, hi[C], tmp, sh);                                       \
-        tmp = mfma_f4f6<C>(a, lo[C], tmp, sl_);                                      \
-        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                              \
-            float sc;                                                                \
-            if (SF16) {                                                              \
-                const uint32_t raw = sl.s[e][gi[C] >> 1];                            \
-                sc = f16_to_f32((uint16_t)(gi[C] & 1 ? raw >> 16 : raw));            \
-            } else {                                                                 \
-                sc = __uint_as_float(sl.s[e][gi[C]]);                                \
-            }                                                                        \
-            acc[e] -= sc * tmp[e];                                                   \
-        }                                                                            \
+    for (int r = 0; r < kRing; ++r) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) issue_w(ring[r], t);
+        issue_s(ring[r]);
+        l_advance();
     }
-                            BD_G(0) BD_G(1) BD_G(2) BD_G(3)
-#undef BD_G
-                        } else {
-                            const u32x4 a0 = expand(sl.w[0]), a1 = expand(sl.w[1]);
-                            const u32x4 a2 = expand(sl.w[2]), a3 = expand(sl.w[3]);
-                            acc = mfma_f4f6<0>(a0, hi[0], acc, sh);
-                            acc2 = mfma_f4f6<0>(a0, lo[0], acc2, sl_);
-                            acc = mfma_f4f6<1>(a1, hi[1], acc, sh);
-                            acc2 = mfma_f4f6<1>(a1, lo[1], acc2, sl_);
-                            acc = mfma_f4f6<2>(a2, hi[2], acc, sh);
-                            acc2 = mfma_f4f6<2>(a2, lo[2], acc2, sl_);
-                            acc = mfma_f4f6<3>(a3, hi[3], acc, sh);
-                            acc2 = mfma_f4f6<3>(a3, lo[3], acc2, sl_);
+    i32x6 hi[4], lo[4];
+    uint32_t cdh = 0, cdl = 0;
+    uint32_t cidx[RT][4];  // GROUP: window index of product c's scale, per row tile
+    bool gfast = true;     // GROUP: every lane's index of product c is c
+    f32x4 acc[RT], acc2[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cidx[t][c] = (uint32_t)c;
+    }
+    for (int k = 0; k < total; k += kRing) {
+#pragma unroll
+        for (int r = 0; r < kRing; ++r) {
+            if (cj == 0) {
+                // open step s: its operands are in (every wave's copies landed),
+                // buffer (s + 2) % 3 was last read in step s - 1
+                {
+                    // wait until at most the loads issued after this step's copy
+                    // (capped at kRing - 1 slots) are in flight
+                    const int after = nslot - mark0;
+                    if (after >= kRing - 1) {
+                        BD_WAIT_VMCNT((kRing - 1) * L);
+                    } else {
+                        switch (after) {
+                            case 0: BD_WAIT_VMCNT(0); break;
+                            case 1: BD_WAIT_VMCNT(1 * L); break;
+                            case 2: BD_WAIT_VMCNT(2 * L); break;
+                            case 3: BD_WAIT_VMCNT(3 * L); break;
+                            case 4: BD_WAIT_VMCNT(4 * L); break;
+                            case 5: BD_WAIT_VMCNT(5 * L); break;
+                            default: BD_WAIT_VMCNT(6 * L); break;
                         }
                     }
-                    __builtin_amdgcn_sched_barrier(0);
                 }
-                j0 += RB;
-            } while (j0 < nusR);
-            ++u;
-        } while (u < nunit);
-        // the ring's loads past the tile (zeros) land before the next tile's barrier
-        BD_WAIT_VMCNT(0);
-
-        // epilogue: Y[tok][rows] += f * sum; rows 4G + e of this wave's 16
-        if (tok >= 0 && r0 < d_out) {
-            const f32x4 v = acc + acc2;
-            const size_t ubs = (size_t)tok_user * per_user;
+                asm volatile("s_barrier" ::: "memory");
+                if (s + 2 < S) issue_enc(s + 2, bufe);
+                mark0 = mark1;
+                mark1 = nslot;
+                const char* sb = sbuf + bufc * kEncUnitBytes;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t o = r0 + 4 * G + e;
-                if (o >= d_out) continue;
-                float f;
-                if (MODE == BD_SCALE_MATRIX || MODE == BD_SCALE_ROW) {
-                    const size_t i = ubs + (MODE == BD_SCALE_ROW ? (size_t)o : 0);
-                    f = SF16 ? -f16_to_f32(((const uint16_t*)scales)[i]) : -((const float*)scales)[i];
-                } else if (MODE == BD_SCALE_COL) {
-                    f = -1.f;  // the scales are inside the encoded tokens
-                } else {
-                    f = 1.f;  // the group scales (negated) are applied per product
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 c0 = *(const u32x4*)(sb + (3 * q + 0) * 1024 + 16 * lane);
+                    const u32x4 c1 = *(const u32x4*)(sb + (3 * q + 1) * 1024 + 16 * lane);
+                    const u32x4 c2 = *(const u32x4*)(sb + (3 * q + 2) * 1024 + 16 * lane);
+                    hi[q] = i32x6{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y};
+                    lo[q] = i32x6{(int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
                 }
-                y[(int64_t)tok * d_out + o] += f * v[e];
+                const u32x4 cd = *(const u32x4*)(sb + 12 * 1024 + 16 * lane);
+                cdh = cd.x;
+                cdl = cd.y;
+                if (GRP) {
+                    bool moved = false;
+#pragma unroll
+                    for (int t = 0; t < RT; ++t) {
+                        const uint32_t w0 = swin(cu, t);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            uint32_t g = (4u * (uint32_t)cu + c) >> bsh;
+                            g = g < gpr ? g : gpr - 1u;
+                            cidx[t][c] = (srow[t] + g * SB - w0) / SB;
+                            moved |= cidx[t][c] != (uint32_t)c;
+                        }
+                    }
+                    gfast = __ballot(moved) == 0ull;
+                }
+            }
+            Slot& sl = ring[r];
+            const bool live = cj < c_nus;  // uniform
+            int usr = 0;
+            uint32_t sh = 0u, sl_ = 0u;
+            if (live) {
+                usr = __builtin_amdgcn_readlane(c_users, cj);
+                const bool mine = c_tuser == usr;
+                sh = mine ? cdh : 0u;
+                sl_ = mine ? cdl : 0u;
+            }
+            // every row tile's sign words expanded first (materialised here, not sunk
+            // into the branch below: the words must be dead before they are reloaded),
+            // then all reloads, then the products of all row tiles (independent chains)
+            u32x4 bx[RT][4];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                u32x4 wq = sl.w[t];
+                if (GRP) {
+                    // lane (j, g) holds group g's k-blocks 0..3; product c needs group c's
+                    // k-block g: a 4 x 4 transpose over the lane groups
+                    auto s32a = __builtin_amdgcn_permlane32_swap(wq.x, wq.z, false, false);
+                    auto s32b = __builtin_amdgcn_permlane32_swap(wq.y, wq.w, false, false);
+                    auto s16a = __builtin_amdgcn_permlane16_swap(s32a[0], s32b[0], false, false);
+                    auto s16b = __builtin_amdgcn_permlane16_swap(s32a[1], s32b[1], false, false);
+                    wq = u32x4{s16a[0], s16a[1], s16b[0], s16b[1]};
+                }
+                bx[t][0] = expand(wq.x);
+                bx[t][1] = expand(wq.y);
+                bx[t][2] = expand(wq.z);
+                bx[t][3] = expand(wq.w);
+                asm volatile("" ::"v"(bx[t][0]), "v"(bx[t][1]), "v"(bx[t][2]), "v"(bx[t][3]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) issue_w(sl, t);  // the slot kRing ahead, in place
+            __builtin_amdgcn_sched_barrier(0);
+            if (live) {
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    const u32x4 b0 = bx[t][0], b1 = bx[t][1], b2 = bx[t][2], b3 = bx[t][3];
+                    if (GRP) {
+                        u32x4 sv = sl.s4[t];
+                        if (!gfast) {  // (rare: the last rows, or groups above 128)
+                            auto pick = [&](uint32_t i) __attribute__((always_inline)) {
+                                if (SF16) {
+                                    const uint32_t d = i < 4u ? (i < 2u ? sv.x : sv.y) : (i < 6u ? sv.z : sv.w);
+                                    return i & 1u ? d >> 16 : d & 0xFFFFu;
+                                }
+                                return i < 2u ? (i == 0u ? sv.x : sv.y) : (i == 2u ? sv.z : sv.w);
+                            };
+                            sv = u32x4{pick(cidx[t][0]), pick(cidx[t][1]), pick(cidx[t][2]), pick(cidx[t][3])};
+                        } else if (SF16) {
+                            sv = u32x4{sv.x & 0xFFFFu, sv.x >> 16, sv.y & 0xFFFFu, sv.y >> 16};
+                        }
+#define BD_G(C, B, SC)                                                 \
+    {                                                                  \
+        f32x4 tt = {0.f, 0.f, 0.f, 0.f};                               \
+        tt = mfma_f6f4<C>(hi[C], B, tt, sh);                           \
+        tt = mfma_f6f4<C>(lo[C], B, tt, sl_);                          \
+        const float sc = SF16 ? f16_to_f32((uint16_t)(SC)) : __uint_as_float(SC); \
+        acc[t] -= sc * tt;                                             \
+    }
+                        BD_G(0, b0, sv.x) BD_G(1, b1, sv.y) BD_G(2, b2, sv.z) BD_G(3, b3, sv.w)
+#undef BD_G
+                    } else if (COL) {
+                        acc[t] = mfma_f6f4<0>(hi[0], b0, acc[t], sh);
+                        acc2[t] = mfma_f6f4<0>(lo[0], b0, acc2[t], sl_);
+                        acc[t] = mfma_f6f4<1>(hi[1], b1, acc[t], sh);
+                        acc2[t] = mfma_f6f4<1>(lo[1], b1, acc2[t], sl_);
+                        acc[t] = mfma_f6f4<2>(hi[2], b2, acc[t], sh);
+                        acc2[t] = mfma_f6f4<2>(lo[2], b2, acc2[t], sl_);
+                        acc[t] = mfma_f6f4<3>(hi[3], b3, acc[t], sh);
+                        acc2[t] = mfma_f6f4<3>(lo[3], b3, acc2[t], sl_);
+                    } else {
+                        f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};
+                        ta = mfma_f6f4<0>(hi[0], b0, ta, sh);
+                        tb = mfma_f6f4<0>(lo[0], b0, tb, sl_);
+                        ta = mfma_f6f4<1>(hi[1], b1, ta, sh);
+                        tb = mfma_f6f4<1>(lo[1], b1, tb, sl_);
+                        ta = mfma_f6f4<2>(hi[2], b2, ta, sh);
+                        tb = mfma_f6f4<2>(lo[2], b2, tb, sl_);
+                        ta = mfma_f6f4<3>(hi[3], b3, ta, sh);
+                        tb = mfma_f6f4<3>(lo[3], b3, tb, sl_);
+                        const uint32_t raw = sl.s1[MODE == BD_SCALE_ROW ? t : 0];
+                        const float sc = SF16 ? f16_to_f32((uint16_t)raw) : __uint_as_float(raw);
+                        acc[t] -= sc * (ta + tb);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue_s(sl);  // its scales, after their last use
+            l_advance();
+            ++nslot;
+            if (++cj == c_nusP) {
+                cj = 0;
+                ++s;
+                bufc = bufc == kNBuf - 1 ? 0 : bufc + 1;
+                bufe = bufe == kNBuf - 1 ? 0 : bufe + 1;
+                if (++cu == nunit) {
+                    // tile done: Y[token][row] += its sum; one add per element
+                    // (no-return atomics: nothing waits on them)
+                    cu = 0;
+                    const int32_t* tm = smeta + ct * kTileMetaInts;
+                    int tok[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tok[e] = tm[4 * G + e];
+#pragma unroll
+                    for (int t = 0; t < RT; ++t) {
+                        const int64_t o = rw0 + 16 * t + n;
+                        const f32x4 v = COL ? -(acc[t] + acc2[t]) : acc[t];
+                        if (o < d_out) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (tok[e] >= 0) unsafeAtomicAdd(y + (int64_t)tok[e] * d_out + o, v[e]);
+                        }
+                        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    ++ct;
+                    c_tile();
+                }
             }
         }
     }
 }
 
 // ---------------------------------------------------------------- host side
+hipError_t launch_tile_plan(const BatchPlan& bp, char* batch, hipStream_t s) {
+    if (bp.xdtype != BD_BF16 || bp.T == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(64), 0, s, (const int4*)(batch + bp.off_items),
+                       (uint32_t*)(batch + bp.off_meta), (int32_t*)(batch + bp.off_tiles),
+                       (int)bp.ntiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, const void* x,
                          const uint64_t* signs, const void* scales, float* y, hipStream_t s) {
     const uint32_t* meta = (const uint32_t*)(batch + bp.off_meta);
@@ -410,38 +629,63 @@ hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, 
     const int ntiles = (int)bp.ntiles, nunit = (int)bp.nunit;
     const bool grp = dp.mode == BD_SCALE_GROUP, col = dp.mode == BD_SCALE_COL;
     const dim3 ge((unsigned)ntiles, (unsigned)nunit);
+    const int32_t* tiles = (const int32_t*)(batch + bp.off_tiles);
 #define BD_ENC(G, C)                                                                           \
     hipLaunchKernelGGL((k_tile_encode<G, C>), ge, dim3(256), 0, s, (const uint16_t*)x, bp.T,   \
-                       bp.d_in, perm, suser, meta, scales, dp.sdtype, dp.per_user, tmeta, enc)
+                       bp.d_in, perm, suser, meta, tiles, scales, dp.sdtype, dp.per_user, tmeta, \
+                       enc)
     if (grp) BD_ENC(true, false);
     else if (col) BD_ENC(false, true);
     else BD_ENC(false, false);
 #undef BD_ENC
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // enough blocks for four per CU: tiles per block from the row tiles and the tiles
-    const int64_t rtiles = (dp.d_out + 63) / 64;
-    int64_t tpb = rtiles * ntiles / 1024;
-    tpb = tpb < 1 ? 1 : (tpb > ntiles ? ntiles : tpb);
-    const dim3 gd((unsigned)rtiles, (unsigned)((ntiles + tpb - 1) / tpb));
-    const int bpg = grp ? dp.group / 128 : 1;
-#define BD_D6(MODE, F16)                                                                         \
-    hipLaunchKernelGGL((k_delta6<MODE, F16>), gd, dim3(256), 0, s, signs, scales, dp.per_user,  \
-                       bpg, (const int32_t*)tmeta, (const char*)enc, meta, y, bp.d_in, dp.d_out, \
+    // row tiles per wave: the most (fewer copies of the tile operands per sign byte)
+    // that still give every CU two blocks of work at one tile per block; GROUP and ROW
+    // at most two (register budget)
+    const int rtmax = grp || dp.mode == BD_SCALE_ROW ? 2 : 4;
+    int rt = 1;
+    const int64_t ntyp = (bp.T + 15) / 16;  // tiles of a batch of small users, about
+    while (rt < rtmax && ((dp.d_out + 128 * rt - 1) / (128 * rt)) * ntyp >= 512) rt *= 2;
+    // one tile per block (grid rows for the bound of tiles; blocks past the batch's
+    // tiles exit at once): every block has the same work, whatever the tile count
+    const int64_t rtiles = (dp.d_out + 64 * rt - 1) / (64 * rt);
+    const int64_t tpb = 1;
+    const dim3 gd((unsigned)rtiles, (unsigned)ntiles);
+    int bsh = 0;
+    while (grp && (128 << bsh) < dp.group) ++bsh;
+#define BD_D6(MODE, F16, RT)                                                                      \
+    hipLaunchKernelGGL((k_delta6<MODE, F16, RT>), gd, dim3(256), 0, s, signs, scales, dp.per_user, \
+                       bsh, (const int32_t*)tmeta, (const char*)enc, meta, y, bp.d_in, dp.d_out,   \
                        nunit, (int)tpb)
+#define BD_D6R(MODE, F16)                              \
+    do {                                               \
+        if (rt == 4) BD_D6(MODE, F16, 4);              \
+        else if (rt == 2) BD_D6(MODE, F16, 2);         \
+        else BD_D6(MODE, F16, 1);                      \
+    } while (0)
     const bool f16 = dp.sdtype == BD_F16;
     switch (dp.mode) {
         case BD_SCALE_MATRIX:
-            if (f16) BD_D6(BD_SCALE_MATRIX, true); else BD_D6(BD_SCALE_MATRIX, false);
+            if (f16) BD_D6R(BD_SCALE_MATRIX, true); else BD_D6R(BD_SCALE_MATRIX, false);
             break;
         case BD_SCALE_GROUP:
-            if (f16) BD_D6(BD_SCALE_GROUP, true); else BD_D6(BD_SCALE_GROUP, false);
+            if (f16) {
+                if (rt == 2) BD_D6(BD_SCALE_GROUP, true, 2); else BD_D6(BD_SCALE_GROUP, true, 1);
+            } else {
+                if (rt == 2) BD_D6(BD_SCALE_GROUP, false, 2); else BD_D6(BD_SCALE_GROUP, false, 1);
+            }
             break;
         case BD_SCALE_ROW:
-            if (f16) BD_D6(BD_SCALE_ROW, true); else BD_D6(BD_SCALE_ROW, false);
+            if (f16) {
+                if (rt == 2) BD_D6(BD_SCALE_ROW, true, 2); else BD_D6(BD_SCALE_ROW, true, 1);
+            } else {
+                if (rt == 2) BD_D6(BD_SCALE_ROW, false, 2); else BD_D6(BD_SCALE_ROW, false, 1);
+            }
             break;
-        default: BD_D6(BD_SCALE_COL, false); break;
+        default: BD_D6R(BD_SCALE_COL, false); break;
     }
+#undef BD_D6R
 #undef BD_D6
     return hipGetLastError();
 }

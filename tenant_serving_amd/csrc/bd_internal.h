@@ -49,9 +49,11 @@ constexpr int kMaxGroupT = 8192;  // tokens the one-block grouping kernel sorts 
 constexpr int kMaxUsers = (1 << 17) - 1;
 
 // Prepared batch (bd_batch_prepare): tokens grouped by user into work items; for
-// bf16 inputs also the tiles of the delta products (bd_delta.hip): per tile of 16
-// sorted positions kTileMetaInts ints of meta, per (tile, 512-column unit)
-// kEncUnitBytes of encoded token operands.
+// bf16 inputs also the tiles of the delta products (bd_delta.hip): runs of at most
+// 16 sorted positions that split no user of at most 16 tokens (their number, at
+// most 2 ceil(T / 16) + 1, in meta[3]; start and length per tile), per tile
+// kTileMetaInts ints of meta, per (tile, 512-column unit) kEncUnitBytes of encoded
+// token operands.
 constexpr int kTileMetaInts = 64;
 constexpr int kEncUnitBytes = 13 * 1024;
 struct BatchPlan {
@@ -59,7 +61,8 @@ struct BatchPlan {
     int32_t U = 0;
     int xdtype = 0;
     int64_t max_items = 0, ntiles = 0, nunit = 0;
-    size_t off_meta = 0, off_perm = 0, off_user = 0, off_items = 0, off_tmeta = 0, off_enc = 0;
+    size_t off_meta = 0, off_perm = 0, off_user = 0, off_items = 0, off_tiles = 0, off_tmeta = 0,
+           off_enc = 0;
     size_t total = 0;
 };
 
@@ -108,6 +111,7 @@ hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 // bf16 delta products of a prepared batch (writes the batch's tile meta and encoded
 // tokens, then adds into y).
+hipError_t launch_tile_plan(const BatchPlan& bp, char* batch, hipStream_t s);
 hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, const void* x,
                          const uint64_t* signs, const void* scales, float* y, hipStream_t s);
 
