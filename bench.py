@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="output rows of the oracle's sampled apply")
+    ap.add_argument("--workloads", action="store_true",
+                    help="also time one layer step of workloads 3-5 (stderr, one JSON line each)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device 3 times (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters)")
@@ -278,6 +280,88 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ids_np, args.cpu_rows, bytes_step)
     print(json.dumps(out), flush=True)
+    if args.workloads:
+        for line in workloads_leg():
+            print(json.dumps(line), file=sys.stderr, flush=True)
+
+
+def workloads_leg(reps=10):
+    """One layer step of workloads 3, 4 and 5 through the prepared-batch calls: per
+    distinct input width one bd_batch_prepare (the grouping and tile packing of the
+    batch), then per matrix bd_base_gemm and bd_delta_apply.  Random banks (the time
+    does not depend on the bit values; parity at these sizes is tested separately).
+    The step is captured `reps` times in a HIP graph and replayed."""
+    import torch
+
+    from tenant_serving_amd import bitdelta as B
+    from tenant_serving_amd import synth as S
+
+    dev = torch.device("cuda:0")
+    out = []
+    for wid in (3, 4, 5):
+        w = S.workload(wid)
+        ids_np = S.user_ids(w)
+        ids = torch.from_numpy(ids_np).to(dev)
+        T, U = w.T, w.n_users
+        nact = len(set(int(u) for u in ids_np if 0 <= u < U))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 + wid)
+        xs, batches, mats = {}, {}, []
+        tot_bytes = tot_flops = 0
+        for m in w.matrices:
+            p = B.params(m.mode, w.group_size, w.clip_k,
+                         B.BD_F16 if m.scale_dtype == S.S_F16 else B.BD_F32)
+            wb = (torch.randn(m.d_out, m.d_in, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+            signs = torch.randint(-2**62, 2**62, (U, m.d_out, m.d_in // 64), dtype=torch.int64,
+                                  device=dev, generator=gen)
+            n_sc = B.bd_scales_count(p, m.d_out, m.d_in)
+            scales = (torch.rand(U, n_sc, device=dev, generator=gen) * 1e-3).to(B.scales_dtype(p))
+            if m.xgroup not in xs:
+                xs[m.xgroup] = torch.randn(T, m.d_in, device=dev, generator=gen).to(torch.bfloat16)
+            if m.d_in not in batches:
+                batches[m.d_in] = (xs[m.xgroup], B.workspace(
+                    B.bd_batch_workspace_bytes(T, U, m.d_in, B.BD_BF16), dev))
+            y = torch.empty(T, m.d_out, device=dev)
+            mats.append((xs[m.xgroup], p, wb, signs, scales, y, batches[m.d_in][1]))
+            tot_bytes += (m.d_out * m.d_in * 2 + nact * (m.d_out * m.d_in // 8 + scales.element_size() * n_sc)
+                          + T * m.d_in * 2 + T * m.d_out * 4 + 4 * T)
+            tot_flops += 2 * T * m.d_out * m.d_in
+
+        def step():
+            for x, bt in batches.values():
+                assert B.bd_batch_prepare(x, ids, U, bt) == B.BD_OK
+            for x, p, wb, signs, scales, y, bt in mats:
+                assert B.bd_base_gemm(x, wb, y) == B.BD_OK
+                assert B.bd_delta_apply(bt, x, U, signs, scales, p, y) == B.BD_OK
+
+        step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                step()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out.append({"workload": w.name, "matrices": len(w.matrices), "tokens": T, "n_users": U,
+                    "active_users": nact, "us_per_step": round(us, 1),
+                    "algorithmic_bytes": tot_bytes, "achieved_GBs": round(tot_bytes / us / 1e3, 1),
+                    "frac_of_hbm_peak": round(tot_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                    "base_TFLOPs": round(tot_flops / us / 1e6, 1)})
+        del mats, xs, batches, g
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, ids_np, rows, bytes_step):

@@ -8,16 +8,12 @@
 // Kernels, in launch order (bf16 path):
 //   k_group      one block: sorts (user, token) keys with a bitonic network in
 //                LDS, so tokens of a user are contiguous and in token order;
-//                emits work items of <= kItemTokens tokens of one user.
-//   k_base_gemm  Y = X W_base^T with v_mfma_f32_16x16x32_bf16, fp32 out.
-//   k_delta      per (64-row tile, work item): gathers the item's X rows into
-//                LDS with every 32-column block permuted to the order in which
-//                bit pairs are unpacked (COL scales applied there), streams the
-//                user's packed rows once, turns bits into +-1 bf16 MFMA
-//                operands in registers, accumulates X S^T in fp32 and adds
-//                scale * sum into Y.  Each Y element belongs to one item: no
-//                atomics.
-// fp32 inputs take plain VALU kernels (reference-grade, fp32 FMA).
+//                emits work items of <= kItemTokens tokens of one user (the tile
+//                packing of bd_delta.hip reads them).
+//   k_base_gemm  Y = X W_base^T with v_mfma_f32_16x16x32_bf16, fp32 out, for
+//                16 < T <= 64 (larger batches: k_gemm, bd_gemm.hip).
+// The delta products of bf16 batches are in bd_delta.hip; fp32 inputs take plain
+// VALU kernels (reference-grade, fp32 FMA).
 #include "bd_internal.h"
 
 namespace bd {
@@ -26,7 +22,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -187,29 +182,7 @@ k_group_wave(const int32_t* __restrict__ ids, int T, int U, int32_t* __restrict_
     }
 }
 
-constexpr int kDeltaWaves = 4;           // 64 output rows per block
-constexpr int kChunk = 512;               // columns per bit-word load of a lane (non-GROUP)
-constexpr int kStageBytes = 40 * 1024;    // LDS for the staged activations of one item (4 blocks/CU)
-static_assert((kItemTokens + 1) * (kChunk / 8 + kChunk / 128 + 1) * 16 <= kStageBytes,
-              "a full item (plus its zero row) must fit one chunk-wide LDS stage");
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset past num_records: the load returns 0
-
-// Columns of one LDS stage for an item of n tokens: the largest multiple of 4
-// chunks whose n+1 padded rows fit kStageBytes, else of one chunk; capped at
-// d_in rounded up to a chunk.
-// A staged row of KC columns takes KC/8 16-byte units plus one pad unit per
-// 16 units (so the 4 lane groups, 256 bytes apart, start in different banks)
-// plus one (an odd pitch spreads consecutive rows over the banks).
-__device__ __forceinline__ int stage_pitch16(int64_t KC) { return (int)(KC / 8 + KC / 128 + 1); }
-__device__ __forceinline__ int stage_phys16(int c16) { return c16 + (c16 >> 4); }
-__device__ __forceinline__ int64_t stage_cols(int n, int64_t d_in) {
-    const int64_t dpad = (d_in + kChunk - 1) / kChunk * kChunk;
-    const int64_t fit16 = (int64_t)kStageBytes / 16 / (n + 1) - 1;  // units per row
-    const int64_t fit = fit16 * 128 / 17;                            // columns
-    int64_t kc = fit / (4 * kChunk) * (4 * kChunk);
-    if (kc == 0) kc = fit / kChunk * kChunk;
-    return kc < dpad ? kc : dpad;
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
     const int nrec = bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
@@ -217,9 +190,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
@@ -312,278 +282,9 @@ k_base_gemm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, floa
     }
 }
 
-// ------------------------------------------------------------ delta apply
-// A operand of one MFMA step from a 32-bit word of packed signs: element pair
-// j of step q takes bits (4q + j) and (4q + j + 16) into the two bf16 sign
-// positions.  Bit 1 (+1) gives -1.0 and bit 0 gives +1.0, so the accumulator
-// holds -(X S^T); the epilogue multiplies by -scale.
-__device__ __forceinline__ u32x4 expand_pairs(uint32_t d, int q, uint32_t mask, uint32_t one) {
-    u32x4 a;
-    a.x = ((d << (15 - 4 * q)) & mask) | one;
-    a.y = ((d << (14 - 4 * q)) & mask) | one;
-    a.z = ((d << (13 - 4 * q)) & mask) | one;
-    a.w = ((d << (12 - 4 * q)) & mask) | one;
-    return a;
-}
-
+// Scale i of a user (fp32 or fp16 storage).
 __device__ __forceinline__ float load_scale(const void* s, int sdtype, int64_t i) {
     return sdtype == BD_F16 ? f16_to_f32(((const uint16_t*)s)[i]) : ((const float*)s)[i];
-}
-
-
-// One block = 64 output rows (4 waves x 16) of one work item (one user, <= 32
-// of its tokens).  The item's reordered activations are staged in LDS, as many
-// columns per stage as fit (the whole row for decode-sized items), with one
-// all-zero row that lanes of absent tokens read.  Every lane streams its row's
-// packed bits through a ring of 4 register slots (16 bytes = 512 columns per
-// slot), each reloaded in place right after use, so 4 KB per wave stay in
-// flight from HBM while the MFMAs run.  Each 512-column chunk is 16 MFMA steps
-// per 16-token tile:
-//  non-GROUP: lane group g owns columns [128g, 128g+128) of the chunk;
-//  GROUP:     128-column block c of the chunk is one MFMA step set, lane group
-//             g takes its 32-column quarter g, so every step stays in one group.
-// NTL (token tiles) is a template parameter so accumulators stay in registers.
-template <int MODE, int NTL, bool BIG>
-__device__ __forceinline__ void delta_item(
-    const uint16_t* __restrict__ x, int64_t T, const uint64_t* __restrict__ signs,
-    const void* __restrict__ scales, int sdtype, int64_t per_user, int group, int u, int b, int n,
-    const int32_t* __restrict__ perm, float* __restrict__ y, int64_t d_in, int64_t d_out) {
-    extern __shared__ u32x4 xs_raw[];  // kStageBytes, dynamic
-    __shared__ int32_t tok[kItemTokens];
-    if (threadIdx.x < n) tok[threadIdx.x] = perm[b + threadIdx.x];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
-    const int64_t r0 = (int64_t)blockIdx.x * (16 * kDeltaWaves) + 16 * wv;
-    const bool wave_active = r0 < d_out;
-    const int64_t rowA = r0 + m < d_out ? r0 + m : d_out - 1;
-
-    // stage geometry (in 16-byte units): rows 0..n-1 hold tokens, row n is zero.
-    // BIG: KC is a multiple of 4 chunks (or covers d_in), so stages start only at
-    // ring-group boundaries.
-    const int64_t KC = stage_cols(n, d_in);
-    const int pitch16 = stage_pitch16(KC);  // 16-byte units per staged row (padded)
-    const int pieces_row = (int)(KC / 8);
-
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)T * d_in * 2);
-    const __amdgpu_buffer_rsrc_t br =
-        make_rsrc(signs + (int64_t)u * d_out * (d_in / 64), (uint64_t)d_out * (d_in / 8));
-    const uint32_t row_byte = (uint32_t)(rowA * (d_in / 8));
-    const void* su = (const char*)scales + (size_t)u * per_user * (sdtype == BD_F16 ? 2 : 4);
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(su, (uint64_t)per_user * (sdtype == BD_F16 ? 2 : 4));
-    // operand constants kept in registers: gfx9 VOP3 encodings take no literals,
-    // so this lets the expansion use v_and_or_b32
-    uint32_t kmask, kone;
-    asm volatile("v_mov_b32 %0, 0x80008000" : "=v"(kmask));
-    asm volatile("s_mov_b32 %0, 0x3f803f80" : "=s"(kone));
-
-    auto bload = [&](int64_t kb) {
-        u32x4 D;
-        if (MODE == BD_SCALE_GROUP) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int64_t col = kb + 128 * c + 32 * g;
-                D[c] = buf_load4(br, col < d_in ? row_byte + (uint32_t)(col / 8) : kOOB);
-            }
-        } else {
-            // columns past d_in in the last word read the next row's bits (or 0 past
-            // the bank): they meet zero activations, so they add nothing
-            const int64_t col = kb + 128 * g;
-            D = buf_load16(br, col < d_in ? row_byte + (uint32_t)(col / 8) : kOOB);
-        }
-        return D;
-    };
-    u32x4 D0 = bload(0), D1 = bload(kChunk), D2 = bload(2 * kChunk), D3 = bload(3 * kChunk);
-
-    for (int p = threadIdx.x; p < pieces_row; p += 64 * kDeltaWaves)
-        xs_raw[n * pitch16 + stage_phys16(p)] = u32x4{0, 0, 0, 0};
-
-    f32x4 acc[NTL], accp[NTL];
-    int xrow16[NTL];  // staged row of this lane's token, in 16-byte units
-#pragma unroll
-    for (int nt = 0; nt < NTL; ++nt) {
-        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accp[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int slot = 16 * nt + m;
-        xrow16[nt] = (slot < n ? slot : n) * pitch16;
-    }
-    const int64_t gpr = MODE == BD_SCALE_GROUP ? d_in / group : 1;
-    const int bpg = MODE == BD_SCALE_GROUP ? group / 128 : 1;
-
-    // Stage KC columns of the item's activations starting at column s0 (whole
-    // block).  Piece (row, c16) is LDS columns 8*c16 .. +7 of the stage, i.e.
-    // positions 8q..8q+7 of a 32-column block, which hold the natural columns
-    // 4q..4q+3 and 4q+16..4q+19 interleaved (the bit-pair order of expand_pairs).
-    auto stage = [&](int64_t s0) {
-        __syncthreads();  // readers of the previous stage are done (and tok[] is set)
-        const int total = n * pieces_row;
-        for (int p0 = threadIdx.x; p0 < total; p0 += 2 * 64 * kDeltaWaves) {
-            u32x2 va[2], vb[2];
-            int64_t kcol[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int p = p0 + j * 64 * kDeltaWaves;
-                const int row = p < total ? p / pieces_row : 0, c16 = p - row * pieces_row;
-                const int64_t k0 = s0 + 32 * (c16 >> 2) + 4 * (c16 & 3);
-                kcol[j] = k0;
-                const bool ok = p < total && k0 < d_in;
-                const uint32_t off = ok ? (uint32_t)((tok[row] * d_in + k0) * 2) : kOOB;
-                va[j] = buf_load8(xr, off);
-                vb[j] = buf_load8(xr, ok ? off + 32 : kOOB);
-            }
-            // every load is consumed (pieces past the item store their zeros into the
-            // zero row), so no load stays pending on a register the loop reuses
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int p = p0 + j * 64 * kDeltaWaves;
-                const int row = p < total ? p / pieces_row : 0, c16 = p - row * pieces_row;
-                u32x4 o;
-                if (MODE == BD_SCALE_COL) {
-                    // column scales of this user: natural columns k0..k0+3, k0+16..k0+19
-                    const int64_t k0 = kcol[j] < d_in ? kcol[j] : 0;
-                    float sa[4], sb[4];
-                    if (sdtype == BD_F16) {
-                        const u32x2 ha = buf_load8(sr, (uint32_t)(k0 * 2));
-                        const u32x2 hb = buf_load8(sr, (uint32_t)((k0 + 16) * 2));
-                        sa[0] = f16_to_f32((uint16_t)ha.x); sa[1] = f16_to_f32((uint16_t)(ha.x >> 16));
-                        sa[2] = f16_to_f32((uint16_t)ha.y); sa[3] = f16_to_f32((uint16_t)(ha.y >> 16));
-                        sb[0] = f16_to_f32((uint16_t)hb.x); sb[1] = f16_to_f32((uint16_t)(hb.x >> 16));
-                        sb[2] = f16_to_f32((uint16_t)hb.y); sb[3] = f16_to_f32((uint16_t)(hb.y >> 16));
-                    } else {
-                        const u32x4 fa = buf_load16(sr, (uint32_t)(k0 * 4));
-                        const u32x4 fb = buf_load16(sr, (uint32_t)((k0 + 16) * 4));
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            sa[e] = __uint_as_float(fa[e]);
-                            sb[e] = __uint_as_float(fb[e]);
-                        }
-                    }
-                    const float xa[4] = {bf16_lo(va[j].x), bf16_hi(va[j].x), bf16_lo(va[j].y), bf16_hi(va[j].y)};
-                    const float xb[4] = {bf16_lo(vb[j].x), bf16_hi(vb[j].x), bf16_lo(vb[j].y), bf16_hi(vb[j].y)};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o[e] = (uint32_t)f32_to_bf16(xa[e] * sa[e]) | ((uint32_t)f32_to_bf16(xb[e] * sb[e]) << 16);
-                } else {
-                    o.x = (va[j].x & 0xFFFFu) | (vb[j].x << 16);
-                    o.y = (va[j].x >> 16) | (vb[j].x & 0xFFFF0000u);
-                    o.z = (va[j].y & 0xFFFFu) | (vb[j].y << 16);
-                    o.w = (va[j].y >> 16) | (vb[j].y & 0xFFFF0000u);
-                }
-                xs_raw[p < total ? row * pitch16 + stage_phys16(c16)
-                                 : n * pitch16 + stage_phys16(p % pieces_row)] =
-                    p < total ? o : u32x4{0, 0, 0, 0};
-            }
-        }
-        __syncthreads();
-    };
-    // One 512-column chunk: 16 MFMA steps per token tile with the bit words D.
-    auto chunk = [&](int64_t kb, const u32x4 D) {
-        if (!BIG && kb % KC == 0) stage(kb);  // uniform over the block
-        if (!wave_active) return;
-        const int lc16 = (int)((kb % KC) / 8);  // chunk start inside the stage, 16-byte units
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // 16-byte unit of this MFMA step set (4 consecutive units, one per q); the
-            // 4 units never cross a 16-unit boundary, so one pad offset serves them
-            const int col16 = stage_phys16(lc16 + (MODE == BD_SCALE_GROUP ? 16 * c + 4 * g : 16 * g + 4 * c));
-            u32x4 A[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) A[q] = expand_pairs(D[c], q, kmask, kone);
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                u32x4 Bv[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) Bv[q] = xs_raw[xrow16[nt] + col16 + q];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (MODE == BD_SCALE_GROUP) accp[nt] = mfma_bf16(A[q], Bv[q], accp[nt]);
-                    else acc[nt] = mfma_bf16(A[q], Bv[q], acc[nt]);
-                }
-            }
-            if (MODE == BD_SCALE_GROUP) {
-                const int64_t G = kb / 128 + c;  // global 128-column block
-                if (G * 128 < d_in && (G + 1) % bpg == 0) {
-                    const int64_t gi = G / bpg;
-                    float sc[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        int64_t o = r0 + 4 * g + e;
-                        o = o < d_out ? o : d_out - 1;
-                        sc[e] = -load_scale(su, sdtype, o * gpr + gi);
-                    }
-#pragma unroll
-                    for (int nt = 0; nt < NTL; ++nt) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[nt][e] += accp[nt][e] * sc[e];
-                        accp[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
-                }
-            }
-        }
-    };
-    for (int64_t kb = 0; kb < d_in; kb += 4 * kChunk) {
-        if (BIG && kb % KC == 0) stage(kb);
-        chunk(kb, D0);
-        D0 = bload(kb + 4 * kChunk);
-        if (kb + kChunk < d_in) chunk(kb + kChunk, D1);
-        D1 = bload(kb + 5 * kChunk);
-        if (kb + 2 * kChunk < d_in) chunk(kb + 2 * kChunk, D2);
-        D2 = bload(kb + 6 * kChunk);
-        if (kb + 3 * kChunk < d_in) chunk(kb + 3 * kChunk, D3);
-        D3 = bload(kb + 7 * kChunk);
-    }
-    if (!wave_active) return;
-
-    // epilogue: Y[t][o] += factor * acc (one 16-byte read-modify-write per lane and tile)
-    float f[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        int64_t o = r0 + 4 * g + e;
-        o = o < d_out ? o : d_out - 1;
-        if (MODE == BD_SCALE_MATRIX) f[e] = -load_scale(su, sdtype, 0);
-        else if (MODE == BD_SCALE_ROW) f[e] = -load_scale(su, sdtype, o);
-        else if (MODE == BD_SCALE_COL) f[e] = -1.0f;
-        else f[e] = 1.0f;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NTL; ++nt) {
-        const int slot = 16 * nt + m;
-        if (slot >= n) continue;
-        const int64_t t = perm[b + slot];
-        const int64_t o = r0 + 4 * g;
-        float* dst = y + t * d_out + o;
-        if (o + 3 < d_out && (d_out & 3) == 0) {
-            f32x4 v = *(f32x4*)dst;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] += acc[nt][e] * f[e];
-            *(f32x4*)dst = v;
-        } else {
-            for (int e = 0; e < 4; ++e)
-                if (o + e < d_out) dst[e] += acc[nt][e] * f[e];
-        }
-    }
-}
-
-template <int MODE>
-__global__ void __launch_bounds__(64 * kDeltaWaves)
-k_delta(const uint16_t* __restrict__ x, int64_t T, const uint64_t* __restrict__ signs,
-        const void* __restrict__ scales, int sdtype, int64_t per_user, int group,
-        const int4* __restrict__ items, const uint32_t* __restrict__ meta,
-        const int32_t* __restrict__ perm, float* __restrict__ y, int64_t d_in, int64_t d_out) {
-    const int item = blockIdx.y;
-    if (item >= (int)meta[1]) return;  // uniform over the block
-    const int4 it = items[item];
-    const bool big = stage_cols(it.z, d_in) % (4 * kChunk) == 0 || stage_cols(it.z, d_in) >= d_in;
-#define BD_ITEM(NTL, BIG)                                                                          \
-    delta_item<MODE, NTL, BIG>(x, T, signs, scales, sdtype, per_user, group, it.x, it.y, it.z, perm, \
-                               y, d_in, d_out)
-    if (it.z <= 16) {
-        if (big) BD_ITEM(1, true);
-        else BD_ITEM(1, false);
-    } else {
-        if (big) BD_ITEM(2, true);
-        else BD_ITEM(2, false);
-    }
-#undef BD_ITEM
 }
 
 __global__ void __launch_bounds__(256) k_cast_bf16(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
@@ -819,30 +520,14 @@ hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                         hipStream_t s) {
     if (bp.T == 0) return hipSuccess;
     if (bp.xdtype == BD_BF16) return launch_delta6(bp, dp, batch, x, signs, scales, y, s);
-    const uint32_t* meta = (const uint32_t*)(batch + bp.off_meta);
-    const int32_t* perm = (const int32_t*)(batch + bp.off_perm);
     const int32_t* row_user = (const int32_t*)(batch + bp.off_user);
-    const int4* items = (const int4*)(batch + bp.off_items);
     if (bp.xdtype == BD_F32) {
         hipLaunchKernelGGL(k_delta_f32, dim3(grid_1d(bp.T * dp.d_out, 256, 1ll << 30)), dim3(256), 0,
                            s, (const float*)x, row_user, bp.U, signs, scales, dp.sdtype, dp.per_user,
                            dp.mode, dp.group, y, bp.T, bp.d_in, dp.d_out);
         return hipGetLastError();
     }
-    const dim3 gd((unsigned)((dp.d_out + 16 * kDeltaWaves - 1) / (16 * kDeltaWaves)),
-                  (unsigned)bp.max_items);
-#define BD_DELTA(MODE)                                                                              \
-    hipLaunchKernelGGL(k_delta<MODE>, gd, dim3(64 * kDeltaWaves), kStageBytes, s,                  \
-                       (const uint16_t*)x, bp.T, signs, scales, dp.sdtype, dp.per_user, dp.group,  \
-                       items, meta, perm, y, bp.d_in, dp.d_out)
-    switch (dp.mode) {
-        case BD_SCALE_MATRIX: BD_DELTA(BD_SCALE_MATRIX); break;
-        case BD_SCALE_GROUP: BD_DELTA(BD_SCALE_GROUP); break;
-        case BD_SCALE_ROW: BD_DELTA(BD_SCALE_ROW); break;
-        default: BD_DELTA(BD_SCALE_COL); break;
-    }
-#undef BD_DELTA
-    return hipGetLastError();
+    return hipErrorInvalidValue;  // (unreachable: bf16 and fp32 are the only x dtypes)
 }
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
