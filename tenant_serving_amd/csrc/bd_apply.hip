@@ -403,7 +403,7 @@ bd_status make_batch_plan(int64_t T, int32_t U, int64_t d_in, int xdtype, BatchP
     off += align_up(sizeof(int4) * (size_t)q.max_items);
     if (xdtype == BD_BF16) {
         q.ntiles = 2 * (int64_t)((Tn + 15) / 16) + 1;  // bound of the packed tiles
-        q.nunit = (d_in + 511) / 512;
+        q.nunit = 2 * ((d_in + 1023) / 1024);  // even: the delta steps take two units
         q.off_tiles = off;
         off += align_up(sizeof(int32_t) * ((size_t)q.ntiles + 1));
         q.off_tmeta = off;

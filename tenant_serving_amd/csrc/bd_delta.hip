@@ -216,62 +216,57 @@ k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
 }
 
 // ------------------------------------------------------------ delta products
-// Block (64 RT output rows, tiles [t0, t0 + ntb)), 4 waves of RT row tiles of 16
-// rows.  The block's work is one sequence of slots: tile by tile, unit by unit (a
-// step), one slot per user of the tile.  Each wave keeps the loads of its next
-// kRing slots in flight in a ring of registers: a slot's sign words are expanded
-// first, and only then are its registers reloaded, in place, with the slot kRing
-// ahead (its scales likewise after their last use), so no register copy on a loop
-// edge ever waits for a load in flight.  The tile operands of step s are in LDS
-// buffer s % 3; their copy is issued right after the barrier that opens step s - 2,
-// and the opening of step s waits until at most as many loads are in flight as
-// were issued after that copy (at most kRing - 1 slots' worth).  RT row tiles share
-// each copy of the tile operands: the copies, which also pass through the L1 of the
-// CU, cost 13 KB per step against 4 KB of sign rows per user and row tile.  MFMA:
-// A = the tile's 16 tokens (fp6 hi and lo; tokens of other users take block code 0,
-// i.e. scale 2^-127), B = 16 sign rows (fp4 +-1); lane (j, g) of D holds tokens
-// 4 g .. 4 g + 3 of output row j of the row tile.
-constexpr int kNBuf = 3;     // LDS buffers of tile operands
-constexpr int kMaxTpb = 64;  // tiles per block, at most (their meta is held in LDS)
+// Block (128 RT output rows, one tile), 8 waves of RT row tiles of 16 rows.  The
+// work is a sequence of slots: step by step (two 512-column units, 2s and 2s + 1),
+// user by user of the tile, two slots per user: its sign rows' 64 bytes of unit 2s
+// and then of unit 2s + 1, so the two halves of every 128-byte line are read by
+// consecutive loads of a wave (a row's next bytes come RT loads later).  Each wave
+// keeps the loads of its next kRing slots in flight in a ring of registers: a slot's
+// sign words are expanded first and only then reloaded, in place, with the slot
+// kRing ahead (its scales likewise after their last use), so no register copy on a
+// loop edge waits for a load in flight.  A step's encoded tokens (26 KB) come into
+// LDS buffer s % 3, copied two steps ahead and shared by the 8 waves; the opening of
+// step s waits until no more loads are in flight than were issued after that copy.
+// Each slot reads its unit's operands from LDS (13 KB per wave and slot, read while
+// the sign words are expanded).  Steps hold an even number of slots and kRing is
+// even, so the unit of the slot at ring position r is r & 1.
+// MFMA: A = the tile's 16 tokens (fp6 hi and lo; tokens of other users take block
+// code 0, i.e. scale 2^-127), B = 16 sign rows (fp4 +-1); lane (j, g) of D holds
+// tokens 4 g .. 4 g + 3 of output row j of the row tile.
+constexpr int kNBuf = 3;                       // LDS buffers of step operands
+constexpr int kStepBytes = 2 * kEncUnitBytes;  // two units
+constexpr int kWaves = 8;
 
 template <int MODE, bool SF16, int RT>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(64 * kWaves)
 k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, int64_t per_user,
          int bsh, const int32_t* __restrict__ tmeta, const char* __restrict__ enc,
          const uint32_t* __restrict__ meta, float* __restrict__ y, int64_t d_in, int64_t d_out,
-         int nunit, int tpb) {
-    // bsh: log2 of the group size / 128 (GROUP sizes are powers of two >= 128)
+         int nunit) {
+    // bsh: log2 of the group size / 128 (GROUP sizes are powers of two >= 128);
+    // nunit: even (units past d_in are encoded as zeros)
     constexpr bool GRP = MODE == BD_SCALE_GROUP;
     constexpr bool COL = MODE == BD_SCALE_COL;
-    constexpr int kRing = RT == 1 ? 8 : (RT == 2 ? 6 : 4);  // slots in flight per wave
+    constexpr int kRing = RT == 1 ? 8 : (GRP ? 4 : 6);              // slots in flight per wave
     constexpr int NS = COL ? 0 : (MODE == BD_SCALE_MATRIX ? 1 : RT);  // scale loads per slot
-    constexpr int L = RT + NS;                                // loads per slot
-    constexpr uint32_t SB = SF16 ? 2 : 4;                     // bytes per scale
+    constexpr int L = RT + NS;                                       // loads per slot
+    constexpr uint32_t SB = SF16 ? 2 : 4;                            // bytes per scale
     static_assert((kRing - 1) * L <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(16))) char sbuf[kNBuf * kEncUnitBytes];
-    __shared__ int32_t smeta[kMaxTpb * kTileMetaInts];
+    static_assert(kRing % 2 == 0, "the unit of a ring position is its parity");
+    __shared__ __attribute__((aligned(16))) char sbuf[kNBuf * kStepBytes];
+    __shared__ int32_t smeta[kTileMetaInts];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, G = lane >> 4;
-    const int64_t rw0 = (int64_t)blockIdx.x * (64 * RT) + 16 * RT * wv;  // the wave's first row
-    // this block's share of the batch's tiles (at most kMaxTpb)
-    const int ntv = (int)meta[3];
-    const int t0 = (int)(((int64_t)blockIdx.y * ntv) / gridDim.y);
-    const int ntb = (int)(((int64_t)(blockIdx.y + 1) * ntv) / gridDim.y) - t0;
-    if (ntb <= 0) return;  // uniform over the block
-    (void)tpb;
-
-    for (int i = threadIdx.x; i < ntb * kTileMetaInts; i += 256)
-        smeta[i] = tmeta[(size_t)t0 * kTileMetaInts + i];
+    const int64_t rw0 = (int64_t)blockIdx.x * (16 * kWaves * RT) + 16 * RT * wv;  // the wave's first row
+    const int tile = blockIdx.y;
+    if (tile >= (int)meta[3]) return;  // uniform: no such tile in this batch
+    // (wave 0: a uniform branch, so the values around it stay scalar)
+    if (wv == 0) smeta[lane] = tmeta[(size_t)tile * kTileMetaInts + lane];
     __syncthreads();
-    int total = 0;  // slots of the block
-    for (int t = 0; t < ntb; ++t) {
-        const int c = __builtin_amdgcn_readfirstlane(smeta[t * kTileMetaInts + 48]);
-        total += c;
-    }
-    total *= nunit;
-    total = (total + kRing - 1) / kRing * kRing;  // padded with empty slots past the last tile
-    const int S = ntb * nunit;  // steps
+    const int nus = __builtin_amdgcn_readfirstlane(smeta[48]);  // >= 1
+    const int S = nunit / 2;                                    // steps
+    const int total = (2 * S * nus + kRing - 1) / kRing * kRing;  // slots, padded past the end
 
     const uint32_t bank_row = (uint32_t)(d_in / 8);
     const uint64_t user_bytes = (uint64_t)d_out * bank_row;
@@ -288,7 +283,7 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
         srow[t] = GRP ? rowB * gpr * SB : (MODE == BD_SCALE_ROW ? rowB * SB : 0u);
     }
     const __amdgpu_buffer_rsrc_t er =
-        make_rsrc(enc + (size_t)t0 * nunit * kEncUnitBytes, (uint64_t)S * kEncUnitBytes);
+        make_rsrc(enc + (size_t)tile * nunit * kEncUnitBytes, (uint64_t)nunit * kEncUnitBytes);
     uint32_t kmask, kone;  // operand constants in registers (gfx9 VOP3 takes no literal)
     asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
     asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
@@ -300,14 +295,14 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
         a.w = (wq & kmask) | kone;
         return a;
     };
-    // the tile operands of step st into LDS buffer b (1 KB chunk i by wave i % 4)
+    // the operands of step st into LDS buffer b (1 KB chunk i by wave i % 8)
     auto issue_enc = [&](int st, int b) __attribute__((always_inline)) {
-        const uint32_t src = (uint32_t)st * kEncUnitBytes + 16 * lane;
+        const uint32_t src = (uint32_t)st * kStepBytes + 16 * lane;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = wv + 4 * i;
-            if (c < kEncUnitBytes / 1024)  // uniform
-                lds_copy16(er, sbuf + b * kEncUnitBytes + c * 1024, src + (uint32_t)c * 1024);
+            const int c = wv + kWaves * i;
+            if (c < kStepBytes / 1024)  // uniform
+                lds_copy16(er, sbuf + b * kStepBytes + c * 1024, src + (uint32_t)c * 1024);
         }
     };
     // GROUP: per unit and row tile, each lane loads a 16-byte window of its row's
@@ -320,55 +315,50 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
         const uint32_t o = srow[t] + g0 * SB;
         return o < swmax ? o : swmax;
     };
-
-    // ---- loading side: slot (lt, lu, lj), the users of tile lt
-    int lt = 0, lu = 0, lj = 0, l_nus = 0, l_nusP = 0;
-    uint32_t ub_lo = 0, ub_hi = 0, sb_lo = 0, sb_hi = 0;
-    auto l_tile = [&]() __attribute__((always_inline)) {
-        const int32_t* tm = smeta + lt * kTileMetaInts;
-        l_nus = __builtin_amdgcn_readfirstlane(tm[48]);
-        l_nusP = l_nus;
-        const int uj = tm[32 + n];
-        const uint64_t usr = n < l_nus ? (uint64_t)(uint32_t)uj : 0ull;
+    // lane j < nus: base addresses of user j's bank and scales (read back with readlane)
+    uint32_t ub_lo, ub_hi, sb_lo, sb_hi;
+    {
+        const uint64_t usr = n < nus ? (uint64_t)(uint32_t)smeta[32 + n] : 0ull;
         const uint64_t ub = (uint64_t)(const char*)signs + usr * user_bytes;
         const uint64_t sbp = (uint64_t)(const char*)scales + usr * sc_bytes;
         ub_lo = (uint32_t)ub;
         ub_hi = (uint32_t)(ub >> 32);
         sb_lo = (uint32_t)sbp;
         sb_hi = (uint32_t)(sbp >> 32);
+    }
+    const int c_tuser = smeta[16 + n];  // lane n: user of token n (or -1)
+    const int c_users = smeta[32 + n];  // lane j < nus: user j
+    // (readlane returns int: widen through uint32_t, no sign extension)
+    auto lbase = [&](uint32_t lo, uint32_t hi, int jj) __attribute__((always_inline)) {
+        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, jj) << 32) |
+               (uint64_t)(uint32_t)__builtin_amdgcn_readlane(lo, jj);
     };
-    l_tile();
-    uint32_t lwin[RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) lwin[t] = GRP ? swin(0, t) : 0u;
+
+    // ---- loading side: slot (step ls, user lj, unit 2 ls + lh)
+    int ls = 0, lj = 0, lh = 0;
     struct Slot {
         u32x4 w[RT];                // per row tile 16 bytes of sign words: 4 products
                                     // (GROUP: group G's 4 k-blocks)
         u32x4 s4[GRP ? RT : 1];     // GROUP: per row tile the scale window
         uint32_t s1[GRP ? 1 : RT];  // MATRIX: s1[0]; ROW: per row tile the row's scale
     };
-    // (readlane returns int: widen through uint32_t, no sign extension)
-    auto lbase = [&](uint32_t lo, uint32_t hi, int jj) __attribute__((always_inline)) {
-        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, jj) << 32) |
-               (uint64_t)(uint32_t)__builtin_amdgcn_readlane(lo, jj);
-    };
     auto issue_w = [&](Slot& sl, int t) __attribute__((always_inline)) {
-        const bool ok = lt < ntb && lj < l_nus;  // uniform
+        const bool ok = ls < S;                  // uniform
         const uint32_t oob = ok ? 0u : kOOB;     // (offsets stay below 2^31)
         const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)lbase(ub_lo, ub_hi, ok ? lj : 0), (short)0, nrec_bits, 0x00020000);
-        sl.w[t] = buf_load16(br, (brow[t] + (uint32_t)(64 * lu + 16 * G)) | oob);
+            (void*)lbase(ub_lo, ub_hi, lj), (short)0, nrec_bits, 0x00020000);
+        sl.w[t] = buf_load16(br, (brow[t] + (uint32_t)(64 * (2 * ls + lh) + 16 * G)) | oob);
     };
     auto issue_s = [&](Slot& sl) __attribute__((always_inline)) {
         if (NS == 0) return;
-        const bool ok = lt < ntb && lj < l_nus;  // uniform
-        const uint32_t oob = ok ? 0u : kOOB;     // (offsets stay below 2^31)
+        const bool ok = ls < S;                  // uniform
+        const uint32_t oob = ok ? 0u : kOOB;
         const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)lbase(sb_lo, sb_hi, ok ? lj : 0), (short)0, nrec_sc, 0x00020000);
+            (void*)lbase(sb_lo, sb_hi, lj), (short)0, nrec_sc, 0x00020000);
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
             if (GRP) {
-                sl.s4[t] = buf_load16(sr, lwin[t] | oob);
+                sl.s4[t] = buf_load16(sr, swin(2 * ls + lh, t) | oob);
             } else {
                 sl.s1[t] = SF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(sr, (int)(srow[t] | oob), 0, 0)
                                 : buf_load4(sr, srow[t] | oob);
@@ -376,38 +366,17 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
         }
     };
     auto l_advance = [&]() __attribute__((always_inline)) {
-        if (++lj == l_nusP) {
+        lh ^= 1;
+        if (lh == 0 && ++lj == nus) {
             lj = 0;
-            if (++lu == nunit) {
-                lu = 0;
-                if (++lt < ntb) l_tile();
-            }
-            if (GRP) {
-#pragma unroll
-                for (int t = 0; t < RT; ++t) lwin[t] = swin(lu, t);
-            }
+            ++ls;
         }
     };
 
-    // ---- consumption side: step s (tile ct, unit cu), user cj
-    int s = 0, cu = 0, cj = 0, ct = 0, c_nus = 0, c_nusP = 0, bufc = 0, bufe = 2;
-    int c_tuser = -1, c_users = 0;  // lane n: user of token n; lane j: user j
-    auto c_tile = [&]() __attribute__((always_inline)) {
-        // past the last tile: no users and no step ends (empty slots to the end)
-        const bool in = ct < ntb;
-        const int32_t* tm = smeta + (in ? ct : 0) * kTileMetaInts;
-        const int nus = __builtin_amdgcn_readfirstlane(tm[48]);
-        c_nus = in ? nus : 0;
-        c_nusP = in ? nus : 0x40000000;
-        c_tuser = tm[16 + n];
-        c_users = tm[32 + n];
-    };
-    c_tile();
-
+    // ---- consumption side: step cs, slot q of the step (user q >> 1, unit 2 cs + (q & 1))
+    int cs = 0, q = 0, bufc = 0, bufe = 2;
     issue_enc(0, 0);
     if (S > 1) issue_enc(1, 1);
-    // slots whose loads were issued; at that count the copies of steps s and s + 1 were issued
-    int nslot = kRing, mark0 = 0, mark1 = 0;
     Slot ring[kRing];
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
@@ -415,25 +384,23 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
         for (int t = 0; t < RT; ++t) issue_w(ring[r], t);
         issue_s(ring[r]);
         l_advance();
+        // (in ring order: slot 0's loads must be the oldest when the loop starts)
+        __builtin_amdgcn_sched_barrier(0);
     }
-    i32x6 hi[4], lo[4];
-    uint32_t cdh = 0, cdl = 0;
-    uint32_t cidx[RT][4];  // GROUP: window index of product c's scale, per row tile
-    bool gfast = true;     // GROUP: every lane's index of product c is c
+    // slots whose loads were issued; at that count the copies of steps cs and cs + 1 were issued
+    int nslot = kRing, mark0 = 0, mark1 = 0;
+    bool gfast[2] = {true, true};  // GROUP: the unit's four groups are its window's four words
     f32x4 acc[RT], acc2[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) cidx[t][c] = (uint32_t)c;
     }
     for (int k = 0; k < total; k += kRing) {
 #pragma unroll
         for (int r = 0; r < kRing; ++r) {
-            if (cj == 0) {
-                // open step s: its operands are in (every wave's copies landed),
-                // buffer (s + 2) % 3 was last read in step s - 1
+            const int h = r & 1;  // the slot's unit within the step
+            if (q == 0 && cs < S) {
                 {
                     // wait until at most the loads issued after this step's copy
                     // (capped at kRing - 1 slots) are in flight
@@ -453,50 +420,53 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                     }
                 }
                 asm volatile("s_barrier" ::: "memory");
-                if (s + 2 < S) issue_enc(s + 2, bufe);
+                if (cs + 2 < S) issue_enc(cs + 2, bufe);
                 mark0 = mark1;
                 mark1 = nslot;
-                const char* sb = sbuf + bufc * kEncUnitBytes;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const u32x4 c0 = *(const u32x4*)(sb + (3 * q + 0) * 1024 + 16 * lane);
-                    const u32x4 c1 = *(const u32x4*)(sb + (3 * q + 1) * 1024 + 16 * lane);
-                    const u32x4 c2 = *(const u32x4*)(sb + (3 * q + 2) * 1024 + 16 * lane);
-                    hi[q] = i32x6{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y};
-                    lo[q] = i32x6{(int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
-                }
-                const u32x4 cd = *(const u32x4*)(sb + 12 * 1024 + 16 * lane);
-                cdh = cd.x;
-                cdl = cd.y;
-                if (GRP) {
-                    bool moved = false;
+                for (int uh = 0; uh < 2; ++uh) {
+                    if (GRP) {
+                        const int u = 2 * cs + uh;
+                        bool moved = false;
 #pragma unroll
-                    for (int t = 0; t < RT; ++t) {
-                        const uint32_t w0 = swin(cu, t);
+                        for (int t = 0; t < RT; ++t) {
+                            const uint32_t w0 = swin(u, t);
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            uint32_t g = (4u * (uint32_t)cu + c) >> bsh;
-                            g = g < gpr ? g : gpr - 1u;
-                            cidx[t][c] = (srow[t] + g * SB - w0) / SB;
-                            moved |= cidx[t][c] != (uint32_t)c;
+                            for (int c = 0; c < 4; ++c) {
+                                uint32_t g = (4u * (uint32_t)u + c) >> bsh;
+                                g = g < gpr ? g : gpr - 1u;
+                                moved |= (srow[t] + g * SB - w0) / SB != (uint32_t)c;
+                            }
                         }
+                        gfast[uh] = __ballot(moved) == 0ull;
                     }
-                    gfast = __ballot(moved) == 0ull;
                 }
             }
             Slot& sl = ring[r];
-            const bool live = cj < c_nus;  // uniform
-            int usr = 0;
-            uint32_t sh = 0u, sl_ = 0u;
-            if (live) {
-                usr = __builtin_amdgcn_readlane(c_users, cj);
+            const bool live = cs < S;  // uniform
+            // this slot's unit operands (hi, lo per product, block codes), from LDS (also
+            // for the empty slots past the end: no value then merges at a branch)
+            i32x6 hi[4], lo[4];
+            uint32_t sh, sl_;
+            {
+                const char* sb = sbuf + bufc * kStepBytes + h * kEncUnitBytes;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const u32x4 c0 = *(const u32x4*)(sb + (3 * p + 0) * 1024 + 16 * lane);
+                    const u32x4 c1 = *(const u32x4*)(sb + (3 * p + 1) * 1024 + 16 * lane);
+                    const u32x4 c2 = *(const u32x4*)(sb + (3 * p + 2) * 1024 + 16 * lane);
+                    hi[p] = i32x6{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y};
+                    lo[p] = i32x6{(int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
+                }
+                const u32x4 cd = *(const u32x4*)(sb + 12 * 1024 + 16 * lane);
+                const int usr = __builtin_amdgcn_readlane(c_users, q >> 1);
                 const bool mine = c_tuser == usr;
-                sh = mine ? cdh : 0u;
-                sl_ = mine ? cdl : 0u;
+                sh = mine ? cd.x : 0u;
+                sl_ = mine ? cd.y : 0u;
             }
             // every row tile's sign words expanded first (materialised here, not sunk
             // into the branch below: the words must be dead before they are reloaded),
-            // then all reloads, then the products of all row tiles (independent chains)
+            // then all reloads, then the products of all row tiles
             u32x4 bx[RT][4];
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
@@ -526,23 +496,28 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                     const u32x4 b0 = bx[t][0], b1 = bx[t][1], b2 = bx[t][2], b3 = bx[t][3];
                     if (GRP) {
                         u32x4 sv = sl.s4[t];
-                        if (!gfast) {  // (rare: the last rows, or groups above 128)
-                            auto pick = [&](uint32_t i) __attribute__((always_inline)) {
+                        if (!gfast[h]) {  // (rare: the last rows, or groups above 128)
+                            const int u = 2 * cs + h;
+                            const uint32_t w0 = swin(u, t);
+                            auto pick = [&](int c) __attribute__((always_inline)) {
+                                uint32_t g = (4u * (uint32_t)u + c) >> bsh;
+                                g = g < gpr ? g : gpr - 1u;
+                                const uint32_t i = (srow[t] + g * SB - w0) / SB;
                                 if (SF16) {
                                     const uint32_t d = i < 4u ? (i < 2u ? sv.x : sv.y) : (i < 6u ? sv.z : sv.w);
                                     return i & 1u ? d >> 16 : d & 0xFFFFu;
                                 }
                                 return i < 2u ? (i == 0u ? sv.x : sv.y) : (i == 2u ? sv.z : sv.w);
                             };
-                            sv = u32x4{pick(cidx[t][0]), pick(cidx[t][1]), pick(cidx[t][2]), pick(cidx[t][3])};
+                            sv = u32x4{pick(0), pick(1), pick(2), pick(3)};
                         } else if (SF16) {
                             sv = u32x4{sv.x & 0xFFFFu, sv.x >> 16, sv.y & 0xFFFFu, sv.y >> 16};
                         }
 #define BD_G(C, B, SC)                                                 \
     {                                                                  \
         f32x4 tt = {0.f, 0.f, 0.f, 0.f};                               \
-        tt = mfma_f6f4<C>(hi[C], B, tt, sh);                           \
-        tt = mfma_f6f4<C>(lo[C], B, tt, sl_);                          \
+        tt = mfma_f6f4<C>(hi[C], B, tt, sh);                        \
+        tt = mfma_f6f4<C>(lo[C], B, tt, sl_);                       \
         const float sc = SF16 ? f16_to_f32((uint16_t)(SC)) : __uint_as_float(SC); \
         acc[t] -= sc * tt;                                             \
     }
@@ -577,35 +552,26 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
             issue_s(sl);  // its scales, after their last use
             l_advance();
             ++nslot;
-            if (++cj == c_nusP) {
-                cj = 0;
-                ++s;
+            if (++q == 2 * nus) {
+                q = 0;
+                ++cs;
                 bufc = bufc == kNBuf - 1 ? 0 : bufc + 1;
                 bufe = bufe == kNBuf - 1 ? 0 : bufe + 1;
-                if (++cu == nunit) {
-                    // tile done: Y[token][row] += its sum; one add per element
-                    // (no-return atomics: nothing waits on them)
-                    cu = 0;
-                    const int32_t* tm = smeta + ct * kTileMetaInts;
-                    int tok[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) tok[e] = tm[4 * G + e];
-#pragma unroll
-                    for (int t = 0; t < RT; ++t) {
-                        const int64_t o = rw0 + 16 * t + n;
-                        const f32x4 v = COL ? -(acc[t] + acc2[t]) : acc[t];
-                        if (o < d_out) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (tok[e] >= 0) unsafeAtomicAdd(y + (int64_t)tok[e] * d_out + o, v[e]);
-                        }
-                        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
-                    ++ct;
-                    c_tile();
-                }
             }
+        }
+    }
+    // Y[token][row] += the tile's sum; one add per element (no-return atomics)
+    int tok[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tok[e] = smeta[4 * G + e];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int64_t o = rw0 + 16 * t + n;
+        const f32x4 v = COL ? -(acc[t] + acc2[t]) : acc[t];
+        if (o < d_out) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (tok[e] >= 0) unsafeAtomicAdd(y + (int64_t)tok[e] * d_out + o, v[e]);
         }
     }
 }
@@ -640,52 +606,40 @@ hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, 
 #undef BD_ENC
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // row tiles per wave: the most (fewer copies of the tile operands per sign byte)
-    // that still give every CU two blocks of work at one tile per block; GROUP and ROW
-    // at most two (register budget)
-    const int rtmax = grp || dp.mode == BD_SCALE_ROW ? 2 : 4;
-    int rt = 1;
+    // row tiles per wave: two (256 rows per block: fewer copies of the step operands
+    // per sign byte; more do not fit the registers) when that still gives every CU a
+    // block of work at the typical tile count, else one
     const int64_t ntyp = (bp.T + 15) / 16;  // tiles of a batch of small users, about
-    while (rt < rtmax && ((dp.d_out + 128 * rt - 1) / (128 * rt)) * ntyp >= 512) rt *= 2;
+    const int rt = ((dp.d_out + 255) / 256) * ntyp >= 256 ? 2 : 1;
     // one tile per block (grid rows for the bound of tiles; blocks past the batch's
     // tiles exit at once): every block has the same work, whatever the tile count
-    const int64_t rtiles = (dp.d_out + 64 * rt - 1) / (64 * rt);
-    const int64_t tpb = 1;
+    const int64_t rtiles = (dp.d_out + 128 * rt - 1) / (128 * rt);
     const dim3 gd((unsigned)rtiles, (unsigned)ntiles);
     int bsh = 0;
     while (grp && (128 << bsh) < dp.group) ++bsh;
 #define BD_D6(MODE, F16, RT)                                                                      \
-    hipLaunchKernelGGL((k_delta6<MODE, F16, RT>), gd, dim3(256), 0, s, signs, scales, dp.per_user, \
-                       bsh, (const int32_t*)tmeta, (const char*)enc, meta, y, bp.d_in, dp.d_out,   \
-                       nunit, (int)tpb)
-#define BD_D6R(MODE, F16)                              \
+    hipLaunchKernelGGL((k_delta6<MODE, F16, RT>), gd, dim3(64 * kWaves), 0, s, signs, scales,     \
+                       dp.per_user, bsh, (const int32_t*)tmeta, (const char*)enc, meta, y,        \
+                       bp.d_in, dp.d_out, nunit)
+#define BD_D6R2(MODE, F16)                             \
     do {                                               \
-        if (rt == 4) BD_D6(MODE, F16, 4);              \
-        else if (rt == 2) BD_D6(MODE, F16, 2);         \
+        if (rt == 2) BD_D6(MODE, F16, 2);              \
         else BD_D6(MODE, F16, 1);                      \
     } while (0)
     const bool f16 = dp.sdtype == BD_F16;
     switch (dp.mode) {
         case BD_SCALE_MATRIX:
-            if (f16) BD_D6R(BD_SCALE_MATRIX, true); else BD_D6R(BD_SCALE_MATRIX, false);
+            if (f16) BD_D6R2(BD_SCALE_MATRIX, true); else BD_D6R2(BD_SCALE_MATRIX, false);
             break;
         case BD_SCALE_GROUP:
-            if (f16) {
-                if (rt == 2) BD_D6(BD_SCALE_GROUP, true, 2); else BD_D6(BD_SCALE_GROUP, true, 1);
-            } else {
-                if (rt == 2) BD_D6(BD_SCALE_GROUP, false, 2); else BD_D6(BD_SCALE_GROUP, false, 1);
-            }
+            if (f16) BD_D6R2(BD_SCALE_GROUP, true); else BD_D6R2(BD_SCALE_GROUP, false);
             break;
         case BD_SCALE_ROW:
-            if (f16) {
-                if (rt == 2) BD_D6(BD_SCALE_ROW, true, 2); else BD_D6(BD_SCALE_ROW, true, 1);
-            } else {
-                if (rt == 2) BD_D6(BD_SCALE_ROW, false, 2); else BD_D6(BD_SCALE_ROW, false, 1);
-            }
+            if (f16) BD_D6R2(BD_SCALE_ROW, true); else BD_D6R2(BD_SCALE_ROW, false);
             break;
-        default: BD_D6R(BD_SCALE_COL, false); break;
+        default: BD_D6R2(BD_SCALE_COL, false); break;
     }
-#undef BD_D6R
+#undef BD_D6R2
 #undef BD_D6
     return hipGetLastError();
 }
