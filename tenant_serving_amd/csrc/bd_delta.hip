@@ -248,10 +248,12 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
     constexpr bool GRP = MODE == BD_SCALE_GROUP;
     constexpr bool COL = MODE == BD_SCALE_COL;
     constexpr int kRing = RT == 1 ? 8 : (GRP ? 4 : 6);              // slots in flight per wave
-    constexpr int NS = COL ? 0 : (MODE == BD_SCALE_MATRIX ? 1 : RT);  // scale loads per slot
-    constexpr int L = RT + NS;                                       // loads per slot
+    // loads: RT sign loads per slot; GROUP one scale-window load per user and step (in
+    // its second slot).  L: the fewest loads of a slot (the counted waits use it)
+    constexpr int L = RT;
+    constexpr int LMAX = RT + (GRP ? 1 : 0);
     constexpr uint32_t SB = SF16 ? 2 : 4;                            // bytes per scale
-    static_assert((kRing - 1) * L <= 63, "vmcnt range");
+    static_assert((kRing - 1) * LMAX <= 63, "vmcnt range");
     static_assert(kRing % 2 == 0, "the unit of a ring position is its parity");
     __shared__ __attribute__((aligned(16))) char sbuf[kNBuf * kStepBytes];
     __shared__ int32_t smeta[kTileMetaInts];
@@ -337,11 +339,13 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
     // ---- loading side: slot (step ls, user lj, unit 2 ls + lh)
     int ls = 0, lj = 0, lh = 0;
     struct Slot {
-        u32x4 w[RT];                // per row tile 16 bytes of sign words: 4 products
-                                    // (GROUP: group G's 4 k-blocks)
-        u32x4 s4[GRP ? RT : 1];     // GROUP: per row tile the scale window
-        uint32_t s1[GRP ? 1 : RT];  // MATRIX: s1[0]; ROW: per row tile the row's scale
+        u32x4 w[RT];  // per row tile 16 bytes of sign words: 4 products
+                      // (GROUP: group G's 4 k-blocks)
     };
+    // GROUP: per user and step, one load of the scale windows of both row tiles and both
+    // units: lane (j, g) takes row tile g % RT, unit g / RT; the slots read them with
+    // ds_bpermute.  Entry i belongs to ring positions 2 i and 2 i + 1.
+    u32x4 wring[GRP ? kRing / 2 : 1];
     auto issue_w = [&](Slot& sl, int t) __attribute__((always_inline)) {
         const bool ok = ls < S;                  // uniform
         const uint32_t oob = ok ? 0u : kOOB;     // (offsets stay below 2^31)
@@ -349,21 +353,14 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
             (void*)lbase(ub_lo, ub_hi, lj), (short)0, nrec_bits, 0x00020000);
         sl.w[t] = buf_load16(br, (brow[t] + (uint32_t)(64 * (2 * ls + lh) + 16 * G)) | oob);
     };
-    auto issue_s = [&](Slot& sl) __attribute__((always_inline)) {
-        if (NS == 0) return;
+    auto issue_s = [&](u32x4& sw) __attribute__((always_inline)) {
+        // (called in the second slot of a pair: ls, lj are the pair's step and user)
         const bool ok = ls < S;                  // uniform
         const uint32_t oob = ok ? 0u : kOOB;
         const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)lbase(sb_lo, sb_hi, lj), (short)0, nrec_sc, 0x00020000);
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-            if (GRP) {
-                sl.s4[t] = buf_load16(sr, swin(2 * ls + lh, t) | oob);
-            } else {
-                sl.s1[t] = SF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(sr, (int)(srow[t] | oob), 0, 0)
-                                : buf_load4(sr, srow[t] | oob);
-            }
-        }
+        const int t = G % RT, hh = (G / RT) & 1;
+        sw = buf_load16(sr, swin(2 * ls + hh, t) | oob);
     };
     auto l_advance = [&]() __attribute__((always_inline)) {
         lh ^= 1;
@@ -382,7 +379,7 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
     for (int r = 0; r < kRing; ++r) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) issue_w(ring[r], t);
-        issue_s(ring[r]);
+        if (GRP && (r & 1)) issue_s(wring[r / 2]);
         l_advance();
         // (in ring order: slot 0's loads must be the oldest when the loop starts)
         __builtin_amdgcn_sched_barrier(0);
@@ -495,7 +492,13 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                 for (int t = 0; t < RT; ++t) {
                     const u32x4 b0 = bx[t][0], b1 = bx[t][1], b2 = bx[t][2], b3 = bx[t][3];
                     if (GRP) {
-                        u32x4 sv = sl.s4[t];
+                        // this lane's row, unit h, row tile t: the window of lane group t + RT h
+                        const u32x4 swv = wring[r / 2];
+                        const int src = 4 * (n + 16 * (t + RT * h));
+                        u32x4 sv = {(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)swv.x),
+                                    (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)swv.y),
+                                    (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)swv.z),
+                                    (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)swv.w)};
                         if (!gfast[h]) {  // (rare: the last rows, or groups above 128)
                             const int u = 2 * cs + h;
                             const uint32_t w0 = swin(u, t);
@@ -516,14 +519,15 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
 #define BD_G(C, B, SC)                                                 \
     {                                                                  \
         f32x4 tt = {0.f, 0.f, 0.f, 0.f};                               \
-        tt = mfma_f6f4<C>(hi[C], B, tt, sh);                        \
-        tt = mfma_f6f4<C>(lo[C], B, tt, sl_);                       \
+        tt = mfma_f6f4<C>(hi[C], B, tt, sh);                           \
+        tt = mfma_f6f4<C>(lo[C], B, tt, sl_);                          \
         const float sc = SF16 ? f16_to_f32((uint16_t)(SC)) : __uint_as_float(SC); \
         acc[t] -= sc * tt;                                             \
     }
                         BD_G(0, b0, sv.x) BD_G(1, b1, sv.y) BD_G(2, b2, sv.z) BD_G(3, b3, sv.w)
 #undef BD_G
-                    } else if (COL) {
+                    } else {
+                        // MATRIX, ROW and COL: the scale is applied per token at the end
                         acc[t] = mfma_f6f4<0>(hi[0], b0, acc[t], sh);
                         acc2[t] = mfma_f6f4<0>(lo[0], b0, acc2[t], sl_);
                         acc[t] = mfma_f6f4<1>(hi[1], b1, acc[t], sh);
@@ -532,24 +536,11 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                         acc2[t] = mfma_f6f4<2>(lo[2], b2, acc2[t], sl_);
                         acc[t] = mfma_f6f4<3>(hi[3], b3, acc[t], sh);
                         acc2[t] = mfma_f6f4<3>(lo[3], b3, acc2[t], sl_);
-                    } else {
-                        f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tb = {0.f, 0.f, 0.f, 0.f};
-                        ta = mfma_f6f4<0>(hi[0], b0, ta, sh);
-                        tb = mfma_f6f4<0>(lo[0], b0, tb, sl_);
-                        ta = mfma_f6f4<1>(hi[1], b1, ta, sh);
-                        tb = mfma_f6f4<1>(lo[1], b1, tb, sl_);
-                        ta = mfma_f6f4<2>(hi[2], b2, ta, sh);
-                        tb = mfma_f6f4<2>(lo[2], b2, tb, sl_);
-                        ta = mfma_f6f4<3>(hi[3], b3, ta, sh);
-                        tb = mfma_f6f4<3>(lo[3], b3, tb, sl_);
-                        const uint32_t raw = sl.s1[MODE == BD_SCALE_ROW ? t : 0];
-                        const float sc = SF16 ? f16_to_f32((uint16_t)raw) : __uint_as_float(raw);
-                        acc[t] -= sc * (ta + tb);
                     }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            issue_s(sl);  // its scales, after their last use
+            if (GRP && (r & 1)) issue_s(wring[r / 2]);  // the pair's windows, after their last use
             l_advance();
             ++nslot;
             if (++q == 2 * nus) {
@@ -560,18 +551,32 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
             }
         }
     }
-    // Y[token][row] += the tile's sum; one add per element (no-return atomics)
-    int tok[4];
+    // Y[token][row] += the tile's sum; one add per element (no-return atomics).  Token
+    // row 4 g + e holds -X S^T of its own user: MATRIX and ROW scale it here by that
+    // user's scale (the other users' products in it are 2^-127-scaled, below rounding)
+    int tok[4], tus[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tok[e] = smeta[4 * G + e];
+    for (int e = 0; e < 4; ++e) {
+        tok[e] = smeta[4 * G + e];
+        tus[e] = smeta[16 + 4 * G + e];
+    }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const int64_t o = rw0 + 16 * t + n;
-        const f32x4 v = COL ? -(acc[t] + acc2[t]) : acc[t];
         if (o < d_out) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (tok[e] >= 0) unsafeAtomicAdd(y + (int64_t)tok[e] * d_out + o, v[e]);
+            for (int e = 0; e < 4; ++e) {
+                if (tok[e] < 0) continue;
+                float f = 1.f;
+                if (MODE == BD_SCALE_MATRIX || MODE == BD_SCALE_ROW) {
+                    const size_t i = (size_t)tus[e] * per_user + (MODE == BD_SCALE_ROW ? (size_t)o : 0);
+                    f = -(SF16 ? f16_to_f32(((const uint16_t*)scales)[i]) : ((const float*)scales)[i]);
+                } else if (COL) {
+                    f = -1.f;
+                }
+                const float v = GRP ? acc[t][e] : f * (acc[t][e] + acc2[t][e]);
+                unsafeAtomicAdd(y + (int64_t)tok[e] * d_out + o, v);
+            }
         }
     }
 }
