@@ -235,7 +235,7 @@ k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
 // tokens 4 g .. 4 g + 3 of output row j of the row tile.
 constexpr int kNBuf = 3;                       // LDS buffers of step operands
 constexpr int kStepBytes = 2 * kEncUnitBytes;  // two units
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;  // (two blocks per CU: one block's start overlaps the other's work)
 
 template <int MODE, bool SF16, int RT>
 __global__ void __launch_bounds__(64 * kWaves)
@@ -301,7 +301,7 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
     auto issue_enc = [&](int st, int b) __attribute__((always_inline)) {
         const uint32_t src = (uint32_t)st * kStepBytes + 16 * lane;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < (kStepBytes / 1024 + kWaves - 1) / kWaves; ++i) {
             const int c = wv + kWaves * i;
             if (c < kStepBytes / 1024)  // uniform
                 lds_copy16(er, sbuf + b * kStepBytes + c * 1024, src + (uint32_t)c * 1024);
@@ -615,10 +615,10 @@ hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, 
     // per sign byte; more do not fit the registers) when that still gives every CU a
     // block of work at the typical tile count, else one
     const int64_t ntyp = (bp.T + 15) / 16;  // tiles of a batch of small users, about
-    const int rt = ((dp.d_out + 255) / 256) * ntyp >= 256 ? 2 : 1;
+    const int rt = ((dp.d_out + 32 * kWaves - 1) / (32 * kWaves)) * ntyp >= 512 ? 2 : 1;
     // one tile per block (grid rows for the bound of tiles; blocks past the batch's
     // tiles exit at once): every block has the same work, whatever the tile count
-    const int64_t rtiles = (dp.d_out + 128 * rt - 1) / (128 * rt);
+    const int64_t rtiles = (dp.d_out + 16 * kWaves * rt - 1) / (16 * kWaves * rt);
     const dim3 gd((unsigned)rtiles, (unsigned)ntiles);
     int bsh = 0;
     while (grp && (128 << bsh) < dp.group) ++bsh;
