@@ -4,7 +4,7 @@
 Workload (default): the Llama-3.1-8B-shaped q_proj, W_base 4096x4096 bf16,
 16 users' packed 1-bit deltas with one fp32 scale per matrix, a decode batch
 of 16 tokens (one per user, in a seeded shuffled order), fp32 output.  A step
-is one bd_apply of that layer: a single kernel (k_decode_fused) that groups the
+is one bd_apply of that layer: a single kernel (k_decode_unit) that groups the
 batch by user, encodes the tokens for the delta products, and computes the
 shared base product and every user's delta product in one pass over W_base and
 the packed banks.  The K timed steps are captured in a HIP graph and replayed,
@@ -192,9 +192,9 @@ def main():
     bytes_x, bytes_y = T * d_in * 2, T * d_out * 4
     bytes_step = bytes_w + bytes_bits + bytes_x + bytes_y + 4 * T
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
-    # the step is one launch of k_decode_fused: it reads the ids, X, W, the active users'
+    # the step is one launch of k_decode_unit: it reads the ids, X, W, the active users'
     # bits and scales once from HBM and writes y once
-    dom, dom_us, dom_bytes = "k_decode_fused", gpu_step_us, bytes_step
+    dom, dom_us, dom_bytes = "k_decode_unit", gpu_step_us, bytes_step
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -254,12 +254,12 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": bytes_step,
         "gpu_step_us_events": round(gpu_step_us, 3),
-        "timing": "the K steps (one k_decode_fused launch each) captured in one HIP graph, "
+        "timing": "the K steps (one k_decode_unit launch each) captured in one HIP graph, "
                   "replayed once between device synchronisations (wall clock -> ms_per_step; "
                   "HIP events on the same stream -> gpu_step_us_events = the kernel's average "
                   "launch time); the two-launch path timed the same way from graphs of its K "
                   "prepare and K apply launches",
-        "kernels_us": {"k_decode_fused": round(gpu_step_us, 3)},
+        "kernels_us": {"k_decode_unit": round(gpu_step_us, 3)},
         "two_launch_path_us": {"k_decode_prep": round(prep_us, 3), "k_decode": round(main_us, 3)},
         "roofline": roofline,
         "compress": compress,

@@ -5,10 +5,12 @@
 // base product per batch, each request adds its user's 1-bit delta product,
 // the bits cross HBM packed and are expanded on chip).
 //
-// One launch (k_decode_fused, MATRIX and ROW scales, rows of up to 5120 columns):
-//   every block stages the batch's tokens in LDS and encodes them itself, as two
-//   fp6 e2m3 parts per 32-column block (below); the delta products run the
-//   block-scaled MFMA with fp4 signs and fp6 tokens.
+// One launch (MATRIX and ROW scales): k_decode_unit for rows of up to 4096
+// columns (one wave per 512-column unit streams that unit's sign rows and W_base
+// rows through one register ring), k_decode_fused for rows of up to 5120 (base
+// and delta waves apart).  Every block stages the batch's tokens in LDS and
+// encodes them itself, as two fp6 e2m3 parts per 32-column block (below); the
+// delta products run the block-scaled MFMA with fp4 signs and fp6 tokens.
 //
 // Two launches (any row width, and COL scales):
 //   k_decode_prep  sorts the (<= 16) tokens by user in one wave and encodes X
@@ -517,6 +519,13 @@ __device__ __forceinline__ f32x4 mfma_f4f6(u32x4 a, i32x6 b, f32x4 c, uint32_t s
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 2, 0, 127, SEL, (int)sc);
 }
 
+template <int SEL>
+__device__ __forceinline__ f32x4 mfma_f4f6k(u32x4 a, i32x6 b, f32x4 c, uint32_t sc, uint32_t ka) {
+    const i32x8 a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const i32x8 b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, 4, 5, -1, -1);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 2, 0, (int)ka, SEL, (int)sc);
+}
+
 // Encodes, for lane (m, G), product q of unit u: the 32 columns 512 u + 128 G + 32 q
 // of token m (the LDS chunks c0 .. c0 + 3, c0 = 64 u + 16 G + 4 q); see
 // encode_fp6_block for the encoding.
@@ -870,6 +879,284 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
     }
 }
 
+// ------------------------------------------------------- one wave per unit
+// One launch for decode batches whose rows have at most 512 * kUnitWaves columns
+// (bf16 X, at most 16 tokens, MATRIX or ROW scales).  Wave w of a block owns the
+// 512-column unit w of the block's 16 output rows, for the base and the delta
+// product alike, so no wave waits for another before the final sum.
+//  - Tokens: the wave copies its unit of every token row into its own 16 KB of
+//    LDS (buffer loads that write LDS directly; rows in an order rotated by the
+//    block's place on its XCD, so the blocks of one XCD, which all read the same
+//    tokens, do not queue on the same lines at once) and encodes them from there
+//    as soon as they land (fp6 hi/lo, the operands of k_decode_fused).
+//  - One stream per wave: the sign rows of the batch's users in order of first
+//    appearance (16 bytes of 16 rows per user, padded to a multiple of 8 users
+//    with empty loads), then the unit's 16 steps of W_base rows, through an
+//    8-slot register ring.  A CU keeps about 64 loads in flight, which is what 8
+//    waves x 8 slots issue (16 slots, 128 loads, made every step several times
+//    slower; 4 waves of two units with 16 slots each drew about 40% less memory
+//    throughput per CU); a wave refills a slot as it consumes it, so its encoding
+//    and its products overlap the CU's stream.  The two waves of a SIMD do not
+//    progress evenly (whichever has the issue priority finishes about 4 us
+//    earlier), which bounds the kernel rather than the memory system.
+//  - Delta: for each user, eight block-scaled MFMAs 16x16x128 (fp4 signs x fp6
+//    tokens), while the next slot's signs are expanded (as in k_decode_fused).
+//  - Base: one bf16 MFMA 16x16x32 per step, the tokens read back from LDS.
+// The partial tiles are summed in LDS in wave order, as in k_decode_fused, so the
+// base sum does not depend on the users and y repeats bit for bit.
+constexpr int kUnitWaves = 8;
+constexpr int kUnitRing = 8;
+
+template <int MODE>
+__global__ void __launch_bounds__(64 * kUnitWaves)
+k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int T, int U,
+              int64_t d_in, const uint16_t* __restrict__ w, int64_t d_out,
+              const uint64_t* __restrict__ signs, const void* __restrict__ scales, int sdtype,
+              int64_t per_user, void* __restrict__ y, int ydtype, uint32_t* __restrict__ status) {
+    __shared__ f32x4 red[2 * kUnitWaves * 64];  // base then delta partial tiles, wave order
+    __shared__ __attribute__((aligned(16))) char xlds[kUnitWaves * 16384];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t r0 = (int64_t)blockIdx.x * 16;
+    const int64_t rowA = r0 + m < d_out ? r0 + m : d_out - 1;
+    char* xs = xlds + wv * 16384;  // token t's unit at t * 1024; chunk c at slot xslot(t, c, 1024)
+
+    // the batch's user ids (scalar loads, in flight beside the copies)
+    int sid[kDecodeMaxT];
+#pragma unroll
+    for (int j = 0; j < kDecodeMaxT; ++j) sid[j] = ids[j < T ? j : T - 1];  // in bounds
+
+    // ---- tokens of this wave's unit into LDS
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint64_t)T * (uint64_t)d_in * 2);
+    {
+        const int rot = (int)((blockIdx.x >> 3) & 15);
+#pragma unroll
+        for (int tt = 0; tt < kDecodeMaxT; ++tt) {
+            const int t = (tt + rot) & 15;
+            const int cl = (lane & 48) | ((lane & 15) ^ t);  // the chunk that belongs at slot lane
+            const int64_t col = (int64_t)512 * wv + 8 * cl;
+            const bool ok = t < T && col < d_in;
+            lds_copy16(xr, xs + t * 1024, ok ? (uint32_t)(((int64_t)t * d_in + col) * 2) : kOOB);
+        }
+    }
+
+    // ---- group the batch by user (every wave for itself): lane j of utab holds the
+    // j-th distinct valid user in order of first appearance
+    int uid = -1;
+#pragma unroll
+    for (int j = 0; j < kDecodeMaxT; ++j) uid = lane == j && j < T ? sid[j] : uid;
+    const bool valid = lane < T && uid >= 0 && uid < U;
+    bool dup = false;
+#pragma unroll
+    for (int j = 0; j < kDecodeMaxT; ++j)
+        dup |= (j < lane) & (__builtin_amdgcn_readlane(uid, j) == uid);
+    const uint64_t fmask = __ballot(valid && !dup);
+    const int nseg = __popcll(fmask);
+    int utab = 0;
+    {
+        uint64_t mk = fmask;
+        for (int j = 0; j < nseg; ++j) {
+            const int src = __ffsll((unsigned long long)mk) - 1;
+            mk &= mk - 1;
+            const int us = __builtin_amdgcn_readlane(uid, src);
+            if (lane == j) utab = us;
+        }
+    }
+    const int tok_user = __shfl(valid ? uid : -1, m);  // user of this lane's token column
+    if (wv == 0 && blockIdx.x == 0) {
+        const bool bad = lane < T && !valid && uid != -1;
+        const bool anybad = __ballot(bad) != 0ull;
+        if (lane == 0) status[0] = anybad ? ST_USER_ID : 0u;
+    }
+
+    // ---- the stream: item i < nsegR is the sign rows of user i (empty past nseg), item
+    // nsegR + s the W_base step s (unit columns 32 s .. + 31; empty past 16)
+    const int nsegR = (nseg + kUnitRing - 1) / kUnitRing * kUnitRing;
+    const int64_t bank_row = d_in / 8;
+    const uint64_t user_bytes = (uint64_t)d_out * (uint64_t)bank_row;
+    const uint64_t w_bytes = (uint64_t)d_out * (uint64_t)d_in * 2;
+    // lane (m, g): sign bytes of row rowA for columns 512 w + 128 g .. + 127 (word q: k-group
+    // g of product q); W_base columns 512 w + 32 s + 8 g .. + 7 of row rowA
+    const uint32_t soff = (int64_t)512 * wv + 128 * g < d_in
+                              ? (uint32_t)(rowA * bank_row + 64 * wv + 16 * g)
+                              : kOOB;
+    const int64_t c0 = (int64_t)512 * wv + 8 * g;
+    const uint32_t woff = (uint32_t)((rowA * d_in + c0) * 2);
+    // (branch-free: a branch here splits the loop body into blocks, and the compiler then
+    // gathers the products of a whole iteration at its end)
+    const uint64_t wbase = (uint64_t)(uintptr_t)w;
+    auto load_item = [&](int i) __attribute__((always_inline)) {
+        const uint64_t msk = 0ull - (uint64_t)(i < nsegR);  // uniform: all ones for sign rows
+        const int s = i - nsegR;
+        const int usr = __builtin_amdgcn_readlane(utab, i < nseg ? i : 0);
+        const uint64_t sbase = (uint64_t)(uintptr_t)signs + (uint64_t)(uint32_t)usr * user_bytes;
+        const uint64_t base = wbase + ((sbase - wbase) & msk);
+        const uint64_t bytes = w_bytes + ((user_bytes - w_bytes) & msk);
+        const uint32_t so = i < nseg ? soff : kOOB;
+        const bool okw = ((uint32_t)s < 16u) & (c0 + 32 * s < d_in);  // no short-circuit branch
+        const uint32_t wo = okw ? woff + 64u * (uint32_t)s : kOOB;
+        const uint32_t off = wo + ((so - wo) & (uint32_t)msk);
+        return buf_load16(make_rsrc((const void*)(uintptr_t)base, bytes), off);
+    };
+    u32x4 ring[kUnitRing];
+#pragma unroll
+    for (int r = 0; r < kUnitRing; ++r) {
+        ring[r] = load_item(r);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    BD_WAIT_VMCNT(kUnitRing);  // this wave's token copies have landed (the ring is younger)
+    uint32_t sraw[4] = {0u, 0u, 0u, 0u};  // wave 0: the scales of its outputs (bits)
+    if (wv == 0 && tok_user >= 0 && m < T) {
+        const int64_t o = r0 + 4 * g;
+        const int64_t s0 = (int64_t)tok_user * per_user;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i =
+                s0 + (MODE == BD_SCALE_MATRIX ? 0 : (o + e < d_out ? o + e : d_out - 1));
+            sraw[e] = sdtype == BD_F16 ? (uint32_t)((const uint16_t*)scales)[i]
+                                       : ((const uint32_t*)scales)[i];
+        }
+    }
+
+    // ---- encode the unit's tokens for the delta products (from LDS)
+    uint32_t kb_lo, kb_hi;  // the bf16 pairs (1, 0) and (0, 1), in registers
+    asm volatile("v_mov_b32 %0, 0x3f80" : "=v"(kb_lo));
+    asm volatile("v_mov_b32 %0, 0x3f800000" : "=v"(kb_hi));
+    Unit6 X6;
+    if (nseg > 0) fused_encode6(xs, 1024u, 0, lane, kb_lo, kb_hi, X6);
+
+    // ---- delta products, user by user (the k_decode_fused pipeline)
+    uint32_t kmask, kone;  // operand constants in registers (gfx9 VOP3 takes no literal)
+    asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
+    asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
+    uint32_t ka;  // the A operands' block scale (2^0), kept in one register
+    asm volatile("v_mov_b32 %0, 0x7f" : "=v"(ka));
+    auto expand = [&](uint32_t wq, uint32_t one) {
+        u32x4 a;
+        a.x = ((wq << 3) & kmask) | one;
+        a.y = ((wq << 2) & kmask) | one;
+        a.z = ((wq << 1) & kmask) | one;
+        a.w = (wq & kmask) | one;
+        return a;
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+    u32x4 A0[4], A1[4];
+    // user j's products from Ac while the next slot (user j + 1; zeros for padding) is
+    // expanded into An and refilled with item j + 1 + kUnitRing
+    auto step = [&](int j, int r, bool next, u32x4* Ac, u32x4* An)
+                    __attribute__((always_inline)) {
+        const int usr = __builtin_amdgcn_readlane(utab, j < nseg ? j : 0);
+        const bool mine = j < nseg && tok_user == usr;
+        const uint32_t sh = mine ? X6.ehi : 0u, sl = mine ? X6.elo : 0u;
+        const uint32_t onen = j + 1 < nseg ? kone : 0u;
+        const u32x4 Dn = ring[(r + 1) % kUnitRing];
+        acc = mfma_f4f6k<0>(Ac[0], X6.hi[0], acc, sh, ka);
+        acc2 = mfma_f4f6k<0>(Ac[0], X6.lo[0], acc2, sl, ka);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) An[0] = expand(Dn[0], onen);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_f4f6k<1>(Ac[1], X6.hi[1], acc, sh, ka);
+        acc2 = mfma_f4f6k<1>(Ac[1], X6.lo[1], acc2, sl, ka);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) An[1] = expand(Dn[1], onen);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_f4f6k<2>(Ac[2], X6.hi[2], acc, sh, ka);
+        acc2 = mfma_f4f6k<2>(Ac[2], X6.lo[2], acc2, sl, ka);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) An[2] = expand(Dn[2], onen);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_f4f6k<3>(Ac[3], X6.hi[3], acc, sh, ka);
+        acc2 = mfma_f4f6k<3>(Ac[3], X6.lo[3], acc2, sl, ka);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next) {
+            An[3] = expand(Dn[3], onen);
+            ring[(r + 1) % kUnitRing] = load_item(j + 1 + kUnitRing);
+        }
+        // Ac stays allocated to the end of the step: no expansion reuses the registers
+        // of an operand that a product in flight still reads
+        asm volatile("" ::"v"(Ac[0]), "v"(Ac[1]), "v"(Ac[2]), "v"(Ac[3]));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nsegR > 0) {  // uniform
+        {
+            const uint32_t one0 = nseg > 0 ? kone : 0u;
+            const u32x4 D0 = ring[0];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) A0[q] = expand(D0[q], one0);
+            ring[0] = load_item(kUnitRing);
+        }
+        int j0 = 0;
+        do {  // every slot is consumed at one fixed point on every path
+#pragma unroll
+            for (int r = 0; r + 1 < kUnitRing; ++r) {
+                if (r & 1) step(j0 + r, r, true, A1, A0);
+                else step(j0 + r, r, true, A0, A1);
+            }
+            if (j0 + kUnitRing < nsegR) step(j0 + kUnitRing - 1, kUnitRing - 1, true, A1, A0);
+            else step(j0 + kUnitRing - 1, kUnitRing - 1, false, A1, A0);
+            j0 += kUnitRing;
+        } while (j0 < nsegR);
+    }
+    acc += acc2;
+
+    // ---- base product: item nsegR + s in slot s % kUnitRing (nsegR is a multiple of it)
+    f32x4 accb = {0.f, 0.f, 0.f, 0.f};
+    auto tok = [&](int s) {  // B operand of step s: token m, columns 32 s + 8 g .. + 7
+        return *(const u32x4*)(xs + xslot(m, 4 * s + g, 1024u));
+    };
+    u32x4 bnext = tok(0);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const u32x4 b = bnext;
+        if (s + 1 < 16) bnext = tok(s + 1);
+        accb = mfma_bf16(ring[s % kUnitRing], b, accb);
+        ring[s % kUnitRing] = load_item(nsegR + s + kUnitRing);  // empty past step 15
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    BD_WAIT_VMCNT(0);  // the empty loads past the end have landed
+
+    // ---- reduction in wave order
+    red[wv * 64 + lane] = accb;
+    red[(kUnitWaves + wv) * 64 + lane] = acc;
+    __syncthreads();
+    if (wv != 0) return;  // wave 0 holds the factors
+    f32x4 vb = {0.f, 0.f, 0.f, 0.f}, vd = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < kUnitWaves; ++q) vb += red[q * 64 + lane];
+    for (int q = 0; q < kUnitWaves; ++q) vd += red[(kUnitWaves + q) * 64 + lane];
+    if (m >= T) return;
+    const int64_t o = r0 + 4 * g;
+    f32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // -scale (the fp4 operands carry -sign); 0 for tokens without a valid user
+        const float f = tok_user < 0 ? 0.f
+                        : sdtype == BD_F16 ? -f16_to_f32((uint16_t)sraw[e])
+                                           : -__uint_as_float(sraw[e]);
+        out[e] = vb[e] + f * vd[e];
+    }
+    if (ydtype == BD_F32) {
+        float* dst = (float*)y + (int64_t)m * d_out + o;
+        if (o + 3 < d_out && (d_out & 3) == 0) {
+            *(f32x4*)dst = out;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (o + e < d_out) dst[e] = out[e];
+        }
+    } else {
+        uint16_t* dst = (uint16_t*)y + (int64_t)m * d_out + o;
+        if (o + 3 < d_out && (d_out & 3) == 0) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16);
+            *(uint2*)dst = pk;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (o + e < d_out) dst[e] = f32_to_bf16(out[e]);
+        }
+    }
+}
+
 bool decode_path_supported(int xdtype, int64_t T, int mode) {
     return xdtype == BD_BF16 && T >= 1 && T <= kDecodeMaxT && mode != BD_SCALE_GROUP;
 }
@@ -946,6 +1233,16 @@ hipError_t launch_decode_fused(int64_t T, int U, int64_t d_in, const DeltaPlan& 
     const size_t lds = (size_t)32 * dpad > (size_t)kFusedRedBytes ? (size_t)32 * dpad
                                                                   : (size_t)kFusedRedBytes;
     const dim3 grid((unsigned)((dp.d_out + 15) / 16));
+    if (dpad <= 512 * kUnitWaves) {
+#define BD_UNIT(MODE)                                                                         \
+    k_decode_unit<MODE><<<grid, dim3(64 * kUnitWaves), 0, s>>>(                               \
+        (const uint16_t*)x, ids, (int)T, U, d_in, (const uint16_t*)wb, dp.d_out, signs, scales, \
+        dp.sdtype, dp.per_user, y, ydtype, (uint32_t*)ws)
+        if (dp.mode == BD_SCALE_MATRIX) BD_UNIT(BD_SCALE_MATRIX);
+        else BD_UNIT(BD_SCALE_ROW);
+#undef BD_UNIT
+        return hipGetLastError();
+    }
 #define BD_FUSED(MODE)                                                                          \
     k_decode_fused<MODE><<<grid, dim3(64 * kFusedWaves), lds, s>>>(                             \
         (const uint16_t*)x, ids, (int)T, U, d_in, dpad, (const uint16_t*)wb, dp.d_out, signs,   \
