@@ -49,6 +49,9 @@ def parse():
                     help="output rows of the oracle's sampled apply")
     ap.add_argument("--workloads", action="store_true",
                     help="also time one layer step of workloads 3-5 (stderr, one JSON line each)")
+    ap.add_argument("--merge", action="store_true",
+                    help="also time the dense merge path for one hot user against the fused "
+                         "delta apply, per token count (stderr, one JSON line per shape)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device 3 times (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters)")
@@ -280,6 +283,9 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ids_np, args.cpu_rows, bytes_step)
     print(json.dumps(out), flush=True)
+    if args.merge:
+        for line in merge_leg():
+            print(json.dumps(line), file=sys.stderr, flush=True)
     if args.workloads:
         for line in workloads_leg():
             print(json.dumps(line), file=sys.stderr, flush=True)
@@ -360,6 +366,79 @@ def workloads_leg(reps=10):
                     "frac_of_hbm_peak": round(tot_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
                     "base_TFLOPs": round(tot_flops / us / 1e6, 1)})
         del mats, xs, batches, g
+        torch.cuda.empty_cache()
+    return out
+
+
+def merge_leg(reps=20, token_counts=(16, 32, 64, 128, 256, 512, 1024)):
+    """The dense merge path for a hot user ([P2] "Systems Mechanics": the per-user weight
+    W_u = W_base + scale (.) sign materialised, then one plain GEMM for the user's tokens)
+    against the fused path (the shared base GEMM over the user's tokens plus its delta
+    apply), on the Llama-3.1-8B q_proj and gate shapes with MATRIX fp32 scales, n tokens
+    of one user.  Per shape: bd_reconstruct (W_base + delta into bf16) once; per n:
+    bd_base_gemm on W_base, bd_delta_apply on a prepared batch of the n tokens, and
+    bd_base_gemm on W_u.  Each call is captured `reps` times in a HIP graph and replayed.
+    fused = base + delta; merged with W_u kept = the GEMM on W_u; merged afresh = that
+    plus the reconstruct."""
+    import torch
+
+    from tenant_serving_amd import bitdelta as B
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    out = []
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    for name, d_out, d_in in (("q_proj", 4096, 4096), ("gate_proj", 14336, 4096)):
+        p = B.params("matrix")
+        wb = (torch.randn(d_out, d_in, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+        signs = torch.randint(-2**62, 2**62, (1, d_out, d_in // 64), dtype=torch.int64,
+                              device=dev, generator=gen)
+        scales = torch.full((1, 1), 5e-4, device=dev)
+        wu = torch.empty(d_out, d_in, dtype=torch.bfloat16, device=dev)
+        recon_us = timed(lambda: B.bd_reconstruct(signs[0], scales[0], p, d_out, d_in, wb, wu))
+        rows = []
+        for n in token_counts:
+            x = torch.randn(n, d_in, device=dev, generator=gen).to(torch.bfloat16)
+            ids = torch.zeros(n, dtype=torch.int32, device=dev)
+            bt = B.workspace(B.bd_batch_workspace_bytes(n, 1, d_in, B.BD_BF16), dev)
+            assert B.bd_batch_prepare(x, ids, 1, bt) == B.BD_OK
+            y = torch.empty(n, d_out, device=dev)
+            base_us = timed(lambda: B.bd_base_gemm(x, wb, y))
+            delta_us = timed(lambda: B.bd_delta_apply(bt, x, 1, signs, scales, p, y))
+            gemm_u_us = timed(lambda: B.bd_base_gemm(x, wu, y))
+            rows.append({"tokens": n, "base_gemm_us": round(base_us, 2),
+                         "delta_apply_us": round(delta_us, 2), "fused_us": round(base_us + delta_us, 2),
+                         "merged_gemm_us": round(gemm_u_us, 2),
+                         "merged_afresh_us": round(recon_us + gemm_u_us, 2)})
+            del x, ids, bt, y
+        cross = next((r["tokens"] for r in rows if r["merged_afresh_us"] <= r["fused_us"]), None)
+        out.append({"leg": "merge", "matrix": name, "d_out": d_out, "d_in": d_in,
+                    "reconstruct_us": round(recon_us, 2), "merged_weight_bytes": 2 * d_out * d_in,
+                    "crossover_tokens_afresh": cross, "rows": rows})
+        del wb, signs, wu
         torch.cuda.empty_cache()
     return out
 
