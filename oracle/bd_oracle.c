@@ -254,6 +254,64 @@ int64_t orc_compress(const void* wf, const void* wb, int dtype, int64_t d_out, i
     return bad;
 }
 
+/* ------------------------------------------------- O7 per-layer axis choice */
+
+/* [P5] "Key Contributions" 1-2: one scale vector per layer, per output row or per
+ * input column, the axis chosen per layer.  The page keeps the axis with the lower
+ * validation loss; without data this reading keeps the axis whose absmean
+ * reconstruction s * sign(d) is closer to the (clipped, as in compression) delta in
+ * the Frobenius norm.  The errors are summed element by element over both
+ * reconstructions, in binary64:
+ *     err_row = sum_o sum_i (dc[o][i] - srow[o] * sign(dc[o][i]))^2,  srow[o] = mean_i |dc[o][i]|
+ *     err_col = sum_o sum_i (dc[o][i] - scol[i] * sign(dc[o][i]))^2,  scol[i] = mean_o |dc[o][i]|
+ * with sign(0) = +1.  Ties keep ROW.  out = {err_row, err_col, axis (2 ROW, 3 COL)}.
+ * Returns the number of non-finite deltas, or -1 on allocation failure. */
+int64_t orc_select_axis(const void* wf, const void* wb, int dtype, int64_t d_out, int64_t d_in,
+                        double clip_k, double* out) {
+    int64_t n = d_out * d_in;
+    float* delta = (float*)malloc(sizeof(float) * (size_t)n);
+    double* dc = (double*)malloc(sizeof(double) * (size_t)n);
+    double* srow = (double*)calloc((size_t)d_out, sizeof(double));
+    double* scol = (double*)calloc((size_t)d_in, sizeof(double));
+    if (!delta || !dc || !srow || !scol) {
+        free(delta);
+        free(dc);
+        free(srow);
+        free(scol);
+        return -1;
+    }
+    orc_delta(wf, wb, dtype, n, delta);
+    int64_t bad = orc_count_nonfinite(delta, n);
+    double st[4] = {0.0, 0.0, 0.0, 0.0};
+    int clip = clip_k > 0.0;
+    if (clip) orc_clip_stats(delta, n, clip_k, st);
+    orc_clamp(delta, n, clip, st[2], st[3], dc);
+    for (int64_t o = 0; o < d_out; ++o)
+        for (int64_t i = 0; i < d_in; ++i) {
+            srow[o] += fabs(dc[o * d_in + i]);
+            scol[i] += fabs(dc[o * d_in + i]);
+        }
+    for (int64_t o = 0; o < d_out; ++o) srow[o] /= (double)d_in;
+    for (int64_t i = 0; i < d_in; ++i) scol[i] /= (double)d_out;
+    double er = 0.0, ec = 0.0;
+    for (int64_t o = 0; o < d_out; ++o)
+        for (int64_t i = 0; i < d_in; ++i) {
+            double d = dc[o * d_in + i];
+            double sg = d < 0.0 ? -1.0 : 1.0;
+            double a = d - srow[o] * sg, b = d - scol[i] * sg;
+            er += a * a;
+            ec += b * b;
+        }
+    out[0] = er;
+    out[1] = ec;
+    out[2] = er <= ec ? (double)O_ROW : (double)O_COL;
+    free(delta);
+    free(dc);
+    free(srow);
+    free(scol);
+    return bad;
+}
+
 /* -------------------------------------------------------- O6 reconstruct */
 
 static double o_scale_at(const void* scales, int mode, int64_t g, int sdtype, int64_t d_in,

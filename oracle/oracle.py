@@ -64,6 +64,8 @@ def lib():
         L.orc_absmean_scales.restype = None
         L.orc_compress.argtypes = [vp, vp, i32, i64, i64, i32, i64, dbl, i32, vp, vp, vp]
         L.orc_compress.restype = i64
+        L.orc_select_axis.argtypes = [vp, vp, i32, i64, i64, dbl, vp]
+        L.orc_select_axis.restype = i64
         L.orc_reconstruct.argtypes = [vp, vp, i32, i64, i32, i64, i64, vp, i32, vp]
         L.orc_reconstruct.restype = None
         L.orc_apply.argtypes = [vp, i32, i64, i64, vp, i32, i64, vp, vp, i32, i64, i32, i32, vp,
@@ -160,6 +162,21 @@ def compress(wf: np.ndarray, wb, mode: int, g: int = 128, clip_k: float = 0.0,
     if bad < 0:
         raise MemoryError("oracle compress: allocation failed")
     return words, scales, tuple(float(v) for v in stats), int(bad)
+
+
+def select_axis(wf: np.ndarray, wb, clip_k: float = 0.0, dtype=None):
+    """Per-layer choice between ROW and COL absmean scales ([P5] "Key Contributions" 2,
+    read without data: the axis whose reconstruction is closer to the delta).
+    Returns (err_row, err_col, axis, n_nonfinite)."""
+    wf = np.ascontiguousarray(wf)
+    d_out, d_in = wf.shape
+    wbc = None if wb is None else np.ascontiguousarray(wb)
+    out = np.zeros(3, dtype=np.float64)
+    bad = lib().orc_select_axis(_p(wf), _p(wbc), _dtype_of(wf, dtype), d_out, d_in,
+                                float(clip_k), _p(out))
+    if bad < 0:
+        raise MemoryError("oracle select_axis: allocation failed")
+    return float(out[0]), float(out[1]), int(out[2]), int(bad)
 
 
 def reconstruct(words: np.ndarray, scales: np.ndarray, mode: int, d_out: int, d_in: int,

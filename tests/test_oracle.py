@@ -276,3 +276,58 @@ def test_llama8b_scalar_artifact_size(golden):
     g = golden["llama8b_scalar_artifact"]
     total_mb = (bits + 2 * g["vocab"] * g["hidden"] * 2) / 1e6
     assert round(total_mb) == g["printed_mb"]
+
+
+# ------------------------------------------------- per-layer axis selection
+
+def _closed_form_axis_errors(wf, wb, clip_k):
+    """The errors from per-unit sums only: a unit of n deltas with absmean s has
+    sum (|d| - s)^2 = sum d^2 - (sum |d|)^2 / n.  Delta and clipping with numpy."""
+    d = wf.astype(np.float32) - wb.astype(np.float32)
+    dc = d.astype(np.float64)
+    if clip_k > 0:
+        mu, sd = dc.mean(), dc.std(ddof=1)
+        dc = np.clip(dc, mu - clip_k * sd, mu + clip_k * sd)
+    ss = np.sum(dc * dc)
+    a = np.abs(dc)
+    er = ss - np.sum(a.sum(axis=1) ** 2) / dc.shape[1]
+    ec = ss - np.sum(a.sum(axis=0) ** 2) / dc.shape[0]
+    return er, ec
+
+
+@pytest.mark.parametrize("clip_k", [0.0, 3.0])
+@pytest.mark.parametrize("shape", [(7, 64), (64, 192), (130, 128)])
+def test_axis_errors_match_the_closed_form(shape, clip_k):
+    rng = np.random.default_rng(31 + shape[0] + int(clip_k))
+    wb = rng.normal(0, 0.02, shape).astype(np.float32)
+    d = rng.laplace(0, 1e-3, shape)
+    d[rng.random(shape) < 0.01] *= 50  # outliers, so that clipping bites
+    wf = (wb + d).astype(np.float32)
+    er, ec, axis, bad = O.select_axis(wf, wb, clip_k)
+    cer, cec = _closed_form_axis_errors(wf, wb, clip_k)
+    assert bad == 0
+    assert rel(er, cer) <= 1e-9 and rel(ec, cec) <= 1e-9
+    assert axis == (O.ROW if cer <= cec else O.COL)
+
+
+def test_axis_choice_on_rows_or_columns_of_one_magnitude():
+    rng = np.random.default_rng(5)
+    sgn = np.where(rng.random((8, 64)) < 0.5, -1.0, 1.0)
+    # every row of one magnitude: the row scales reconstruct it exactly
+    rows = (sgn * (2.0 ** -np.arange(1, 9))[:, None]).astype(np.float32)
+    er, ec, axis, _ = O.select_axis(rows, None)
+    assert er == 0.0 and ec > 0.0 and axis == O.ROW
+    # every column of one magnitude: the column scales do
+    cols = (sgn * (2.0 ** -(np.arange(64) % 9 + 1))[None, :]).astype(np.float32)
+    er, ec, axis, _ = O.select_axis(cols, None)
+    assert ec == 0.0 and er > 0.0 and axis == O.COL
+
+
+def test_axis_errors_swap_under_transposition_and_scale_quadratically():
+    rng = np.random.default_rng(9)
+    d = rng.laplace(0, 1e-3, (24, 128)).astype(np.float32)
+    er, ec, _, _ = O.select_axis(d, None)
+    er_t, ec_t, _, _ = O.select_axis(np.ascontiguousarray(d.T), None)
+    assert rel(er_t, ec) <= 1e-12 and rel(ec_t, er) <= 1e-12
+    er2, ec2, _, _ = O.select_axis(d * np.float32(4.0), None)  # exact power-of-two scaling
+    assert rel(er2, 16 * er) <= 1e-12 and rel(ec2, 16 * ec) <= 1e-12
