@@ -246,6 +246,42 @@ def main():
                 "achieved": round(comp_gbs, 1), "unit": "GB/s",
                 "frac": round(comp_gbs / HBM_PEAK_GBS, 4)}
 
+    # per-layer axis choice on the same matrices (no clipping): one statistics pass
+    # over W_fine and W_base, then two small reductions
+    a_ws = B.workspace(B.bd_select_axis_workspace_bytes(d_out, d_in, 0.0), dev)
+    a_err = torch.empty(2, dtype=torch.float64, device=dev)
+    a_axis = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def axis_sel(k):
+        return B.bd_select_axis(wfs[k % n_c][0], wfs[k % n_c][1], 0.0, a_err, a_axis, a_ws)
+
+    for k in range(4):
+        assert axis_sel(k) == B.BD_OK
+    torch.cuda.synchronize()
+    g_ax = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        axis_sel(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g_ax):
+        for k in range(KC):
+            axis_sel(k)
+    g_ax.replay()
+    torch.cuda.synchronize()
+    ce0.record()
+    g_ax.replay()
+    ce1.record()
+    torch.cuda.synchronize()
+    assert B.bd_device_status(a_ws) == B.BD_OK
+    ax_us = ce0.elapsed_time(ce1) * 1e3 / KC
+    ax_bytes = 2 * d_out * d_in * 2
+    ax_gbs = ax_bytes / (ax_us * 1e-6) / 1e9
+    axis_select = {"call_us": round(ax_us, 3), "algorithmic_bytes": ax_bytes,
+                   "achieved": round(ax_gbs, 1), "unit": "GB/s",
+                   "frac": round(ax_gbs / HBM_PEAK_GBS, 4)}
+
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -266,6 +302,7 @@ def main():
         "two_launch_path_us": {"k_decode_prep": round(prep_us, 3), "k_decode": round(main_us, 3)},
         "roofline": roofline,
         "compress": compress,
+        "axis_select": axis_select,
         "kernel_source_digest": kernel_source_digest(),
     }
 

@@ -103,6 +103,9 @@ int64_t bd_scales_count(const bd_compress_params* p, int64_t d_out, int64_t d_in
 /* Workspace bytes bd_compress needs for this shape (0 if invalid). */
 size_t bd_compress_workspace_bytes(const bd_compress_params* p, int64_t d_out, int64_t d_in);
 
+/* Workspace bytes bd_select_axis needs for this shape and clip_k (0 if invalid). */
+size_t bd_select_axis_workspace_bytes(int64_t d_out, int64_t d_in, float clip_k);
+
 /* Workspace bytes bd_apply needs (0 if invalid). */
 size_t bd_apply_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t n_users,
                                 int64_t d_out, int64_t d_in, bd_dtype x_dtype, bd_dtype y_dtype);
@@ -133,6 +136,32 @@ size_t bd_apply_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t 
 bd_status bd_compress(const void* w_fine, const void* w_base, bd_dtype w_dtype, int64_t d_out,
                       int64_t d_in, const bd_compress_params* p, uint64_t* signs_out,
                       void* scales_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Per-layer choice between per-row and per-column scales, without data.
+ *
+ * [P5] "Key Contributions" 1-2 store one scale vector per layer, either per
+ * output row or per input column, and keep, per layer, the axis whose model
+ * has the lower validation loss.  Without data this call keeps the axis whose
+ * absmean reconstruction s (.) sign(delta) is closer to the delta in the
+ * Frobenius norm, over the same delta and clipping bd_compress uses.  For a
+ * unit (row or column) of n deltas with absmean s = sum|d| / n the squared
+ * error is sum d^2 - (sum |d|)^2 / n, so one pass over the delta gives both:
+ *     err_row = sum d^2 - sum over rows    (sum |d|)^2 / d_in
+ *     err_col = sum d^2 - sum over columns (sum |d|)^2 / d_out
+ * and the axis is BD_SCALE_ROW when err_row <= err_col, else BD_SCALE_COL.
+ * Every sum is binary64 in a fixed order, so repeated calls agree bit for bit.
+ *
+ *  w_fine, w_base, w_dtype, d_out, d_in : as in bd_compress.
+ *  clip_k    : as bd_compress_params.clip_k (0 = no clipping).
+ *  errors    : device double[2] = {err_row, err_col}, or NULL.
+ *  axis      : device int32 = BD_SCALE_ROW or BD_SCALE_COL, or NULL.
+ *  workspace : >= bd_select_axis_workspace_bytes(d_out, d_in, clip_k) bytes,
+ *              256-byte aligned; its status word is reset by the call.
+ * Same shape rules as bd_compress.  A NaN/Inf delta sets BD_ERR_NONFINITE in
+ * the status word (the errors are then NaN and the axis BD_SCALE_COL). */
+bd_status bd_select_axis(const void* w_fine, const void* w_base, bd_dtype w_dtype, int64_t d_out,
+                         int64_t d_in, float clip_k, double* errors, int32_t* axis,
+                         void* workspace, size_t ws_bytes, void* stream);
 
 /* -------------------------------------------------------- reconstruction */
 

@@ -66,6 +66,11 @@ def lib() -> ctypes.CDLL:
         L.bd_apply_workspace_bytes.argtypes = [P, i64, i32, i64, i64, ctypes.c_int, ctypes.c_int]
         L.bd_compress.restype = ctypes.c_int
         L.bd_compress.argtypes = [vp, vp, ctypes.c_int, i64, i64, P, vp, vp, vp, sz, vp]
+        L.bd_select_axis_workspace_bytes.restype = sz
+        L.bd_select_axis_workspace_bytes.argtypes = [i64, i64, ctypes.c_float]
+        L.bd_select_axis.restype = ctypes.c_int
+        L.bd_select_axis.argtypes = [vp, vp, ctypes.c_int, i64, i64, ctypes.c_float, vp, vp, vp,
+                                     sz, vp]
         L.bd_reconstruct.restype = ctypes.c_int
         L.bd_reconstruct.argtypes = [vp, vp, P, i64, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp]
         L.bd_apply.restype = ctypes.c_int
@@ -142,6 +147,10 @@ def bd_scales_count(p: bd_compress_params, d_out: int, d_in: int) -> int:
 
 def bd_compress_workspace_bytes(p: bd_compress_params, d_out: int, d_in: int) -> int:
     return int(lib().bd_compress_workspace_bytes(ctypes.byref(p), d_out, d_in))
+
+
+def bd_select_axis_workspace_bytes(d_out: int, d_in: int, clip_k: float = 0.0) -> int:
+    return int(lib().bd_select_axis_workspace_bytes(d_out, d_in, float(clip_k)))
 
 
 def bd_apply_workspace_bytes(p: bd_compress_params, T: int, n_users: int, d_out: int, d_in: int,
@@ -252,6 +261,29 @@ def compress(w_fine: torch.Tensor, w_base: Optional[torch.Tensor], p: bd_compres
     if check:
         _check(bd_device_status(ws, stream), "bd_compress (device)")
     return signs_out, scales_out
+
+
+def bd_select_axis(w_fine, w_base, clip_k, errors, axis, workspace, stream=None) -> int:
+    d_out, d_in = w_fine.shape
+    return int(lib().bd_select_axis(_ptr(w_fine), _ptr(w_base), _dtype_code(w_fine), d_out, d_in,
+                                    float(clip_k), _ptr(errors), _ptr(axis), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(w_fine, stream)))
+
+
+def select_axis(w_fine: torch.Tensor, w_base: Optional[torch.Tensor], clip_k: float = 0.0,
+                ws=None, stream=None, check: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Returns (errors float64[2] = {ROW, COL}, axis int32[1]) on the device."""
+    d_out, d_in = w_fine.shape
+    dev = w_fine.device
+    errors = torch.empty(2, dtype=torch.float64, device=dev)
+    axis = torch.empty(1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(bd_select_axis_workspace_bytes(d_out, d_in, clip_k), dev)
+    _check(bd_select_axis(w_fine, w_base, clip_k, errors, axis, ws, stream), "bd_select_axis")
+    if check:
+        _check(bd_device_status(ws, stream), "bd_select_axis (device)")
+    return errors, axis
 
 
 def reconstruct(signs, scales, p, d_out, d_in, w_base=None, out_dtype=torch.float32, stream=None):

@@ -55,6 +55,12 @@ size_t bd_compress_workspace_bytes(const bd_compress_params* p, int64_t d_out, i
     return pl.total;
 }
 
+size_t bd_select_axis_workspace_bytes(int64_t d_out, int64_t d_in, float clip_k) {
+    AxisPlan ap;
+    if (make_axis_plan(clip_k, d_out, d_in, &ap) != BD_OK) return 0;
+    return ap.total;
+}
+
 size_t bd_apply_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t n_users,
                                 int64_t d_out, int64_t d_in, bd_dtype x_dtype, bd_dtype y_dtype) {
     ApplyPlan pl;
@@ -82,6 +88,23 @@ bd_status bd_compress(const void* w_fine, const void* w_base, bd_dtype w_dtype, 
         return BD_ERR_INVALID_ARG;
     hipError_t e = launch_compress(pl, w_fine, w_base, w_dtype, signs_out, scales_out,
                                    (char*)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_select_axis(const void* w_fine, const void* w_base, bd_dtype w_dtype, int64_t d_out,
+                         int64_t d_in, float clip_k, double* errors, int32_t* axis,
+                         void* workspace, size_t ws_bytes, void* stream) {
+    if (!w_fine) return BD_ERR_INVALID_ARG;
+    if (!valid_wdtype(w_dtype)) return BD_ERR_DTYPE;
+    AxisPlan ap;
+    bd_status st = make_axis_plan(clip_k, d_out, d_in, &ap);
+    if (st != BD_OK) return st;
+    if (!workspace || ws_bytes < ap.total || !aligned(workspace, kAlign)) return BD_ERR_WORKSPACE;
+    if (!aligned(w_fine, 16) || (w_base && !aligned(w_base, 16)) || (errors && !aligned(errors, 8)) ||
+        (axis && !aligned(axis, 4)))
+        return BD_ERR_INVALID_ARG;
+    hipError_t e = launch_select_axis(ap, w_fine, w_base, w_dtype, errors, axis, (char*)workspace,
+                                      (hipStream_t)stream);
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 

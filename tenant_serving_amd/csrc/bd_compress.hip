@@ -78,7 +78,10 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
     return r;  // valid in thread 0
 }
 
-// PASS 0: sum of delta; PASS 1: sum of (delta - mu)^2; PASS 2: pack + scales.
+// PASS 0: sum of delta; PASS 1: sum of (delta - mu)^2; PASS 2: pack + scales; PASS 3:
+// the statistics of the per-layer axis choice (sum d^2 per block, sum |d| per row and
+// segment, sum |d| per column and row chunk, of the clipped delta), at
+// part[0 .. n_blocks), part[n_blocks ..) and part[n_blocks + d_out n_seg ..).
 template <typename WT, bool HAS_BASE, int PASS, int MODE, bool CLIP>
 __global__ void __launch_bounds__(kCompressThreads)
 k_compress(const WT* __restrict__ wf, const WT* __restrict__ wb, int64_t d_out, int64_t d_in,
@@ -86,7 +89,7 @@ k_compress(const WT* __restrict__ wf, const WT* __restrict__ wb, int64_t d_out, 
            void* __restrict__ scales, const Stats* __restrict__ st, double* __restrict__ part,
            uint32_t* __restrict__ status) {
     __shared__ double sh[kCompressThreads / 64];
-    constexpr bool kCol = PASS == 2 && MODE == BD_SCALE_COL;
+    constexpr bool kCol = (PASS == 2 && MODE == BD_SCALE_COL) || PASS == 3;
     __shared__ double colsh[kCol ? kCompressThreads / 64 : 1][kCol ? kSegCols : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t seg = blockIdx.x, rc = blockIdx.y;
@@ -98,7 +101,8 @@ k_compress(const WT* __restrict__ wf, const WT* __restrict__ wb, int64_t d_out, 
 
     double mu = 0.0, lo = 0.0, hi = 0.0;
     if (PASS == 1) mu = st->mu;
-    if (PASS == 2 && CLIP) { lo = st->lo; hi = st->hi; }
+    if (PASS >= 2 && CLIP) { lo = st->lo; hi = st->hi; }
+    const int64_t n_blocks = n_seg * (int64_t)gridDim.y;
 
     double acc = 0.0;        // PASS 0/1 and MATRIX partial
     double colacc[8];        // COL partial
@@ -137,6 +141,25 @@ k_compress(const WT* __restrict__ wf, const WT* __restrict__ wb, int64_t d_out, 
                     double e = (double)d[j] - mu;
                     acc += active ? e * e : 0.0;
                 }
+                continue;
+            }
+            if (PASS == 3) {
+                double rs = 0.0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    bad |= (__float_as_uint(d[j]) & 0x7F800000u) == 0x7F800000u;
+                    double xv = (double)d[j];
+                    if (CLIP) {
+                        if (xv < lo) xv = lo;
+                        if (xv > hi) xv = hi;
+                    }
+                    const double a = active ? fabs(xv) : 0.0;
+                    acc += a * a;
+                    rs += a;
+                    colacc[j] += a;
+                }
+                rs = wave_sum(rs);
+                if (lane == 0) part[n_blocks + r * n_seg + seg] = rs;
                 continue;
             }
             // PASS 2: clamp, signs, |delta| partials
@@ -195,11 +218,13 @@ k_compress(const WT* __restrict__ wf, const WT* __restrict__ wb, int64_t d_out, 
         }
     }
 
-    if (PASS == 2 && __ballot(bad) != 0ull && lane == 0) atomicOr(status, ST_NONFINITE);
-    if (PASS < 2 || MODE == BD_SCALE_MATRIX) {
+    if (PASS >= 2 && __ballot(bad) != 0ull && lane == 0) atomicOr(status, ST_NONFINITE);
+    if (PASS < 2 || PASS == 3 || MODE == BD_SCALE_MATRIX) {
         const double tot = block_sum(acc, sh);
         if (threadIdx.x == 0) part[rc * n_seg + seg] = tot;
-    } else if (kCol) {
+    }
+    if (kCol) {
+        double* pc = PASS == 3 ? part + n_blocks + d_out * n_seg : part;
 #pragma unroll
         for (int j = 0; j < 8; ++j) colsh[wave][8 * lane + j] = colacc[j];
         __syncthreads();
@@ -208,7 +233,7 @@ k_compress(const WT* __restrict__ wf, const WT* __restrict__ wb, int64_t d_out, 
             if (col < d_in) {
                 double v = 0.0;
                 for (int w = 0; w < kCompressThreads / 64; ++w) v += colsh[w][c];
-                part[rc * d_in + col] = v;
+                pc[rc * d_in + col] = v;
             }
         }
     }
@@ -264,13 +289,74 @@ k_scales_finalize(int mode, const double* __restrict__ part, int64_t n_seg, int6
     if (mode == BD_SCALE_ROW) {
         if (i >= d_out) return;
         double s = 0.0;
+#pragma unroll 8
         for (int64_t c = 0; c < n_seg; ++c) s += part[i * n_seg + c];
         store_scale(scales, sdtype, i, s / (double)d_in);
     } else {  // COL
         if (i >= d_in) return;
         double s = 0.0;
+#pragma unroll 8
         for (int64_t c = 0; c < n_rchunk; ++c) s += part[c * d_in + i];
         store_scale(scales, sdtype, i, s / (double)d_out);
+    }
+}
+
+// Axis choice, step 1 (thread per row and per column): the squared sum of |d| of each
+// row (over its segments) and of each column (over its row chunks), in a fixed order.
+__global__ void __launch_bounds__(256)
+k_axis_sums(const double* __restrict__ part, int64_t n_seg, int64_t n_rchunk, int64_t n_blocks,
+            int64_t d_out, int64_t d_in, double* __restrict__ rsq, double* __restrict__ csq) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const double* prow = part + n_blocks;
+    const double* pcol = prow + d_out * n_seg;
+    // (unrolled so that the loads of a run go out together; the sum keeps its order)
+    if (i < d_out) {
+        double v = 0.0;
+#pragma unroll 8
+        for (int64_t c = 0; c < n_seg; ++c) v += prow[i * n_seg + c];
+        rsq[i] = v * v;
+    }
+    if (i < d_in) {
+        double v = 0.0;
+#pragma unroll 8
+        for (int64_t c = 0; c < n_rchunk; ++c) v += pcol[c * d_in + i];
+        csq[i] = v * v;
+    }
+}
+
+// Axis choice, step 2 (one block): for a unit of n deltas with absmean s = sum|d| / n,
+// sum (|d| - s)^2 = sum d^2 - (sum |d|)^2 / n, so
+//   err_row = sum d^2 - sum_rows (sum |d|)^2 / d_in,  err_col = sum d^2 - sum_cols (..)^2 / d_out;
+// ROW when err_row <= err_col.  Every sum runs in a fixed order.
+__global__ void __launch_bounds__(256)
+k_axis_finalize(const double* __restrict__ part, int64_t n_blocks, const double* __restrict__ rsq,
+                const double* __restrict__ csq, int64_t d_out, int64_t d_in,
+                double* __restrict__ errors, int32_t* __restrict__ axis) {
+    __shared__ double sh[3][256];
+    double a = 0.0, b = 0.0, c = 0.0;
+#pragma unroll 8
+    for (int64_t i = threadIdx.x; i < n_blocks; i += 256) a += part[i];
+#pragma unroll 8
+    for (int64_t i = threadIdx.x; i < d_out; i += 256) b += rsq[i];
+#pragma unroll 8
+    for (int64_t i = threadIdx.x; i < d_in; i += 256) c += csq[i];
+    sh[0][threadIdx.x] = a;
+    sh[1][threadIdx.x] = b;
+    sh[2][threadIdx.x] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double ss = 0.0, R = 0.0, C = 0.0;
+        for (int i = 0; i < 256; ++i) {
+            ss += sh[0][i];
+            R += sh[1][i];
+            C += sh[2][i];
+        }
+        const double er = ss - R / (double)d_in, ec = ss - C / (double)d_out;
+        if (errors) {
+            errors[0] = er;
+            errors[1] = ec;
+        }
+        if (axis) axis[0] = er <= ec ? BD_SCALE_ROW : BD_SCALE_COL;
     }
 }
 
@@ -322,7 +408,81 @@ hipError_t launch_typed(const CompressPlan& pl, const WT* wf, const WT* wb, uint
     return hipGetLastError();
 }
 
+template <typename WT, bool HB>
+hipError_t launch_axis_typed(const AxisPlan& ap, const WT* wf, const WT* wb, double* errors,
+                             int32_t* axis, char* ws, hipStream_t s) {
+    const CompressPlan& pl = ap.c;
+    uint32_t* status = (uint32_t*)(ws + pl.off_status);
+    Stats* st = (Stats*)(ws + pl.off_stats);
+    double* psum = (double*)(ws + pl.off_part_sum);
+    double* pm2 = (double*)(ws + pl.off_part_m2);
+    double* part = (double*)(ws + ap.off_part);
+    double* rsq = (double*)(ws + ap.off_rsq);
+    double* csq = (double*)(ws + ap.off_csq);
+    const dim3 grid((unsigned)pl.n_seg, (unsigned)pl.n_rchunk), block(kCompressThreads);
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, status, (int64_t)(kAlign / 4));
+    if (pl.clip) {
+        hipLaunchKernelGGL((k_compress<WT, HB, 0, 0, false>), grid, block, 0, s, wf, wb, pl.d_out,
+                           pl.d_in, pl.rows_per_block, 0, BD_F32, nullptr, nullptr, st, psum,
+                           status);
+        hipLaunchKernelGGL(k_stats_finalize<0>, dim3(1), dim3(256), 0, s, psum, pl.n_blocks, pl.n,
+                           pl.clip_k, st);
+        hipLaunchKernelGGL((k_compress<WT, HB, 1, 0, false>), grid, block, 0, s, wf, wb, pl.d_out,
+                           pl.d_in, pl.rows_per_block, 0, BD_F32, nullptr, nullptr, st, pm2,
+                           status);
+        hipLaunchKernelGGL(k_stats_finalize<1>, dim3(1), dim3(256), 0, s, pm2, pl.n_blocks, pl.n,
+                           pl.clip_k, st);
+        hipLaunchKernelGGL((k_compress<WT, HB, 3, BD_SCALE_COL, true>), grid, block, 0, s, wf, wb,
+                           pl.d_out, pl.d_in, pl.rows_per_block, 0, BD_F32, nullptr, nullptr, st,
+                           part, status);
+    } else {
+        hipLaunchKernelGGL((k_compress<WT, HB, 3, BD_SCALE_COL, false>), grid, block, 0, s, wf, wb,
+                           pl.d_out, pl.d_in, pl.rows_per_block, 0, BD_F32, nullptr, nullptr, st,
+                           part, status);
+    }
+    const int64_t nmax = pl.d_out > pl.d_in ? pl.d_out : pl.d_in;
+    hipLaunchKernelGGL(k_axis_sums, dim3((unsigned)((nmax + 255) / 256)), dim3(256), 0, s, part,
+                       pl.n_seg, pl.n_rchunk, pl.n_blocks, pl.d_out, pl.d_in, rsq, csq);
+    hipLaunchKernelGGL(k_axis_finalize, dim3(1), dim3(256), 0, s, part, pl.n_blocks, rsq, csq,
+                       pl.d_out, pl.d_in, errors, axis);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bd_status make_axis_plan(float clip_k, int64_t d_out, int64_t d_in, AxisPlan* ap) {
+    if (!ap) return BD_ERR_INVALID_ARG;
+    bd_compress_params p;
+    p.bits = 1;
+    p.mode = BD_SCALE_COL;  // the row chunks of the column partials
+    p.group_size = 0;
+    p.clip_k = clip_k;
+    p.scale_dtype = BD_F32;
+    AxisPlan q;
+    const bd_status st = make_compress_plan(&p, d_out, d_in, &q.c);
+    if (st != BD_OK) return st;
+    size_t off = q.c.off_part_abs;  // the compress layout up to its partials, then ours
+    q.off_part = off;
+    off += align_up(sizeof(double) * (size_t)(q.c.n_blocks + d_out * q.c.n_seg +
+                                              q.c.n_rchunk * d_in));
+    q.off_rsq = off;
+    off += align_up(sizeof(double) * (size_t)d_out);
+    q.off_csq = off;
+    off += align_up(sizeof(double) * (size_t)d_in);
+    q.total = off;
+    *ap = q;
+    return BD_OK;
+}
+
+hipError_t launch_select_axis(const AxisPlan& ap, const void* wf, const void* wb, int wdtype,
+                              double* errors, int32_t* axis, char* ws, hipStream_t s) {
+    if (wdtype == BD_BF16) {
+        if (wb) return launch_axis_typed<uint16_t, true>(ap, (const uint16_t*)wf, (const uint16_t*)wb, errors, axis, ws, s);
+        return launch_axis_typed<uint16_t, false>(ap, (const uint16_t*)wf, nullptr, errors, axis, ws, s);
+    }
+    if (wb) return launch_axis_typed<float, true>(ap, (const float*)wf, (const float*)wb, errors, axis, ws, s);
+    return launch_axis_typed<float, false>(ap, (const float*)wf, nullptr, errors, axis, ws, s);
+}
 
 bd_status make_compress_plan(const bd_compress_params* p, int64_t d_out, int64_t d_in,
                              CompressPlan* pl) {

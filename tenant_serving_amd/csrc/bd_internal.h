@@ -43,6 +43,16 @@ bd_status make_compress_plan(const bd_compress_params* p, int64_t d_out, int64_t
 hipError_t launch_compress(const CompressPlan& pl, const void* wf, const void* wb, int wdtype,
                            uint64_t* signs, void* scales, char* ws, hipStream_t s);
 
+// Per-layer axis choice (bd_select_axis): the compress plan's grid and clip passes, then
+// one statistics pass (the ROW and COL absmean partials and sum d^2) and two reductions.
+struct AxisPlan {
+    CompressPlan c;
+    size_t off_part = 0, off_rsq = 0, off_csq = 0, total = 0;
+};
+bd_status make_axis_plan(float clip_k, int64_t d_out, int64_t d_in, AxisPlan* plan);
+hipError_t launch_select_axis(const AxisPlan& ap, const void* wf, const void* wb, int wdtype,
+                              double* errors, int32_t* axis, char* ws, hipStream_t s);
+
 // ------------------------------------------------------------------- apply
 constexpr int kItemTokens = 32;   // max tokens of one (user, chunk) work item (<= 2 MFMA tiles)
 constexpr int kMaxGroupT = 8192;  // tokens the one-block grouping kernel sorts in LDS

@@ -102,3 +102,27 @@ def test_apply_rejects_bad_arguments_synchronously():
     assert call(ws_bytes=16) == B.BD_ERR_WORKSPACE
     assert call(x=0) == B.BD_ERR_INVALID_ARG
     assert call(x=(1 << 12) + 2) == B.BD_ERR_INVALID_ARG
+
+
+def _select_raw(d_out=64, d_in=128, dtype=B.BD_BF16, clip_k=0.0, wf=1 << 12, ws=1 << 16,
+                ws_bytes=1 << 30, errors=1 << 20, axis=1 << 20):
+    # fake, never dereferenced device addresses: every case fails before any launch
+    L = B.lib()
+    return int(L.bd_select_axis(wf, None, dtype, d_out, d_in, clip_k, errors, axis, ws, ws_bytes,
+                                None))
+
+
+def test_select_axis_sizes_and_synchronous_errors():
+    assert B.bd_select_axis_workspace_bytes(256, 512, 0.0) > 0
+    assert B.bd_select_axis_workspace_bytes(256, 512, 3.0) > B.bd_select_axis_workspace_bytes(256, 512, 0.0)
+    assert B.bd_select_axis_workspace_bytes(256, 100, 0.0) == 0
+    assert _select_raw(wf=0) == B.BD_ERR_INVALID_ARG
+    assert _select_raw(d_in=100) == B.BD_ERR_SHAPE
+    assert _select_raw(d_out=0) == B.BD_ERR_SHAPE
+    assert _select_raw(dtype=B.BD_F16) == B.BD_ERR_DTYPE
+    assert _select_raw(clip_k=float("nan")) == B.BD_ERR_INVALID_ARG
+    assert _select_raw(ws=0) == B.BD_ERR_WORKSPACE
+    assert _select_raw(ws_bytes=8) == B.BD_ERR_WORKSPACE
+    assert _select_raw(ws=256 + 8) == B.BD_ERR_WORKSPACE
+    assert _select_raw(wf=256 + 8) == B.BD_ERR_INVALID_ARG
+    assert _select_raw(errors=(1 << 20) + 4) == B.BD_ERR_INVALID_ARG
