@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--merge", action="store_true",
                     help="also time the dense merge path for one hot user against the fused "
                          "delta apply, per token count (stderr, one JSON line per shape)")
+    ap.add_argument("--load", action="store_true",
+                    help="also time loading one user's packed deltas of the Llama-3.1-8B linear "
+                         "stack from pinned host memory, against the dense bf16 weights (stderr)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device 3 times (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters)")
@@ -320,6 +323,8 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ids_np, args.cpu_rows, bytes_step)
     print(json.dumps(out), flush=True)
+    if args.load:
+        print(json.dumps(load_leg()), file=sys.stderr, flush=True)
     if args.merge:
         for line in merge_leg():
             print(json.dumps(line), file=sys.stderr, flush=True)
@@ -405,6 +410,74 @@ def workloads_leg(reps=10):
         del mats, xs, batches, g
         torch.cuda.empty_cache()
     return out
+
+
+LLAMA8B_LINEARS = ((4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096),  # q k v o
+                   (14336, 4096), (14336, 4096), (4096, 14336))            # gate up down
+
+
+def load_leg(layers=32, reps=3):
+    """Cold load of one user's deltas for the Llama-3.1-8B linear stack ([P5] "Key
+    Contributions" 4: the packed delta moved in one transfer per module; [P1] "How
+    BitDelta Works": the base stays resident and only deltas move).  Pinned host
+    buffers, device-resident destination, graph-free timed copies on one stream:
+    (a) one transfer per layer (all its matrices packed), (b) one per matrix, and
+    (c) the dense bf16 weights of the same matrices, one transfer per layer."""
+    import torch
+
+    from tenant_serving_amd.banks import module_layout
+
+    dev = torch.device("cuda:0")
+    offs, layer_bytes = module_layout(LLAMA8B_LINEARS, [1] * len(LLAMA8B_LINEARS))
+    dense_layer = sum(o * i * 2 for o, i in LLAMA8B_LINEARS)
+    hb = torch.empty(layers * layer_bytes, dtype=torch.uint8, pin_memory=True)
+    db = torch.empty(layers * layer_bytes, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            t = time.perf_counter() - t0
+            best = t if best is None or t < best else best
+        return best
+
+    def per_layer():
+        for l in range(layers):
+            a = l * layer_bytes
+            db[a:a + layer_bytes].copy_(hb[a:a + layer_bytes], non_blocking=True)
+
+    def per_matrix():
+        for l in range(layers):
+            a = l * layer_bytes
+            for (s_off, c_off), (o, i) in zip(offs, LLAMA8B_LINEARS):
+                n = o * i // 8
+                db[a + s_off:a + s_off + n].copy_(hb[a + s_off:a + s_off + n], non_blocking=True)
+                db[a + c_off:a + c_off + 4].copy_(hb[a + c_off:a + c_off + 4], non_blocking=True)
+
+    t_layer, t_matrix = timed(per_layer), timed(per_matrix)
+    del db
+    hd = torch.empty(layers * dense_layer, dtype=torch.uint8, pin_memory=True)
+    dd = torch.empty(layers * dense_layer, dtype=torch.uint8, device=dev)
+
+    def dense():
+        for l in range(layers):
+            a = l * dense_layer
+            dd[a:a + dense_layer].copy_(hd[a:a + dense_layer], non_blocking=True)
+
+    t_dense = timed(dense)
+    del hd, dd, hb
+    torch.cuda.empty_cache()
+    return {"leg": "load", "model": "Llama-3.1-8B linear stack (32 x q,k,v,o,gate,up,down)",
+            "delta_bytes": layers * layer_bytes, "dense_bf16_bytes": layers * dense_layer,
+            "delta_one_transfer_per_layer_s": round(t_layer, 4),
+            "delta_one_transfer_per_matrix_s": round(t_matrix, 4),
+            "dense_one_transfer_per_layer_s": round(t_dense, 4),
+            "delta_GBs": round(layers * layer_bytes / t_layer / 1e9, 1),
+            "dense_GBs": round(layers * dense_layer / t_dense / 1e9, 1),
+            "speedup_vs_dense": round(t_dense / t_layer, 2)}
 
 
 def merge_leg(reps=20, token_counts=(16, 32, 64, 128, 256, 512, 1024)):
