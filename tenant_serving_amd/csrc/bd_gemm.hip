@@ -3,7 +3,7 @@
 // gfx950 matrix cores ([P2] "Systems Mechanics" 1: one dense product of the
 // whole batch with the shared base weight).
 //
-// Block tile: BR rows of W x BT tokens (128 x 256 or 128 x 128), 4 waves
+// Block tile: BR rows of W x BT tokens (128 x 256, 128 x 128, 64 x 128 or 64 x 64), 4 waves
 // (2 x 2), each BR/2 x BT/2 =
 // (BR/64) x (BT/64) tiles of v_mfma_f32_32x32x16_bf16 with the accumulators in
 // AGPRs.  K advances BK columns per stage through a ring of NS LDS stages.
@@ -199,13 +199,16 @@ bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out) {
            d_out * d_in * 2 < ((int64_t)1 << 31) && d_out < ((int64_t)1 << 30);
 }
 
-// Two tile shapes: 128 rows x 256 tokens (more reuse per copied byte) when it
-// still yields enough blocks to cover the chip, else 128 x 128 (twice the blocks).
+// The largest tile that still yields enough blocks to cover the chip: 128 rows x 256
+// tokens (most reuse per copied byte), 128 x 128, 64 x 128, else 64 x 64 (small
+// matrices and batches, where idle CUs cost more than the extra copies).
 hipError_t launch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb, int64_t d_out,
                        float* y, hipStream_t s) {
-    const int64_t big_blocks = ((d_out + 127) / 128) * ((T + 255) / 256);
-    if (big_blocks >= 200) return launch_tile<128, 256, 64, 3>(x, T, d_in, wb, d_out, y, s);
-    return launch_tile<128, 128, 64, 4>(x, T, d_in, wb, d_out, y, s);
+    auto blocks = [&](int64_t br, int64_t bt) { return ((d_out + br - 1) / br) * ((T + bt - 1) / bt); };
+    if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 3>(x, T, d_in, wb, d_out, y, s);
+    if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 4>(x, T, d_in, wb, d_out, y, s);
+    if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 4>(x, T, d_in, wb, d_out, y, s);
+    return launch_tile<64, 64, 64, 4>(x, T, d_in, wb, d_out, y, s);
 }
 
 }  // namespace bd
