@@ -384,3 +384,60 @@ void orc_apply(const void* x, int xdtype, int64_t T, int64_t d_in, const void* w
         }
     }
 }
+
+/* ---------------------------------------------- O8 quantized base weights */
+
+/* [P2] "Systems Mechanics" (production notes): the 1-bit delta applied on an INT8
+ * base.  The page names no quantizer; this reading is symmetric per output row:
+ * s[o] = max_i |w[o][i]| / 127 and q[o][i] = round-half-even(w[o][i] / s[o]) clamped
+ * to [-127, 127], both divisions in binary32 (a zero row gets s = 0 and q = 0). */
+void orc_quantize_rows(const void* w, int dtype, int64_t d_out, int64_t d_in, int8_t* q,
+                       float* s) {
+    for (int64_t o = 0; o < d_out; ++o) {
+        float m = 0.0f;
+        for (int64_t i = 0; i < d_in; ++i) {
+            float a = fabsf(o_load(w, dtype, o * d_in + i));
+            if (a > m) m = a;
+        }
+        float so = m / 127.0f;
+        s[o] = so;
+        for (int64_t i = 0; i < d_in; ++i) {
+            float v = so > 0.0f ? o_load(w, dtype, o * d_in + i) / so : 0.0f;
+            float r = rintf(v);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            q[o * d_in + i] = (int8_t)r;
+        }
+    }
+}
+
+/* The apply of orc_apply with the base weight given as (q, s): for every token t and
+ * row o, base = s[o] * sum_i x[t][i] q[o][i], delta as in orc_apply, y = base + delta,
+ * in binary64. */
+void orc_apply_q8(const void* x, int xdtype, int64_t T, int64_t d_in, const int8_t* q,
+                  const float* s, int64_t n_rows, const uint64_t* words_bank,
+                  const void* scales_bank, int mode, int64_t g, int sdtype, int32_t n_users,
+                  const int32_t* user_ids, double* y, double* y_base, double* y_delta) {
+    int64_t wpr = orc_words_per_row(d_in);
+    int64_t spu = orc_scales_count(mode, n_rows, d_in, g);
+    size_t ssz = (sdtype == O_F16) ? 2 : 4;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t u = user_ids[t];
+        int has = u >= 0 && u < n_users;
+        const uint64_t* wu = has ? words_bank + (int64_t)u * n_rows * wpr : NULL;
+        const void* su = has ? (const void*)((const char*)scales_bank + (size_t)u * spu * ssz) : NULL;
+        for (int64_t o = 0; o < n_rows; ++o) {
+            double base = 0.0, delta = 0.0;
+            for (int64_t i = 0; i < d_in; ++i) {
+                double xv = (double)o_load(x, xdtype, t * d_in + i);
+                base += xv * (double)q[o * d_in + i];
+                if (has) delta += xv * o_sign_at(wu, wpr, o, i) * o_scale_at(su, mode, g, sdtype, d_in, o, i);
+            }
+            base *= (double)s[o];
+            y[t * n_rows + o] = base + delta;
+            if (y_base) y_base[t * n_rows + o] = base;
+            if (y_delta) y_delta[t * n_rows + o] = delta;
+        }
+    }
+}

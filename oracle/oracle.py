@@ -66,6 +66,11 @@ def lib():
         L.orc_compress.restype = i64
         L.orc_select_axis.argtypes = [vp, vp, i32, i64, i64, dbl, vp]
         L.orc_select_axis.restype = i64
+        L.orc_quantize_rows.argtypes = [vp, i32, i64, i64, vp, vp]
+        L.orc_quantize_rows.restype = None
+        L.orc_apply_q8.argtypes = [vp, i32, i64, i64, vp, vp, i64, vp, vp, i32, i64, i32, i32,
+                                   vp, vp, vp, vp]
+        L.orc_apply_q8.restype = None
         L.orc_reconstruct.argtypes = [vp, vp, i32, i64, i32, i64, i64, vp, i32, vp]
         L.orc_reconstruct.restype = None
         L.orc_apply.argtypes = [vp, i32, i64, i64, vp, i32, i64, vp, vp, i32, i64, i32, i32, vp,
@@ -162,6 +167,38 @@ def compress(wf: np.ndarray, wb, mode: int, g: int = 128, clip_k: float = 0.0,
     if bad < 0:
         raise MemoryError("oracle compress: allocation failed")
     return words, scales, tuple(float(v) for v in stats), int(bad)
+
+
+def quantize_rows(w: np.ndarray, dtype=None):
+    """INT8 base weights, symmetric per output row (the reading of the pages' INT8
+    base): returns (q int8 [d_out][d_in], s float32 [d_out])."""
+    w = np.ascontiguousarray(w)
+    d_out, d_in = w.shape
+    q = np.zeros((d_out, d_in), dtype=np.int8)
+    s = np.zeros(d_out, dtype=np.float32)
+    lib().orc_quantize_rows(_p(w), _dtype_of(w, dtype), d_out, d_in, _p(q), _p(s))
+    return q, s
+
+
+def apply_q8(x: np.ndarray, q: np.ndarray, s: np.ndarray, words_bank: np.ndarray,
+             scales_bank: np.ndarray, mode: int, user_ids: np.ndarray, g: int = 128,
+             sdtype: int = F32, xdtype=None):
+    """apply() with the base weight given as INT8 rows and their scales."""
+    x = np.ascontiguousarray(x)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    words_bank = np.ascontiguousarray(words_bank, dtype=np.uint64)
+    scales_bank = np.ascontiguousarray(scales_bank)
+    ids = np.ascontiguousarray(user_ids, dtype=np.int32)
+    T, d_in = x.shape
+    n_rows = q.shape[0]
+    U = words_bank.shape[0]
+    y = np.empty((T, n_rows), dtype=np.float64)
+    yb = np.empty_like(y)
+    yd = np.empty_like(y)
+    lib().orc_apply_q8(_p(x), _dtype_of(x, xdtype), T, d_in, _p(q), _p(s), n_rows, _p(words_bank),
+                       _p(scales_bank), mode, g, sdtype, U, _p(ids), _p(y), _p(yb), _p(yd))
+    return y, yb, yd
 
 
 def select_axis(wf: np.ndarray, wb, clip_k: float = 0.0, dtype=None):

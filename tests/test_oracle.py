@@ -331,3 +331,40 @@ def test_axis_errors_swap_under_transposition_and_scale_quadratically():
     assert rel(er_t, ec) <= 1e-12 and rel(ec_t, er) <= 1e-12
     er2, ec2, _, _ = O.select_axis(d * np.float32(4.0), None)  # exact power-of-two scaling
     assert rel(er2, 16 * er) <= 1e-12 and rel(ec2, 16 * ec) <= 1e-12
+
+
+# ------------------------------------------------------ INT8 base weights
+
+def test_row_quantizer_matches_numpy_and_its_bounds():
+    rng = np.random.default_rng(17)
+    w = rng.normal(0, 0.02, (12, 192)).astype(np.float32)
+    w[3] = 0.0  # a zero row
+    w[5, 7] = -0.5  # a row whose maximum is negative
+    q, s = O.quantize_rows(w)
+    m = np.abs(w).max(axis=1)
+    ns = (m / np.float32(127.0)).astype(np.float32)  # binary32 division, as the reading states
+    assert np.array_equal(s, ns)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(ns[:, None] > 0, w / ns[:, None], 0).astype(np.float32)
+    assert np.array_equal(q, np.clip(np.rint(v), -127, 127).astype(np.int8))
+    assert np.all(q[3] == 0) and s[3] == 0.0 and q[5, 7] == -127
+    err = np.abs(w.astype(np.float64) - q * s[:, None].astype(np.float64))
+    assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-6) + 1e-30)  # half a step per element
+
+
+def test_apply_on_int8_base_reduces_to_numpy_matmul():
+    rng = np.random.default_rng(19)
+    T, d_out, d_in, U = 5, 24, 128, 3
+    x = rng.normal(0, 1, (T, d_in)).astype(np.float32)
+    wb = rng.normal(0, 0.02, (d_out, d_in)).astype(np.float32)
+    q, s = O.quantize_rows(wb)
+    d = rng.laplace(0, 1e-3, (U, d_out, d_in))
+    words = np.stack([O.pack_signs(d[u]) for u in range(U)])
+    scales = np.stack([O.absmean_scales(d[u], O.ROW) for u in range(U)])
+    ids = np.array([2, 0, -1, 1, 2], dtype=np.int32)
+    y, yb, yd = O.apply_q8(x, q, s, words, scales, O.ROW, ids)
+    deq = q.astype(np.float64) * s[:, None].astype(np.float64)
+    assert np.allclose(yb, x.astype(np.float64) @ deq.T, rtol=1e-12, atol=1e-15)
+    _, _, yd_ref = O.apply(x, np.zeros((d_out, d_in), np.float32), words, scales, O.ROW, ids)
+    assert np.allclose(yd, yd_ref, rtol=1e-12, atol=1e-15)
+    assert np.allclose(y, yb + yd, rtol=1e-15, atol=0)
