@@ -191,6 +191,24 @@ def main():
     _, prep_us = timed_replay(g_prep)
     _, main_us = timed_replay(g_main)
 
+    # the same steps on an INT8 base (bd_quantize_base once per set, then bd_apply_q8):
+    # one byte per base weight instead of two
+    q8 = [B.quantize_base(sets[r][0]) for r in range(R)]
+    y8 = [torch.empty((T, d_out), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    def step_q8(k):
+        wb, signs, scales, x, y = sets[k % R]
+        q, qs = q8[k % R]
+        return B.bd_apply_q8(x, q, qs, signs, scales, p, U, ids, y8[k % R], wss[k % R])
+
+    for k in range(R):
+        assert step_q8(k) == B.BD_OK
+    g_q8 = capture(step_q8)
+    g_q8.replay()
+    torch.cuda.synchronize()
+    _, q8_us = timed_replay(g_q8)
+    assert B.bd_device_status(wss[0]) == B.BD_OK
+
     # algorithmic bytes (each byte the math must touch once)
     n_active = len(set(int(u) for u in ids_np if 0 <= u < U))
     bytes_w = d_out * d_in * 2
@@ -306,6 +324,11 @@ def main():
         "roofline": roofline,
         "compress": compress,
         "axis_select": axis_select,
+        "int8_base_step": {"kernel": "k_decode_unit (INT8 base)", "us": round(q8_us, 3),
+                           "algorithmic_bytes": bytes_step - d_out * d_in + 4 * d_out,
+                           "achieved": round((bytes_step - d_out * d_in + 4 * d_out) / (q8_us * 1e-6) / 1e9, 1),
+                           "unit": "GB/s",
+                           "frac": round((bytes_step - d_out * d_in + 4 * d_out) / (q8_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "kernel_source_digest": kernel_source_digest(),
     }
 

@@ -211,6 +211,31 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
  * batch once, then run the shared base product and the per-user delta product
  * of each matrix ([P2] "Systems Mechanics" 1: Y = Y_base + Y_delta). */
 
+/* ------------------------------------------------- INT8 base weights */
+
+/* INT8 base weights for the apply below ([P2] "Systems Mechanics": the 1-bit delta
+ * on top of an INT8-quantized base).  The pages name no quantizer; this one is
+ * symmetric per output row: scales_out[o] = max_i |w[o][i]| / 127 and
+ * q_out[o][i] = round-half-even(w[o][i] / scales_out[o]) clamped to [-127, 127],
+ * both divisions in binary32 (a zero row gets scale 0 and codes 0).
+ *  w          : [d_out][d_in] of w_dtype (BD_F32 or BD_BF16).
+ *  q_out      : [d_out][d_in] int8.   scales_out : [d_out] fp32. */
+bd_status bd_quantize_base(const void* w, bd_dtype w_dtype, int64_t d_out, int64_t d_in,
+                           int8_t* q_out, float* scales_out, void* stream);
+
+/* bd_apply with the base weight given as INT8 rows (bd_quantize_base):
+ *     y[t] = wscales (.) (X[t] . wq^T) + scale_u (.) (X[t] . S_u^T),
+ * in one launch for decode batches: bf16 X, 1..16 tokens, MATRIX or ROW scales,
+ * d_in <= 4096 (BD_ERR_UNSUPPORTED otherwise).  The base weight crosses HBM at one
+ * byte per element; its codes are widened to bf16 exactly on chip.  Other
+ * arguments, the workspace (bd_apply_workspace_bytes) and the status word as for
+ * bd_apply. */
+bd_status bd_apply_q8(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const int8_t* wq,
+                      const float* wscales, int64_t d_out, const uint64_t* signs_bank,
+                      const void* scales_bank, const bd_compress_params* p, int32_t n_users,
+                      const int32_t* user_ids, void* y, bd_dtype y_dtype, void* workspace,
+                      size_t ws_bytes, void* stream);
+
 /* Workspace of a prepared batch: the grouping of the tokens by user and, for
  * bf16 inputs, room for the tokens encoded as delta-product operands. */
 size_t bd_batch_workspace_bytes(int64_t T, int32_t n_users, int64_t d_in, bd_dtype x_dtype);

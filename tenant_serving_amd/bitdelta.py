@@ -66,6 +66,11 @@ def lib() -> ctypes.CDLL:
         L.bd_apply_workspace_bytes.argtypes = [P, i64, i32, i64, i64, ctypes.c_int, ctypes.c_int]
         L.bd_compress.restype = ctypes.c_int
         L.bd_compress.argtypes = [vp, vp, ctypes.c_int, i64, i64, P, vp, vp, vp, sz, vp]
+        L.bd_quantize_base.restype = ctypes.c_int
+        L.bd_quantize_base.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp]
+        L.bd_apply_q8.restype = ctypes.c_int
+        L.bd_apply_q8.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, vp, vp, P, i32, vp, vp,
+                                  ctypes.c_int, vp, sz, vp]
         L.bd_select_axis_workspace_bytes.restype = sz
         L.bd_select_axis_workspace_bytes.argtypes = [i64, i64, ctypes.c_float]
         L.bd_select_axis.restype = ctypes.c_int
@@ -269,6 +274,48 @@ def bd_select_axis(w_fine, w_base, clip_k, errors, axis, workspace, stream=None)
                                     float(clip_k), _ptr(errors), _ptr(axis), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
                                     _stream(w_fine, stream)))
+
+
+def bd_quantize_base(w, q_out, scales_out, stream=None) -> int:
+    d_out, d_in = w.shape
+    return int(lib().bd_quantize_base(_ptr(w), _dtype_code(w), d_out, d_in, _ptr(q_out),
+                                      _ptr(scales_out), _stream(w, stream)))
+
+
+def bd_apply_q8(x, wq, wscales, signs_bank, scales_bank, p, n_users, user_ids, y, workspace,
+                stream=None) -> int:
+    T, d_in = x.shape
+    d_out = wq.shape[0]
+    return int(lib().bd_apply_q8(_ptr(x), _dtype_code(x), T, d_in, _ptr(wq), _ptr(wscales), d_out,
+                                 _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p),
+                                 int(n_users), _ptr(user_ids), _ptr(y), _dtype_code(y),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(x, stream)))
+
+
+def quantize_base(w: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """INT8 rows and their fp32 scales (bd_quantize_base)."""
+    d_out, d_in = w.shape
+    q = torch.empty((d_out, d_in), dtype=torch.int8, device=w.device)
+    s = torch.empty(d_out, dtype=torch.float32, device=w.device)
+    _check(bd_quantize_base(w, q, s, stream), "bd_quantize_base")
+    return q, s
+
+
+def apply_q8(x, wq, wscales, signs_bank, scales_bank, p, user_ids, y_dtype=torch.float32,
+             ws=None, stream=None, check: bool = False) -> torch.Tensor:
+    T, d_in = x.shape
+    d_out = wq.shape[0]
+    U = signs_bank.shape[0]
+    y = torch.empty((T, d_out), dtype=y_dtype, device=x.device)
+    if ws is None:
+        ws = workspace(bd_apply_workspace_bytes(p, T, U, d_out, d_in, _dtype_code(x),
+                                                _dtype_code(y)), x.device)
+    _check(bd_apply_q8(x, wq, wscales, signs_bank, scales_bank, p, U, user_ids, y, ws, stream),
+           "bd_apply_q8")
+    if check:
+        _check(bd_device_status(ws, stream), "bd_apply_q8 (device)")
+    return y
 
 
 def select_axis(w_fine: torch.Tensor, w_base: Optional[torch.Tensor], clip_k: float = 0.0,

@@ -171,6 +171,41 @@ bd_status bd_delta_apply(void* batch, const void* x, bd_dtype x_dtype, int64_t T
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
+bd_status bd_quantize_base(const void* w, bd_dtype w_dtype, int64_t d_out, int64_t d_in,
+                           int8_t* q_out, float* scales_out, void* stream) {
+    if (!w || !q_out || !scales_out) return BD_ERR_INVALID_ARG;
+    if (!valid_wdtype(w_dtype)) return BD_ERR_DTYPE;
+    if (d_out <= 0 || d_in <= 0 || d_out > ((int64_t)1 << 31) - 1 || d_in > (int64_t)1 << 31)
+        return BD_ERR_SHAPE;
+    hipError_t e = launch_quantize_rows(w, w_dtype, d_out, d_in, q_out, scales_out,
+                                        (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_apply_q8(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const int8_t* wq,
+                      const float* wscales, int64_t d_out, const uint64_t* signs_bank,
+                      const void* scales_bank, const bd_compress_params* p, int32_t n_users,
+                      const int32_t* user_ids, void* y, bd_dtype y_dtype, void* workspace,
+                      size_t ws_bytes, void* stream) {
+    if (!p) return BD_ERR_INVALID_ARG;
+    ApplyPlan pl;
+    bd_status st = make_apply_plan(p, T, n_users, d_out, d_in, x_dtype, y_dtype, &pl);
+    if (st != BD_OK) return st;
+    if (T == 0) return BD_OK;
+    if (!q8_path_supported(x_dtype, T, p->mode, d_in)) return BD_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < pl.total || !aligned(workspace, kAlign)) return BD_ERR_WORKSPACE;
+    if (!x || !wq || !wscales || !y || !user_ids) return BD_ERR_INVALID_ARG;
+    if (n_users > 0 && (!signs_bank || !scales_bank)) return BD_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(wscales, 4) || !aligned(y, 16) ||
+        !aligned(user_ids, 4) || (signs_bank && !aligned(signs_bank, 16)) ||
+        (scales_bank && !aligned(scales_bank, 16)))
+        return BD_ERR_INVALID_ARG;
+    hipError_t e = launch_decode_q8(T, n_users, d_in, pl.delta, x, user_ids, wq, wscales,
+                                    signs_bank, scales_bank, y, y_dtype, (char*)workspace,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
 bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const void* w_base,
                    int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
                    const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,

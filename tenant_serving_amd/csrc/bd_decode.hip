@@ -907,12 +907,17 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
 constexpr int kUnitWaves = 8;
 constexpr int kUnitRing = 8;
 
-template <int MODE>
+// Q8: the base weight as INT8 rows with one fp32 scale per row (wq[o][i] * wscale[o]):
+// half the base bytes.  A ring item then carries 16 columns per lane, two MFMA steps,
+// whose codes are widened to bf16 exactly (|q| <= 127 has 7 significant bits); the
+// base sum is multiplied by the row's scale in the epilogue.
+template <int MODE, bool Q8>
 __global__ void __launch_bounds__(64 * kUnitWaves)
 k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int T, int U,
-              int64_t d_in, const uint16_t* __restrict__ w, int64_t d_out,
-              const uint64_t* __restrict__ signs, const void* __restrict__ scales, int sdtype,
-              int64_t per_user, void* __restrict__ y, int ydtype, uint32_t* __restrict__ status) {
+              int64_t d_in, const void* __restrict__ w, const float* __restrict__ wscale,
+              int64_t d_out, const uint64_t* __restrict__ signs, const void* __restrict__ scales,
+              int sdtype, int64_t per_user, void* __restrict__ y, int ydtype,
+              uint32_t* __restrict__ status) {
     __shared__ f32x4 red[2 * kUnitWaves * 64];  // base then delta partial tiles, wave order
     __shared__ __attribute__((aligned(16))) char xlds[kUnitWaves * 16384];
     const int lane = threadIdx.x & 63;
@@ -975,14 +980,17 @@ k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, i
     const int nsegR = (nseg + kUnitRing - 1) / kUnitRing * kUnitRing;
     const int64_t bank_row = d_in / 8;
     const uint64_t user_bytes = (uint64_t)d_out * (uint64_t)bank_row;
-    const uint64_t w_bytes = (uint64_t)d_out * (uint64_t)d_in * 2;
+    constexpr int kWBytes = Q8 ? 1 : 2;  // bytes per base weight
+    constexpr int kWItems = Q8 ? 8 : 16;  // base ring items per unit
+    const uint64_t w_bytes = (uint64_t)d_out * (uint64_t)d_in * kWBytes;
     // lane (m, g): sign bytes of row rowA for columns 512 w + 128 g .. + 127 (word q: k-group
-    // g of product q); W_base columns 512 w + 32 s + 8 g .. + 7 of row rowA
+    // g of product q); W_base columns 512 w + 32 s + 8 g .. + 7 of row rowA (Q8: the INT8
+    // codes of columns 512 w + 64 s + 16 g .. + 15, steps 2 s and 2 s + 1)
     const uint32_t soff = (int64_t)512 * wv + 128 * g < d_in
                               ? (uint32_t)(rowA * bank_row + 64 * wv + 16 * g)
                               : kOOB;
-    const int64_t c0 = (int64_t)512 * wv + 8 * g;
-    const uint32_t woff = (uint32_t)((rowA * d_in + c0) * 2);
+    const int64_t c0 = (int64_t)512 * wv + (Q8 ? 16 : 8) * g;
+    const uint32_t woff = (uint32_t)((rowA * d_in + c0) * kWBytes);
     // (branch-free: a branch here splits the loop body into blocks, and the compiler then
     // gathers the products of a whole iteration at its end)
     const uint64_t wbase = (uint64_t)(uintptr_t)w;
@@ -994,8 +1002,8 @@ k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, i
         const uint64_t base = wbase + ((sbase - wbase) & msk);
         const uint64_t bytes = w_bytes + ((user_bytes - w_bytes) & msk);
         const uint32_t so = i < nseg ? soff : kOOB;
-        const bool okw = ((uint32_t)s < 16u) & (c0 + 32 * s < d_in);  // no short-circuit branch
-        const uint32_t wo = okw ? woff + 64u * (uint32_t)s : kOOB;
+        const bool okw = ((uint32_t)s < (uint32_t)kWItems) & (c0 + (Q8 ? 64 : 32) * s < d_in);
+        const uint32_t wo = okw ? woff + 64u * (uint32_t)s : kOOB;  // no short-circuit branch
         const uint32_t off = wo + ((so - wo) & (uint32_t)msk);
         return buf_load16(make_rsrc((const void*)(uintptr_t)base, bytes), off);
     };
@@ -1007,6 +1015,14 @@ k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, i
     }
     BD_WAIT_VMCNT(kUnitRing);  // this wave's token copies have landed (the ring is younger)
     uint32_t sraw[4] = {0u, 0u, 0u, 0u};  // wave 0: the scales of its outputs (bits)
+    float wsc[4] = {1.f, 1.f, 1.f, 1.f};  // wave 0, Q8: the rows' base scales
+    if (Q8 && wv == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t o = r0 + 4 * g + e;
+            wsc[e] = wscale[o < d_out ? o : d_out - 1];
+        }
+    }
     if (wv == 0 && tok_user >= 0 && m < T) {
         const int64_t o = r0 + 4 * g;
         const int64_t s0 = (int64_t)tok_user * per_user;
@@ -1105,14 +1121,42 @@ k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, i
     auto tok = [&](int s) {  // B operand of step s: token m, columns 32 s + 8 g .. + 7
         return *(const u32x4*)(xs + xslot(m, 4 * s + g, 1024u));
     };
-    u32x4 bnext = tok(0);
+    if (Q8) {
+        // item s: lane (m, g) holds the codes of columns 64 s + 16 g .. + 15 of row m; the
+        // tokens of the same columns are LDS chunks 8 s + 2 g and 8 s + 2 g + 1
+        // four codes -> two dwords of bf16 pairs (the upper halves of their exact fp32 values)
+        auto widen = [&](uint32_t wd, uint32_t* out) {
+            const float f0 = (float)(int8_t)(wd & 0xFFu), f1 = (float)(int8_t)((wd >> 8) & 0xFFu);
+            const float f2 = (float)(int8_t)((wd >> 16) & 0xFFu), f3 = (float)(int8_t)(wd >> 24);
+            out[0] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+            out[1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+        };
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-        const u32x4 b = bnext;
-        if (s + 1 < 16) bnext = tok(s + 1);
-        accb = mfma_bf16(ring[s % kUnitRing], b, accb);
-        ring[s % kUnitRing] = load_item(nsegR + s + kUnitRing);  // empty past step 15
-        __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < kWItems; ++s) {
+            const u32x4 b0 = *(const u32x4*)(xs + xslot(m, 8 * s + 2 * g, 1024u));
+            const u32x4 b1 = *(const u32x4*)(xs + xslot(m, 8 * s + 2 * g + 1, 1024u));
+            const u32x4 wq = ring[s % kUnitRing];
+            uint32_t v[8];
+            widen(wq.x, v);
+            widen(wq.y, v + 2);
+            widen(wq.z, v + 4);
+            widen(wq.w, v + 6);
+            const u32x4 a0 = {v[0], v[1], v[2], v[3]}, a1 = {v[4], v[5], v[6], v[7]};
+            accb = mfma_bf16(a0, b0, accb);
+            accb = mfma_bf16(a1, b1, accb);
+            ring[s % kUnitRing] = load_item(nsegR + s + kUnitRing);  // empty past the unit
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        u32x4 bnext = tok(0);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const u32x4 b = bnext;
+            if (s + 1 < 16) bnext = tok(s + 1);
+            accb = mfma_bf16(ring[s % kUnitRing], b, accb);
+            ring[s % kUnitRing] = load_item(nsegR + s + kUnitRing);  // empty past step 15
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     BD_WAIT_VMCNT(0);  // the empty loads past the end have landed
 
@@ -1133,7 +1177,7 @@ k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, i
         const float f = tok_user < 0 ? 0.f
                         : sdtype == BD_F16 ? -f16_to_f32((uint16_t)sraw[e])
                                            : -__uint_as_float(sraw[e]);
-        out[e] = vb[e] + f * vd[e];
+        out[e] = (Q8 ? wsc[e] * vb[e] : vb[e]) + f * vd[e];
     }
     if (ydtype == BD_F32) {
         float* dst = (float*)y + (int64_t)m * d_out + o;
@@ -1226,6 +1270,27 @@ bool fused_path_supported(int xdtype, int64_t T, int mode, int64_t d_in) {
            (d_in + 511) / 512 * 512 <= kFusedMaxDpad;
 }
 
+bool q8_path_supported(int xdtype, int64_t T, int mode, int64_t d_in) {
+    return xdtype == BD_BF16 && T >= 1 && T <= kDecodeMaxT &&
+           (mode == BD_SCALE_MATRIX || mode == BD_SCALE_ROW) &&
+           (d_in + 511) / 512 * 512 <= 512 * kUnitWaves;
+}
+
+hipError_t launch_decode_q8(int64_t T, int U, int64_t d_in, const DeltaPlan& dp, const void* x,
+                            const int32_t* ids, const int8_t* wq, const float* wscale,
+                            const uint64_t* signs, const void* scales, void* y, int ydtype, char* ws,
+                            hipStream_t s) {
+    const dim3 grid((unsigned)((dp.d_out + 15) / 16));
+#define BD_UNITQ(MODE)                                                                        \
+    k_decode_unit<MODE, true><<<grid, dim3(64 * kUnitWaves), 0, s>>>(                         \
+        (const uint16_t*)x, ids, (int)T, U, d_in, wq, wscale, dp.d_out, signs, scales,           \
+        dp.sdtype, dp.per_user, y, ydtype, (uint32_t*)ws)
+    if (dp.mode == BD_SCALE_MATRIX) BD_UNITQ(BD_SCALE_MATRIX);
+    else BD_UNITQ(BD_SCALE_ROW);
+#undef BD_UNITQ
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_fused(int64_t T, int U, int64_t d_in, const DeltaPlan& dp, const void* x,
                                const int32_t* ids, const void* wb, const uint64_t* signs,
                                const void* scales, void* y, int ydtype, char* ws, hipStream_t s) {
@@ -1235,8 +1300,8 @@ hipError_t launch_decode_fused(int64_t T, int U, int64_t d_in, const DeltaPlan& 
     const dim3 grid((unsigned)((dp.d_out + 15) / 16));
     if (dpad <= 512 * kUnitWaves) {
 #define BD_UNIT(MODE)                                                                         \
-    k_decode_unit<MODE><<<grid, dim3(64 * kUnitWaves), 0, s>>>(                               \
-        (const uint16_t*)x, ids, (int)T, U, d_in, (const uint16_t*)wb, dp.d_out, signs, scales, \
+    k_decode_unit<MODE, false><<<grid, dim3(64 * kUnitWaves), 0, s>>>(                        \
+        (const uint16_t*)x, ids, (int)T, U, d_in, wb, nullptr, dp.d_out, signs, scales,          \
         dp.sdtype, dp.per_user, y, ydtype, (uint32_t*)ws)
         if (dp.mode == BD_SCALE_MATRIX) BD_UNIT(BD_SCALE_MATRIX);
         else BD_UNIT(BD_SCALE_ROW);

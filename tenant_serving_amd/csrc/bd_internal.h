@@ -43,6 +43,16 @@ bd_status make_compress_plan(const bd_compress_params* p, int64_t d_out, int64_t
 hipError_t launch_compress(const CompressPlan& pl, const void* wf, const void* wb, int wdtype,
                            uint64_t* signs, void* scales, char* ws, hipStream_t s);
 
+// INT8 base weights (bd_quantize_base) and the one-launch decode apply on them.
+hipError_t launch_quantize_rows(const void* w, int wdtype, int64_t d_out, int64_t d_in, int8_t* q,
+                                float* s, hipStream_t st);
+bool q8_path_supported(int xdtype, int64_t T, int mode, int64_t d_in);
+struct DeltaPlan;
+hipError_t launch_decode_q8(int64_t T, int U, int64_t d_in, const DeltaPlan& dp, const void* x,
+                            const int32_t* ids, const int8_t* wq, const float* wscale,
+                            const uint64_t* signs, const void* scales, void* y, int ydtype, char* ws,
+                            hipStream_t s);
+
 // Per-layer axis choice (bd_select_axis): the compress plan's grid and clip passes, then
 // one statistics pass (the ROW and COL absmean partials and sum d^2) and two reductions.
 struct AxisPlan {

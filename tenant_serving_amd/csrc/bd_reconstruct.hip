@@ -68,3 +68,53 @@ hipError_t launch_reconstruct(const uint64_t* signs, const void* scales, int mod
 }
 
 }  // namespace bd
+
+namespace bd {
+namespace {
+
+__device__ __forceinline__ float load_w(const uint16_t* p, int64_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);  // bf16 -> fp32, exact
+}
+__device__ __forceinline__ float load_w(const float* p, int64_t i) { return p[i]; }
+
+// INT8 base weights, one block per row: s = max |w| / 127 and q = round-half-even(w / s)
+// clamped to [-127, 127], both divisions in binary32 (correctly rounded); a zero row
+// gets s = 0 and q = 0.
+template <typename WT>
+__global__ void __launch_bounds__(256)
+k_quantize_rows(const WT* __restrict__ w, int64_t d_in, int8_t* __restrict__ q,
+                float* __restrict__ s) {
+    __shared__ float sh[256];
+    const int64_t o = blockIdx.x;
+    const WT* row = w + o * d_in;
+    float m = 0.f;
+    for (int64_t i = threadIdx.x; i < d_in; i += 256) m = fmaxf(m, fabsf(load_w(row, i)));
+    sh[threadIdx.x] = m;
+    __syncthreads();
+    for (int k = 128; k > 0; k >>= 1) {
+        if ((int)threadIdx.x < k) sh[threadIdx.x] = fmaxf(sh[threadIdx.x], sh[threadIdx.x + k]);
+        __syncthreads();
+    }
+    const float so = sh[0] / 127.0f;
+    if (threadIdx.x == 0) s[o] = so;
+    for (int64_t i = threadIdx.x; i < d_in; i += 256) {
+        float r = so > 0.f ? rintf(load_w(row, i) / so) : 0.f;
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        q[o * d_in + i] = (int8_t)r;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const void* w, int wdtype, int64_t d_out, int64_t d_in, int8_t* q,
+                                float* s, hipStream_t st) {
+    if (wdtype == BD_BF16)
+        hipLaunchKernelGGL(k_quantize_rows<uint16_t>, dim3((unsigned)d_out), dim3(256), 0, st,
+                           (const uint16_t*)w, d_in, q, s);
+    else
+        hipLaunchKernelGGL(k_quantize_rows<float>, dim3((unsigned)d_out), dim3(256), 0, st,
+                           (const float*)w, d_in, q, s);
+    return hipGetLastError();
+}
+
+}  // namespace bd
