@@ -126,3 +126,24 @@ def test_select_axis_sizes_and_synchronous_errors():
     assert _select_raw(ws=256 + 8) == B.BD_ERR_WORKSPACE
     assert _select_raw(wf=256 + 8) == B.BD_ERR_INVALID_ARG
     assert _select_raw(errors=(1 << 20) + 4) == B.BD_ERR_INVALID_ARG
+
+
+def test_int8_base_entry_points_reject_bad_arguments_synchronously():
+    L = B.lib()
+    # fake, never dereferenced device addresses: every case fails before any launch
+    assert L.bd_quantize_base(None, B.BD_BF16, 64, 128, 1 << 12, 1 << 12, None) == B.BD_ERR_INVALID_ARG
+    assert L.bd_quantize_base(1 << 12, B.BD_F16, 64, 128, 1 << 12, 1 << 12, None) == B.BD_ERR_DTYPE
+    assert L.bd_quantize_base(1 << 12, B.BD_BF16, 0, 128, 1 << 12, 1 << 12, None) == B.BD_ERR_SHAPE
+
+    def q8(p, T=4, d_in=512, xdt=B.BD_BF16, wq=1 << 12, ws=1 << 16, ws_bytes=1 << 30):
+        return int(L.bd_apply_q8(1 << 12, xdt, T, d_in, wq, 1 << 12, 64, 1 << 12, 1 << 12,
+                                 ctypes.byref(p), 2, 1 << 12, 1 << 12, B.BD_F32, ws, ws_bytes, None))
+
+    assert q8(B.params("group", 128)) == B.BD_ERR_UNSUPPORTED
+    assert q8(B.params("matrix"), T=17) == B.BD_ERR_UNSUPPORTED
+    assert q8(B.params("matrix"), d_in=4608) == B.BD_ERR_UNSUPPORTED
+    assert q8(B.params("matrix"), xdt=B.BD_F32) == B.BD_ERR_UNSUPPORTED
+    assert q8(B.params("matrix"), d_in=100) == B.BD_ERR_SHAPE
+    assert q8(B.params("matrix"), ws=0) == B.BD_ERR_WORKSPACE
+    assert q8(B.params("matrix"), wq=0) == B.BD_ERR_INVALID_ARG
+    assert q8(B.params("matrix"), wq=(1 << 12) + 8) == B.BD_ERR_INVALID_ARG
