@@ -500,6 +500,8 @@ hipError_t launch_base_gemm(const void* x, int xdtype, int64_t T, int64_t d_in, 
         return hipGetLastError();
     }
     if (gemm_path_supported(T, d_in, d_out)) return launch_gemm(x, T, d_in, wb, d_out, y, s);
+    if (small_batch_gemm_supported(T, d_in, d_out))
+        return launch_small_batch_gemm(x, T, d_in, wb, d_out, y, s);
     const dim3 gb((unsigned)((d_out + 15) / 16), 1);
     if (T <= 16) {
         hipLaunchKernelGGL(k_base_gemm<1>, gb, dim3(64 * kGemmWaves), 0, s, (const uint16_t*)x,

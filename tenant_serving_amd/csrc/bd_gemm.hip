@@ -194,6 +194,19 @@ hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const void* wb, i
 
 }  // namespace
 
+// 17..64 tokens on a wide matrix: one 64-token tile per 64 rows copies the tokens once
+// per 64 rows (the streaming kernel re-reads them from L2 for every 16 rows), and at
+// >= 160 row tiles the grid still covers most of the chip.
+bool small_batch_gemm_supported(int64_t T, int64_t d_in, int64_t d_out) {
+    return T > 16 && T <= kGemmMinT && d_in % kGemmK == 0 && (d_out + 63) / 64 >= 160 &&
+           T * d_in * 2 < ((int64_t)1 << 31) && d_out * d_in * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_small_batch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb,
+                                   int64_t d_out, float* y, hipStream_t s) {
+    return launch_tile<64, 64, 64, 4>(x, T, d_in, wb, d_out, y, s);
+}
+
 bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out) {
     return T > kGemmMinT && d_in % kGemmK == 0 && T * d_in * 2 < ((int64_t)1 << 31) &&
            d_out * d_in * 2 < ((int64_t)1 << 31) && d_out < ((int64_t)1 << 30);

@@ -139,6 +139,9 @@ hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, 
 // bf16 tokens (smaller batches take the streaming kernel of bd_apply.hip).
 constexpr int64_t kGemmMinT = 64;
 bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out);
+bool small_batch_gemm_supported(int64_t T, int64_t d_in, int64_t d_out);
+hipError_t launch_small_batch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb,
+                                   int64_t d_out, float* y, hipStream_t s);
 hipError_t launch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb, int64_t d_out,
                        float* y, hipStream_t s);
 

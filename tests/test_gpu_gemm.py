@@ -25,6 +25,7 @@ SHAPES = [  # (T, d_out, d_in)
     (512, 4096, 256),    # 64 x 128
     (256, 14336, 128),   # 128 x 128
     (2048, 4096, 128),   # 128 x 256
+    (40, 10240, 256),    # 17..64 tokens on a wide matrix: 64 x 64 tiles
 ]
 
 
