@@ -1,23 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the multi-user BitDelta decode apply on one MI355X.
 
-Workload (default): the Llama-3.1-8B-shaped q_proj, W_base 4096x4096 bf16,
-16 users' packed 1-bit deltas with one fp32 scale per matrix, a decode batch
-of 16 tokens (one per user, in a seeded shuffled order), fp32 output.  A step
-is one bd_apply of that layer: a single kernel (k_decode_unit) that groups the
-batch by user, encodes the tokens for the delta products, and computes the
-shared base product and every user's delta product in one pass over W_base and
-the packed banks.  The K timed steps are captured in a HIP graph and replayed,
-as a serving loop would issue them, so host launch overhead is not part of the
-GPU time.  Steps rotate over R independent input sets (weights, banks,
-activations) so consecutive steps do not hit the 256 MB last-level cache; all
-inputs are resident in HBM before the timed region starts.  The two-launch
-decode calls (bd_decode_prepare + bd_decode_apply) are timed beside it.
+Workload (the headline): the Llama-3.1-8B-shaped stack, 32 layers x {q, k, v,
+o, gate, up, down} bf16 base weights (13.96 GB) with 128 users' packed 1-bit
+deltas and one fp32 scale per matrix resident in HBM (111.7 GB, built by
+bd_compress from seeded synthetic fine-tunes), and one decode step of 512
+tokens whose users are Zipf(1.1) draws.  A step applies every matrix to the
+batch: per distinct input width one bd_batch_prepare (tokens grouped by user),
+per distinct activation tensor one bd_batch_encode (q/k/v and gate/up share
+theirs), per matrix bd_base_gemm (y = X W_base^T) and bd_delta_apply_encoded
+(y += scale_u (.) X S_u^T).  Each matrix reads its own activation tensor; no
+attention, norms or activations (not on the path).  The K timed steps are
+captured in one HIP graph and replayed between device synchronisations.
 
-Printed: one JSON line with the apply throughput in algorithmic HBM GB/s
-(value), tokens/s, per-kernel HIP-event timings, the roofline of the dominant
-kernel, the compress leg (bd_compress on the same matrix shape), and the CPU
-oracle timed on a bounded sample on the host.
+Printed: one JSON line with the step's throughput in algorithmic HBM GB/s
+(value), tokens/s, the per-phase kernel times (HIP events around graphs of one
+phase's launches), the roofline of the dominant kernel, the base GEMM's
+TFLOP/s, the q_proj decode step and the compress legs, and the CPU oracle
+timed on a bounded sample of the same workload on the host.
 """
 from __future__ import annotations
 
@@ -40,15 +40,19 @@ METRIC = ("multi-user BitDelta decode apply: achieved HBM GB/s (% peak) and toke
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--sets", type=int, default=16, help="rotating input sets")
-    ap.add_argument("--compress-steps", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=10, help="timed steps of the stack")
+    ap.add_argument("--warmup", type=int, default=3, help="eager steps of the stack before timing")
+    ap.add_argument("--decode-steps", type=int, default=400,
+                    help="timed steps of the q_proj decode leg")
+    ap.add_argument("--sets", type=int, default=16, help="rotating input sets of the decode leg")
+    ap.add_argument("--compress-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096,
-                    help="output rows of the oracle's sampled apply")
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="output rows per matrix of the oracle's sampled apply")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="time the stack only (no decode, compress, axis or INT8 legs)")
     ap.add_argument("--workloads", action="store_true",
-                    help="also time one layer step of workloads 3-5 (stderr, one JSON line each)")
+                    help="also time one layer step of workloads 3 and 4 (stderr)")
     ap.add_argument("--merge", action="store_true",
                     help="also time the dense merge path for one hot user against the fused "
                          "delta apply, per token count (stderr, one JSON line per shape)")
@@ -61,11 +65,16 @@ def parse():
     return ap.parse_args()
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("bd_apply.hip", "bd_compress.hip", "bd_decode.hip", "bd_internal.h"):
-        with open(os.path.join(ROOT, "tenant_serving_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(os.path.join(ROOT, "tenant_serving_amd", "csrc"))):
+        if f.endswith((".hip", ".h")) and f.startswith("bd_"):
+            with open(os.path.join(ROOT, "tenant_serving_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -83,29 +92,247 @@ def measured_traffic(kernel: str, workload: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+# ---------------------------------------------------------------- HIP-graph timing
+def capture(fn, reps):
+    """fn() captured `reps` times into one HIP graph (after one eager call on the
+    capture stream)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    return g
 
-    import numpy as np
+
+def replay_timed(g, reps):
+    """(wall us, HIP-event us) per repetition of one replay of g."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e6 / reps, e0.elapsed_time(e1) * 1e3 / reps
+
+
+# ---------------------------------------------------------------- the stack
+class Stack:
+    """Resident inputs of the 32-layer workload: base weights, 128 users' banks from
+    bd_compress, activations, outputs, prepared batches."""
+
+    # matrices of a layer that read one activation tensor: (first, count)
+    GROUPS = ((0, 3), (3, 1), (4, 2), (6, 1))
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+
+        from tenant_serving_amd import bitdelta as B
+        from tenant_serving_amd import synth as S
+
+        self.B = B
+        w = self.w = S.workload(5)
+        self.U, self.T = w.n_users, w.T
+        self.ids_np = S.user_ids(w)
+        self.ids = torch.from_numpy(self.ids_np).to(dev)
+        self.p = B.params("matrix")
+        self.active = sorted(set(int(u) for u in self.ids_np if 0 <= u < self.U))
+        mats = w.matrices
+        big = max(m.d_out * m.d_in for m in mats)
+        wf = torch.empty(big, dtype=torch.bfloat16, device=dev)
+        cws = B.workspace(max(B.bd_compress_workspace_bytes(self.p, m.d_out, m.d_in)
+                              for m in mats), dev)
+        self.wb, self.signs, self.scales, self.y = [], [], [], []
+        t0 = time.perf_counter()
+        for mi, m in enumerate(mats):
+            wb = S.dev_wbase(w, mi)
+            signs = torch.empty((self.U, m.d_out, m.d_in // 64), dtype=torch.int64, device=dev)
+            scales = torch.empty((self.U, 1), dtype=torch.float32, device=dev)
+            wfv = wf[:m.d_out * m.d_in].view(m.d_out, m.d_in)
+            for u in range(self.U):
+                S.dev_wfine(w, mi, u, wb, out=wfv)
+                st = B.bd_compress(wfv, wb, self.p, signs[u], scales[u], cws)
+                assert st == B.BD_OK, st
+            self.wb.append(wb)
+            self.signs.append(signs)
+            self.scales.append(scales)
+            self.y.append(torch.empty((self.T, m.d_out), dtype=torch.float32, device=dev))
+            if mi % 28 == 27:
+                torch.cuda.synchronize()
+                log(f"stack: {mi + 1}/{len(mats)} matrices compressed for {self.U} users "
+                    f"({time.perf_counter() - t0:.1f} s)")
+        torch.cuda.synchronize()
+        assert B.bd_device_status(cws) == B.BD_OK
+        del wf, cws
+        self.xs = [S.dev_x(w, g) for g in range(len(w.xgroups))]
+        self.batches = {}
+        for d_in in sorted(set(w.xgroups)):
+            self.batches[d_in] = B.workspace(
+                B.bd_batch_workspace_bytes(self.T, self.U, d_in, B.BD_BF16), dev)
+        self.first_x = {d: next(x for x in self.xs if x.shape[1] == d) for d in self.batches}
+        torch.cuda.synchronize()
+        self.setup_s = time.perf_counter() - t0
+
+        # algorithmic bytes (each byte the math must touch once, summed per matrix apply)
+        na, T = len(self.active), self.T
+        self.bytes_step = self.bytes_delta = self.flops_gemm = 0
+        for m in mats:
+            self.bytes_step += (m.d_out * m.d_in * 2 + na * (m.d_out * m.d_in // 8 + 4)
+                                + T * m.d_in * 2 + T * m.d_out * 4 + 4 * T)
+            self.bytes_delta += na * (m.d_out * m.d_in // 8 + 4) + T * m.d_out * 4
+            self.flops_gemm += 2 * T * m.d_out * m.d_in
+        self.n_mats = len(mats)
+        self.n_layers = len(mats) // 7
+
+    # one phase at a time (graphs of one kind of launch, for per-kernel timing)
+    def prepare(self):
+        B = self.B
+        for d_in, bt in self.batches.items():
+            assert B.bd_batch_prepare(self.first_x[d_in], self.ids, self.U, bt) == B.BD_OK
+
+    def _groups(self):
+        for l in range(self.n_layers):
+            for gi, (first, cnt) in enumerate(self.GROUPS):
+                x = self.xs[4 * l + gi]
+                yield x, self.batches[x.shape[1]], range(7 * l + first, 7 * l + first + cnt)
+
+    def encode_all(self):
+        B = self.B
+        for x, bt, _ in self._groups():
+            assert B.bd_batch_encode(bt, x, self.U, None, self.p) == B.BD_OK
+
+    def _gemm(self, x, ms):
+        B = self.B
+        assert B.bd_base_gemm_n(x, [self.wb[m] for m in ms], [self.y[m] for m in ms]) == B.BD_OK
+
+    def _delta(self, x, bt, ms):
+        B = self.B
+        assert B.bd_delta_apply_encoded_n(bt, self.T, x.shape[1], self.U,
+                                          [self.signs[m] for m in ms],
+                                          [self.scales[m] for m in ms], self.p,
+                                          [self.y[m] for m in ms]) == B.BD_OK
+
+    def gemm_all(self):
+        for x, _, ms in self._groups():
+            self._gemm(x, ms)
+
+    def delta_all(self):
+        """The delta products of every matrix on the batch's current encoding (the
+        products' time does not depend on which activations are encoded)."""
+        for x, bt, ms in self._groups():
+            self._delta(x, bt, ms)
+
+    def step(self):
+        B = self.B
+        self.prepare()
+        for x, bt, ms in self._groups():
+            assert B.bd_batch_encode(bt, x, self.U, None, self.p) == B.BD_OK
+            self._gemm(x, ms)
+            self._delta(x, bt, ms)
+
+
+def stack_leg(args, dev):
+    import torch
+
+    S = Stack(dev)
+    B = S.B
+    log(f"stack ready: {S.n_mats} matrices, {S.U} users' banks, {len(S.active)} active "
+        f"({S.setup_s:.1f} s)")
+    K = max(1, args.steps)
+    for _ in range(max(1, args.warmup)):
+        S.step()
+    torch.cuda.synchronize()
+    for bt in S.batches.values():
+        assert B.bd_device_status(bt) == B.BD_OK
+    check = [0, 4, 6, S.n_mats - 1]
+    y_eager = {m: S.y[m].clone() for m in check}
+
+    g = capture(S.step, K)
+    g.replay()
+    torch.cuda.synchronize()
+    wall_us, ev_us = replay_timed(g, K)
+    for m in check:  # every replayed step reproduces the eager result bit for bit
+        assert torch.equal(S.y[m], y_eager[m]), f"graph replay differs from eager (matrix {m})"
+    del g
+    log(f"stack step: {wall_us / 1e3:.3f} ms (events {ev_us / 1e3:.3f} ms)")
+
+    phases = {}
+    for name, fn in (("prepare", S.prepare), ("encode", S.encode_all), ("gemm", S.gemm_all),
+                     ("delta", S.delta_all)):
+        gp = capture(fn, K)
+        gp.replay()
+        _, phases[name] = replay_timed(gp, K)
+        del gp
+    torch.cuda.synchronize()
+    log("phases (us per step): " + ", ".join(f"{k} {v:.1f}" for k, v in phases.items()))
+
+    ms_per_step = wall_us * 1e-3
+    value = S.bytes_step / (ms_per_step * 1e-3) / 1e9
+    n_delta = n_gemm = 4 * S.n_layers  # grouped launches: q|k|v, o, gate|up, down
+    delta_gbs = S.bytes_delta / (phases["delta"] * 1e-6) / 1e9
+    gemm_tfs = S.flops_gemm / (phases["gemm"] * 1e-6) / 1e12
+    rl_delta = {"bound": "hbm", "kernel": "k_delta7", "achieved": round(delta_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(delta_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("k_delta7", S.w.name),
+                "algorithmic_bytes_per_launch": S.bytes_delta // n_delta,
+                "avg_launch_us": round(phases["delta"] / n_delta, 3)}
+    rl_gemm = {"bound": "mfma", "kernel": "k_gemm", "achieved": round(gemm_tfs, 1),
+               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+               "frac": round(gemm_tfs / BF16_PEAK_TFLOPS, 4),
+               "traffic": measured_traffic("k_gemm", S.w.name),
+               "flops_per_launch": S.flops_gemm // n_gemm,
+               "avg_launch_us": round(phases["gemm"] / n_gemm, 3)}
+    dominant, other = (rl_delta, rl_gemm) if phases["delta"] >= phases["gemm"] else (rl_gemm, rl_delta)
+    out = {
+        "value": round(value, 1), "ms_per_step": round(ms_per_step, 4),
+        "config": {"workload": S.w.name, "layers": S.n_layers, "matrices": S.n_mats,
+                   "n_users": S.U, "active_users": len(S.active), "tokens": S.T,
+                   "scale": "matrix fp32", "y_dtype": "fp32", "user_ids": "Zipf(1.1), seed 0",
+                   "banks": "bd_compress of seeded synthetic fine-tunes (Laplace b=5e-4)",
+                   "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(S.T / (ms_per_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": S.bytes_step,
+        "gpu_step_us_events": round(ev_us, 1),
+        "phases_us_per_step": {k: round(v, 1) for k, v in phases.items()},
+        "phase_launches_per_step": {"prepare": len(S.batches), "encode": 4 * S.n_layers,
+                                    "gemm": n_gemm, "delta": n_delta},
+        "matrices_per_launch": "q|k|v, o, gate|up, down (grouped calls on one encoding)",
+        "roofline": dominant,
+        "roofline_secondary": other,
+        "base_gemm": {"TFLOPs": round(gemm_tfs, 1), "frac_of_bf16_peak": round(gemm_tfs / BF16_PEAK_TFLOPS, 4),
+                      "flops_per_step": S.flops_gemm},
+        "setup_s": round(S.setup_s, 1),
+    }
+    return out, S
+
+
+# ---------------------------------------------------------------- q_proj decode leg
+def decode_leg(args, dev):
+    """The Llama-3.1-8B q_proj decode step: 16 users x 1 token on 4096 x 4096, one
+    bd_apply (one k_decode_unit launch), rotating over R input sets so consecutive
+    steps do not hit the last-level cache; the two-launch path and the INT8 base
+    timed beside it."""
     import torch
 
     from tenant_serving_amd import bitdelta as B
     from tenant_serving_amd import synth as S
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     R = max(1, args.sets)
     w0 = S.workload(2)
     mat = w0.matrices[0]
     d_out, d_in, U, T = mat.d_out, mat.d_in, w0.n_users, w0.T
     w = dataclasses.replace(w0, matrices=[mat] * R, xgroups=[d_in] * R)
     p = B.params("matrix")
-
-    # ---------------------------------------------------------- resident inputs
     ids_np = S.user_ids(w0)
     ids = torch.from_numpy(ids_np).to(dev)
     sets = []
@@ -122,111 +349,103 @@ def main():
         y = torch.empty((T, d_out), dtype=torch.float32, device=dev)
         sets.append((wb, signs, scales, x, y))
     ws_bytes = B.bd_apply_workspace_bytes(p, T, U, d_out, d_in, B.BD_BF16, B.BD_F32)
-    wss = [B.workspace(ws_bytes, dev) for _ in range(R)]  # one prepared batch per input set
+    wss = [B.workspace(ws_bytes, dev) for _ in range(R)]
     torch.cuda.synchronize()
     assert B.bd_device_status(cws) == B.BD_OK
+    K = max(R, args.decode_steps)
+    ctr = [0]
+
+    def rot(fn):
+        def f():
+            k = ctr[0]
+            ctr[0] += 1
+            return fn(k)
+        return f
 
     def step(k):
         wb, signs, scales, x, y = sets[k % R]
-        return B.bd_apply(x, wb, signs, scales, p, U, ids, y, wss[k % R])
+        assert B.bd_apply(x, wb, signs, scales, p, U, ids, y, wss[k % R]) == B.BD_OK
 
-    def prep(k):  # the two-launch decode path, timed beside the step
+    def prep(k):
         wb, signs, scales, x, y = sets[k % R]
-        return B.bd_decode_prepare(x, ids, U, scales, p, wss[k % R])
+        assert B.bd_decode_prepare(x, ids, U, scales, p, wss[k % R]) == B.BD_OK
 
     def main_pass(k):
         wb, signs, scales, x, y = sets[k % R]
-        return B.bd_decode_apply(x, wb, signs, scales, p, U, y, wss[k % R])
+        assert B.bd_decode_apply(x, wb, signs, scales, p, U, y, wss[k % R]) == B.BD_OK
 
-    # eager warmup, and the eager result of every set (the graph replays must match it)
-    for k in range(max(args.warmup, R)):
-        assert step(k) == B.BD_OK
+    for k in range(2 * R):
+        step(k)
     torch.cuda.synchronize()
     y_eager = [sets[r][4].clone() for r in range(R)]
-
-    # The K timed steps are captured once into a HIP graph and replayed, so host launch
-    # overhead (Python, ctypes) is not part of the measured GPU time.
-    K = args.steps
-
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for k in range(min(K, R)):  # warm the side stream before capture
-                assert fn(k) == B.BD_OK
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for k in range(K):
-                fn(k)
-        return g
-
-    def timed_replay(g):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        return (t1 - t0) * 1e6 / K, e0.elapsed_time(e1) * 1e3 / K
-
-    # ------------------------------------------------------------- timed steps
-    g_step = capture(step)
-    g_step.replay()
+    g = capture(rot(step), K)
+    g.replay()
     torch.cuda.synchronize()
-    wall_us, gpu_step_us = timed_replay(g_step)
+    wall_us, ev_us = replay_timed(g, K)
     assert B.bd_device_status(wss[0]) == B.BD_OK
-    for r in range(R):  # every replayed step reproduces the eager result bit for bit
+    for r in range(R):
         assert torch.equal(sets[r][4], y_eager[r]), f"graph replay differs from eager (set {r})"
-    ms_per_step = wall_us * 1e-3
+    ctr[0] = 0
+    gp = capture(rot(prep), K)
+    ctr[0] = 0
+    gm = capture(rot(main_pass), K)
+    gp.replay()
+    gm.replay()
+    _, prep_us = replay_timed(gp, K)
+    _, main_us = replay_timed(gm, K)
 
-    # the two-launch decode path on the same inputs (not the step; for comparison)
-    g_prep, g_main = capture(prep), capture(main_pass)
-    g_prep.replay()
-    g_main.replay()
-    torch.cuda.synchronize()
-    _, prep_us = timed_replay(g_prep)
-    _, main_us = timed_replay(g_main)
-
-    # the same steps on an INT8 base (bd_quantize_base once per set, then bd_apply_q8):
-    # one byte per base weight instead of two
     q8 = [B.quantize_base(sets[r][0]) for r in range(R)]
     y8 = [torch.empty((T, d_out), dtype=torch.float32, device=dev) for _ in range(R)]
 
     def step_q8(k):
         wb, signs, scales, x, y = sets[k % R]
         q, qs = q8[k % R]
-        return B.bd_apply_q8(x, q, qs, signs, scales, p, U, ids, y8[k % R], wss[k % R])
+        assert B.bd_apply_q8(x, q, qs, signs, scales, p, U, ids, y8[k % R], wss[k % R]) == B.BD_OK
 
-    for k in range(R):
-        assert step_q8(k) == B.BD_OK
-    g_q8 = capture(step_q8)
-    g_q8.replay()
-    torch.cuda.synchronize()
-    _, q8_us = timed_replay(g_q8)
+    ctr[0] = 0
+    g8 = capture(rot(step_q8), K)
+    g8.replay()
+    _, q8_us = replay_timed(g8, K)
     assert B.bd_device_status(wss[0]) == B.BD_OK
 
-    # algorithmic bytes (each byte the math must touch once)
     n_active = len(set(int(u) for u in ids_np if 0 <= u < U))
-    bytes_w = d_out * d_in * 2
-    bytes_bits = n_active * (d_out * d_in // 8 + 4)
-    bytes_x, bytes_y = T * d_in * 2, T * d_out * 4
-    bytes_step = bytes_w + bytes_bits + bytes_x + bytes_y + 4 * T
-    value = bytes_step / (ms_per_step * 1e-3) / 1e9
-    # the step is one launch of k_decode_unit: it reads the ids, X, W, the active users'
-    # bits and scales once from HBM and writes y once
-    dom, dom_us, dom_bytes = "k_decode_unit", gpu_step_us, bytes_step
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, w0.name),
-                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)}
+    bytes_step = (d_out * d_in * 2 + n_active * (d_out * d_in // 8 + 4) + T * d_in * 2
+                  + T * d_out * 4 + 4 * T)
+    bytes_q8 = bytes_step - d_out * d_in + 4 * d_out
+    gbs = bytes_step / (ev_us * 1e-6) / 1e9
+    out = {"workload": w0.name, "kernel": "k_decode_unit", "d_out": d_out, "d_in": d_in,
+           "n_users": U, "tokens": T, "rotating_sets": R, "steps": K,
+           "us_per_step_wall": round(wall_us, 3), "us_per_step_events": round(ev_us, 3),
+           "algorithmic_bytes": bytes_step, "achieved": round(gbs, 1), "unit": "GB/s",
+           "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "traffic": measured_traffic("k_decode_unit", w0.name),
+           "tokens_per_s": round(T / (wall_us * 1e-6), 1),
+           "two_launch_path_us": {"k_decode_prep": round(prep_us, 3), "k_decode": round(main_us, 3)},
+           "int8_base_step": {"kernel": "k_decode_unit (INT8 base)", "us": round(q8_us, 3),
+                              "algorithmic_bytes": bytes_q8,
+                              "achieved": round(bytes_q8 / (q8_us * 1e-6) / 1e9, 1),
+                              "frac": round(bytes_q8 / (q8_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del g, gp, gm, g8
+    return out, (w, sets, cws)
 
-    # ------------------------------------------------------------ compress leg
-    n_c = min(8, U)
+
+def compress_legs(args, dev, decode_state):
+    """bd_compress per call: (a) one user's q_proj, MATRIX scale, no clipping (one
+    streaming pass); (b) one user's MLP gate_proj 14336 x 4096 of the clipped MLP
+    workload, GROUP 128 fp32 scales, 3-sigma clipping (three passes: mean, squared
+    deviations, pack); (c) bd_select_axis on (a)'s matrices."""
+    import torch
+
+    from tenant_serving_amd import bitdelta as B
+    from tenant_serving_amd import synth as S
+
+    w, sets, cws = decode_state
+    R = len(sets)
+    mat = w.matrices[0]
+    d_out, d_in = mat.d_out, mat.d_in
+    p = B.params("matrix")
+    KC = max(1, args.compress_steps)
+    n_c = min(8, w.n_users)
     wfs = []
     for u in range(n_c):
         t = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)
@@ -234,103 +453,118 @@ def main():
         wfs.append((t, sets[u % R][0]))
     c_signs = torch.empty((d_out, d_in // 64), dtype=torch.int64, device=dev)
     c_scales = torch.empty(1, dtype=torch.float32, device=dev)
-    KC = max(1, args.compress_steps)
+    ctr = [0]
 
-    def comp(k):
-        return B.bd_compress(wfs[k % n_c][0], wfs[k % n_c][1], p, c_signs, c_scales, cws)
+    def comp():
+        k = ctr[0]
+        ctr[0] += 1
+        assert B.bd_compress(wfs[k % n_c][0], wfs[k % n_c][1], p, c_signs, c_scales, cws) == B.BD_OK
 
-    for k in range(4):
-        assert comp(k) == B.BD_OK
-    torch.cuda.synchronize()
-    g_comp = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        comp(0)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g_comp):
-        for k in range(KC):
-            comp(k)
-    g_comp.replay()
-    torch.cuda.synchronize()
-    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ce0.record()
-    g_comp.replay()
-    ce1.record()
-    torch.cuda.synchronize()
+    g = capture(comp, KC)
+    g.replay()
+    _, comp_us = replay_timed(g, KC)
     assert B.bd_device_status(cws) == B.BD_OK
-    comp_us = ce0.elapsed_time(ce1) * 1e3 / KC
     comp_bytes = 2 * d_out * d_in * 2 + d_out * d_in // 8 + 4
     comp_gbs = comp_bytes / (comp_us * 1e-6) / 1e9
-    compress = {"call_us": round(comp_us, 3), "algorithmic_bytes": comp_bytes,
-                "achieved": round(comp_gbs, 1), "unit": "GB/s",
-                "frac": round(comp_gbs / HBM_PEAK_GBS, 4)}
+    out = {"compress": {"matrix": "q_proj 4096 x 4096 bf16, MATRIX fp32, no clip",
+                        "call_us": round(comp_us, 3), "algorithmic_bytes": comp_bytes,
+                        "achieved": round(comp_gbs, 1), "unit": "GB/s",
+                        "frac": round(comp_gbs / HBM_PEAK_GBS, 4)}}
 
-    # per-layer axis choice on the same matrices (no clipping): one statistics pass
-    # over W_fine and W_base, then two small reductions
+    # (b) the clipped GROUP compress of the MLP workload
+    w3 = S.workload(3)
+    m3 = w3.matrices[0]
+    p3 = B.params("group", w3.group_size, w3.clip_k, B.BD_F32)
+    wb3 = S.dev_wbase(w3, 0)
+    wf3 = [S.dev_wfine(w3, 0, u, wb3) for u in range(2)]
+    s3 = torch.empty((m3.d_out, m3.d_in // 64), dtype=torch.int64, device=dev)
+    n_sc3 = B.bd_scales_count(p3, m3.d_out, m3.d_in)
+    c3 = torch.empty(n_sc3, dtype=torch.float32, device=dev)
+    ws3 = B.workspace(B.bd_compress_workspace_bytes(p3, m3.d_out, m3.d_in), dev)
+    ctr[0] = 0
+
+    def comp3():
+        k = ctr[0]
+        ctr[0] += 1
+        assert B.bd_compress(wf3[k % 2], wb3, p3, s3, c3, ws3) == B.BD_OK
+
+    KC3 = max(1, KC // 4)
+    g3 = capture(comp3, KC3)
+    g3.replay()
+    _, c3_us = replay_timed(g3, KC3)
+    assert B.bd_device_status(ws3) == B.BD_OK
+    N3 = m3.d_out * m3.d_in
+    c3_bytes = 3 * (2 * N3 * 2) + N3 // 8 + 4 * n_sc3
+    c3_gbs = c3_bytes / (c3_us * 1e-6) / 1e9
+    out["compress_clip3_group128"] = {
+        "matrix": f"{w3.name} gate_proj {m3.d_out} x {m3.d_in} bf16, GROUP 128 fp32, clip 3 sigma "
+                  "(0.1% injected +-50 sigma outliers)",
+        "passes": 3, "call_us": round(c3_us, 3), "algorithmic_bytes": c3_bytes,
+        "achieved": round(c3_gbs, 1), "unit": "GB/s", "frac": round(c3_gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_one_pass_statistics": 2 * (2 * N3 * 2) + N3 // 8 + 4 * n_sc3}
+    del g, g3, wf3, wb3
+
+    # (c) the per-layer axis choice on (a)'s matrices
     a_ws = B.workspace(B.bd_select_axis_workspace_bytes(d_out, d_in, 0.0), dev)
     a_err = torch.empty(2, dtype=torch.float64, device=dev)
     a_axis = torch.empty(1, dtype=torch.int32, device=dev)
+    ctr[0] = 0
 
-    def axis_sel(k):
-        return B.bd_select_axis(wfs[k % n_c][0], wfs[k % n_c][1], 0.0, a_err, a_axis, a_ws)
+    def axis_sel():
+        k = ctr[0]
+        ctr[0] += 1
+        assert B.bd_select_axis(wfs[k % n_c][0], wfs[k % n_c][1], 0.0, a_err, a_axis, a_ws) == B.BD_OK
 
-    for k in range(4):
-        assert axis_sel(k) == B.BD_OK
-    torch.cuda.synchronize()
-    g_ax = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        axis_sel(0)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g_ax):
-        for k in range(KC):
-            axis_sel(k)
-    g_ax.replay()
-    torch.cuda.synchronize()
-    ce0.record()
-    g_ax.replay()
-    ce1.record()
-    torch.cuda.synchronize()
+    ga = capture(axis_sel, KC)
+    ga.replay()
+    _, ax_us = replay_timed(ga, KC)
     assert B.bd_device_status(a_ws) == B.BD_OK
-    ax_us = ce0.elapsed_time(ce1) * 1e3 / KC
     ax_bytes = 2 * d_out * d_in * 2
     ax_gbs = ax_bytes / (ax_us * 1e-6) / 1e9
-    axis_select = {"call_us": round(ax_us, 3), "algorithmic_bytes": ax_bytes,
-                   "achieved": round(ax_gbs, 1), "unit": "GB/s",
-                   "frac": round(ax_gbs / HBM_PEAK_GBS, 4)}
+    out["axis_select"] = {"call_us": round(ax_us, 3), "algorithmic_bytes": ax_bytes,
+                          "achieved": round(ax_gbs, 1), "unit": "GB/s",
+                          "frac": round(ax_gbs / HBM_PEAK_GBS, 4)}
+    return out
 
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w0.name, "d_out": d_out, "d_in": d_in, "n_users": U,
-                   "active_users": n_active, "tokens": T, "scale": "matrix fp32",
-                   "y_dtype": "fp32", "rotating_sets": R, "parallelism": "none (1 GPU)"},
-        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
-        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "algorithmic_bytes_per_step": bytes_step,
-        "gpu_step_us_events": round(gpu_step_us, 3),
-        "timing": "the K steps (one k_decode_unit launch each) captured in one HIP graph, "
-                  "replayed once between device synchronisations (wall clock -> ms_per_step; "
-                  "HIP events on the same stream -> gpu_step_us_events = the kernel's average "
-                  "launch time); the two-launch path timed the same way from graphs of its K "
-                  "prepare and K apply launches",
-        "kernels_us": {"k_decode_unit": round(gpu_step_us, 3)},
-        "two_launch_path_us": {"k_decode_prep": round(prep_us, 3), "k_decode": round(main_us, 3)},
-        "roofline": roofline,
-        "compress": compress,
-        "axis_select": axis_select,
-        "int8_base_step": {"kernel": "k_decode_unit (INT8 base)", "us": round(q8_us, 3),
-                           "algorithmic_bytes": bytes_step - d_out * d_in + 4 * d_out,
-                           "achieved": round((bytes_step - d_out * d_in + 4 * d_out) / (q8_us * 1e-6) / 1e9, 1),
-                           "unit": "GB/s",
-                           "frac": round((bytes_step - d_out * d_in + 4 * d_out) / (q8_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
-        "kernel_source_digest": kernel_source_digest(),
-    }
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("building the 32-layer stack (128 users' banks through bd_compress)")
+    st, S = stack_leg(args, dev)
+    out = {"metric": METRIC, "value": st.pop("value"), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": st.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    out.update(st)
+    out["timing"] = ("the K steps captured in one HIP graph, replayed once between device "
+                     "synchronisations (wall clock -> ms_per_step; HIP events on the replay "
+                     "stream -> gpu_step_us_events); each phase's launches of K steps captured "
+                     "and replayed alone the same way (HIP events -> phases_us_per_step; the "
+                     "roofline's avg_launch_us is the phase time over its launches)")
+    out["kernel_source_digest"] = kernel_source_digest()
+    cpu_sample = None
+    if not args.no_cpu_baseline:
+        cpu_sample = (S.ids_np, S.active, S.bytes_step)
+    del S
+    torch.cuda.empty_cache()
+
+    if not args.no_legs:
+        log("q_proj decode leg")
+        dec, state = decode_leg(args, dev)
+        out["decode_q_proj_16users"] = dec
+        log("compress legs")
+        out.update(compress_legs(args, dev, state))
+        del state
+        torch.cuda.empty_cache()
 
     if args.calib_copy_mib > 0:
         nb = args.calib_copy_mib << 20
@@ -341,10 +575,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = nb
+        del src, dst
 
-    # --------------------------------------------------- CPU oracle baseline
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, ids_np, args.cpu_rows, bytes_step, R)
+    if cpu_sample is not None:
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(*cpu_sample, rows=args.cpu_rows)
     print(json.dumps(out), flush=True)
     if args.load:
         print(json.dumps(load_leg()), file=sys.stderr, flush=True)
@@ -356,8 +591,63 @@ def main():
             print(json.dumps(line), file=sys.stderr, flush=True)
 
 
+def cpu_baseline(ids_np, active, bytes_step, rows=64, seconds=12.0, max_calls=200):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: the 7
+    matrices of layer 0 of the stack, `rows` seeded output rows of each, all 512
+    tokens and every active user.  The oracle compresses those rows of each active
+    user's fine-tune itself (not timed; the scale is the absmean of the sampled rows),
+    then applies the batch to them repeatedly until about `seconds` of apply time."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "oracle"))
+    import oracle as O
+
+    from tenant_serving_amd import synth as S
+
+    w = S.workload(5)
+    rng = np.random.default_rng(5)
+    remap = {u: i for i, u in enumerate(active)}
+    sub_ids = np.array([remap.get(int(u), -1) for u in ids_np], dtype=np.int32)
+    t0 = time.perf_counter()
+    layer = []
+    sample_bytes = 0
+    for m in range(7):
+        mat = w.matrices[m]
+        r = sorted(rng.choice(mat.d_out, size=min(rows, mat.d_out), replace=False).tolist())
+        wb = S.host_wbase(w, m, rows=r)
+        words, scs = [], []
+        for u in active:
+            wf = S.host_wfine(w, m, u, rows=r, wbase=wb)
+            ww, ss, _, _ = O.compress(wf, wb, O.MATRIX, dtype=O.BF16)
+            words.append(ww)
+            scs.append(ss)
+        x = S.host_x(w, mat.xgroup)
+        layer.append((x, wb, np.stack(words), np.stack(scs)))
+        na, T = len(active), w.T
+        full = (mat.d_out * mat.d_in * 2 + na * (mat.d_out * mat.d_in // 8 + 4)
+                + T * mat.d_in * 2 + T * mat.d_out * 4 + 4 * T)
+        sample_bytes += full * len(r) / mat.d_out  # the sampled rows' share of the apply
+    t1 = time.perf_counter()
+    calls, spent = 0, 0.0
+    while calls < max_calls and (calls == 0 or spent < seconds):
+        t2 = time.perf_counter()
+        for x, wb, words, scs in layer:
+            O.apply(x, wb, words, scs, O.MATRIX, sub_ids)
+        spent += time.perf_counter() - t2
+        calls += 1
+    return {"value": round(calls * sample_bytes / spent / 1e9, 4), "unit": "GB/s",
+            "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{calls} passes over layer 0's 7 matrices of the stack, {rows} seeded "
+                      f"output rows each, all {w.T} tokens, {len(active)} active users (the "
+                      f"oracle's own compress of those rows, untimed); fp64 plain loops, "
+                      f"OpenMP over tokens; rate = passes x the sampled rows' share of those "
+                      f"matrices' algorithmic bytes / total oracle apply time",
+            "passes": calls, "apply_s": round(spent, 3), "sample_bytes": int(sample_bytes),
+            "oracle_compress_s": round(t1 - t0, 3), "host_cpus": os.cpu_count()}
+
+
 def workloads_leg(reps=10):
-    """One layer step of workloads 3, 4 and 5 through the prepared-batch calls: per
+    """One layer step of workloads 3 and 4 through the prepared-batch calls: per
     distinct input width one bd_batch_prepare (the grouping and tile packing of the
     batch), then per matrix bd_base_gemm and bd_delta_apply.  Random banks (the time
     does not depend on the bit values; parity at these sizes is tested separately).
@@ -369,7 +659,7 @@ def workloads_leg(reps=10):
 
     dev = torch.device("cuda:0")
     out = []
-    for wid in (3, 4, 5):
+    for wid in (3, 4):
         w = S.workload(wid)
         ids_np = S.user_ids(w)
         ids = torch.from_numpy(ids_np).to(dev)
@@ -433,6 +723,8 @@ def workloads_leg(reps=10):
         del mats, xs, batches, g
         torch.cuda.empty_cache()
     return out
+
+
 
 
 LLAMA8B_LINEARS = ((4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096),  # q k v o
@@ -576,48 +868,6 @@ def merge_leg(reps=20, token_counts=(16, 32, 64, 128, 256, 512, 1024)):
     return out
 
 
-def cpu_baseline(w, ids_np, rows, bytes_step, n_sets, seconds=12.0, max_calls=2048):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    applies of all tokens on `rows` output rows of input set 0's bank (compressed
-    by the oracle first, not timed in the rate), one per token set, cycling over
-    the token sets until about `seconds` of apply time (at most `max_calls`)."""
-    import numpy as np
-
-    sys.path.insert(0, os.path.join(ROOT, "oracle"))
-    import oracle as O
-
-    from tenant_serving_amd import synth as S
-
-    mat = w.matrices[0]
-    d_out, d_in, U = mat.d_out, mat.d_in, w.n_users
-    rows = max(1, min(rows, d_out))
-    t0 = time.perf_counter()
-    wb = S.host_wbase(w, 0)
-    words, scs = [], []
-    for u in range(U):
-        wf = S.host_wfine(w, 0, u, wbase=wb)
-        ww, ss, _, _ = O.compress(wf, wb, O.MATRIX, dtype=O.BF16)
-        words.append(ww[:rows])
-        scs.append(ss)
-    t1 = time.perf_counter()
-    xs = [S.host_x(w, g) for g in range(max(1, n_sets))]
-    wrows, wst, sst = wb[:rows], np.stack(words), np.stack(scs)
-    calls, spent = 0, 0.0
-    while calls < max_calls and (calls == 0 or spent < seconds):
-        x = xs[calls % len(xs)]
-        t2 = time.perf_counter()
-        O.apply(x, wrows, wst, sst, O.MATRIX, ids_np)
-        spent += time.perf_counter() - t2
-        calls += 1
-    sample_bytes = bytes_step * rows / d_out
-    return {"value": round(calls * sample_bytes / spent / 1e9, 4), "unit": "GB/s",
-            "cores": min(O.num_threads(), w.T), "kind": "oracle",
-            "sample": f"{calls} applies of all {w.T} tokens on {rows} of {d_out} output rows "
-                      f"of one bank, cycling over {len(xs)} token sets (fp64 plain loops, "
-                      f"OpenMP over tokens); rate = calls x that share of the step's "
-                      f"algorithmic bytes / total oracle apply time",
-            "apply_calls": calls, "apply_s": round(spent, 3),
-            "compress_16_users_s": round(t1 - t0, 3), "host_cpus": os.cpu_count()}
 
 
 if __name__ == "__main__":

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 1
+#define BD_ABI_VERSION 2
 
 typedef enum {
     BD_OK = 0,
@@ -58,7 +58,9 @@ typedef enum {
     BD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the query returns */
     BD_ERR_DEVICE = 6,      /* a HIP call or launch failed */
     BD_ERR_NONFINITE = 7,   /* (async) a delta was NaN or Inf */
-    BD_ERR_USER_ID = 8      /* (async) a user id outside [-1, n_users) */
+    BD_ERR_USER_ID = 8,     /* (async) a user id outside [-1, n_users) */
+    BD_ERR_BATCH = 9        /* (async) delta products asked of a prepared batch whose tokens
+                               were encoded for another scale mode (bd_batch_encode) */
 } bd_status;
 
 typedef enum { BD_F32 = 0, BD_BF16 = 1, BD_F16 = 2 } bd_dtype;
@@ -197,10 +199,15 @@ bd_status bd_reconstruct(const uint64_t* signs, const void* scales, const bd_com
  *  workspace   : >= bd_apply_workspace_bytes(...) bytes, 256-byte aligned.
  * Accumulation is fp32.  T == 0 is a no-op.  bf16 inputs: T <= 8192 tokens
  * per call and GROUP group_size >= 128 (BD_ERR_UNSUPPORTED otherwise).
- * bf16 batches of 1..16 tokens with MATRIX, ROW or COL scales take a one-pass
- * path, equivalent to bd_decode_prepare + bd_decode_apply on the workspace;
- * every other batch is equivalent to bd_batch_prepare + bd_base_gemm +
- * bd_delta_apply (+ a cast for bf16 y) on one workspace. */
+ * bf16 batches of 1..16 tokens with MATRIX, ROW or COL scales take the decode path:
+ * for MATRIX or ROW scales and d_in <= 5120 one launch that writes only y and the
+ * status word (the workspace is NOT left prepared for bd_decode_apply; callers
+ * that share one batch across matrices call bd_decode_prepare themselves), else
+ * bd_decode_prepare + bd_decode_apply on the workspace.  The one-launch kernels
+ * encode the tokens differently from bd_decode_prepare, so the two agree within
+ * the bf16 tolerance, not bit for bit.  Every other batch is computed as
+ * bd_batch_prepare + bd_base_gemm + bd_delta_apply (+ a cast for bf16 y) on one
+ * workspace. */
 bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const void* w_base,
                    int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
                    const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
@@ -256,17 +263,65 @@ bd_status bd_base_gemm(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
                        const void* w_base, int64_t d_out, float* y, void* stream);
 
 /* Per-user delta product added into y: y[t] += scale_u (.) (X[t] . S_u^T) for
- * every token of the prepared batch whose user is valid.  `batch` must come
- * from bd_batch_prepare with the same user ids, x_dtype, T, d_in and n_users;
- * x is [T][d_in] (any activation tensor of that batch, e.g. the input of q, k
- * or v); y is fp32 [T][d_out].  For bf16 inputs the call first writes this x
- * (times the column scales, for COL) into `batch` as tiles of 16 user-sorted
- * tokens encoded as fp6 e2m3 operands, so calls on one batch must not overlap;
- * the grouping itself is left unchanged. */
-bd_status bd_delta_apply(void* batch, const void* x, bd_dtype x_dtype, int64_t T,
-                         int64_t d_in, int32_t n_users, int64_t d_out, const uint64_t* signs_bank,
-                         const void* scales_bank, const bd_compress_params* p, float* y,
-                         void* stream);
+ * every token of the prepared batch whose user is valid.  `batch` (batch_bytes
+ * long, >= bd_batch_workspace_bytes) must come from bd_batch_prepare with the
+ * same user ids, x_dtype, T, d_in and n_users; x is [T][d_in] (any activation
+ * tensor of that batch, e.g. the input of q, k or v); y is fp32 [T][d_out].  For
+ * bf16 inputs the call is bd_batch_encode followed by bd_delta_apply_encoded:
+ * it first writes this x (times the column scales, for COL) into `batch` as
+ * tiles of 16 user-sorted tokens encoded as fp6 e2m3 operands, so calls on one
+ * batch must not overlap; the grouping itself is left unchanged. */
+bd_status bd_delta_apply(void* batch, size_t batch_bytes, const void* x, bd_dtype x_dtype,
+                         int64_t T, int64_t d_in, int32_t n_users, int64_t d_out,
+                         const uint64_t* signs_bank, const void* scales_bank,
+                         const bd_compress_params* p, float* y, void* stream);
+
+/* The two halves of bd_delta_apply for bf16 inputs, so that matrices reading the
+ * same activations (q, k and v; gate and up) share one encoding of them.
+ *
+ * bd_batch_encode writes x [T][d_in] bf16 into the prepared `batch` as the
+ * delta-product operands: per tile of 16 user-sorted tokens and 512-column unit,
+ * two fp6 e2m3 parts per value under one power-of-two scale per 32 columns (the
+ * hi part is x rounded to 3 fraction bits under the block's scale, the lo part
+ * the rounded residual; together they keep the bf16 value exactly for every
+ * element of at least a quarter of its block's largest magnitude).  The column
+ * order depends on p->mode (GROUP or not); for COL, x is first multiplied by the
+ * column scales of each token's user (scales_bank, rounded to bf16), so a COL
+ * encoding belongs to one matrix's scales.  Other modes do not read scales_bank
+ * (it may be NULL).  Overwrites the previous encoding of the batch.
+ *
+ * bd_delta_apply_encoded adds y[t] += scale_u (.) (X[t] . S_u^T) for one matrix
+ * from the batch's current encoding ([P2] "Systems Mechanics" 1-2).  p->mode must
+ * be the mode the batch was encoded for (GROUP / COL / the others): otherwise
+ * nothing is added and the batch's status word reports BD_ERR_BATCH. */
+bd_status bd_batch_encode(void* batch, size_t batch_bytes, const void* x, bd_dtype x_dtype,
+                          int64_t T, int64_t d_in, int32_t n_users, const void* scales_bank,
+                          const bd_compress_params* p, void* stream);
+bd_status bd_delta_apply_encoded(void* batch, size_t batch_bytes, bd_dtype x_dtype, int64_t T,
+                                 int64_t d_in, int32_t n_users, int64_t d_out,
+                                 const uint64_t* signs_bank, const void* scales_bank,
+                                 const bd_compress_params* p, float* y, void* stream);
+
+/* Grouped forms for matrices that read the same activations (q, k and v; gate and
+ * up), up to 4 per call: one launch each instead of one per matrix, so small
+ * matrices (k and v) share the grid with large ones.  Results equal, bit for bit,
+ * n_mats calls of bd_base_gemm / bd_delta_apply_encoded with the same arguments.
+ *  n_mats      : 1..4.
+ *  d_outs      : host int64[n_mats], the output rows of each matrix.
+ *  w_bases     : host array of n_mats device pointers, [d_outs[i]][d_in] each.
+ *  signs_banks, scales_banks : host arrays of n_mats device pointers, each as for
+ *                bd_delta_apply_encoded with d_out = d_outs[i].
+ *  ys          : host array of n_mats device pointers, fp32 [T][d_outs[i]] each.
+ * bd_base_gemm_n falls back to one launch per matrix for batches the tiled GEMM
+ * does not take (T <= 64, fp32). */
+bd_status bd_base_gemm_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                         int32_t n_mats, const void* const* w_bases, const int64_t* d_outs,
+                         float* const* ys, void* stream);
+bd_status bd_delta_apply_encoded_n(void* batch, size_t batch_bytes, bd_dtype x_dtype, int64_t T,
+                                   int64_t d_in, int32_t n_users, int32_t n_mats,
+                                   const int64_t* d_outs, const uint64_t* const* signs_banks,
+                                   const void* const* scales_banks, const bd_compress_params* p,
+                                   float* const* ys, void* stream);
 
 /* The two launches of bd_apply's one-pass path for decode batches: bf16 x and
  * w_base, 1 <= T <= 16, MATRIX, ROW or COL scales (BD_ERR_UNSUPPORTED for any
@@ -300,8 +355,8 @@ bd_status bd_decode_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_
 
 /* Synchronises `stream`, then returns the status recorded in the workspace (or
  * prepared batch) of the last bd_compress / bd_apply / bd_batch_prepare that
- * used it (BD_OK, BD_ERR_NONFINITE or BD_ERR_USER_ID), or BD_ERR_DEVICE if the
- * copy fails. */
+ * used it (BD_OK, BD_ERR_NONFINITE, BD_ERR_USER_ID or BD_ERR_BATCH), or
+ * BD_ERR_DEVICE if the copy fails. */
 bd_status bd_device_status(const void* workspace, void* stream);
 
 #ifdef __cplusplus

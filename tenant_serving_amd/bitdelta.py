@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libbitdelta.so")
 
 # enums of the C ABI
 BD_OK, BD_ERR_INVALID_ARG, BD_ERR_SHAPE, BD_ERR_DTYPE, BD_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
-BD_ERR_WORKSPACE, BD_ERR_DEVICE, BD_ERR_NONFINITE, BD_ERR_USER_ID = 5, 6, 7, 8
+BD_ERR_WORKSPACE, BD_ERR_DEVICE, BD_ERR_NONFINITE, BD_ERR_USER_ID, BD_ERR_BATCH = 5, 6, 7, 8, 9
 BD_F32, BD_BF16, BD_F16 = 0, 1, 2
 BD_SCALE_MATRIX, BD_SCALE_GROUP, BD_SCALE_ROW, BD_SCALE_COL = 0, 1, 2, 3
 MODE_NAMES = {"matrix": BD_SCALE_MATRIX, "group": BD_SCALE_GROUP, "row": BD_SCALE_ROW,
@@ -90,7 +90,18 @@ def lib() -> ctypes.CDLL:
         L.bd_base_gemm.restype = ctypes.c_int
         L.bd_base_gemm.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp]
         L.bd_delta_apply.restype = ctypes.c_int
-        L.bd_delta_apply.argtypes = [vp, vp, ctypes.c_int, i64, i64, i32, i64, vp, vp, P, vp, vp]
+        L.bd_delta_apply.argtypes = [vp, sz, vp, ctypes.c_int, i64, i64, i32, i64, vp, vp, P, vp,
+                                     vp]
+        L.bd_batch_encode.restype = ctypes.c_int
+        L.bd_batch_encode.argtypes = [vp, sz, vp, ctypes.c_int, i64, i64, i32, vp, P, vp]
+        L.bd_delta_apply_encoded.restype = ctypes.c_int
+        L.bd_delta_apply_encoded.argtypes = [vp, sz, ctypes.c_int, i64, i64, i32, i64, vp, vp, P,
+                                             vp, vp]
+        L.bd_base_gemm_n.restype = ctypes.c_int
+        L.bd_base_gemm_n.argtypes = [vp, ctypes.c_int, i64, i64, i32, vp, vp, vp, vp]
+        L.bd_delta_apply_encoded_n.restype = ctypes.c_int
+        L.bd_delta_apply_encoded_n.argtypes = [vp, sz, ctypes.c_int, i64, i64, i32, i32, vp, vp,
+                                               vp, P, vp, vp]
         L.bd_decode_prepare.restype = ctypes.c_int
         L.bd_decode_prepare.argtypes = [vp, ctypes.c_int, i64, i64, vp, i32, vp, P, vp, sz, vp]
         L.bd_decode_apply.restype = ctypes.c_int
@@ -140,6 +151,51 @@ def _check(st: int, where: str):
         raise BitDeltaError(st, where)
 
 
+# Argument checks done before any pointer reaches the library: the C ABI takes raw
+# device pointers, so a host tensor, a strided view, int64 user ids or a scales bank
+# too small for the scale mode would otherwise be read as something else on the GPU.
+
+def _dev(t, name: str, dtypes=None, shape=None, device=None, optional: bool = False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ids(user_ids, T, device):
+    _dev(user_ids, "user_ids", (torch.int32,), (T,), device)
+
+
+def _bank(signs_bank, scales_bank, p, n_users, d_out, d_in, device):
+    _dev(signs_bank, "signs_bank", (torch.int64,), (n_users, d_out, d_in // 64), device)
+    _scales(scales_bank, p, n_users, d_out, d_in, device)
+
+
+def _scales(scales_bank, p, n_users, d_out, d_in, device, optional=False):
+    if scales_bank is not None and isinstance(scales_bank, torch.Tensor):
+        need = n_users * max(bd_scales_count(p, d_out, d_in), 0)
+        if scales_bank.numel() < need:
+            raise ValueError(f"scales_bank holds {scales_bank.numel()} values, the scale mode "
+                             f"needs {need} ({n_users} users)")
+    _dev(scales_bank, "scales_bank", (scales_dtype(p),), None, device, optional)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 # ------------------------------------------------------------------ queries
 
 def bd_signs_bytes(d_out: int, d_in: int) -> int:
@@ -167,30 +223,55 @@ def bd_apply_workspace_bytes(p: bd_compress_params, T: int, n_users: int, d_out:
 # -------------------------------------------------------------- entry points
 
 def bd_compress(w_fine, w_base, p, signs_out, scales_out, workspace, stream=None) -> int:
+    _dev(w_fine, "w_fine", (torch.float32, torch.bfloat16))
     d_out, d_in = w_fine.shape
+    dev = w_fine.device
+    _dev(w_base, "w_base", (w_fine.dtype,), (d_out, d_in), dev, optional=True)
+    _dev(signs_out, "signs_out", (torch.int64,), (d_out, d_in // 64), dev)
+    _scales(scales_out, p, 1, d_out, d_in, dev)
+    _dev(workspace, "workspace", None, None, dev)
     return int(lib().bd_compress(_ptr(w_fine), _ptr(w_base), _dtype_code(w_fine), d_out, d_in,
                                  ctypes.byref(p), _ptr(signs_out), _ptr(scales_out),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(w_fine, stream)))
+                                 _ptr(workspace), _nbytes(workspace), _stream(w_fine, stream)))
 
 
 def bd_reconstruct(signs, scales, p, d_out, d_in, w_base, out, stream=None) -> int:
+    _dev(signs, "signs", (torch.int64,), (d_out, d_in // 64))
+    dev = signs.device
+    _scales(scales, p, 1, d_out, d_in, dev)
+    _dev(w_base, "w_base", (torch.float32, torch.bfloat16), (d_out, d_in), dev, optional=True)
+    _dev(out, "out", (torch.float32, torch.bfloat16), (d_out, d_in), dev)
     return int(lib().bd_reconstruct(_ptr(signs), _ptr(scales), ctypes.byref(p), d_out, d_in,
                                     _ptr(w_base), _dtype_code(w_base) if w_base is not None else 0,
                                     _ptr(out), _dtype_code(out), _stream(out, stream)))
 
 
+def _apply_args(x, w_base_rows, signs_bank, scales_bank, p, n_users, user_ids, y, workspace,
+                wdtypes=None):
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    T, d_in = x.shape
+    dev = x.device
+    d_out = w_base_rows.shape[0]
+    _dev(w_base_rows, "w_base", wdtypes or (x.dtype,), (d_out, d_in), dev)
+    _bank(signs_bank, scales_bank, p, n_users, d_out, d_in, dev)
+    _ids(user_ids, T, dev)
+    _dev(y, "y", (torch.float32, torch.bfloat16), (T, d_out), dev)
+    _dev(workspace, "workspace", None, None, dev)
+    return T, d_in, d_out
+
+
 def bd_apply(x, w_base, signs_bank, scales_bank, p, n_users, user_ids, y, workspace,
              stream=None) -> int:
-    T, d_in = x.shape
-    d_out = w_base.shape[0]
+    T, d_in, d_out = _apply_args(x, w_base, signs_bank, scales_bank, p, n_users, user_ids, y,
+                                 workspace)
     return int(lib().bd_apply(_ptr(x), _dtype_code(x), T, d_in, _ptr(w_base), d_out,
                               _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p), int(n_users),
                               _ptr(user_ids), _ptr(y), _dtype_code(y), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(x, stream)))
+                              _nbytes(workspace), _stream(x, stream)))
 
 
 def bd_device_status(workspace, stream=None) -> int:
+    _dev(workspace, "workspace")
     return int(lib().bd_device_status(_ptr(workspace), _stream(workspace, stream)))
 
 
@@ -199,42 +280,136 @@ def bd_batch_workspace_bytes(T: int, n_users: int, d_in: int, x_dtype: int) -> i
 
 
 def bd_batch_prepare(x, user_ids, n_users, batch, stream=None) -> int:
+    _dev(x, "x", (torch.float32, torch.bfloat16))
     T, d_in = x.shape
+    _ids(user_ids, T, x.device)
+    _dev(batch, "batch", None, None, x.device)
     return int(lib().bd_batch_prepare(_ptr(x), _dtype_code(x), T, d_in, _ptr(user_ids),
-                                      int(n_users), _ptr(batch),
-                                      batch.numel() * batch.element_size(), _stream(x, stream)))
+                                      int(n_users), _ptr(batch), _nbytes(batch),
+                                      _stream(x, stream)))
 
 
 def bd_base_gemm(x, w_base, y, stream=None) -> int:
+    _dev(x, "x", (torch.float32, torch.bfloat16))
     T, d_in = x.shape
+    _dev(w_base, "w_base", (x.dtype,), (w_base.shape[0], d_in), x.device)
+    _dev(y, "y", (torch.float32,), (T, w_base.shape[0]), x.device)
     return int(lib().bd_base_gemm(_ptr(x), _dtype_code(x), T, d_in, _ptr(w_base),
                                   w_base.shape[0], _ptr(y), _stream(x, stream)))
 
 
 def bd_delta_apply(batch, x, n_users, signs_bank, scales_bank, p, y, stream=None) -> int:
+    _dev(x, "x", (torch.float32, torch.bfloat16))
     T, d_in = x.shape
+    dev = x.device
+    _dev(y, "y", (torch.float32,), None, dev)
+    if y.dim() != 2 or y.shape[0] != T:
+        raise ValueError(f"y has shape {tuple(y.shape)}, expected ({T}, d_out)")
     d_out = y.shape[1]
-    return int(lib().bd_delta_apply(_ptr(batch), _ptr(x), _dtype_code(x), T, d_in, int(n_users),
-                                    d_out, _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p),
-                                    _ptr(y), _stream(y, stream)))
+    _bank(signs_bank, scales_bank, p, n_users, d_out, d_in, dev)
+    _dev(batch, "batch", None, None, dev)
+    return int(lib().bd_delta_apply(_ptr(batch), _nbytes(batch), _ptr(x), _dtype_code(x), T, d_in,
+                                    int(n_users), d_out, _ptr(signs_bank), _ptr(scales_bank),
+                                    ctypes.byref(p), _ptr(y), _stream(y, stream)))
+
+
+def bd_batch_encode(batch, x, n_users, scales_bank, p, stream=None) -> int:
+    _dev(x, "x", (torch.bfloat16,))
+    T, d_in = x.shape
+    dev = x.device
+    _dev(batch, "batch", None, None, dev)
+    if p.mode == BD_SCALE_COL:
+        _scales(scales_bank, p, n_users, 1, d_in, dev)
+    else:
+        _dev(scales_bank, "scales_bank", None, None, dev, optional=True)
+    return int(lib().bd_batch_encode(_ptr(batch), _nbytes(batch), _ptr(x), _dtype_code(x), T,
+                                     d_in, int(n_users), _ptr(scales_bank), ctypes.byref(p),
+                                     _stream(x, stream)))
+
+
+def bd_delta_apply_encoded(batch, T, d_in, n_users, signs_bank, scales_bank, p, y,
+                           stream=None) -> int:
+    _dev(y, "y", (torch.float32,))
+    dev = y.device
+    if y.dim() != 2 or y.shape[0] != T:
+        raise ValueError(f"y has shape {tuple(y.shape)}, expected ({T}, d_out)")
+    d_out = y.shape[1]
+    _bank(signs_bank, scales_bank, p, n_users, d_out, d_in, dev)
+    _dev(batch, "batch", None, None, dev)
+    return int(lib().bd_delta_apply_encoded(_ptr(batch), _nbytes(batch), BD_BF16, int(T),
+                                            int(d_in), int(n_users), d_out, _ptr(signs_bank),
+                                            _ptr(scales_bank), ctypes.byref(p), _ptr(y),
+                                            _stream(y, stream)))
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def bd_base_gemm_n(x, w_bases, ys, stream=None) -> int:
+    """Base products of up to 4 matrices that read x, in one launch."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    T, d_in = x.shape
+    if not 1 <= len(w_bases) <= 4 or len(ys) != len(w_bases):
+        raise ValueError("1..4 matrices, one output each")
+    for w, y in zip(w_bases, ys):
+        _dev(w, "w_base", (x.dtype,), (w.shape[0], d_in), x.device)
+        _dev(y, "y", (torch.float32,), (T, w.shape[0]), x.device)
+    d_outs = (ctypes.c_int64 * len(ys))(*[w.shape[0] for w in w_bases])
+    return int(lib().bd_base_gemm_n(_ptr(x), _dtype_code(x), T, d_in, len(ys),
+                                    _ptr_array(w_bases), d_outs, _ptr_array(ys),
+                                    _stream(x, stream)))
+
+
+def bd_delta_apply_encoded_n(batch, T, d_in, n_users, signs_banks, scales_banks, p, ys,
+                             stream=None) -> int:
+    """Delta products of up to 4 matrices on one encoded batch, in one launch."""
+    if not 1 <= len(ys) <= 4 or len(signs_banks) != len(ys) or len(scales_banks) != len(ys):
+        raise ValueError("1..4 matrices, one bank and one output each")
+    dev = ys[0].device if isinstance(ys[0], torch.Tensor) else None
+    for sb, sc, y in zip(signs_banks, scales_banks, ys):
+        _dev(y, "y", (torch.float32,), None, dev)
+        if y.dim() != 2 or y.shape[0] != T:
+            raise ValueError(f"y has shape {tuple(y.shape)}, expected ({T}, d_out)")
+        _bank(sb, sc, p, n_users, y.shape[1], d_in, dev)
+    _dev(batch, "batch", None, None, dev)
+    d_outs = (ctypes.c_int64 * len(ys))(*[y.shape[1] for y in ys])
+    return int(lib().bd_delta_apply_encoded_n(_ptr(batch), _nbytes(batch), BD_BF16, int(T),
+                                              int(d_in), int(n_users), len(ys), d_outs,
+                                              _ptr_array(signs_banks), _ptr_array(scales_banks),
+                                              ctypes.byref(p), _ptr_array(ys),
+                                              _stream(ys[0], stream)))
 
 
 def bd_decode_prepare(x, user_ids, n_users, scales_bank, p, workspace, stream=None) -> int:
+    _dev(x, "x", (torch.float32, torch.bfloat16))
     T, d_in = x.shape
+    dev = x.device
+    _ids(user_ids, T, dev)
+    if p.mode == BD_SCALE_COL:
+        _scales(scales_bank, p, n_users, 1, d_in, dev)
+    else:
+        _dev(scales_bank, "scales_bank", None, None, dev, optional=True)
+    _dev(workspace, "workspace", None, None, dev)
     return int(lib().bd_decode_prepare(_ptr(x), _dtype_code(x), T, d_in, _ptr(user_ids),
                                        int(n_users), _ptr(scales_bank), ctypes.byref(p),
-                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                       _stream(x, stream)))
+                                       _ptr(workspace), _nbytes(workspace), _stream(x, stream)))
 
 
 def bd_decode_apply(x, w_base, signs_bank, scales_bank, p, n_users, y, workspace,
                     stream=None) -> int:
+    _dev(x, "x", (torch.float32, torch.bfloat16))
     T, d_in = x.shape
+    dev = x.device
+    d_out = w_base.shape[0]
+    _dev(w_base, "w_base", (x.dtype,), (d_out, d_in), dev)
+    _bank(signs_bank, scales_bank, p, n_users, d_out, d_in, dev)
+    _dev(y, "y", (torch.float32, torch.bfloat16), (T, d_out), dev)
+    _dev(workspace, "workspace", None, None, dev)
     return int(lib().bd_decode_apply(_ptr(x), _dtype_code(x), T, d_in, _ptr(w_base),
-                                     w_base.shape[0], _ptr(signs_bank), _ptr(scales_bank),
+                                     d_out, _ptr(signs_bank), _ptr(scales_bank),
                                      ctypes.byref(p), int(n_users), _ptr(y), _dtype_code(y),
-                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _stream(x, stream)))
+                                     _ptr(workspace), _nbytes(workspace), _stream(x, stream)))
 
 
 # ------------------------------------------------------- allocating helpers
@@ -269,7 +444,13 @@ def compress(w_fine: torch.Tensor, w_base: Optional[torch.Tensor], p: bd_compres
 
 
 def bd_select_axis(w_fine, w_base, clip_k, errors, axis, workspace, stream=None) -> int:
+    _dev(w_fine, "w_fine", (torch.float32, torch.bfloat16))
     d_out, d_in = w_fine.shape
+    dev = w_fine.device
+    _dev(w_base, "w_base", (w_fine.dtype,), (d_out, d_in), dev, optional=True)
+    _dev(errors, "errors", (torch.float64,), (2,), dev, optional=True)
+    _dev(axis, "axis", (torch.int32,), (1,), dev, optional=True)
+    _dev(workspace, "workspace", None, None, dev)
     return int(lib().bd_select_axis(_ptr(w_fine), _ptr(w_base), _dtype_code(w_fine), d_out, d_in,
                                     float(clip_k), _ptr(errors), _ptr(axis), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
@@ -277,19 +458,23 @@ def bd_select_axis(w_fine, w_base, clip_k, errors, axis, workspace, stream=None)
 
 
 def bd_quantize_base(w, q_out, scales_out, stream=None) -> int:
+    _dev(w, "w", (torch.float32, torch.bfloat16))
     d_out, d_in = w.shape
+    _dev(q_out, "q_out", (torch.int8,), (d_out, d_in), w.device)
+    _dev(scales_out, "scales_out", (torch.float32,), (d_out,), w.device)
     return int(lib().bd_quantize_base(_ptr(w), _dtype_code(w), d_out, d_in, _ptr(q_out),
                                       _ptr(scales_out), _stream(w, stream)))
 
 
 def bd_apply_q8(x, wq, wscales, signs_bank, scales_bank, p, n_users, user_ids, y, workspace,
                 stream=None) -> int:
-    T, d_in = x.shape
-    d_out = wq.shape[0]
+    T, d_in, d_out = _apply_args(x, wq, signs_bank, scales_bank, p, n_users, user_ids, y,
+                                 workspace, wdtypes=(torch.int8,))
+    _dev(wscales, "wscales", (torch.float32,), (d_out,), x.device)
     return int(lib().bd_apply_q8(_ptr(x), _dtype_code(x), T, d_in, _ptr(wq), _ptr(wscales), d_out,
                                  _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p),
                                  int(n_users), _ptr(user_ids), _ptr(y), _dtype_code(y),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _ptr(workspace), _nbytes(workspace),
                                  _stream(x, stream)))
 
 

@@ -29,6 +29,7 @@ const char* bd_status_string(bd_status s) {
         case BD_ERR_DEVICE: return "HIP error";
         case BD_ERR_NONFINITE: return "non-finite delta";
         case BD_ERR_USER_ID: return "user id out of range";
+        case BD_ERR_BATCH: return "prepared batch encoded for another scale mode";
     }
     return "unknown status";
 }
@@ -150,10 +151,10 @@ bd_status bd_base_gemm(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
-bd_status bd_delta_apply(void* batch, const void* x, bd_dtype x_dtype, int64_t T,
-                         int64_t d_in, int32_t n_users, int64_t d_out, const uint64_t* signs_bank,
-                         const void* scales_bank, const bd_compress_params* p, float* y,
-                         void* stream) {
+bd_status bd_delta_apply(void* batch, size_t batch_bytes, const void* x, bd_dtype x_dtype,
+                         int64_t T, int64_t d_in, int32_t n_users, int64_t d_out,
+                         const uint64_t* signs_bank, const void* scales_bank,
+                         const bd_compress_params* p, float* y, void* stream) {
     BatchPlan bp;
     DeltaPlan dp;
     bd_status st = make_batch_plan(T, n_users, d_in, x_dtype, &bp);
@@ -161,6 +162,7 @@ bd_status bd_delta_apply(void* batch, const void* x, bd_dtype x_dtype, int64_t T
     st = make_delta_plan(p, bp, d_out, &dp);
     if (st != BD_OK) return st;
     if (!batch || !aligned(batch, kAlign)) return BD_ERR_INVALID_ARG;
+    if (batch_bytes < bp.total) return BD_ERR_WORKSPACE;
     if (T == 0) return BD_OK;
     if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return BD_ERR_INVALID_ARG;
     if (n_users > 0 && (!signs_bank || !scales_bank || !aligned(signs_bank, 16) ||
@@ -168,6 +170,113 @@ bd_status bd_delta_apply(void* batch, const void* x, bd_dtype x_dtype, int64_t T
         return BD_ERR_INVALID_ARG;
     hipError_t e = launch_delta(bp, dp, (char*)batch, x, signs_bank, scales_bank, y,
                                 (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_batch_encode(void* batch, size_t batch_bytes, const void* x, bd_dtype x_dtype,
+                          int64_t T, int64_t d_in, int32_t n_users, const void* scales_bank,
+                          const bd_compress_params* p, void* stream) {
+    if (x_dtype != BD_BF16) return BD_ERR_DTYPE;
+    BatchPlan bp;
+    DeltaPlan dp;
+    bd_status st = make_batch_plan(T, n_users, d_in, x_dtype, &bp);
+    if (st != BD_OK) return st;
+    st = make_delta_plan(p, bp, 1, &dp);
+    if (st != BD_OK) return st;
+    if (!batch || !aligned(batch, kAlign)) return BD_ERR_INVALID_ARG;
+    if (batch_bytes < bp.total) return BD_ERR_WORKSPACE;
+    if (T == 0) return BD_OK;
+    if (!x || !aligned(x, 16)) return BD_ERR_INVALID_ARG;
+    if (p->mode == BD_SCALE_COL && n_users > 0 && (!scales_bank || !aligned(scales_bank, 16)))
+        return BD_ERR_INVALID_ARG;
+    hipError_t e = launch_tile_encode(bp, dp, (char*)batch, x, scales_bank, (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_delta_apply_encoded(void* batch, size_t batch_bytes, bd_dtype x_dtype, int64_t T,
+                                 int64_t d_in, int32_t n_users, int64_t d_out,
+                                 const uint64_t* signs_bank, const void* scales_bank,
+                                 const bd_compress_params* p, float* y, void* stream) {
+    if (x_dtype != BD_BF16) return BD_ERR_DTYPE;
+    BatchPlan bp;
+    DeltaPlan dp;
+    bd_status st = make_batch_plan(T, n_users, d_in, x_dtype, &bp);
+    if (st != BD_OK) return st;
+    st = make_delta_plan(p, bp, d_out, &dp);
+    if (st != BD_OK) return st;
+    if (!batch || !aligned(batch, kAlign)) return BD_ERR_INVALID_ARG;
+    if (batch_bytes < bp.total) return BD_ERR_WORKSPACE;
+    if (T == 0) return BD_OK;
+    if (!y || !aligned(y, 16)) return BD_ERR_INVALID_ARG;
+    if (n_users > 0 && (!signs_bank || !scales_bank || !aligned(signs_bank, 16) ||
+                        !aligned(scales_bank, 16)))
+        return BD_ERR_INVALID_ARG;
+    hipError_t e = launch_delta6_encoded(bp, dp, (char*)batch, signs_bank, scales_bank, y,
+                                         (hipStream_t)stream);
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_base_gemm_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                         int32_t n_mats, const void* const* w_bases, const int64_t* d_outs,
+                         float* const* ys, void* stream) {
+    if (!valid_wdtype(x_dtype)) return BD_ERR_DTYPE;
+    if (T < 0 || n_mats < 1 || n_mats > kMaxMats || !w_bases || !d_outs || !ys)
+        return BD_ERR_INVALID_ARG;
+    if (d_in <= 0 || d_in % 64 != 0) return BD_ERR_SHAPE;
+    for (int i = 0; i < n_mats; ++i) {
+        if (d_outs[i] <= 0) return BD_ERR_SHAPE;
+        if (x_dtype == BD_BF16 && (d_outs[i] * d_in * 2 >= ((int64_t)1 << 31) ||
+                                   T * d_in * 2 >= ((int64_t)1 << 31)))
+            return BD_ERR_UNSUPPORTED;  // 32-bit buffer offsets
+    }
+    if (T == 0) return BD_OK;
+    if (!x || !aligned(x, 16)) return BD_ERR_INVALID_ARG;
+    for (int i = 0; i < n_mats; ++i)
+        if (!w_bases[i] || !ys[i] || !aligned(w_bases[i], 16) || !aligned(ys[i], 16))
+            return BD_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    bool tiled = x_dtype == BD_BF16;
+    for (int i = 0; i < n_mats; ++i) tiled = tiled && gemm_path_supported(T, d_in, d_outs[i]);
+    hipError_t e = hipSuccess;
+    if (tiled) {
+        GemmMatArg m[kMaxMats];
+        for (int i = 0; i < n_mats; ++i) m[i] = GemmMatArg{w_bases[i], ys[i], d_outs[i]};
+        e = launch_gemm_set(x, T, d_in, m, n_mats, s);
+    } else {
+        for (int i = 0; i < n_mats && e == hipSuccess; ++i)
+            e = launch_base_gemm(x, x_dtype, T, d_in, w_bases[i], d_outs[i], ys[i], s);
+    }
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+bd_status bd_delta_apply_encoded_n(void* batch, size_t batch_bytes, bd_dtype x_dtype, int64_t T,
+                                   int64_t d_in, int32_t n_users, int32_t n_mats,
+                                   const int64_t* d_outs, const uint64_t* const* signs_banks,
+                                   const void* const* scales_banks, const bd_compress_params* p,
+                                   float* const* ys, void* stream) {
+    if (x_dtype != BD_BF16) return BD_ERR_DTYPE;
+    if (n_mats < 1 || n_mats > kMaxMats || !d_outs || !signs_banks || !scales_banks || !ys)
+        return BD_ERR_INVALID_ARG;
+    BatchPlan bp;
+    bd_status st = make_batch_plan(T, n_users, d_in, x_dtype, &bp);
+    if (st != BD_OK) return st;
+    DeltaPlan dp;
+    DeltaMatArg m[kMaxMats];
+    for (int i = 0; i < n_mats; ++i) {
+        st = make_delta_plan(p, bp, d_outs[i], &dp);
+        if (st != BD_OK) return st;
+        m[i] = DeltaMatArg{signs_banks[i], scales_banks[i], ys[i], d_outs[i]};
+    }
+    if (!batch || !aligned(batch, kAlign)) return BD_ERR_INVALID_ARG;
+    if (batch_bytes < bp.total) return BD_ERR_WORKSPACE;
+    if (T == 0) return BD_OK;
+    for (int i = 0; i < n_mats; ++i) {
+        if (!ys[i] || !aligned(ys[i], 16)) return BD_ERR_INVALID_ARG;
+        if (n_users > 0 && (!signs_banks[i] || !scales_banks[i] || !aligned(signs_banks[i], 16) ||
+                            !aligned(scales_banks[i], 16)))
+            return BD_ERR_INVALID_ARG;
+    }
+    hipError_t e = launch_delta6_set(bp, dp, (char*)batch, m, n_mats, (hipStream_t)stream);
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
@@ -304,6 +413,7 @@ bd_status bd_device_status(const void* workspace, void* stream) {
     if (e != hipSuccess) return BD_ERR_DEVICE;
     if (word & ST_NONFINITE) return BD_ERR_NONFINITE;
     if (word & ST_USER_ID) return BD_ERR_USER_ID;
+    if (word & ST_ENCODING) return BD_ERR_BATCH;
     return BD_OK;
 }
 

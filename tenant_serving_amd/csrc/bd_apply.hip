@@ -59,7 +59,10 @@ k_group(const int32_t* __restrict__ ids, int T, int U, int P, int32_t* __restric
     }
     if (tid == 0) nvalid_sh = T;
     const int anybad = __syncthreads_or((int)badid);
-    if (tid == 0) meta[0] = anybad ? ST_USER_ID : 0u;  // the status word is owned by this kernel
+    if (tid == 0) {  // the status word is owned by this kernel; no tokens are encoded yet
+        meta[0] = anybad ? ST_USER_ID : 0u;
+        meta[kEncTagWord] = 0u;
+    }
     for (int k = 2; k <= P; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = tid; i < P; i += kGroupThreads) {
@@ -177,6 +180,7 @@ k_group_wave(const int32_t* __restrict__ ids, int T, int U, int32_t* __restrict_
     const bool anybad = __ballot(bad) != 0ull;
     if (l == 0) {
         meta[0] = anybad ? ST_USER_ID : 0u;
+        meta[kEncTagWord] = 0u;
         meta[1] = (uint32_t)total;
         meta[2] = (uint32_t)nv;
     }
@@ -406,6 +410,8 @@ bd_status make_batch_plan(int64_t T, int32_t U, int64_t d_in, int xdtype, BatchP
         q.nunit = 2 * ((d_in + 1023) / 1024);  // even: the delta steps take two units
         q.off_tiles = off;
         off += align_up(sizeof(int32_t) * ((size_t)q.ntiles + 1));
+        q.off_torder = off;
+        off += align_up(sizeof(int32_t) * (size_t)q.ntiles);
         q.off_tmeta = off;
         off += align_up(sizeof(int32_t) * kTileMetaInts * (size_t)q.ntiles);
         q.off_enc = off;

@@ -78,9 +78,17 @@ __device__ __forceinline__ f32x4 mfma_f6f4(i32x6 a, u32x4 b, f32x4 c, uint32_t s
 // length is a short serial recurrence over the items (scalar, 64 per round); the
 // tile starts are then written by the items' lanes.  tiles[t] = first position of
 // tile t, tiles[ntiles] = number of valid positions, meta[3] = ntiles.
+// The delta kernel's cost of a tile grows with its number of distinct users (one
+// product pass and one bank stream per user), so the tiles are also listed by that
+// number, largest first (torder, a counting sort, stable within a count): the grid
+// starts the longest blocks first and the short ones fill the end.
+constexpr int kMaxTilesLds = 2 * (kMaxGroupT / 16) + 1;
 __global__ void __launch_bounds__(64)
-k_tile_plan(const int4* __restrict__ items, uint32_t* __restrict__ meta, int32_t* __restrict__ tiles,
-            int maxt) {
+k_tile_plan(const int4* __restrict__ items, const int32_t* __restrict__ suser,
+            uint32_t* __restrict__ meta, int32_t* __restrict__ tiles,
+            int32_t* __restrict__ torder, int maxt) {
+    __shared__ int32_t st[kMaxTilesLds + 1];
+    __shared__ uint8_t snu[kMaxTilesLds];
     const int lane = threadIdx.x;
     const int nit = (int)meta[1];
     int cl = 0, nt = 0;  // open tile length, tiles started (uniform)
@@ -91,25 +99,56 @@ k_tile_plan(const int4* __restrict__ items, uint32_t* __restrict__ meta, int32_t
         for (int k = 0; k < m; ++k) {
             const int c = __builtin_amdgcn_readlane(it.z, k);
             const int c0 = c > 16 ? 16 : c;
-            const bool st = cl == 0 || cl + c0 > 16;
-            smask |= (uint64_t)st << k;
-            cl = c > 16 ? c - 16 : (st ? c : cl + c);
+            const bool stt = cl == 0 || cl + c0 > 16;
+            smask |= (uint64_t)stt << k;
+            cl = c > 16 ? c - 16 : (stt ? c : cl + c);
         }
-        const bool st = (smask >> lane) & 1ull;
+        const bool stt = (smask >> lane) & 1ull;
         const bool big = lane < m && it.z > 16;
         const uint64_t bmask = __ballot(big);
         const uint64_t below = (1ull << lane) - 1ull;
         const int idx = nt + __popcll(smask & below) + __popcll(bmask & below);
         if (lane < m) {
-            if (st && idx < maxt) tiles[idx] = it.y;
-            if (big && idx + (int)st < maxt) tiles[idx + (int)st] = it.y + 16;
+            if (stt && idx < maxt) {
+                tiles[idx] = it.y;
+                st[idx] = it.y;
+            }
+            if (big && idx + (int)stt < maxt) {
+                tiles[idx + (int)stt] = it.y + 16;
+                st[idx + (int)stt] = it.y + 16;
+            }
         }
         nt += __popcll(smask) + __popcll(bmask);
     }
     nt = nt < maxt ? nt : maxt;
+    const int nv = (int)meta[2];
     if (lane == 0) {
-        tiles[nt] = (int)meta[2];
+        tiles[nt] = nv;
+        st[nt] = nv;
         meta[3] = (uint32_t)nt;
+    }
+    __syncthreads();
+    // distinct users of each tile: user changes over its (sorted) positions
+    for (int t = lane; t < nt; t += 64) {
+        const int a = st[t], e = st[t + 1];
+        int cnt = 0, prev = -1;
+        for (int q = a; q < e; ++q) {
+            const int u = suser[q];
+            cnt += u != prev;
+            prev = u;
+        }
+        snu[t] = (uint8_t)cnt;
+    }
+    __syncthreads();
+    int pos = 0;
+    for (int v = 16; v >= 0; --v) {  // (a tile holds 1..16 positions; 0 keeps every tile ranked)
+        for (int b = 0; b < nt; b += 64) {
+            const int t = b + lane;
+            const bool hit = t < nt && snu[t] == v;
+            const uint64_t mk = __ballot(hit);
+            if (hit) torder[pos + __popcll(mk & ((1ull << lane) - 1ull))] = t;
+            pos += __popcll(mk);
+        }
     }
 }
 
@@ -123,21 +162,26 @@ k_tile_plan(const int4* __restrict__ items, uint32_t* __restrict__ meta, int32_t
 // dword 0 (hi) and dword 1 (lo).
 template <bool GRP, bool COL>
 __global__ void __launch_bounds__(256)
-k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
+k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int U, int64_t d_in,
               const int32_t* __restrict__ perm, const int32_t* __restrict__ suser,
-              const uint32_t* __restrict__ meta, const int32_t* __restrict__ tiles,
+              const uint32_t* __restrict__ meta_r, const int32_t* __restrict__ tiles,
               const void* __restrict__ scales, int sdtype, int64_t per_user,
-              int32_t* __restrict__ tmeta, char* __restrict__ enc) {
+              int32_t* __restrict__ tmeta, char* __restrict__ enc, uint32_t* __restrict__ meta_w) {
     const int t = blockIdx.x, u = blockIdx.y, nunit = gridDim.y;
     const int lane = threadIdx.x & 63;
     const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15, G = lane >> 4;
-    const int ntv = (int)meta[3];
+    const int ntv = (int)meta_r[3];
     if (t >= ntv) return;  // uniform: no such tile in this batch
+    if (t == 0 && u == 0 && threadIdx.x == 0) meta_w[kEncTagWord] = enc_tag(GRP, COL);
     const int ts = tiles[t], tl = tiles[t + 1] - ts;  // start, length
     const int p = ts + m;
-    const int tok = m < tl ? perm[p] : -1;
-    const int usr = m < tl ? suser[p] : -1;
+    const int tok0 = m < tl ? perm[p] : -1;
+    const int usr0 = m < tl ? suser[p] : -1;
+    // (a batch prepared for other sizes: such tokens are encoded as absent)
+    const bool okp = tok0 >= 0 && tok0 < T && usr0 >= 0 && usr0 < U;
+    const int tok = okp ? tok0 : -1;
+    const int usr = okp ? usr0 : -1;
     if (u == 0 && q == 0) {
         // tile meta: tokens, their users, the distinct users in order, their number
         int32_t* tm = tmeta + (size_t)t * kTileMetaInts;
@@ -216,33 +260,87 @@ k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
 }
 
 // ------------------------------------------------------------ delta products
-// Block (128 RT output rows, one tile), 8 waves of RT row tiles of 16 rows.  The
-// work is a sequence of slots: step by step (two 512-column units, 2s and 2s + 1),
-// user by user of the tile, two slots per user: its sign rows' 64 bytes of unit 2s
-// and then of unit 2s + 1, so the two halves of every 128-byte line are read by
-// consecutive loads of a wave (a row's next bytes come RT loads later).  Each wave
-// keeps the loads of its next kRing slots in flight in a ring of registers: a slot's
-// sign words are expanded first and only then reloaded, in place, with the slot
-// kRing ahead (its scales likewise after their last use), so no register copy on a
-// loop edge waits for a load in flight.  A step's encoded tokens (26 KB) come into
-// LDS buffer s % 3, copied two steps ahead and shared by the 8 waves; the opening of
-// step s waits until no more loads are in flight than were issued after that copy.
-// Each slot reads its unit's operands from LDS (13 KB per wave and slot, read while
-// the sign words are expanded).  Steps hold an even number of slots and kRing is
-// even, so the unit of the slot at ring position r is r & 1.
+// Block (16 kWaves RT output rows of one matrix of the set, one tile), kWaves waves of
+// RT row tiles of 16 rows.  The work is a sequence of slots: step by step (two
+// 512-column units, 2s and 2s + 1), user by user of the tile, two slots per user: its
+// sign rows' 64 bytes of unit 2s and then of unit 2s + 1, so the two halves of every
+// 128-byte line are read by consecutive loads of a wave (a row's next bytes come RT
+// loads later).  Each wave keeps the loads of its next kRing slots in flight in a ring
+// of registers: a slot's sign words are expanded first and only then reloaded, in
+// place, with the slot kRing ahead (its scales likewise after their last use), so no
+// register copy on a loop edge waits for a load in flight.  A step's encoded tokens
+// (26 KB) come into LDS buffer s % 3, copied two steps ahead and shared by the block's
+// waves; the opening of step s waits until no more loads are in flight than were
+// issued after that copy.  Each slot reads its unit's operands from LDS (13 KB per
+// wave and slot, read while the sign words are expanded).  Steps hold an even number
+// of slots and kRing is even, so the unit of the slot at ring position r is r & 1.
 // MFMA: A = the tile's 16 tokens (fp6 hi and lo; tokens of other users take block
 // code 0, i.e. scale 2^-127), B = 16 sign rows (fp4 +-1); lane (j, g) of D holds
 // tokens 4 g .. 4 g + 3 of output row j of the row tile.
+// Grid: one block per (tile rank, row block), tile ranks in the order of k_tile_plan
+// (most users first).  Block b runs on XCD b % 8 and takes, within its XCD's sequence,
+// all of that XCD's row blocks of one tile rank before the next rank: consecutive
+// tiles of one hot user (adjacent ranks) then re-read its sign rows from that XCD's L2.
 constexpr int kNBuf = 3;                       // LDS buffers of step operands
 constexpr int kStepBytes = 2 * kEncUnitBytes;  // two units
-constexpr int kWaves = 4;  // (two blocks per CU: one block's start overlaps the other's work)
+constexpr int kWaves = 4;  // 64 RT rows per block of 256 threads; two blocks per CU
+
+// Up to kMaxMats matrices that read the same encoded batch (q, k and v; gate and up),
+// their row blocks back to back: matrix m owns row blocks [rb_begin[m], rb_begin[m + 1]).
+struct DeltaMats {
+    const uint64_t* signs[kMaxMats];
+    const void* scales[kMaxMats];
+    float* y[kMaxMats];
+    int64_t d_out[kMaxMats];
+    int64_t per_user[kMaxMats];
+    int rb_begin[kMaxMats + 1];
+    int n;
+};
+
+// Values every lane of a wave holds alike, pinned to scalar registers: derived from a
+// memory load or a select, the compiler cannot prove them uniform and would wrap every
+// buffer load whose descriptor uses them in a loop over the lanes' distinct values.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+    const uint64_t u = (uint64_t)v;
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                     (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+}
+template <typename P>
+__device__ __forceinline__ P* uni_ptr(P* p) {
+    return (P*)(uintptr_t)uni64((int64_t)(uintptr_t)p);
+}
+
+// Entry m of a kernel-argument array, chosen with scalar selects written out (a plain
+// select chain is turned into an indexed load from a private copy of the arguments).
+template <int K>
+__device__ __forceinline__ uint64_t s_sel64(int m, uint64_t a, uint64_t b) {  // m == K ? a : b
+    uint64_t r;
+    asm volatile("s_cmp_eq_u32 %1, %4\n\ts_cselect_b64 %0, %2, %3"
+                 : "=s"(r) : "s"(m), "s"(a), "s"(b), "i"(K) : "scc");
+    return r;
+}
+template <typename T>
+__device__ __forceinline__ T pick_mat(const T (&a)[kMaxMats], int m) {
+    static_assert(sizeof(T) == 8 && kMaxMats == 4, "64-bit entries, four matrices");
+    uint64_t v = __builtin_bit_cast(uint64_t, a[0]);
+    v = s_sel64<1>(m, __builtin_bit_cast(uint64_t, a[1]), v);
+    v = s_sel64<2>(m, __builtin_bit_cast(uint64_t, a[2]), v);
+    v = s_sel64<3>(m, __builtin_bit_cast(uint64_t, a[3]), v);
+    return __builtin_bit_cast(T, v);
+}
+__device__ __forceinline__ int pick_rb(const int (&a)[kMaxMats + 1], int m) {
+    uint64_t v = (uint64_t)(uint32_t)a[0];
+    v = s_sel64<1>(m, (uint64_t)(uint32_t)a[1], v);
+    v = s_sel64<2>(m, (uint64_t)(uint32_t)a[2], v);
+    return (int)(uint32_t)s_sel64<3>(m, (uint64_t)(uint32_t)a[3], v);
+}
 
 template <int MODE, bool SF16, int RT>
 __global__ void __launch_bounds__(64 * kWaves)
-k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, int64_t per_user,
-         int bsh, const int32_t* __restrict__ tmeta, const char* __restrict__ enc,
-         const uint32_t* __restrict__ meta, float* __restrict__ y, int64_t d_in, int64_t d_out,
-         int nunit) {
+k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
+         const int32_t* __restrict__ torder, const char* __restrict__ enc,
+         uint32_t* __restrict__ meta, int64_t d_in, int nunit, int T, int U) {
     // bsh: log2 of the group size / 128 (GROUP sizes are powers of two >= 128);
     // nunit: even (units past d_in are encoded as zeros)
     constexpr bool GRP = MODE == BD_SCALE_GROUP;
@@ -253,20 +351,55 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
     constexpr int L = RT;
     constexpr int LMAX = RT + (GRP ? 1 : 0);
     constexpr uint32_t SB = SF16 ? 2 : 4;                            // bytes per scale
-    static_assert((kRing - 1) * LMAX <= 63, "vmcnt range");
+    static_assert((kRing - 1) * LMAX <= 63 && kRing <= 16, "vmcnt range");
     static_assert(kRing % 2 == 0, "the unit of a ring position is its parity");
     __shared__ __attribute__((aligned(16))) char sbuf[kNBuf * kStepBytes];
     __shared__ int32_t smeta[kTileMetaInts];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, G = lane >> 4;
-    const int64_t rw0 = (int64_t)blockIdx.x * (16 * kWaves * RT) + 16 * RT * wv;  // the wave's first row
-    const int tile = blockIdx.y;
-    if (tile >= (int)meta[3]) return;  // uniform: no such tile in this batch
+    // block -> (tile rank, row block of the matrix set)
+    const int nrb = dm.rb_begin[kMaxMats];  // (entries past the set repeat the total)
+    const int nrb8 = (nrb + 7) >> 3;
+    const int bk = (int)blockIdx.x >> 3;
+    const int rb = (bk % nrb8) * 8 + ((int)blockIdx.x & 7);
+    const int trank = bk / nrb8;
+    if (rb >= nrb || trank >= (int)meta[3]) return;  // uniform: no such row block or tile
+    // The tile lists and operands exist only once the batch is encoded for this mode
+    // (bd_batch_prepare clears the tag): nothing of them is read before this check.
+    if (meta[kEncTagWord] != enc_tag(GRP, COL)) {
+        if (threadIdx.x == 0) atomicOr(meta, ST_ENCODING);
+        return;
+    }
+    const int tile = uni(torder[trank]);
+    int mi = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxMats; ++j) mi += (j < dm.n && rb >= dm.rb_begin[j]) ? 1 : 0;
+    mi = uni(mi);
+    const uint64_t* const signs = pick_mat(dm.signs, mi);
+    const void* const scales = pick_mat(dm.scales, mi);
+    float* const y = pick_mat(dm.y, mi);
+    const int64_t d_out = pick_mat(dm.d_out, mi);
+    const int64_t per_user = pick_mat(dm.per_user, mi);
+    const int rbl = rb - pick_rb(dm.rb_begin, mi);
+    const int64_t rw0 = (int64_t)rbl * (16 * kWaves * RT) + 16 * RT * wv;  // the wave's first row
     // (wave 0: a uniform branch, so the values around it stay scalar)
     if (wv == 0) smeta[lane] = tmeta[(size_t)tile * kTileMetaInts + lane];
     __syncthreads();
     const int nus = __builtin_amdgcn_readfirstlane(smeta[48]);  // >= 1
+    {
+        // the tile's tokens, their users and its user list must fit this call's T and
+        // n_users (a batch prepared for other sizes): checked before any becomes an address
+        const int v = smeta[lane];
+        const bool bad = lane < 16 ? v < -1 || v >= T
+                         : lane < 32 ? v < -1 || v >= U
+                         : lane < 48 ? (lane - 32 < nus && (v < 0 || v >= U))
+                                     : lane == 48 && (v < 1 || v > 16);
+        if (__ballot(bad) != 0ull) {  // uniform
+            if (threadIdx.x == 0) atomicOr(meta, ST_ENCODING);
+            return;
+        }
+    }
     const int S = nunit / 2;                                    // steps
     const int total = (2 * S * nus + kRing - 1) / kRing * kRing;  // slots, padded past the end
 
@@ -289,12 +422,14 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
     uint32_t kmask, kone;  // operand constants in registers (gfx9 VOP3 takes no literal)
     asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
     asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
-    auto expand = [&](uint32_t wq) __attribute__((always_inline)) {
+    // (ko = kone, or 0 for the empty slots past the end: their words load as 0, so their
+    // operands are exact zeros and the products add nothing)
+    auto expand = [&](uint32_t wq, uint32_t ko) __attribute__((always_inline)) {
         u32x4 a;
-        a.x = ((wq << 3) & kmask) | kone;
-        a.y = ((wq << 2) & kmask) | kone;
-        a.z = ((wq << 1) & kmask) | kone;
-        a.w = (wq & kmask) | kone;
+        a.x = ((wq << 3) & kmask) | ko;
+        a.y = ((wq << 2) & kmask) | ko;
+        a.z = ((wq << 1) & kmask) | ko;
+        a.w = (wq & kmask) | ko;
         return a;
     };
     // the operands of step st into LDS buffer b (1 KB chunk i by wave i % 8)
@@ -405,14 +540,22 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                     if (after >= kRing - 1) {
                         BD_WAIT_VMCNT((kRing - 1) * L);
                     } else {
-                        switch (after) {
+                        switch (after) {  // (after < kRing - 1 <= 15)
                             case 0: BD_WAIT_VMCNT(0); break;
                             case 1: BD_WAIT_VMCNT(1 * L); break;
                             case 2: BD_WAIT_VMCNT(2 * L); break;
                             case 3: BD_WAIT_VMCNT(3 * L); break;
                             case 4: BD_WAIT_VMCNT(4 * L); break;
                             case 5: BD_WAIT_VMCNT(5 * L); break;
-                            default: BD_WAIT_VMCNT(6 * L); break;
+                            case 6: BD_WAIT_VMCNT(6 * L); break;
+                            case 7: BD_WAIT_VMCNT(7 * L); break;
+                            case 8: BD_WAIT_VMCNT(8 * L); break;
+                            case 9: BD_WAIT_VMCNT(9 * L); break;
+                            case 10: BD_WAIT_VMCNT(10 * L); break;
+                            case 11: BD_WAIT_VMCNT(11 * L); break;
+                            case 12: BD_WAIT_VMCNT(12 * L); break;
+                            case 13: BD_WAIT_VMCNT(13 * L); break;
+                            default: BD_WAIT_VMCNT(14 * L); break;
                         }
                     }
                 }
@@ -440,7 +583,7 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                 }
             }
             Slot& sl = ring[r];
-            const bool live = cs < S;  // uniform
+            const uint32_t konel = cs < S ? kone : 0u;  // uniform (scalar select)
             // this slot's unit operands (hi, lo per product, block codes), from LDS (also
             // for the empty slots past the end: no value then merges at a branch)
             i32x6 hi[4], lo[4];
@@ -457,7 +600,9 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                 }
                 const u32x4 cd = *(const u32x4*)(sb + 12 * 1024 + 16 * lane);
                 const int usr = __builtin_amdgcn_readlane(c_users, q >> 1);
-                const bool mine = c_tuser == usr;
+                // (an empty slot past the end may read a buffer never written: its block
+                // codes are forced to 0, a finite scale, so its zero operands add exactly 0)
+                const bool mine = cs < S && c_tuser == usr;
                 sh = mine ? cd.x : 0u;
                 sl_ = mine ? cd.y : 0u;
             }
@@ -477,17 +622,19 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
                     auto s16b = __builtin_amdgcn_permlane16_swap(s32a[1], s32b[1], false, false);
                     wq = u32x4{s16a[0], s16a[1], s16b[0], s16b[1]};
                 }
-                bx[t][0] = expand(wq.x);
-                bx[t][1] = expand(wq.y);
-                bx[t][2] = expand(wq.z);
-                bx[t][3] = expand(wq.w);
+                bx[t][0] = expand(wq.x, konel);
+                bx[t][1] = expand(wq.y, konel);
+                bx[t][2] = expand(wq.z, konel);
+                bx[t][3] = expand(wq.w, konel);
                 asm volatile("" ::"v"(bx[t][0]), "v"(bx[t][1]), "v"(bx[t][2]), "v"(bx[t][3]));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < RT; ++t) issue_w(sl, t);  // the slot kRing ahead, in place
             __builtin_amdgcn_sched_barrier(0);
-            if (live) {
+            // (no branch around the products: the accumulators then never merge at a
+            // branch, which kept them moving between register files every slot)
+            {
 #pragma unroll
                 for (int t = 0; t < RT; ++t) {
                     const u32x4 b0 = bx[t][0], b1 = bx[t][1], b2 = bx[t][2], b3 = bx[t][3];
@@ -581,51 +728,369 @@ k_delta6(const uint64_t* __restrict__ signs, const void* __restrict__ scales, in
     }
 }
 
+// ------------------------------------------------ delta products, unit per wave
+// The products of one launch's units [u0, u0 + W) for MATRIX, ROW and COL scales.
+// Block = W waves (one 512-column unit each) over one tile and NCH chunks of 16 W
+// rows.  A wave loads its unit's encoded tokens once (13 KB: the fp6 hi / lo
+// operands of the four products and their block codes) and keeps them in
+// registers; it then streams, chunk by chunk and row tile by row tile, every user
+// of the tile's 16 sign rows x 64 bytes of its unit through a ring of D loads kept
+// in flight (16 bytes per lane, the B operand of the 4 products as they stand),
+// runs the products (hi and lo into two accumulators; other users' tokens carry
+// block code 0, scale 2^-127) and, at the end of a row tile, writes its partial
+// (that unit's share of the 16 x 16 outputs) to LDS.  One barrier per chunk: wave w
+// then sums row tile w of the chunk over the W units in unit order (partials double
+// buffered, so the next chunk's writes never wait for the sums) and keeps it.  At
+// the end of the block each wave scales its row tiles per token (MATRIX / ROW: the
+// scale of the token's user; COL: in the tokens) and adds them to y, one no-return
+// atomic per element.  Launches of one call cover the units in order, so every y
+// element gets its addends (the base product, then one per launch) in a fixed
+// order: the result repeats bit for bit.
+constexpr int kMaxW7 = 8;   // units (waves) per launch
+constexpr int kRing7 = 12;  // sign loads in flight per wave
+
+template <int MODE, bool SF16, int NCH>
+__global__ void __launch_bounds__(64 * kMaxW7)
+k_delta7(const DeltaMats dm, const int32_t* __restrict__ tmeta,
+         const int32_t* __restrict__ torder, const char* __restrict__ enc,
+         uint32_t* __restrict__ meta, int64_t d_in, int nunit, int u0, int units, int T,
+         int U) {
+    // units: the units of d_in (ceil(d_in / 512)); every launch has the same W waves, and
+    // a wave whose unit is past them (the last launch) adds zeros
+    static_assert(MODE != BD_SCALE_GROUP, "GROUP scales take k_delta6");
+    constexpr int D = kRing7;
+    __shared__ __attribute__((aligned(16))) f32x4 part[2][kMaxW7][kMaxW7][64];
+    __shared__ int32_t smeta[kTileMetaInts];
+    const int lane = threadIdx.x & 63;
+    const int wv = uni((int)(threadIdx.x >> 6));
+    const int W = uni((int)(blockDim.x >> 6));
+    const int n = lane & 15, G = lane >> 4;
+    // block -> (tile rank, row block of the matrix set), as k_delta6
+    const int nrb = dm.rb_begin[kMaxMats];  // (entries past the set repeat the total)
+    const int nrb8 = (nrb + 7) >> 3;
+    const int bk = (int)blockIdx.x >> 3;
+    const int rb = (bk % nrb8) * 8 + ((int)blockIdx.x & 7);
+    const int trank = bk / nrb8;
+    if (rb >= nrb || trank >= (int)meta[3]) return;  // uniform
+    if (meta[kEncTagWord] != enc_tag(false, MODE == BD_SCALE_COL)) {
+        if (threadIdx.x == 0) atomicOr(meta, ST_ENCODING);
+        return;
+    }
+    const int tile = uni(torder[trank]);
+    int mi = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxMats; ++j) mi += (j < dm.n && rb >= dm.rb_begin[j]) ? 1 : 0;
+    mi = uni(mi);
+    const uint64_t* const signs = pick_mat(dm.signs, mi);
+    const void* const scales = pick_mat(dm.scales, mi);
+    float* const y = pick_mat(dm.y, mi);
+    const int64_t d_out = pick_mat(dm.d_out, mi);
+    const int64_t per_user = pick_mat(dm.per_user, mi);
+    const int rbl = rb - pick_rb(dm.rb_begin, mi);
+    const int64_t row0 = (int64_t)rbl * (16 * W * NCH);  // the block's first row
+
+    if (wv == 0) smeta[lane] = tmeta[(size_t)tile * kTileMetaInts + lane];
+    __syncthreads();
+    const int nus = uni(smeta[48]);
+    {
+        const int v = smeta[lane];
+        const bool bad = lane < 16 ? v < -1 || v >= T
+                         : lane < 32 ? v < -1 || v >= U
+                         : lane < 48 ? (lane - 32 < nus && (v < 0 || v >= U))
+                                     : lane == 48 && (v < 1 || v > 16);
+        if (__ballot(bad) != 0ull) {  // uniform
+            if (threadIdx.x == 0) atomicOr(meta, ST_ENCODING);
+            return;
+        }
+    }
+    // this wave's unit: its operands into registers (the oldest loads of the wave)
+    const int u = u0 + wv;
+    const bool uact = u < units;  // uniform
+    const __amdgpu_buffer_rsrc_t er = make_rsrc(
+        enc + ((size_t)tile * nunit + (uact ? u : 0)) * kEncUnitBytes,
+        uact ? (uint64_t)kEncUnitBytes : 0ull);  // (no unit: every load reads 0)
+    i32x6 hi[4], lo[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const u32x4 c0 = buf_load16(er, (3 * p + 0) * 1024 + 16 * lane);
+        const u32x4 c1 = buf_load16(er, (3 * p + 1) * 1024 + 16 * lane);
+        const u32x4 c2 = buf_load16(er, (3 * p + 2) * 1024 + 16 * lane);
+        hi[p] = i32x6{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y};
+        lo[p] = i32x6{(int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
+    }
+    const u32x4 cd = buf_load16(er, 12 * 1024 + 16 * lane);
+
+    const uint32_t bank_row = (uint32_t)(d_in / 8);
+    const uint64_t user_bytes = (uint64_t)d_out * bank_row;
+    const int nrec_bits = user_bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)user_bytes;
+    const uint32_t lane_off = (uint32_t)n * bank_row + 64u * (uint32_t)u + 16u * (uint32_t)G;
+    // lane j < nus: base address of user j's bank (read back with readlane)
+    uint32_t ub_lo, ub_hi;
+    {
+        const uint64_t usr = n < nus ? (uint64_t)(uint32_t)smeta[32 + n] : 0ull;
+        const uint64_t ub = (uint64_t)(const char*)signs + usr * user_bytes;
+        ub_lo = (uint32_t)ub;
+        ub_hi = (uint32_t)(ub >> 32);
+    }
+    const int c_tuser = smeta[16 + n];  // A row n of the products: the user of token n
+    const int c_users = smeta[32 + n];  // lane j < nus: user j
+    uint32_t kmask, kone;
+    asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
+    asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
+
+    // slot s = ((chunk c) W + row tile r) nus + user j; row tile c W + r of the block
+    const int per_chunk = W * nus;
+    const int S = NCH * per_chunk;
+    int lj = 0, lr = 0;  // loading side: user, row tile (over the whole block)
+    auto issue = [&](int s) __attribute__((always_inline)) -> u32x4 {
+        const bool ok = s < S;  // uniform
+        const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ub_hi, lj) << 32) |
+                              (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ub_lo, lj);
+        const __amdgpu_buffer_rsrc_t br =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec_bits, 0x00020000);
+        const int64_t row = row0 + 16 * (int64_t)lr;
+        const uint32_t off = ok && uact && row < d_out ? lane_off + (uint32_t)row * bank_row : kOOB;
+        if (++lj == nus) {
+            lj = 0;
+            ++lr;
+        }
+        return buf_load16(br, off);
+    };
+    u32x4 ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        ring[i] = issue(i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 res[NCH];
+    int j = 0, r = 0, c = 0;  // consuming side: user, row tile in chunk, chunk
+    const int total = (S + D - 1) / D * D;
+    for (int s0 = 0; s0 < total; s0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            const int s = s0 + i;
+            BD_WAIT_VMCNT(D - 1);
+            const u32x4 wq = ring[i];
+            const uint32_t ko = s < S ? kone : 0u;  // past the end: zero operands
+            u32x4 bx[4];
+            bx[0] = u32x4{((wq.x << 3) & kmask) | ko, ((wq.x << 2) & kmask) | ko,
+                          ((wq.x << 1) & kmask) | ko, (wq.x & kmask) | ko};
+            bx[1] = u32x4{((wq.y << 3) & kmask) | ko, ((wq.y << 2) & kmask) | ko,
+                          ((wq.y << 1) & kmask) | ko, (wq.y & kmask) | ko};
+            bx[2] = u32x4{((wq.z << 3) & kmask) | ko, ((wq.z << 2) & kmask) | ko,
+                          ((wq.z << 1) & kmask) | ko, (wq.z & kmask) | ko};
+            bx[3] = u32x4{((wq.w << 3) & kmask) | ko, ((wq.w << 2) & kmask) | ko,
+                          ((wq.w << 1) & kmask) | ko, (wq.w & kmask) | ko};
+            asm volatile("" ::"v"(bx[0]), "v"(bx[1]), "v"(bx[2]), "v"(bx[3]));
+            __builtin_amdgcn_sched_barrier(0);
+            ring[i] = issue(s + D);  // in place, after the words are expanded
+            __builtin_amdgcn_sched_barrier(0);
+            const int usr = __builtin_amdgcn_readlane(c_users, j);
+            const bool mine = s < S && c_tuser == usr;
+            const uint32_t sh = mine ? cd.x : 0u, sl = mine ? cd.y : 0u;
+            acc = mfma_f6f4<0>(hi[0], bx[0], acc, sh);
+            acc2 = mfma_f6f4<0>(lo[0], bx[0], acc2, sl);
+            acc = mfma_f6f4<1>(hi[1], bx[1], acc, sh);
+            acc2 = mfma_f6f4<1>(lo[1], bx[1], acc2, sl);
+            acc = mfma_f6f4<2>(hi[2], bx[2], acc, sh);
+            acc2 = mfma_f6f4<2>(lo[2], bx[2], acc2, sl);
+            acc = mfma_f6f4<3>(hi[3], bx[3], acc, sh);
+            acc2 = mfma_f6f4<3>(lo[3], bx[3], acc2, sl);
+            if (s < S && ++j == nus) {  // uniform: the row tile is complete
+                j = 0;
+                part[c & 1][r][wv][lane] = acc + acc2;
+                acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (++r == W) {  // the chunk is complete: sum row tile wv over the units
+                    r = 0;
+                    // this wave's partial writes have landed in LDS; then a bare barrier
+                    // (a fence would also wait for the sign loads in flight)
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+                    asm volatile("s_barrier" ::: "memory");
+                    f32x4 v = part[c & 1][wv][0][lane];
+                    for (int q = 1; q < W; ++q) v += part[c & 1][wv][q][lane];
+#pragma unroll
+                    for (int cc = 0; cc < NCH; ++cc)
+                        if (cc == c) res[cc] = v;
+                    ++c;
+                }
+            }
+        }
+    }
+    // y[token][row] += the sums (-X S^T of the token's own user): MATRIX and ROW take
+    // that user's scale here, COL's are in the tokens
+    BD_WAIT_VMCNT(0);
+    int tok[4], tus[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        tok[e] = smeta[4 * G + e];
+        tus[e] = smeta[16 + 4 * G + e];
+    }
+    // every scale first (one round trip), then the adds
+    constexpr int NF = MODE == BD_SCALE_ROW ? NCH : 1;  // MATRIX: per user; ROW: per row too
+    float fs[NF][4];
+#pragma unroll
+    for (int cc = 0; cc < NF; ++cc) {
+        const int64_t o = row0 + 16 * (int64_t)(cc * W + wv) + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            fs[cc][e] = -1.f;
+            if ((MODE == BD_SCALE_MATRIX || MODE == BD_SCALE_ROW) && tok[e] >= 0 && o < d_out) {
+                const size_t i = (size_t)tus[e] * per_user + (MODE == BD_SCALE_ROW ? (size_t)o : 0);
+                fs[cc][e] = -(SF16 ? f16_to_f32(((const uint16_t*)scales)[i]) : ((const float*)scales)[i]);
+            }
+        }
+    }
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+        const int64_t o = row0 + 16 * (int64_t)(cc * W + wv) + n;
+        if (o < d_out) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (tok[e] >= 0)
+                    unsafeAtomicAdd(y + (int64_t)tok[e] * d_out + o,
+                                    fs[MODE == BD_SCALE_ROW ? cc : 0][e] * res[cc][e]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- host side
 hipError_t launch_tile_plan(const BatchPlan& bp, char* batch, hipStream_t s) {
     if (bp.xdtype != BD_BF16 || bp.T == 0) return hipSuccess;
     hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(64), 0, s, (const int4*)(batch + bp.off_items),
-                       (uint32_t*)(batch + bp.off_meta), (int32_t*)(batch + bp.off_tiles),
+                       (const int32_t*)(batch + bp.off_user), (uint32_t*)(batch + bp.off_meta),
+                       (int32_t*)(batch + bp.off_tiles), (int32_t*)(batch + bp.off_torder),
                        (int)bp.ntiles);
     return hipGetLastError();
 }
 
-hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, const void* x,
-                         const uint64_t* signs, const void* scales, float* y, hipStream_t s) {
-    const uint32_t* meta = (const uint32_t*)(batch + bp.off_meta);
+hipError_t launch_tile_encode(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
+                              const void* x, const void* scales, hipStream_t s) {
+    uint32_t* meta = (uint32_t*)(batch + bp.off_meta);
     const int32_t* perm = (const int32_t*)(batch + bp.off_perm);
     const int32_t* suser = (const int32_t*)(batch + bp.off_user);
     int32_t* tmeta = (int32_t*)(batch + bp.off_tmeta);
     char* enc = batch + bp.off_enc;
-    const int ntiles = (int)bp.ntiles, nunit = (int)bp.nunit;
-    const bool grp = dp.mode == BD_SCALE_GROUP, col = dp.mode == BD_SCALE_COL;
-    const dim3 ge((unsigned)ntiles, (unsigned)nunit);
+    const dim3 ge((unsigned)bp.ntiles, (unsigned)bp.nunit);
     const int32_t* tiles = (const int32_t*)(batch + bp.off_tiles);
 #define BD_ENC(G, C)                                                                           \
     hipLaunchKernelGGL((k_tile_encode<G, C>), ge, dim3(256), 0, s, (const uint16_t*)x, bp.T,   \
-                       bp.d_in, perm, suser, meta, tiles, scales, dp.sdtype, dp.per_user, tmeta, \
-                       enc)
-    if (grp) BD_ENC(true, false);
-    else if (col) BD_ENC(false, true);
+                       (int)bp.U, bp.d_in, perm, suser, meta, tiles, scales, dp.sdtype, dp.per_user, tmeta, \
+                       enc, meta)
+    if (dp.mode == BD_SCALE_GROUP) BD_ENC(true, false);
+    else if (dp.mode == BD_SCALE_COL) BD_ENC(false, true);
     else BD_ENC(false, false);
 #undef BD_ENC
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // row tiles per wave: two (256 rows per block: fewer copies of the step operands
-    // per sign byte; more do not fit the registers) when that still gives every CU a
-    // block of work at the typical tile count, else one
+    return hipGetLastError();
+}
+
+// Non-GROUP modes: unit-per-wave launches (k_delta7), the units of d_in split into
+// ceil(units / 8) launches of equal width, in unit order.
+static hipError_t launch_delta7_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
+                                    const DeltaMatArg* mats, int n, hipStream_t s) {
+    uint32_t* meta = (uint32_t*)(batch + bp.off_meta);
+    const int32_t* tmeta = (const int32_t*)(batch + bp.off_tmeta);
+    const int32_t* torder = (const int32_t*)(batch + bp.off_torder);
+    const char* enc = batch + bp.off_enc;
+    const int nunit = (int)bp.nunit;
+    const int units = (int)((bp.d_in + 511) / 512);  // units past d_in are zero operands
+    const int nl = (units + kMaxW7 - 1) / kMaxW7;
+    const int W = (units + nl - 1) / nl;
+    int64_t rows = 0;
+    for (int i = 0; i < n; ++i) rows += mats[i].d_out;
+    // chunks per block: as many as still leave about 512 blocks at the typical tile count
+    const int64_t ntyp = (bp.T + 15) / 16;
+    const int64_t chunks = (rows + 16 * W - 1) / (16 * W);
+    const int nch = chunks * ntyp >= 4 * 512 ? 4 : chunks * ntyp >= 2 * 512 ? 2 : 1;
+    const int64_t rows_rb = 16 * W * nch;
+    DeltaMats dm = {};
+    dm.n = n;
+    int rb = 0;
+    for (int i = 0; i < n; ++i) {
+        dm.signs[i] = mats[i].signs;
+        dm.scales[i] = mats[i].scales;
+        dm.y[i] = mats[i].y;
+        dm.d_out[i] = mats[i].d_out;
+        dm.per_user[i] = dp.mode == BD_SCALE_MATRIX ? 1
+                         : dp.mode == BD_SCALE_ROW ? mats[i].d_out
+                                                   : bp.d_in;
+        dm.rb_begin[i] = rb;
+        rb += (int)((mats[i].d_out + rows_rb - 1) / rows_rb);
+    }
+    for (int i = n; i <= kMaxMats; ++i) dm.rb_begin[i] = rb;
+    const int64_t nrb8 = (rb + 7) / 8;
+    const dim3 gd((unsigned)(nrb8 * 8 * bp.ntiles));
+    const bool f16 = dp.sdtype == BD_F16;
+    for (int l = 0; l < nl; ++l) {
+        const int u0 = l * W;  // (the last launch may hold fewer units: its extra waves add 0)
+#define BD_D7(MODE, F16, NCH)                                                                  \
+    hipLaunchKernelGGL((k_delta7<MODE, F16, NCH>), gd, dim3(64 * W), 0, s, dm, tmeta, torder,  \
+                       enc, meta, bp.d_in, nunit, u0, units, (int)bp.T, (int)bp.U)
+#define BD_D7N(MODE, F16)                                       \
+    do {                                                        \
+        if (nch == 4) BD_D7(MODE, F16, 4);                      \
+        else if (nch == 2) BD_D7(MODE, F16, 2);                 \
+        else BD_D7(MODE, F16, 1);                               \
+    } while (0)
+        switch (dp.mode) {
+            case BD_SCALE_MATRIX:
+                if (f16) BD_D7N(BD_SCALE_MATRIX, true); else BD_D7N(BD_SCALE_MATRIX, false);
+                break;
+            case BD_SCALE_ROW:
+                if (f16) BD_D7N(BD_SCALE_ROW, true); else BD_D7N(BD_SCALE_ROW, false);
+                break;
+            default: BD_D7N(BD_SCALE_COL, false); break;
+        }
+#undef BD_D7N
+#undef BD_D7
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_delta6_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
+                             const DeltaMatArg* mats, int n, hipStream_t s) {
+    if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
+    if (dp.mode != BD_SCALE_GROUP) return launch_delta7_set(bp, dp, batch, mats, n, s);
+    uint32_t* meta = (uint32_t*)(batch + bp.off_meta);
+    const int32_t* tmeta = (const int32_t*)(batch + bp.off_tmeta);
+    const int32_t* torder = (const int32_t*)(batch + bp.off_torder);
+    const char* enc = batch + bp.off_enc;
+    const int ntiles = (int)bp.ntiles, nunit = (int)bp.nunit;
+    const bool grp = dp.mode == BD_SCALE_GROUP;
+    int64_t rows = 0;
+    for (int i = 0; i < n; ++i) rows += mats[i].d_out;
+    // row tiles per wave: two (fewer copies of the step operands per sign byte; more do
+    // not fit the registers) when that still gives every CU blocks of work at the
+    // typical tile count, else one
     const int64_t ntyp = (bp.T + 15) / 16;  // tiles of a batch of small users, about
-    const int rt = ((dp.d_out + 32 * kWaves - 1) / (32 * kWaves)) * ntyp >= 512 ? 2 : 1;
-    // one tile per block (grid rows for the bound of tiles; blocks past the batch's
-    // tiles exit at once): every block has the same work, whatever the tile count
-    const int64_t rtiles = (dp.d_out + 16 * kWaves * rt - 1) / (16 * kWaves * rt);
-    const dim3 gd((unsigned)rtiles, (unsigned)ntiles);
+    const int rt = ((rows + 32 * kWaves - 1) / (32 * kWaves)) * ntyp >= 512 ? 2 : 1;
+    const int64_t rows_rb = 16 * kWaves * rt;
+    DeltaMats dm = {};
+    dm.n = n;
+    int rb = 0;
+    for (int i = 0; i < n; ++i) {
+        dm.signs[i] = mats[i].signs;
+        dm.scales[i] = mats[i].scales;
+        dm.y[i] = mats[i].y;
+        dm.d_out[i] = mats[i].d_out;
+        dm.per_user[i] = dp.mode == BD_SCALE_MATRIX ? 1
+                         : dp.mode == BD_SCALE_GROUP ? mats[i].d_out * (bp.d_in / dp.group)
+                         : dp.mode == BD_SCALE_ROW ? mats[i].d_out
+                                                   : bp.d_in;
+        dm.rb_begin[i] = rb;
+        rb += (int)((mats[i].d_out + rows_rb - 1) / rows_rb);
+    }
+    for (int i = n; i <= kMaxMats; ++i) dm.rb_begin[i] = rb;
+    const int64_t nrb8 = (rb + 7) / 8;
+    const dim3 gd((unsigned)(nrb8 * 8 * ntiles));
     int bsh = 0;
     while (grp && (128 << bsh) < dp.group) ++bsh;
 #define BD_D6(MODE, F16, RT)                                                                      \
-    hipLaunchKernelGGL((k_delta6<MODE, F16, RT>), gd, dim3(64 * kWaves), 0, s, signs, scales,     \
-                       dp.per_user, bsh, (const int32_t*)tmeta, (const char*)enc, meta, y,        \
-                       bp.d_in, dp.d_out, nunit)
+    hipLaunchKernelGGL((k_delta6<MODE, F16, RT>), gd, dim3(64 * kWaves), 0, s, dm, bsh, tmeta,    \
+                       torder, enc, meta, bp.d_in, nunit, (int)bp.T, (int)bp.U)
 #define BD_D6R2(MODE, F16)                             \
     do {                                               \
         if (rt == 2) BD_D6(MODE, F16, 2);              \
@@ -647,6 +1112,20 @@ hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, 
 #undef BD_D6R2
 #undef BD_D6
     return hipGetLastError();
+}
+
+hipError_t launch_delta6_encoded(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
+                                 const uint64_t* signs, const void* scales, float* y,
+                                 hipStream_t s) {
+    const DeltaMatArg m = {signs, scales, y, dp.d_out};
+    return launch_delta6_set(bp, dp, batch, &m, 1, s);
+}
+
+hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, const void* x,
+                         const uint64_t* signs, const void* scales, float* y, hipStream_t s) {
+    hipError_t err = launch_tile_encode(bp, dp, batch, x, scales, s);
+    if (err != hipSuccess) return err;
+    return launch_delta6_encoded(bp, dp, batch, signs, scales, y, s);
 }
 
 }  // namespace bd

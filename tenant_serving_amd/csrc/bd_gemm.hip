@@ -62,8 +62,7 @@ __device__ __forceinline__ uint32_t swz(int r, int c) {
 // not emit the launch stubs of internal-linkage kernel templates.
 template <int BR, int BT, int BK, int NS>
 __global__ void __launch_bounds__(256)
-k_gemm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ y,
-       int T, int N, int K, int nrt, int ntt) {
+k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt) {
     constexpr int MI = BR / 64, NJ = BT / 64;  // 32 x 32 tiles per wave
     constexpr int CPR = BK / 8, RPI = 64 / CPR;  // chunks per row, rows per copy instruction
     constexpr int kWBytes = BR * BK * 2, kXBytes = BT * BK * 2;
@@ -71,12 +70,21 @@ k_gemm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __
     constexpr int kWInst = kWBytes / 1024 / 4, kXInst = kXBytes / 1024 / 4;  // per wave
     static_assert(kWBytes % 4096 == 0 && kXBytes % 4096 == 0, "whole copy instructions per wave");
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    // block -> (row tile, token tile); the token tiles of one row tile share an XCD
+    // block -> (row tile, token tile); the token tiles of one row tile share an XCD.
+    // Row tiles run over the matrices of the set back to back.
     const int id = blockIdx.x;
     const int q = id >> 3;
     const int tt = q % ntt;
-    const int rt = (q / ntt) * 8 + (id & 7);
-    if (rt >= nrt) return;  // uniform
+    const int rtg = (q / ntt) * 8 + (id & 7);
+    if (rtg >= gm.rt_begin[gm.n]) return;  // uniform
+    int mi = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxMats; ++j) mi += (j < gm.n && rtg >= gm.rt_begin[j]) ? 1 : 0;
+    const uint16_t* const w = mi == 0 ? gm.w[0] : mi == 1 ? gm.w[1] : mi == 2 ? gm.w[2] : gm.w[3];
+    float* const y = mi == 0 ? gm.y[0] : mi == 1 ? gm.y[1] : mi == 2 ? gm.y[2] : gm.y[3];
+    const int N = mi == 0 ? gm.N[0] : mi == 1 ? gm.N[1] : mi == 2 ? gm.N[2] : gm.N[3];
+    const int rt = rtg - (mi == 0 ? gm.rt_begin[0] : mi == 1 ? gm.rt_begin[1]
+                          : mi == 2 ? gm.rt_begin[2] : gm.rt_begin[3]);
     const int r0 = rt * BR, t0 = tt * BT;
 
     const int lane = threadIdx.x & 63;
@@ -181,14 +189,25 @@ k_gemm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __
 namespace {
 
 template <int BR, int BT, int BK, int NS>
-hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const void* wb, int64_t d_out,
-                       float* y, hipStream_t s) {
-    const int nrt = (int)((d_out + BR - 1) / BR), ntt = (int)((T + BT - 1) / BT);
-    const int nrt8 = (nrt + 7) / 8 * 8;
+hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
+                       hipStream_t s) {
+    GemmMats gm = {};
+    gm.n = n;
+    int rt = 0;
+    for (int i = 0; i < n; ++i) {
+        gm.w[i] = (const uint16_t*)mats[i].w;
+        gm.y[i] = mats[i].y;
+        gm.N[i] = (int)mats[i].d_out;
+        gm.rt_begin[i] = rt;
+        rt += (int)((mats[i].d_out + BR - 1) / BR);
+    }
+    for (int i = n; i <= kMaxMats; ++i) gm.rt_begin[i] = rt;
+    const int ntt = (int)((T + BT - 1) / BT);
+    const int nrt8 = (rt + 7) / 8 * 8;
     const unsigned blocks = (unsigned)(nrt8 * ntt);
     constexpr int lds = NS * (BR + BT) * BK * 2;
-    k_gemm<BR, BT, BK, NS><<<dim3(blocks), dim3(256), lds, s>>>(
-        (const uint16_t*)x, (const uint16_t*)wb, y, (int)T, (int)d_out, (int)d_in, nrt, ntt);
+    k_gemm<BR, BT, BK, NS><<<dim3(blocks), dim3(256), lds, s>>>((const uint16_t*)x, gm, (int)T,
+                                                               (int)d_in, ntt);
     return hipGetLastError();
 }
 
@@ -204,7 +223,8 @@ bool small_batch_gemm_supported(int64_t T, int64_t d_in, int64_t d_out) {
 
 hipError_t launch_small_batch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb,
                                    int64_t d_out, float* y, hipStream_t s) {
-    return launch_tile<64, 64, 64, 4>(x, T, d_in, wb, d_out, y, s);
+    const GemmMatArg m = {wb, y, d_out};
+    return launch_tile<64, 64, 64, 4>(x, T, d_in, &m, 1, s);
 }
 
 bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out) {
@@ -215,13 +235,24 @@ bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out) {
 // The largest tile that still yields enough blocks to cover the chip: 128 rows x 256
 // tokens (most reuse per copied byte), 128 x 128, 64 x 128, else 64 x 64 (small
 // matrices and batches, where idle CUs cost more than the extra copies).
+hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
+                           hipStream_t s) {
+    if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
+    auto blocks = [&](int64_t br, int64_t bt) {
+        int64_t r = 0;
+        for (int i = 0; i < n; ++i) r += (mats[i].d_out + br - 1) / br;
+        return r * ((T + bt - 1) / bt);
+    };
+    if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s);
+    if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 4>(x, T, d_in, mats, n, s);
+    if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 4>(x, T, d_in, mats, n, s);
+    return launch_tile<64, 64, 64, 4>(x, T, d_in, mats, n, s);
+}
+
 hipError_t launch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb, int64_t d_out,
                        float* y, hipStream_t s) {
-    auto blocks = [&](int64_t br, int64_t bt) { return ((d_out + br - 1) / br) * ((T + bt - 1) / bt); };
-    if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 3>(x, T, d_in, wb, d_out, y, s);
-    if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 4>(x, T, d_in, wb, d_out, y, s);
-    if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 4>(x, T, d_in, wb, d_out, y, s);
-    return launch_tile<64, 64, 64, 4>(x, T, d_in, wb, d_out, y, s);
+    const GemmMatArg m = {wb, y, d_out};
+    return launch_gemm_set(x, T, d_in, &m, 1, s);
 }
 
 }  // namespace bd

@@ -16,8 +16,9 @@ namespace bd {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Status word bits (first 4 bytes of every workspace).
-enum : uint32_t { ST_NONFINITE = 1u, ST_USER_ID = 2u };
+// Status word bits (first 4 bytes of every workspace).  ST_ENCODING: a delta product
+// was asked of a prepared batch whose tokens were encoded for another scale mode.
+enum : uint32_t { ST_NONFINITE = 1u, ST_USER_ID = 2u, ST_ENCODING = 4u };
 
 // ---------------------------------------------------------------- compress
 // Stream tiling: a wave covers one row segment of kSegCols columns per row
@@ -65,6 +66,7 @@ hipError_t launch_select_axis(const AxisPlan& ap, const void* wf, const void* wb
 
 // ------------------------------------------------------------------- apply
 constexpr int kItemTokens = 32;   // max tokens of one (user, chunk) work item (<= 2 MFMA tiles)
+constexpr int kMaxMats = 4;       // matrices of one grouped launch (they share X)
 constexpr int kMaxGroupT = 8192;  // tokens the one-block grouping kernel sorts in LDS
 constexpr int kMaxUsers = (1 << 17) - 1;
 
@@ -81,8 +83,8 @@ struct BatchPlan {
     int32_t U = 0;
     int xdtype = 0;
     int64_t max_items = 0, ntiles = 0, nunit = 0;
-    size_t off_meta = 0, off_perm = 0, off_user = 0, off_items = 0, off_tiles = 0, off_tmeta = 0,
-           off_enc = 0;
+    size_t off_meta = 0, off_perm = 0, off_user = 0, off_items = 0, off_tiles = 0, off_torder = 0,
+           off_tmeta = 0, off_enc = 0;
     size_t total = 0;
 };
 
@@ -134,6 +136,27 @@ hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStrea
 hipError_t launch_tile_plan(const BatchPlan& bp, char* batch, hipStream_t s);
 hipError_t launch_delta6(const BatchPlan& bp, const DeltaPlan& dp, char* batch, const void* x,
                          const uint64_t* signs, const void* scales, float* y, hipStream_t s);
+// The two halves of launch_delta6: the tokens of x encoded into the batch (k_tile_encode;
+// word kEncTagWord of the batch meta records which encoding), then the products on them.
+constexpr int kEncTagWord = 4;
+__host__ __device__ constexpr uint32_t enc_tag(bool grp, bool col) {
+    return 0x454E4300u | (grp ? 1u : 0u) | (col ? 2u : 0u);
+}
+hipError_t launch_tile_encode(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
+                              const void* x, const void* scales, hipStream_t s);
+hipError_t launch_delta6_encoded(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
+                                 const uint64_t* signs, const void* scales, float* y,
+                                 hipStream_t s);
+// The products of up to kMaxMats matrices of one scale mode on one encoded batch, in
+// one launch (dp gives the mode, group size and scale dtype; each matrix its d_out).
+struct DeltaMatArg {
+    const uint64_t* signs;
+    const void* scales;
+    float* y;
+    int64_t d_out;
+};
+hipError_t launch_delta6_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
+                             const DeltaMatArg* mats, int n, hipStream_t s);
 
 // Tiled matrix-core GEMM for the base product of batches of more than kGemmMinT
 // bf16 tokens (smaller batches take the streaming kernel of bd_apply.hip).
@@ -144,6 +167,22 @@ hipError_t launch_small_batch_gemm(const void* x, int64_t T, int64_t d_in, const
                                    int64_t d_out, float* y, hipStream_t s);
 hipError_t launch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb, int64_t d_out,
                        float* y, hipStream_t s);
+// The base products of up to kMaxMats matrices that read the same X, in one launch
+// (their row tiles back to back in one grid).
+struct GemmMatArg {
+    const void* w;
+    float* y;
+    int64_t d_out;
+};
+struct GemmMats {
+    const uint16_t* w[kMaxMats];
+    float* y[kMaxMats];
+    int N[kMaxMats];
+    int rt_begin[kMaxMats + 1];
+    int n;
+};
+hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
+                           hipStream_t s);
 
 bool decode_path_supported(int xdtype, int64_t T, int mode);
 void make_decode_plan(int64_t T, int64_t d_in, DecodePlan* plan);

@@ -26,11 +26,11 @@ def test_library_exports_every_declared_function():
     assert "bd_compress" in names and "bd_apply" in names and "bd_reconstruct" in names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
-    assert lib.bd_abi_version() == 1
+    assert lib.bd_abi_version() == 2
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert B.status_string(s) and B.status_string(s) != "unknown status"
 
 
@@ -147,3 +147,79 @@ def test_int8_base_entry_points_reject_bad_arguments_synchronously():
     assert q8(B.params("matrix"), ws=0) == B.BD_ERR_WORKSPACE
     assert q8(B.params("matrix"), wq=0) == B.BD_ERR_INVALID_ARG
     assert q8(B.params("matrix"), wq=(1 << 12) + 8) == B.BD_ERR_INVALID_ARG
+
+
+def test_prepared_batch_entry_points_check_the_batch_size():
+    """bd_delta_apply, bd_batch_encode and bd_delta_apply_encoded write into or read a
+    prepared batch whose size depends on T and d_in: a smaller buffer is rejected
+    before anything is enqueued (fake, never dereferenced device addresses)."""
+    L = B.lib()
+    vp = ctypes.c_void_p
+    p = B.params("matrix")
+    T, U, d_in, d_out = 64, 8, 512, 256
+    need = B.bd_batch_workspace_bytes(T, U, d_in, B.BD_BF16)
+    assert need > 0
+    a = vp(1 << 12)
+
+    def delta(nb):
+        return L.bd_delta_apply(a, nb, a, B.BD_BF16, T, d_in, U, d_out, a, a, ctypes.byref(p), a, None)
+
+    def enc(nb, xd=B.BD_BF16):
+        return L.bd_batch_encode(a, nb, a, xd, T, d_in, U, None, ctypes.byref(p), None)
+
+    def applied(nb, xd=B.BD_BF16):
+        return L.bd_delta_apply_encoded(a, nb, xd, T, d_in, U, d_out, a, a, ctypes.byref(p), a, None)
+
+    assert delta(need - 256) == B.BD_ERR_WORKSPACE
+    assert enc(need - 256) == B.BD_ERR_WORKSPACE
+    assert applied(need - 256) == B.BD_ERR_WORKSPACE
+    assert enc(need, xd=B.BD_F32) == B.BD_ERR_DTYPE
+    assert applied(need, xd=B.BD_F32) == B.BD_ERR_DTYPE
+    assert L.bd_batch_encode(a, need, None, B.BD_BF16, T, d_in, U, None, ctypes.byref(p),
+                             None) == B.BD_ERR_INVALID_ARG
+    # COL encodings fold in the column scales: they are required
+    pc = B.params("col", scale_dtype=B.BD_F16)
+    assert L.bd_batch_encode(a, need, a, B.BD_BF16, T, d_in, U, None, ctypes.byref(pc),
+                             None) == B.BD_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_strided_and_mistyped_tensors():
+    """The Python binding checks device, contiguity, dtype and shape before any
+    pointer reaches the library (a host pointer or int64 ids would otherwise be read
+    as device data)."""
+    p = B.params("matrix")
+    T, U, d_out, d_in = 4, 2, 64, 128
+    cpu = torch.device("cpu")
+    x = torch.zeros(T, d_in, dtype=torch.bfloat16, device=cpu)
+    wb = torch.zeros(d_out, d_in, dtype=torch.bfloat16, device=cpu)
+    signs = torch.zeros(U, d_out, d_in // 64, dtype=torch.int64, device=cpu)
+    scales = torch.zeros(U, 1, dtype=torch.float32, device=cpu)
+    ids = torch.zeros(T, dtype=torch.int32, device=cpu)
+    y = torch.zeros(T, d_out, dtype=torch.float32, device=cpu)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8, device=cpu)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.bd_apply(x, wb, signs, scales, p, U, ids, y, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.bd_compress(wb, wb, p, signs[0], scales[0], ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.bd_batch_prepare(x, ids, U, ws)
+    # each argument's dtype, shape and contiguity are checked before its device, so the
+    # checks themselves run here on host tensors
+    with pytest.raises(TypeError, match="int64"):
+        B._ids(torch.zeros(T, dtype=torch.int64), T, None)
+    with pytest.raises(ValueError, match="shape"):
+        B._ids(torch.zeros(T + 1, dtype=torch.int32), T, None)
+    with pytest.raises(ValueError, match="shape"):
+        B._bank(signs[:, :32].contiguous(), scales, p, U, d_out, d_in, None)
+    with pytest.raises(ValueError, match="contiguous"):
+        B._dev(torch.zeros(d_out, T).t(), "y", (torch.float32,), (T, d_out))
+    with pytest.raises(ValueError, match="scales_bank holds"):
+        B._scales(scales, B.params("row"), U, d_out, d_in, None)  # (U, 1) for ROW
+    with pytest.raises(TypeError):
+        B._scales(scales.half(), p, U, d_out, d_in, None)
+    with pytest.raises(TypeError):
+        B._bank(signs.int(), scales, p, U, d_out, d_in, None)
+    with pytest.raises(TypeError):
+        B._dev([1, 2], "x")
+    with pytest.raises(ValueError, match="required"):
+        B._dev(None, "x")

@@ -1,0 +1,110 @@
+"""The two halves of the delta product (bd_batch_encode, bd_delta_apply_encoded): one
+encoding of the activations shared by several matrices gives, bit for bit, what
+bd_delta_apply gives per matrix; a product asked of a batch encoded for another
+scale mode adds nothing and reports BD_ERR_BATCH; the result matches the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import DEV, TOL_BF16, custom, gpu_bank, max_err_vs_rms, o_sdtype, oracle_bank
+from tenant_serving_amd import bitdelta as B
+from tenant_serving_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("mode", ["matrix", "row", "group"])
+def test_shared_encoding_equals_per_matrix_delta_apply(mode):
+    T, U, d_in = 70, 5, 1152  # several tiles, a ragged 512-column unit
+    ids = np.array([(7 * t) % (U + 1) - 1 for t in range(T)], dtype=np.int32)  # -1 .. U-1
+    p = B.params(mode, 128, 0.0, B.BD_F16 if mode == "row" else B.BD_F32)
+    mats = []
+    for k, d_out in enumerate((96, 200)):
+        w = custom(d_out, d_in, S.BF16, n_users=U, T=T, b=5e-3, cid=2600 + k)
+        wb = S.dev_wbase(w, 0)
+        signs, scales = gpu_bank(w, 0, wb, p, list(range(U)))
+        mats.append((w, wb, signs, scales))
+    x = S.dev_x(mats[0][0], 0)
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    bt = B.workspace(B.bd_batch_workspace_bytes(T, U, d_in, B.BD_BF16), DEV)
+    assert B.bd_batch_prepare(x, ids_dev, U, bt) == B.BD_OK
+    ref = []
+    for w, wb, signs, scales in mats:
+        y = torch.zeros(T, wb.shape[0], device=DEV)
+        assert B.bd_delta_apply(bt, x, U, signs, scales, p, y) == B.BD_OK
+        ref.append(y)
+    assert B.bd_batch_encode(bt, x, U, None, p) == B.BD_OK
+    for (w, wb, signs, scales), yr in zip(mats, ref):
+        y = torch.zeros(T, wb.shape[0], device=DEV)
+        assert B.bd_delta_apply_encoded(bt, T, d_in, U, signs, scales, p, y) == B.BD_OK
+        torch.cuda.synchronize()
+        assert torch.equal(y, yr)
+    assert B.bd_device_status(bt) == B.BD_OK
+    # and the delta term against the oracle (zero base)
+    w, wb, signs, scales = mats[1]
+    y = torch.zeros(T, wb.shape[0], device=DEV)
+    assert B.bd_delta_apply_encoded(bt, T, d_in, U, signs, scales, p, y) == B.BD_OK
+    wb_np = S.host_wbase(w, 0)
+    words, scs = oracle_bank(w, 0, wb_np, p, list(range(U)))
+    _, _, yd = O.apply(S.host_x(mats[0][0], 0), wb_np, words, scs, p.mode, ids,
+                       g=p.group_size, sdtype=o_sdtype(p))
+    err, rms = max_err_vs_rms(y.cpu().numpy(), yd)
+    assert err <= TOL_BF16 * rms
+
+
+def test_product_on_another_modes_encoding_reports_batch_error():
+    T, U, d_in, d_out = 20, 2, 512, 64
+    ids = torch.zeros(T, dtype=torch.int32, device=DEV)
+    x = torch.randn(T, d_in, device=DEV).to(torch.bfloat16)
+    bt = B.workspace(B.bd_batch_workspace_bytes(T, U, d_in, B.BD_BF16), DEV)
+    assert B.bd_batch_prepare(x, ids, U, bt) == B.BD_OK
+    pg, pm = B.params("group", 128), B.params("matrix")
+    signs = torch.zeros(U, d_out, d_in // 64, dtype=torch.int64, device=DEV)
+    sc_m = torch.ones(U, 1, device=DEV)
+    # prepared but never encoded: nothing is added
+    y = torch.zeros(T, d_out, device=DEV)
+    assert B.bd_delta_apply_encoded(bt, T, d_in, U, signs, sc_m, pm, y) == B.BD_OK
+    assert B.bd_device_status(bt) == B.BD_ERR_BATCH
+    assert torch.count_nonzero(y) == 0
+    # encoded for GROUP, applied as MATRIX: nothing is added
+    assert B.bd_batch_prepare(x, ids, U, bt) == B.BD_OK
+    assert B.bd_device_status(bt) == B.BD_OK
+    assert B.bd_batch_encode(bt, x, U, None, pg) == B.BD_OK
+    assert B.bd_delta_apply_encoded(bt, T, d_in, U, signs, sc_m, pm, y) == B.BD_OK
+    assert B.bd_device_status(bt) == B.BD_ERR_BATCH
+    assert torch.count_nonzero(y) == 0
+
+
+def test_grouped_calls_equal_per_matrix_calls():
+    """bd_base_gemm_n and bd_delta_apply_encoded_n on q/k/v-like matrices of one input
+    (row counts that pick different tile shapes and row tiles alone) give, bit for bit,
+    the per-matrix calls."""
+    T, U, d_in = 200, 6, 1024
+    ids = np.array([(t * 5) % U if t % 7 else -1 for t in range(T)], dtype=np.int32)
+    p = B.params("matrix")
+    mats = []
+    for k, d_out in enumerate((512, 128, 128, 72)):
+        w = custom(d_out, d_in, S.BF16, n_users=U, T=T, b=5e-3, cid=2700 + k)
+        wb = S.dev_wbase(w, 0)
+        signs, scales = gpu_bank(w, 0, wb, p, list(range(U)))
+        mats.append((wb, signs, scales))
+    x = S.dev_x(custom(64, d_in, S.BF16, T=T, cid=2710), 0)
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    bt = B.workspace(B.bd_batch_workspace_bytes(T, U, d_in, B.BD_BF16), DEV)
+    assert B.bd_batch_prepare(x, ids_dev, U, bt) == B.BD_OK
+    assert B.bd_batch_encode(bt, x, U, None, p) == B.BD_OK
+    ref = []
+    for wb, signs, scales in mats:
+        y = torch.empty(T, wb.shape[0], device=DEV)
+        assert B.bd_base_gemm(x, wb, y) == B.BD_OK
+        assert B.bd_delta_apply_encoded(bt, T, d_in, U, signs, scales, p, y) == B.BD_OK
+        ref.append(y)
+    ys = [torch.empty(T, wb.shape[0], device=DEV) for wb, _, _ in mats]
+    assert B.bd_base_gemm_n(x, [m[0] for m in mats], ys) == B.BD_OK
+    assert B.bd_delta_apply_encoded_n(bt, T, d_in, U, [m[1] for m in mats], [m[2] for m in mats],
+                                      p, ys) == B.BD_OK
+    torch.cuda.synchronize()
+    assert B.bd_device_status(bt) == B.BD_OK
+    for y, yr in zip(ys, ref):
+        assert torch.equal(y, yr)
