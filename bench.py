@@ -280,9 +280,9 @@ def stack_leg(args, dev):
     n_delta = n_gemm = 4 * S.n_layers  # grouped launches: q|k|v, o, gate|up, down
     delta_gbs = S.bytes_delta / (phases["delta"] * 1e-6) / 1e9
     gemm_tfs = S.flops_gemm / (phases["gemm"] * 1e-6) / 1e12
-    rl_delta = {"bound": "hbm", "kernel": "k_delta7", "achieved": round(delta_gbs, 1),
+    rl_delta = {"bound": "hbm", "kernel": "k_delta8", "achieved": round(delta_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(delta_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("k_delta7", S.w.name),
+                "traffic": measured_traffic("k_delta8", S.w.name),
                 "algorithmic_bytes_per_launch": S.bytes_delta // n_delta,
                 "avg_launch_us": round(phases["delta"] / n_delta, 3)}
     rl_gemm = {"bound": "mfma", "kernel": "k_gemm", "achieved": round(gemm_tfs, 1),

@@ -412,6 +412,8 @@ bd_status make_batch_plan(int64_t T, int32_t U, int64_t d_in, int xdtype, BatchP
         off += align_up(sizeof(int32_t) * ((size_t)q.ntiles + 1));
         q.off_torder = off;
         off += align_up(sizeof(int32_t) * (size_t)q.ntiles);
+        q.off_tpre = off;
+        off += align_up(sizeof(int32_t) * ((size_t)q.ntiles + 1));
         q.off_tmeta = off;
         off += align_up(sizeof(int32_t) * kTileMetaInts * (size_t)q.ntiles);
         q.off_enc = off;

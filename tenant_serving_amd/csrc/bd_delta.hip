@@ -28,6 +28,8 @@
 //                  element (each Y element belongs to exactly one tile).
 #include "bd_internal.h"
 
+#include <type_traits>
+
 namespace bd {
 namespace {
 
@@ -86,7 +88,7 @@ constexpr int kMaxTilesLds = 2 * (kMaxGroupT / 16) + 1;
 __global__ void __launch_bounds__(64)
 k_tile_plan(const int4* __restrict__ items, const int32_t* __restrict__ suser,
             uint32_t* __restrict__ meta, int32_t* __restrict__ tiles,
-            int32_t* __restrict__ torder, int maxt) {
+            int32_t* __restrict__ torder, int32_t* __restrict__ tpre, int maxt) {
     __shared__ int32_t st[kMaxTilesLds + 1];
     __shared__ uint8_t snu[kMaxTilesLds];
     const int lane = threadIdx.x;
@@ -140,16 +142,23 @@ k_tile_plan(const int4* __restrict__ items, const int32_t* __restrict__ suser,
         snu[t] = (uint8_t)cnt;
     }
     __syncthreads();
-    int pos = 0;
+    // tpre[k]: the users of the tiles of rank < k (their sum in tpre[nt])
+    int pos = 0, pre = 0;
     for (int v = 16; v >= 0; --v) {  // (a tile holds 1..16 positions; 0 keeps every tile ranked)
         for (int b = 0; b < nt; b += 64) {
             const int t = b + lane;
             const bool hit = t < nt && snu[t] == v;
             const uint64_t mk = __ballot(hit);
-            if (hit) torder[pos + __popcll(mk & ((1ull << lane) - 1ull))] = t;
+            const int below = __popcll(mk & ((1ull << lane) - 1ull));
+            if (hit) {
+                torder[pos + below] = t;
+                tpre[pos + below] = pre + v * below;
+            }
             pos += __popcll(mk);
+            pre += v * __popcll(mk);
         }
     }
+    if (lane == 0) tpre[nt] = pre;
 }
 
 // ------------------------------------------------------------ tile encoding
@@ -316,8 +325,9 @@ __device__ __forceinline__ P* uni_ptr(P* p) {
 template <int K>
 __device__ __forceinline__ uint64_t s_sel64(int m, uint64_t a, uint64_t b) {  // m == K ? a : b
     uint64_t r;
+    const int ms = __builtin_amdgcn_readfirstlane(m);  // (an SGPR even when registers are short)
     asm volatile("s_cmp_eq_u32 %1, %4\n\ts_cselect_b64 %0, %2, %3"
-                 : "=s"(r) : "s"(m), "s"(a), "s"(b), "i"(K) : "scc");
+                 : "=s"(r) : "s"(ms), "s"(a), "s"(b), "i"(K) : "scc");
     return r;
 }
 template <typename T>
@@ -728,231 +738,396 @@ k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
     }
 }
 
-// ------------------------------------------------ delta products, unit per wave
+// ------------------------------------------------ delta products, persistent
 // The products of one launch's units [u0, u0 + W) for MATRIX, ROW and COL scales.
-// Block = W waves (one 512-column unit each) over one tile and NCH chunks of 16 W
-// rows.  A wave loads its unit's encoded tokens once (13 KB: the fp6 hi / lo
-// operands of the four products and their block codes) and keeps them in
-// registers; it then streams, chunk by chunk and row tile by row tile, every user
-// of the tile's 16 sign rows x 64 bytes of its unit through a ring of D loads kept
-// in flight (16 bytes per lane, the B operand of the 4 products as they stand),
-// runs the products (hi and lo into two accumulators; other users' tokens carry
-// block code 0, scale 2^-127) and, at the end of a row tile, writes its partial
-// (that unit's share of the 16 x 16 outputs) to LDS.  One barrier per chunk: wave w
-// then sums row tile w of the chunk over the W units in unit order (partials double
-// buffered, so the next chunk's writes never wait for the sums) and keeps it.  At
-// the end of the block each wave scales its row tiles per token (MATRIX / ROW: the
-// scale of the token's user; COL: in the tokens) and adds them to y, one no-return
-// atomic per element.  Launches of one call cover the units in order, so every y
-// element gets its addends (the base product, then one per launch) in a fixed
-// order: the result repeats bit for bit.
-constexpr int kMaxW7 = 8;   // units (waves) per launch
-constexpr int kRing7 = 12;  // sign loads in flight per wave
+// Work item = (tile rank k, chunk c): 128 output rows (8 row tiles) of the matrix set
+// for the 16 tokens of tile torder[k]; its cost is one sweep per user of the tile.
+// One block per CU, W waves, wave w on unit u0 + w; the block takes the items whose
+// first sweep falls in its equal share of all sweeps (tpre: sweeps of the ranks before
+// k), tile-major, so it keeps one tile's operands for many chunks.  A wave loads its
+// unit's encoded tokens when its tile changes (13 KB into registers: fp6 hi / lo of
+// the four products and their block codes), then streams, sweep after sweep (one user
+// of the item), the 8 row tiles' 16 sign rows x 64 bytes of its unit through a ring of
+// two sweeps of loads in flight (16 bytes per lane, the B operand of the 4 products),
+// running ahead across items and tiles.  Each row tile has its own accumulator over the
+// item's users (other users' tokens carry block code 0, scale 2^-127).  At the end of
+// an item the waves' partials (their units' shares) meet in LDS (double buffered, one
+// barrier per item); wave w sums row tiles w, w + W, ... over the units in unit order,
+// scales them per token (MATRIX / ROW: the scale of the token's user; COL: in the
+// tokens) and adds them to y, one no-return atomic per element.  Every y element gets
+// its addends (the base product, then one per launch) in a fixed order: the result
+// repeats bit for bit.
+constexpr int kRT8 = 8;                // row tiles of a chunk: one sweep
+constexpr int kChunkRows = 16 * kRT8;  // rows of a chunk
+constexpr int kMaxW8 = 8;              // units (waves) per launch
 
-template <int MODE, bool SF16, int NCH>
-__global__ void __launch_bounds__(64 * kMaxW7)
-k_delta7(const DeltaMats dm, const int32_t* __restrict__ tmeta,
-         const int32_t* __restrict__ torder, const char* __restrict__ enc,
-         uint32_t* __restrict__ meta, int64_t d_in, int nunit, int u0, int units, int T,
-         int U) {
-    // units: the units of d_in (ceil(d_in / 512)); every launch has the same W waves, and
-    // a wave whose unit is past them (the last launch) adds zeros
+typedef const __attribute__((address_space(4))) int32_t* cptr_i32;  // uniform: scalar loads
+__device__ __forceinline__ int sload(const void* p, int64_t i) { return ((cptr_i32)p)[i]; }
+
+// y[i] += v, no return, issued from asm: the compiler's own waits do not count it
+__device__ __forceinline__ void atomic_add_nr(float* p, float v) {
+    asm volatile("global_atomic_add_f32 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+
+template <int MODE, bool SF16, int RPW>
+__global__ void __launch_bounds__(64 * kMaxW8)
+k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
+         const int32_t* __restrict__ torder, const int32_t* __restrict__ tpre,
+         const char* __restrict__ enc, uint32_t* __restrict__ meta, int64_t d_in, int nunit,
+         int u0, int units, int T, int U) {
+    // dm.rb_begin: first chunk of each matrix; RPW: row tiles each wave sums per item
+    // (ceil(8 / W)); units: the units of d_in (every launch has W waves; a wave whose
+    // unit is past them adds zeros)
     static_assert(MODE != BD_SCALE_GROUP, "GROUP scales take k_delta6");
-    constexpr int D = kRing7;
-    __shared__ __attribute__((aligned(16))) f32x4 part[2][kMaxW7][kMaxW7][64];
-    __shared__ int32_t smeta[kTileMetaInts];
+    constexpr bool COL = MODE == BD_SCALE_COL;
+    constexpr int RT = kRT8, D = 2 * RT;  // ring: two sweeps
+    __shared__ __attribute__((aligned(16))) f32x4 part[2][RT][kMaxW8][64];
     const int lane = threadIdx.x & 63;
     const int wv = uni((int)(threadIdx.x >> 6));
     const int W = uni((int)(blockDim.x >> 6));
     const int n = lane & 15, G = lane >> 4;
-    // block -> (tile rank, row block of the matrix set), as k_delta6
-    const int nrb = dm.rb_begin[kMaxMats];  // (entries past the set repeat the total)
-    const int nrb8 = (nrb + 7) >> 3;
-    const int bk = (int)blockIdx.x >> 3;
-    const int rb = (bk % nrb8) * 8 + ((int)blockIdx.x & 7);
-    const int trank = bk / nrb8;
-    if (rb >= nrb || trank >= (int)meta[3]) return;  // uniform
-    if (meta[kEncTagWord] != enc_tag(false, MODE == BD_SCALE_COL)) {
+    if ((uint32_t)sload(meta, kEncTagWord) != enc_tag(false, COL)) {
         if (threadIdx.x == 0) atomicOr(meta, ST_ENCODING);
         return;
     }
-    const int tile = uni(torder[trank]);
-    int mi = 0;
-#pragma unroll
-    for (int j = 1; j < kMaxMats; ++j) mi += (j < dm.n && rb >= dm.rb_begin[j]) ? 1 : 0;
-    mi = uni(mi);
-    const uint64_t* const signs = pick_mat(dm.signs, mi);
-    const void* const scales = pick_mat(dm.scales, mi);
-    float* const y = pick_mat(dm.y, mi);
-    const int64_t d_out = pick_mat(dm.d_out, mi);
-    const int64_t per_user = pick_mat(dm.per_user, mi);
-    const int rbl = rb - pick_rb(dm.rb_begin, mi);
-    const int64_t row0 = (int64_t)rbl * (16 * W * NCH);  // the block's first row
-
-    if (wv == 0) smeta[lane] = tmeta[(size_t)tile * kTileMetaInts + lane];
-    __syncthreads();
-    const int nus = uni(smeta[48]);
-    {
-        const int v = smeta[lane];
-        const bool bad = lane < 16 ? v < -1 || v >= T
-                         : lane < 32 ? v < -1 || v >= U
-                         : lane < 48 ? (lane - 32 < nus && (v < 0 || v >= U))
-                                     : lane == 48 && (v < 1 || v > 16);
-        if (__ballot(bad) != 0ull) {  // uniform
-            if (threadIdx.x == 0) atomicOr(meta, ST_ENCODING);
-            return;
-        }
+    const int ntl = sload(meta, 3);
+    const int C = dm.rb_begin[kMaxMats];  // chunks of the matrix set
+    const int tot = sload(tpre, ntl);     // sweeps of one chunk over all tiles
+    // ranks with users: torder lists them first and tpre rises over them
+    int neff = 0;
+    for (int b = 0; b < ntl; b += 64) {
+        const int k = b + lane;
+        neff += __popcll(__ballot(k < ntl && tpre[k] < tot));
     }
-    // this wave's unit: its operands into registers (the oldest loads of the wave)
+    neff = uni(neff);
+    // the first item (linear index k C + c) whose first sweep is at or after sweep w
+    auto locate = [&](int64_t w) -> int64_t {
+        int cnt = 0;
+        for (int b = 0; b < neff; b += 64) {
+            const int k = b + lane;
+            cnt += __popcll(__ballot(k < neff && (int64_t)tpre[k] * C <= w));
+        }
+        const int k = uni(cnt) - 1;  // (>= 0: tpre[0] = 0)
+        if (k < 0 || k >= neff) return (int64_t)neff * C;
+        const int64_t rem = w - (int64_t)sload(tpre, k) * C;
+        int nu = sload(tpre, k + 1) - sload(tpre, k);
+        nu = nu < 1 ? 1 : nu;
+        const int64_t c = (rem + nu - 1) / nu;
+        const int64_t i = (int64_t)k * C + c;
+        return i < (int64_t)neff * C ? i : (int64_t)neff * C;
+    };
+    const int64_t Wt = (int64_t)tot * C;
+    const int64_t i0 = uni64(locate(Wt * (int64_t)blockIdx.x / gridDim.x));
+    const int64_t i1 = uni64(locate(Wt * ((int64_t)blockIdx.x + 1) / gridDim.x));
+    if (i0 >= i1) return;  // uniform: no items
+
     const int u = u0 + wv;
     const bool uact = u < units;  // uniform
-    const __amdgpu_buffer_rsrc_t er = make_rsrc(
-        enc + ((size_t)tile * nunit + (uact ? u : 0)) * kEncUnitBytes,
-        uact ? (uint64_t)kEncUnitBytes : 0ull);  // (no unit: every load reads 0)
-    i32x6 hi[4], lo[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const u32x4 c0 = buf_load16(er, (3 * p + 0) * 1024 + 16 * lane);
-        const u32x4 c1 = buf_load16(er, (3 * p + 1) * 1024 + 16 * lane);
-        const u32x4 c2 = buf_load16(er, (3 * p + 2) * 1024 + 16 * lane);
-        hi[p] = i32x6{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y};
-        lo[p] = i32x6{(int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
-    }
-    const u32x4 cd = buf_load16(er, 12 * 1024 + 16 * lane);
-
     const uint32_t bank_row = (uint32_t)(d_in / 8);
-    const uint64_t user_bytes = (uint64_t)d_out * bank_row;
-    const int nrec_bits = user_bytes > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)user_bytes;
-    const uint32_t lane_off = (uint32_t)n * bank_row + 64u * (uint32_t)u + 16u * (uint32_t)G;
-    // lane j < nus: base address of user j's bank (read back with readlane)
-    uint32_t ub_lo, ub_hi;
-    {
-        const uint64_t usr = n < nus ? (uint64_t)(uint32_t)smeta[32 + n] : 0ull;
-        const uint64_t ub = (uint64_t)(const char*)signs + usr * user_bytes;
-        ub_lo = (uint32_t)ub;
-        ub_hi = (uint32_t)(ub >> 32);
-    }
-    const int c_tuser = smeta[16 + n];  // A row n of the products: the user of token n
-    const int c_users = smeta[32 + n];  // lane j < nus: user j
-    uint32_t kmask, kone;
-    asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(kmask));
-    asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(kone));
+    // a wave's 16 lanes of B column n read 16 bytes of row n at its unit's 64; row tile r
+    // of a chunk 16 r rows further (the chunk's first row is in the descriptor)
+    const uint32_t lane_off = (uint32_t)n * bank_row + 64u * (uint32_t)(uact ? u : 0) + 16u * (uint32_t)G;
+    const uint32_t rstride = 16u * bank_row;
+#define BD_VOFF(r) (lane_off + (uint32_t)(r) * rstride)
 
-    // slot s = ((chunk c) W + row tile r) nus + user j; row tile c W + r of the block
-    const int per_chunk = W * nus;
-    const int S = NCH * per_chunk;
-    int lj = 0, lr = 0;  // loading side: user, row tile (over the whole block)
-    auto issue = [&](int s) __attribute__((always_inline)) -> u32x4 {
-        const bool ok = s < S;  // uniform
-        const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ub_hi, lj) << 32) |
-                              (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ub_lo, lj);
-        const __amdgpu_buffer_rsrc_t br =
-            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec_bits, 0x00020000);
-        const int64_t row = row0 + 16 * (int64_t)lr;
-        const uint32_t off = ok && uact && row < d_out ? lane_off + (uint32_t)row * bank_row : kOOB;
-        if (++lj == nus) {
-            lj = 0;
-            ++lr;
-        }
-        return buf_load16(br, off);
-    };
-    u32x4 ring[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-        ring[i] = issue(i);
-        __builtin_amdgcn_sched_barrier(0);
+    // ---- loading side: item (kL, cL), user jL; scalar state, one descriptor per sweep
+    int kL = (int)(i0 / C), cL = (int)(i0 % C), jL = 0;
+    int64_t leftL = i1 - i0;  // items the loader has not finished
+    int tileL = sload(torder, kL), nuL = 1;
+    {
+        const int nu = sload(tpre, kL + 1) - sload(tpre, kL);
+        nuL = nu < 1 ? 1 : (nu > 16 ? 16 : nu);
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 res[NCH];
-    int j = 0, r = 0, c = 0;  // consuming side: user, row tile in chunk, chunk
-    const int total = (S + D - 1) / D * D;
-    for (int s0 = 0; s0 < total; s0 += D) {
+    auto lsweep = [&]() __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
+        const bool live = leftL > 0;
+        int mi = 0;
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            const int s = s0 + i;
-            BD_WAIT_VMCNT(D - 1);
-            const u32x4 wq = ring[i];
-            const uint32_t ko = s < S ? kone : 0u;  // past the end: zero operands
-            u32x4 bx[4];
-            bx[0] = u32x4{((wq.x << 3) & kmask) | ko, ((wq.x << 2) & kmask) | ko,
-                          ((wq.x << 1) & kmask) | ko, (wq.x & kmask) | ko};
-            bx[1] = u32x4{((wq.y << 3) & kmask) | ko, ((wq.y << 2) & kmask) | ko,
-                          ((wq.y << 1) & kmask) | ko, (wq.y & kmask) | ko};
-            bx[2] = u32x4{((wq.z << 3) & kmask) | ko, ((wq.z << 2) & kmask) | ko,
-                          ((wq.z << 1) & kmask) | ko, (wq.z & kmask) | ko};
-            bx[3] = u32x4{((wq.w << 3) & kmask) | ko, ((wq.w << 2) & kmask) | ko,
-                          ((wq.w << 1) & kmask) | ko, (wq.w & kmask) | ko};
-            asm volatile("" ::"v"(bx[0]), "v"(bx[1]), "v"(bx[2]), "v"(bx[3]));
-            __builtin_amdgcn_sched_barrier(0);
-            ring[i] = issue(s + D);  // in place, after the words are expanded
-            __builtin_amdgcn_sched_barrier(0);
-            const int usr = __builtin_amdgcn_readlane(c_users, j);
-            const bool mine = s < S && c_tuser == usr;
-            const uint32_t sh = mine ? cd.x : 0u, sl = mine ? cd.y : 0u;
-            acc = mfma_f6f4<0>(hi[0], bx[0], acc, sh);
-            acc2 = mfma_f6f4<0>(lo[0], bx[0], acc2, sl);
-            acc = mfma_f6f4<1>(hi[1], bx[1], acc, sh);
-            acc2 = mfma_f6f4<1>(lo[1], bx[1], acc2, sl);
-            acc = mfma_f6f4<2>(hi[2], bx[2], acc, sh);
-            acc2 = mfma_f6f4<2>(lo[2], bx[2], acc2, sl);
-            acc = mfma_f6f4<3>(hi[3], bx[3], acc, sh);
-            acc2 = mfma_f6f4<3>(lo[3], bx[3], acc2, sl);
-            if (s < S && ++j == nus) {  // uniform: the row tile is complete
-                j = 0;
-                part[c & 1][r][wv][lane] = acc + acc2;
-                acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (++r == W) {  // the chunk is complete: sum row tile wv over the units
-                    r = 0;
-                    // this wave's partial writes have landed in LDS; then a bare barrier
-                    // (a fence would also wait for the sign loads in flight)
-                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
-                    asm volatile("s_barrier" ::: "memory");
-                    f32x4 v = part[c & 1][wv][0][lane];
-                    for (int q = 1; q < W; ++q) v += part[c & 1][wv][q][lane];
-#pragma unroll
-                    for (int cc = 0; cc < NCH; ++cc)
-                        if (cc == c) res[cc] = v;
-                    ++c;
+        for (int q = 1; q < kMaxMats; ++q) mi += (q < dm.n && cL >= dm.rb_begin[q]) ? 1 : 0;
+        const int usr = live && (uint32_t)tileL < (uint32_t)ntl
+                            ? sload(tmeta, (int64_t)tileL * kTileMetaInts + 32 + jL) : -1;
+        const bool ok = uact && (uint32_t)usr < (uint32_t)U;
+        const uint64_t* sg = pick_mat(dm.signs, mi);
+        const int64_t d_out = pick_mat(dm.d_out, mi);
+        const int64_t row0 = (int64_t)(cL - pick_rb(dm.rb_begin, mi)) * kChunkRows;
+        const uint64_t base = (uint64_t)(uintptr_t)sg +
+                              (uint64_t)(ok ? usr : 0) * (uint64_t)d_out * bank_row +
+                              (uint64_t)row0 * bank_row;
+        const uint64_t rem = ok && row0 < d_out ? (uint64_t)(d_out - row0) * bank_row : 0ull;
+        const int nrec = rem > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)rem;
+        if (live && ++jL == nuL) {  // next item
+            jL = 0;
+            if (--leftL > 0) {
+                if (++cL == C) {
+                    cL = 0;
+                    ++kL;
+                    tileL = sload(torder, kL);
+                    const int nu = sload(tpre, kL + 1) - sload(tpre, kL);
+                    nuL = nu < 1 ? 1 : (nu > 16 ? 16 : nu);
                 }
             }
         }
-    }
-    // y[token][row] += the sums (-X S^T of the token's own user): MATRIX and ROW take
-    // that user's scale here, COL's are in the tokens
-    BD_WAIT_VMCNT(0);
-    int tok[4], tus[4];
+        return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, 0x00020000);
+    };
+
+    // ---- consuming side
+    // tile state: operands, block codes, tokens and their factors, A c^T (see below)
+    i32x6 hi[4], lo[4];
+    uint32_t cdh = 0, cdl = 0;
+    int trow = -1;  // lane l: word l of the tile's meta (tokens, their users, user list)
+    bool tdead = true;
+    int jt = -1;
+    f32x4 ncor = {0.f, 0.f, 0.f, 0.f};
+    // B operands straight from the sign words: dword d of a product's operand keeps bits
+    // 4 k + d of the word in place (nibble k, bit d) over a constant pattern, so each
+    // nibble is c_d + s (s = +1 for bit 0, -1 for bit 1; e2m1 1110/1111 = -4/-6,
+    // 1100/1110 = -2/-4, 1000/1100 = -0/-2, 0010/1010 = 1/-1: c = -5, -3, -1, 0).  The
+    // constant part, A (c_(k / 8))^T, is the same for every output row: computed once per
+    // tile and the row tiles' sums start from its negative.
+    uint32_t m0, m1, m2, m3, k0, k1, k2, k3;  // (gfx9 VOP3 takes no literal)
+    asm volatile("v_mov_b32 %0, 0x11111111" : "=v"(m0));
+    asm volatile("v_mov_b32 %0, 0x22222222" : "=v"(m1));
+    asm volatile("v_mov_b32 %0, 0x44444444" : "=v"(m2));
+    asm volatile("v_mov_b32 %0, 0x88888888" : "=v"(m3));
+    asm volatile("s_mov_b32 %0, 0xEEEEEEEE" : "=s"(k0));
+    asm volatile("s_mov_b32 %0, 0xCCCCCCCC" : "=s"(k1));
+    asm volatile("s_mov_b32 %0, 0x88888888" : "=s"(k2));
+    asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(k3));
+    int k = (int)(i0 / C), c = (int)(i0 % C);
+    int64_t left = i1 - i0;
+    int tile = -1, nu = 1, j = 0, ci = 0;  // ci: items done (LDS buffer parity)
+    // a new tile (its loads are the youngest: their first use waits for every load in
+    // flight; once or twice per block)
+    auto tile_setup = [&](int t, int nut) __attribute__((always_inline)) {
+        const bool tok_ok = (uint32_t)t < (uint32_t)ntl;
+        const int tt = tok_ok ? t : 0;
+        const int v = tmeta[(size_t)tt * kTileMetaInts + lane];
+        const __amdgpu_buffer_rsrc_t er = make_rsrc(
+            enc + ((size_t)tt * nunit + (uact ? u : 0)) * kEncUnitBytes,
+            uact && tok_ok ? (uint64_t)kEncUnitBytes : 0ull);  // (no unit: zeros)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        tok[e] = smeta[4 * G + e];
-        tus[e] = smeta[16 + 4 * G + e];
-    }
-    // every scale first (one round trip), then the adds
-    constexpr int NF = MODE == BD_SCALE_ROW ? NCH : 1;  // MATRIX: per user; ROW: per row too
-    float fs[NF][4];
+        for (int p = 0; p < 4; ++p) {
+            const u32x4 c0 = buf_load16(er, (3 * p + 0) * 1024 + 16 * lane);
+            const u32x4 c1 = buf_load16(er, (3 * p + 1) * 1024 + 16 * lane);
+            const u32x4 c2 = buf_load16(er, (3 * p + 2) * 1024 + 16 * lane);
+            hi[p] = i32x6{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y};
+            lo[p] = i32x6{(int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
+        }
+        const uint64_t cdw = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                              er, 12 * 1024 + 16 * lane, 0, 0));
+        // the tile's tokens, their users and its user list must fit this call's T and
+        // n_users, and its user count the plan's (a batch prepared for other sizes): a
+        // tile that does not is flagged and adds nothing
+        const bool bad = lane < 16 ? v < -1 || v >= T
+                         : lane < 32 ? v < -1 || v >= U
+                         : lane < 48 ? (lane - 32 < nut && (v < 0 || v >= U))
+                                     : lane == 48 && v != nut;
+        const bool dead = !tok_ok || __ballot(bad) != 0ull;  // uniform
+        if (dead && threadIdx.x == 0) atomicOr(meta, ST_ENCODING);
+        trow = v;
+        tdead = dead;
+        const int c_tuser = __shfl(v, 16 + n);
+        jt = -1;
+        for (int q = 0; q < nut; ++q)
+            if (__shfl(v, 32 + q) == c_tuser) jt = q;
+        cdh = (uint32_t)cdw;
+        cdl = (uint32_t)(cdw >> 32);
+        // c = (-4, -3, -1, 0) + (-1, 0, 0, 0) in e2m1 (1110, 1101, 1010, 0000 and 1010):
+        // two products per part, in the layout of the sign operands
+        u32x4 c1, c2;
+        asm volatile("v_mov_b32 %0, 0xEEEEEEEE" : "=v"(c1.x));
+        asm volatile("v_mov_b32 %0, 0xDDDDDDDD" : "=v"(c1.y));
+        asm volatile("v_mov_b32 %0, 0xAAAAAAAA" : "=v"(c1.z));
+        c1.w = 0u;
+        c2 = u32x4{c1.z, 0u, 0u, 0u};
+        f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+        t4 = mfma_f6f4<0>(hi[0], c1, t4, cdh);
+        t4 = mfma_f6f4<0>(lo[0], c1, t4, cdl);
+        t4 = mfma_f6f4<0>(hi[0], c2, t4, cdh);
+        t4 = mfma_f6f4<0>(lo[0], c2, t4, cdl);
+        t4 = mfma_f6f4<1>(hi[1], c1, t4, cdh);
+        t4 = mfma_f6f4<1>(lo[1], c1, t4, cdl);
+        t4 = mfma_f6f4<1>(hi[1], c2, t4, cdh);
+        t4 = mfma_f6f4<1>(lo[1], c2, t4, cdl);
+        t4 = mfma_f6f4<2>(hi[2], c1, t4, cdh);
+        t4 = mfma_f6f4<2>(lo[2], c1, t4, cdl);
+        t4 = mfma_f6f4<2>(hi[2], c2, t4, cdh);
+        t4 = mfma_f6f4<2>(lo[2], c2, t4, cdl);
+        t4 = mfma_f6f4<3>(hi[3], c1, t4, cdh);
+        t4 = mfma_f6f4<3>(lo[3], c1, t4, cdl);
+        t4 = mfma_f6f4<3>(hi[3], c2, t4, cdh);
+        t4 = mfma_f6f4<3>(lo[3], c2, t4, cdl);
+        ncor = -t4;
+    };
+
+    // item state: its matrix, first row, and the factors of its sums: MATRIX -(scale of
+    // the token's user), ROW -(scale of the token's user at the row), COL -1 (its scales
+    // are in the tokens); sign bit 1 is a positive delta, hence the minus
+    // (the lane's tokens 4 G .. 4 G + 3 and their users, from the tile's meta)
+    auto ltok = [&](int e) __attribute__((always_inline)) { return tdead ? -1 : __shfl(trow, 4 * G + e); };
+    auto lusr = [&](int e) __attribute__((always_inline)) { return __shfl(trow, 16 + 4 * G + e); };
+    float fs[4];
+    const void* isc = nullptr;
+    int64_t ipu = 0;
+    float* iy = nullptr;
+    int64_t idout = 0, irow0 = 0;
+    f32x4 acc[RT];
+    // scale of token e of the lane at row tile r of the item, as loaded (its use
+    // negates it: a use here would wait for every load in flight); every lane loads,
+    // from entry 0 where it has no token
+    // (called with every lane active: a lane shuffle reads 0 from inactive lanes)
+    auto factor = [&](int r, int e) __attribute__((always_inline)) -> float {
+        if constexpr (MODE == BD_SCALE_MATRIX || MODE == BD_SCALE_ROW) {
+            const int te = ltok(e), ue = lusr(e);
+            const int64_t o = irow0 + 16 * (int64_t)r + n;
+            const bool ok = te >= 0 && (MODE == BD_SCALE_MATRIX || o < idout);
+            const size_t i = ok ? (size_t)ue * ipu + (MODE == BD_SCALE_ROW ? (size_t)o : 0) : 0;
+            typedef const __attribute__((address_space(1))) uint16_t* gh;  // global, not flat:
+            typedef const __attribute__((address_space(1))) float* gf;     // counted waits
+            if constexpr (SF16) return __builtin_bit_cast(float, (uint32_t)((gh)isc)[i]);  // raw half
+            else return ((gf)isc)[i];
+        } else {
+            return 1.f;
+        }
+    };
+    auto item_start = [&]() __attribute__((always_inline)) {
+        int mi = 0;
 #pragma unroll
-    for (int cc = 0; cc < NF; ++cc) {
-        const int64_t o = row0 + 16 * (int64_t)(cc * W + wv) + n;
+        for (int q = 1; q < kMaxMats; ++q) mi += (q < dm.n && c >= dm.rb_begin[q]) ? 1 : 0;
+        iy = pick_mat(dm.y, mi);
+        idout = pick_mat(dm.d_out, mi);
+        irow0 = (int64_t)(c - pick_rb(dm.rb_begin, mi)) * kChunkRows;
+        isc = pick_mat(dm.scales, mi);
+        ipu = pick_mat(dm.per_user, mi);
+        // the factors of the wave's first row tile, loaded now (used at the item's end)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            fs[cc][e] = -1.f;
-            if ((MODE == BD_SCALE_MATRIX || MODE == BD_SCALE_ROW) && tok[e] >= 0 && o < d_out) {
-                const size_t i = (size_t)tus[e] * per_user + (MODE == BD_SCALE_ROW ? (size_t)o : 0);
-                fs[cc][e] = -(SF16 ? f16_to_f32(((const uint16_t*)scales)[i]) : ((const float*)scales)[i]);
+        for (int e = 0; e < 4; ++e) fs[e] = factor(wv, e);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = ncor;
+    };
+    // end of an item: the units' partials of each row tile meet in LDS; wave wv sums row
+    // tiles wv, wv + W, ... in unit order and adds them to y
+    auto item_end = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) part[ci & 1][r][wv][lane] = acc[r];
+        // this wave's partial writes have landed in LDS; then a bare barrier (a fence
+        // would also wait for the sign loads in flight)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+        asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < RPW; ++t) {
+            const int r = wv + t * W;
+            if (r < RT) {  // uniform
+                f32x4 v = part[ci & 1][r][0][lane];
+                for (int q = 1; q < W; ++q) v += part[ci & 1][r][q][lane];
+                // tokens and factors first, every lane active (ROW: the wave's further row
+                // tiles load their factors here)
+                int tk[4];
+                float f[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    tk[e] = ltok(e);
+                    f[e] = MODE == BD_SCALE_ROW && t > 0 ? factor(r, e) : fs[e];
+                }
+                const int64_t o = irow0 + 16 * (int64_t)r + n;
+                if (o < idout) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float sc = SF16 ? f16_to_f32((uint16_t)__builtin_bit_cast(uint32_t, f[e])) : f[e];
+                        if (tk[e] >= 0) atomic_add_nr(iy + (int64_t)tk[e] * idout + o, -(sc * v[e]));
+                    }
+                }
             }
         }
+        ++ci;
+    };
+
+    // the ring: the first two sweeps, then the first tile and item
+    u32x4 ring[D];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const __amdgpu_buffer_rsrc_t br = lsweep();
+#pragma unroll
+        for (int r = 0; r < RT; ++r) ring[h * RT + r] = buf_load16(br, BD_VOFF(r));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    tile = sload(torder, k);
+    {
+        const int q = sload(tpre, k + 1) - sload(tpre, k);
+        nu = q < 1 ? 1 : (q > 16 ? 16 : q);
+    }
+    tile_setup(tile, nu);
+    item_start();
+
+    // one sweep (user j of the item) from ring half H; its slots reload with the sweep
+    // two ahead
+    auto sweep = [&](auto hc) __attribute__((always_inline)) {
+        constexpr int H = decltype(hc)::value;
+        // tokens of other users take block code 0
+        const bool mine = jt == j;
+        const uint32_t sh = mine ? cdh : 0u, sl = mine ? cdl : 0u;
+        const __amdgpu_buffer_rsrc_t br = lsweep();
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-        const int64_t o = row0 + 16 * (int64_t)(cc * W + wv) + n;
-        if (o < d_out) {
+        for (int r = 0; r < RT; r += 2) {
+            BD_WAIT_VMCNT(D - 2);  // row tiles r and r + 1 of this sweep have landed
+            const u32x4 w0 = ring[H * RT + r], w1 = ring[H * RT + r + 1];
+            u32x4 b0[4], b1[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (tok[e] >= 0)
-                    unsafeAtomicAdd(y + (int64_t)tok[e] * d_out + o,
-                                    fs[MODE == BD_SCALE_ROW ? cc : 0][e] * res[cc][e]);
+            for (int p = 0; p < 4; ++p) {
+                b0[p] = u32x4{(w0[p] & m0) | k0, (w0[p] & m1) | k1, (w0[p] & m2) | k2, (w0[p] & m3) | k3};
+                b1[p] = u32x4{(w1[p] & m0) | k0, (w1[p] & m1) | k1, (w1[p] & m2) | k2, (w1[p] & m3) | k3};
+            }
+            asm volatile("" ::"v"(b0[0]), "v"(b0[1]), "v"(b0[2]), "v"(b0[3]), "v"(b1[0]),
+                         "v"(b1[1]), "v"(b1[2]), "v"(b1[3]));
+            __builtin_amdgcn_sched_barrier(0);
+            ring[H * RT + r] = buf_load16(br, BD_VOFF(r));  // in place, after the words are expanded
+            ring[H * RT + r + 1] = buf_load16(br, BD_VOFF(r + 1));
+            __builtin_amdgcn_sched_barrier(0);
+            if (left == 0) continue;  // (uniform: the block's items are done)
+            f32x4 a = acc[r], b = acc[r + 1];
+            a = mfma_f6f4<0>(hi[0], b0[0], a, sh);
+            b = mfma_f6f4<0>(hi[0], b1[0], b, sh);
+            a = mfma_f6f4<0>(lo[0], b0[0], a, sl);
+            b = mfma_f6f4<0>(lo[0], b1[0], b, sl);
+            a = mfma_f6f4<1>(hi[1], b0[1], a, sh);
+            b = mfma_f6f4<1>(hi[1], b1[1], b, sh);
+            a = mfma_f6f4<1>(lo[1], b0[1], a, sl);
+            b = mfma_f6f4<1>(lo[1], b1[1], b, sl);
+            a = mfma_f6f4<2>(hi[2], b0[2], a, sh);
+            b = mfma_f6f4<2>(hi[2], b1[2], b, sh);
+            a = mfma_f6f4<2>(lo[2], b0[2], a, sl);
+            b = mfma_f6f4<2>(lo[2], b1[2], b, sl);
+            a = mfma_f6f4<3>(hi[3], b0[3], a, sh);
+            b = mfma_f6f4<3>(hi[3], b1[3], b, sh);
+            a = mfma_f6f4<3>(lo[3], b0[3], a, sl);
+            b = mfma_f6f4<3>(lo[3], b1[3], b, sl);
+            acc[r] = a;
+            acc[r + 1] = b;
         }
-    }
+        if (left > 0 && ++j == nu) {  // uniform: the item is complete
+            j = 0;
+            item_end();
+            if (--left > 0) {
+                if (++c == C) {
+                    c = 0;
+                    ++k;
+                    tile = sload(torder, k);
+                    const int q = sload(tpre, k + 1) - sload(tpre, k);
+                    nu = q < 1 ? 1 : (q > 16 ? 16 : q);
+                    tile_setup(tile, nu);
+                }
+                item_start();
+            }
+        }
+    };
+    // (one exit, both halves in every pass: the second half of the last pass only
+    // keeps the ring's loads going; a mid-pass exit makes the compiler's own waits
+    // count the ring short)
+    do {
+        sweep(std::integral_constant<int, 0>());
+        sweep(std::integral_constant<int, 1>());
+    } while (left > 0);
+    BD_WAIT_VMCNT(0);  // (the ring's last loads, past the block's items, read nothing)
+#undef BD_VOFF
 }
 
 // ---------------------------------------------------------------- host side
@@ -961,7 +1136,7 @@ hipError_t launch_tile_plan(const BatchPlan& bp, char* batch, hipStream_t s) {
     hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(64), 0, s, (const int4*)(batch + bp.off_items),
                        (const int32_t*)(batch + bp.off_user), (uint32_t*)(batch + bp.off_meta),
                        (int32_t*)(batch + bp.off_tiles), (int32_t*)(batch + bp.off_torder),
-                       (int)bp.ntiles);
+                       (int32_t*)(batch + bp.off_tpre), (int)bp.ntiles);
     return hipGetLastError();
 }
 
@@ -985,28 +1160,36 @@ hipError_t launch_tile_encode(const BatchPlan& bp, const DeltaPlan& dp, char* ba
     return hipGetLastError();
 }
 
-// Non-GROUP modes: unit-per-wave launches (k_delta7), the units of d_in split into
+// Compute units of the current device (one persistent block each).
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// Non-GROUP modes: persistent launches (k_delta8), the units of d_in split into
 // ceil(units / 8) launches of equal width, in unit order.
-static hipError_t launch_delta7_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
+static hipError_t launch_delta8_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                                     const DeltaMatArg* mats, int n, hipStream_t s) {
     uint32_t* meta = (uint32_t*)(batch + bp.off_meta);
     const int32_t* tmeta = (const int32_t*)(batch + bp.off_tmeta);
     const int32_t* torder = (const int32_t*)(batch + bp.off_torder);
+    const int32_t* tpre = (const int32_t*)(batch + bp.off_tpre);
     const char* enc = batch + bp.off_enc;
     const int nunit = (int)bp.nunit;
     const int units = (int)((bp.d_in + 511) / 512);  // units past d_in are zero operands
-    const int nl = (units + kMaxW7 - 1) / kMaxW7;
+    const int nl = (units + kMaxW8 - 1) / kMaxW8;
     const int W = (units + nl - 1) / nl;
-    int64_t rows = 0;
-    for (int i = 0; i < n; ++i) rows += mats[i].d_out;
-    // chunks per block: as many as still leave about 512 blocks at the typical tile count
-    const int64_t ntyp = (bp.T + 15) / 16;
-    const int64_t chunks = (rows + 16 * W - 1) / (16 * W);
-    const int nch = chunks * ntyp >= 4 * 512 ? 4 : chunks * ntyp >= 2 * 512 ? 2 : 1;
-    const int64_t rows_rb = 16 * W * nch;
     DeltaMats dm = {};
     dm.n = n;
-    int rb = 0;
+    int cb = 0;
     for (int i = 0; i < n; ++i) {
         dm.signs[i] = mats[i].signs;
         dm.scales[i] = mats[i].scales;
@@ -1015,35 +1198,33 @@ static hipError_t launch_delta7_set(const BatchPlan& bp, const DeltaPlan& dp, ch
         dm.per_user[i] = dp.mode == BD_SCALE_MATRIX ? 1
                          : dp.mode == BD_SCALE_ROW ? mats[i].d_out
                                                    : bp.d_in;
-        dm.rb_begin[i] = rb;
-        rb += (int)((mats[i].d_out + rows_rb - 1) / rows_rb);
+        dm.rb_begin[i] = cb;
+        cb += (int)((mats[i].d_out + kChunkRows - 1) / kChunkRows);
     }
-    for (int i = n; i <= kMaxMats; ++i) dm.rb_begin[i] = rb;
-    const int64_t nrb8 = (rb + 7) / 8;
-    const dim3 gd((unsigned)(nrb8 * 8 * bp.ntiles));
+    for (int i = n; i <= kMaxMats; ++i) dm.rb_begin[i] = cb;
+    const dim3 gd((unsigned)device_cus());
     const bool f16 = dp.sdtype == BD_F16;
     for (int l = 0; l < nl; ++l) {
         const int u0 = l * W;  // (the last launch may hold fewer units: its extra waves add 0)
-#define BD_D7(MODE, F16, NCH)                                                                  \
-    hipLaunchKernelGGL((k_delta7<MODE, F16, NCH>), gd, dim3(64 * W), 0, s, dm, tmeta, torder,  \
-                       enc, meta, bp.d_in, nunit, u0, units, (int)bp.T, (int)bp.U)
-#define BD_D7N(MODE, F16)                                       \
-    do {                                                        \
-        if (nch == 4) BD_D7(MODE, F16, 4);                      \
-        else if (nch == 2) BD_D7(MODE, F16, 2);                 \
-        else BD_D7(MODE, F16, 1);                               \
+#define BD_D8(MODE, F16, RPW)                                                                  \
+    hipLaunchKernelGGL((k_delta8<MODE, F16, RPW>), gd, dim3(64 * W), 0, s, dm, tmeta, torder,  \
+                       tpre, enc, meta, bp.d_in, nunit, u0, units, (int)bp.T, (int)bp.U)
+#define BD_D8W(MODE, F16)                                      \
+    do {                                                       \
+        if (W == kMaxW8) BD_D8(MODE, F16, 1);                  \
+        else BD_D8(MODE, F16, kRT8);                           \
     } while (0)
         switch (dp.mode) {
             case BD_SCALE_MATRIX:
-                if (f16) BD_D7N(BD_SCALE_MATRIX, true); else BD_D7N(BD_SCALE_MATRIX, false);
+                if (f16) BD_D8W(BD_SCALE_MATRIX, true); else BD_D8W(BD_SCALE_MATRIX, false);
                 break;
             case BD_SCALE_ROW:
-                if (f16) BD_D7N(BD_SCALE_ROW, true); else BD_D7N(BD_SCALE_ROW, false);
+                if (f16) BD_D8W(BD_SCALE_ROW, true); else BD_D8W(BD_SCALE_ROW, false);
                 break;
-            default: BD_D7N(BD_SCALE_COL, false); break;
+            default: BD_D8W(BD_SCALE_COL, false); break;
         }
-#undef BD_D7N
-#undef BD_D7
+#undef BD_D8W
+#undef BD_D8
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1053,7 +1234,7 @@ static hipError_t launch_delta7_set(const BatchPlan& bp, const DeltaPlan& dp, ch
 hipError_t launch_delta6_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                              const DeltaMatArg* mats, int n, hipStream_t s) {
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
-    if (dp.mode != BD_SCALE_GROUP) return launch_delta7_set(bp, dp, batch, mats, n, s);
+    if (dp.mode != BD_SCALE_GROUP) return launch_delta8_set(bp, dp, batch, mats, n, s);
     uint32_t* meta = (uint32_t*)(batch + bp.off_meta);
     const int32_t* tmeta = (const int32_t*)(batch + bp.off_tmeta);
     const int32_t* torder = (const int32_t*)(batch + bp.off_torder);

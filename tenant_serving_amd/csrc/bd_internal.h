@@ -84,7 +84,7 @@ struct BatchPlan {
     int xdtype = 0;
     int64_t max_items = 0, ntiles = 0, nunit = 0;
     size_t off_meta = 0, off_perm = 0, off_user = 0, off_items = 0, off_tiles = 0, off_torder = 0,
-           off_tmeta = 0, off_enc = 0;
+           off_tpre = 0, off_tmeta = 0, off_enc = 0;
     size_t total = 0;
 };
 
