@@ -776,12 +776,13 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
          const char* __restrict__ enc, uint32_t* __restrict__ meta, int64_t d_in, int nunit,
          int u0, int units, int T, int U) {
     // dm.rb_begin: first chunk of each matrix; RPW: row tiles each wave sums per item
-    // (ceil(8 / W)); units: the units of d_in (every launch has W waves; a wave whose
+    // (at least ceil(8 / W)); units: the units of d_in (every launch has W waves; a wave whose
     // unit is past them adds zeros)
     static_assert(MODE != BD_SCALE_GROUP, "GROUP scales take k_delta6");
     constexpr bool COL = MODE == BD_SCALE_COL;
     constexpr int RT = kRT8, D = 2 * RT;  // ring: two sweeps
     __shared__ __attribute__((aligned(16))) f32x4 part[2][RT][kMaxW8][64];
+    __shared__ __attribute__((aligned(16))) float sF[kMaxMats][16];  // MATRIX: per matrix and token
     const int lane = threadIdx.x & 63;
     const int wv = uni((int)(threadIdx.x >> 6));
     const int W = uni((int)(blockDim.x >> 6));
@@ -929,6 +930,28 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         jt = -1;
         for (int q = 0; q < nut; ++q)
             if (__shfl(v, 32 + q) == c_tuser) jt = q;
+        if constexpr (MODE == BD_SCALE_MATRIX) {
+            // the scale of each token's user in each matrix of the launch (wave 0, lane:
+            // matrix lane / 16, token lane % 16; 0 for no token), after every wave is done
+            // with the last tile's
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("s_barrier" ::: "memory");
+            if (wv == 0) {
+                float f = 0.f;
+#pragma unroll
+                for (int q = 0; q < kMaxMats; ++q) {
+                    if (q < dm.n && G == q && c_tuser >= 0 && !dead) {
+                        typedef const __attribute__((address_space(1))) uint16_t* gh;
+                        typedef const __attribute__((address_space(1))) float* gf;
+                        const void* sp = pick_mat(dm.scales, q);
+                        f = SF16 ? f16_to_f32(((gh)sp)[c_tuser]) : ((gf)sp)[c_tuser];
+                    }
+                }
+                sF[G][n] = f;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("s_barrier" ::: "memory");
+        }
         cdh = (uint32_t)cdw;
         cdl = (uint32_t)(cdw >> 32);
         // c = (-4, -3, -1, 0) + (-1, 0, 0, 0) in e2m1 (1110, 1101, 1010, 0000 and 1010):
@@ -965,7 +988,9 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
     // (the lane's tokens 4 G .. 4 G + 3 and their users, from the tile's meta)
     auto ltok = [&](int e) __attribute__((always_inline)) { return tdead ? -1 : __shfl(trow, 4 * G + e); };
     auto lusr = [&](int e) __attribute__((always_inline)) { return __shfl(trow, 16 + 4 * G + e); };
-    float fs[4];
+    float fs[4] = {1.f, 1.f, 1.f, 1.f};
+    bool fresh = false;
+    int imi = 0;
     const void* isc = nullptr;
     int64_t ipu = 0;
     float* iy = nullptr;
@@ -998,14 +1023,47 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         irow0 = (int64_t)(c - pick_rb(dm.rb_begin, mi)) * kChunkRows;
         isc = pick_mat(dm.scales, mi);
         ipu = pick_mat(dm.per_user, mi);
-        // the factors of the wave's first row tile, loaded now (used at the item's end)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fs[e] = factor(wv, e);
+        imi = mi;
+        fresh = true;  // (ROW: its factors load in its first sweep)
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = ncor;
     };
-    // end of an item: the units' partials of each row tile meet in LDS; wave wv sums row
-    // tiles wv, wv + W, ... in unit order and adds them to y
+    // end of an item: the units' partials of each row tile meet in LDS (one barrier);
+    // wave wv sums row tiles wv, wv + W, ... in unit order and adds them to y.  The sums
+    // wait for the next item's first products (reduce_prev), whose latency they then
+    // share; the LDS buffer is the other one's until the next item's barrier.
+    bool pend = false;
+    int ptk[4] = {-1, -1, -1, -1};
+    float pfm[4] = {1.f, 1.f, 1.f, 1.f};
+    float* py = nullptr;
+    int64_t pdout = 0, prow0 = 0;
+    int pci = 0;
+    auto reduce_prev = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < RPW; ++t) {
+            const int r = wv + t * W;
+            if (r < RT) {  // uniform
+                f32x4 v = part[pci & 1][r][0][lane];
+                for (int q = 1; q < W; ++q) v += part[pci & 1][r][q][lane];
+                // (ROW: the wave's further row tiles load their factors here, before the
+                // next item changes the item state)
+                float f[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[e] = MODE == BD_SCALE_MATRIX ? pfm[e]
+                           : MODE == BD_SCALE_ROW ? (t > 0 ? factor(r, e) : fs[e]) : 1.f;
+                    if (SF16 && MODE == BD_SCALE_ROW) f[e] = f16_to_f32((uint16_t)__builtin_bit_cast(uint32_t, f[e]));
+                }
+                const int64_t o = prow0 + 16 * (int64_t)r + n;
+                if (o < pdout) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (ptk[e] >= 0) atomic_add_nr(py + (int64_t)ptk[e] * pdout + o, -(f[e] * v[e]));
+                }
+            }
+        }
+        pend = false;
+    };
     auto item_end = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) part[ci & 1][r][wv][lane] = acc[r];
@@ -1014,31 +1072,20 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
         asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-        for (int t = 0; t < RPW; ++t) {
-            const int r = wv + t * W;
-            if (r < RT) {  // uniform
-                f32x4 v = part[ci & 1][r][0][lane];
-                for (int q = 1; q < W; ++q) v += part[ci & 1][r][q][lane];
-                // tokens and factors first, every lane active (ROW: the wave's further row
-                // tiles load their factors here)
-                int tk[4];
-                float f[4];
+        for (int e = 0; e < 4; ++e) ptk[e] = ltok(e);  // (every lane active)
+        if constexpr (MODE == BD_SCALE_MATRIX) {
+            const f32x4 f4 = *(const f32x4*)&sF[imi][4 * G];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    tk[e] = ltok(e);
-                    f[e] = MODE == BD_SCALE_ROW && t > 0 ? factor(r, e) : fs[e];
-                }
-                const int64_t o = irow0 + 16 * (int64_t)r + n;
-                if (o < idout) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float sc = SF16 ? f16_to_f32((uint16_t)__builtin_bit_cast(uint32_t, f[e])) : f[e];
-                        if (tk[e] >= 0) atomic_add_nr(iy + (int64_t)tk[e] * idout + o, -(sc * v[e]));
-                    }
-                }
-            }
+            for (int e = 0; e < 4; ++e) pfm[e] = f4[e];
         }
+        py = iy;
+        pdout = idout;
+        prow0 = irow0;
+        pci = ci;
+        pend = true;
         ++ci;
+        // ROW with several row tiles per wave: their factors follow the item state
+        if constexpr (MODE == BD_SCALE_ROW && RPW > 1) reduce_prev();
     };
 
     // the ring: the first two sweeps, then the first tile and item
@@ -1102,6 +1149,16 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
             b = mfma_f6f4<3>(lo[3], b1[3], b, sl);
             acc[r] = a;
             acc[r + 1] = b;
+            if (r == 0 && fresh) {  // uniform: the item's first sweep
+                if (pend) reduce_prev();  // the previous item's sums
+                // ROW: this item's factors of the wave's first row tile (used when its sums
+                // are added, an item later)
+                if constexpr (MODE == BD_SCALE_ROW) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) fs[e] = factor(wv, e);
+                }
+                fresh = false;
+            }
         }
         if (left > 0 && ++j == nu) {  // uniform: the item is complete
             j = 0;
@@ -1126,6 +1183,7 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         sweep(std::integral_constant<int, 0>());
         sweep(std::integral_constant<int, 1>());
     } while (left > 0);
+    if (pend) reduce_prev();
     BD_WAIT_VMCNT(0);  // (the ring's last loads, past the block's items, read nothing)
 #undef BD_VOFF
 }
@@ -1212,6 +1270,8 @@ static hipError_t launch_delta8_set(const BatchPlan& bp, const DeltaPlan& dp, ch
 #define BD_D8W(MODE, F16)                                      \
     do {                                                       \
         if (W == kMaxW8) BD_D8(MODE, F16, 1);                  \
+        else if (W >= 4) BD_D8(MODE, F16, 2);                  \
+        else if (W >= 2) BD_D8(MODE, F16, 4);                  \
         else BD_D8(MODE, F16, kRT8);                           \
     } while (0)
         switch (dp.mode) {
