@@ -213,6 +213,26 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
                    const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
                    bd_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
 
+/* bd_apply for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument and no allocation of any kind.  The launches use a scratch array of the
+ * library, BD_NOALLOC_SCRATCH_BYTES per device (held by every device the library runs
+ * on until the process ends); a call whose bd_apply workspace would be larger
+ * (bd_apply_workspace_bytes) returns BD_ERR_WORKSPACE and enqueues nothing.  Every
+ * call on one device shares that device's scratch: calls that overlap on one device
+ * (other streams, other host threads) race and give undefined results; calls in
+ * order on one stream are safe.  status (device uint32, may be NULL) receives the
+ * call's status word as written to a workspace by bd_apply (read it as bd_device_status
+ * would: bit 0 non-finite, bit 1 user id, bit 2 batch); other arguments, results and
+ * errors as for
+ * bd_apply. */
+#define BD_NOALLOC_SCRATCH_BYTES (8u << 20)
+bd_status bd_apply_noalloc(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                           const void* w_base, int64_t d_out, const uint64_t* signs_bank,
+                           const void* scales_bank, const bd_compress_params* p,
+                           int32_t n_users, const int32_t* user_ids, void* y, bd_dtype y_dtype,
+                           uint32_t* status, void* stream);
+
 /* The three phases of bd_apply, for callers that apply many matrices to one
  * batch (e.g. q, k and v read the same X and the same user ids): prepare the
  * batch once, then run the shared base product and the per-user delta product

@@ -81,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.bd_apply.restype = ctypes.c_int
         L.bd_apply.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp, P, i32, vp, vp,
                                ctypes.c_int, vp, sz, vp]
+        L.bd_apply_noalloc.restype = ctypes.c_int
+        L.bd_apply_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp, P, i32, vp, vp,
+                                       ctypes.c_int, vp, vp]
         L.bd_device_status.restype = ctypes.c_int
         L.bd_device_status.argtypes = [vp, vp]
         L.bd_batch_workspace_bytes.restype = sz
@@ -268,6 +271,25 @@ def bd_apply(x, w_base, signs_bank, scales_bank, p, n_users, user_ids, y, worksp
                               _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p), int(n_users),
                               _ptr(user_ids), _ptr(y), _dtype_code(y), _ptr(workspace),
                               _nbytes(workspace), _stream(x, stream)))
+
+
+def bd_apply_noalloc(x, w_base, signs_bank, scales_bank, p, n_users, user_ids, y, status=None,
+                     stream=None) -> int:
+    """bd_apply without a workspace (the library's scratch; see include/bitdelta.h);
+    status: optional int32[1] device tensor that receives the call's status word."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    T, d_in = x.shape
+    dev = x.device
+    d_out = w_base.shape[0]
+    _dev(w_base, "w_base", (x.dtype,), (d_out, d_in), dev)
+    _bank(signs_bank, scales_bank, p, n_users, d_out, d_in, dev)
+    _ids(user_ids, T, dev)
+    _dev(y, "y", (torch.float32, torch.bfloat16), (T, d_out), dev)
+    _dev(status, "status", (torch.int32,), (1,), dev, optional=True)
+    return int(lib().bd_apply_noalloc(_ptr(x), _dtype_code(x), T, d_in, _ptr(w_base), d_out,
+                                      _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p),
+                                      int(n_users), _ptr(user_ids), _ptr(y), _dtype_code(y),
+                                      _ptr(status), _stream(x, stream)))
 
 
 def bd_device_status(workspace, stream=None) -> int:

@@ -5,12 +5,41 @@
 // untouched.
 #include "bd_internal.h"
 
+#include <mutex>
+
 using namespace bd;
+
+// Scratch of bd_apply_noalloc: the workspace of its launches, one copy per device for
+// the life of the process (its device address is taken once per device below).
+static __device__ __align__(256) char scratch[BD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
 bool valid_wdtype(int d) { return d == BD_F32 || d == BD_BF16; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Device address of `scratch` on the current device (looked up on the first call per
+// device, with that device current).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+bd_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BD_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return BD_ERR_DEVICE;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return BD_OK;
+}
+
+// *dst = *src (one word, device to device), or *dst = 0 without src
+__global__ void k_copy_word(const uint32_t* src, uint32_t* dst) {
+    if (threadIdx.x == 0) dst[0] = src ? src[0] : 0u;
+}
 
 }  // namespace
 
@@ -315,10 +344,14 @@ bd_status bd_apply_q8(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, 
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
-bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const void* w_base,
-                   int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
-                   const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
-                   bd_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// bd_apply on a workspace of ws_bytes (the caller's, or the no-allocation scratch).
+static bd_status apply_on(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                          const void* w_base, int64_t d_out, const uint64_t* signs_bank,
+                          const void* scales_bank, const bd_compress_params* p, int32_t n_users,
+                          const int32_t* user_ids, void* y, bd_dtype y_dtype, void* workspace,
+                          size_t ws_bytes, void* stream) {
     if (!p) return BD_ERR_INVALID_ARG;
     ApplyPlan pl;
     bd_status st = make_apply_plan(p, T, n_users, d_out, d_in, x_dtype, y_dtype, &pl);
@@ -354,6 +387,38 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
     if (e == hipSuccess && y_dtype == BD_BF16)
         e = launch_cast_bf16(yacc, (uint16_t*)y, T * d_out, s);
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
+extern "C" {
+
+bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const void* w_base,
+                   int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
+                   const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
+                   bd_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream) {
+    return apply_on(x, x_dtype, T, d_in, w_base, d_out, signs_bank, scales_bank, p, n_users,
+                    user_ids, y, y_dtype, workspace, ws_bytes, stream);
+}
+
+bd_status bd_apply_noalloc(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                           const void* w_base, int64_t d_out, const uint64_t* signs_bank,
+                           const void* scales_bank, const bd_compress_params* p,
+                           int32_t n_users, const int32_t* user_ids, void* y, bd_dtype y_dtype,
+                           uint32_t* status, void* stream) {
+    if (!p) return BD_ERR_INVALID_ARG;
+    if (status && !aligned(status, 4)) return BD_ERR_INVALID_ARG;
+    const size_t need = bd_apply_workspace_bytes(p, T, n_users, d_out, d_in, x_dtype, y_dtype);
+    if (need > (size_t)BD_NOALLOC_SCRATCH_BYTES) return BD_ERR_WORKSPACE;  // (0: invalid sizes,
+                                                                           // reported below)
+    void* ws = nullptr;
+    bd_status st = scratch_address(&ws);
+    if (st != BD_OK) return st;
+    st = apply_on(x, x_dtype, T, d_in, w_base, d_out, signs_bank, scales_bank, p, n_users,
+                  user_ids, y, y_dtype, ws, BD_NOALLOC_SCRATCH_BYTES, stream);
+    if (st != BD_OK || !status) return st;
+    // the call's status word (its launches rewrite word 0 of the workspace; none for T == 0)
+    hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                       T > 0 ? (const uint32_t*)ws : (const uint32_t*)nullptr, status);
+    return hipGetLastError() == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
 // Shared validation of the two decode-path entry points.
