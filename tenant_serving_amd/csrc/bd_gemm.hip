@@ -3,10 +3,9 @@
 // gfx950 matrix cores ([P2] "Systems Mechanics" 1: one dense product of the
 // whole batch with the shared base weight).
 //
-// Block tile: BR rows of W x BT tokens (128 x 256, 128 x 128, 64 x 128 or 64 x 64), 4 waves
-// (2 x 2), each BR/2 x BT/2 =
-// (BR/64) x (BT/64) tiles of v_mfma_f32_32x32x16_bf16 with the accumulators in
-// AGPRs.  K advances BK columns per stage through a ring of NS LDS stages.
+// Block tile: BR rows of W x BT tokens (256 x 256 with 8 waves, two per SIMD, in 4 x 2;
+// 128 x 256, 128 x 128, 64 x 128 or 64 x 64 with 4 waves in 2 x 2), each wave a block
+// of (BR / (NW/2) / 32) x (BT / 64) tiles of v_mfma_f32_32x32x16_bf16.  K advances BK columns per stage through a ring of NS LDS stages.
 // Global -> LDS copies are buffer loads that write LDS directly (16 bytes per
 // lane, 1 KB per instruction); each lane picks the global piece that belongs
 // at its LDS slot; with BK = 64 a tile row is one 128-byte global piece, so the
@@ -60,15 +59,19 @@ __device__ __forceinline__ uint32_t swz(int r, int c) {
 
 // Kernel templates live outside the anonymous namespace: the host compiler does
 // not emit the launch stubs of internal-linkage kernel templates.
-template <int BR, int BT, int BK, int NS>
-__global__ void __launch_bounds__(256)
+template <int BR, int BT, int BK, int NS, int NW>
+__global__ void __launch_bounds__(64 * NW)
 k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt) {
-    constexpr int MI = BR / 64, NJ = BT / 64;  // 32 x 32 tiles per wave
+    // NW waves: NW / 2 along the rows, 2 along the tokens
+    constexpr int NWR = NW / 2;
+    constexpr int MI = BR / NWR / 32, NJ = BT / 64;  // 32 x 32 tiles per wave
     constexpr int CPR = BK / 8, RPI = 64 / CPR;  // chunks per row, rows per copy instruction
     constexpr int kWBytes = BR * BK * 2, kXBytes = BT * BK * 2;
     constexpr int kStageBytes = kWBytes + kXBytes;
-    constexpr int kWInst = kWBytes / 1024 / 4, kXInst = kXBytes / 1024 / 4;  // per wave
-    static_assert(kWBytes % 4096 == 0 && kXBytes % 4096 == 0, "whole copy instructions per wave");
+    constexpr int kWInst = kWBytes / 1024 / NW, kXInst = kXBytes / 1024 / NW;  // per wave
+    static_assert(kWBytes % (1024 * NW) == 0 && kXBytes % (1024 * NW) == 0,
+                  "whole copy instructions per wave");
+    static_assert(MI >= 1 && BR % (32 * NWR) == 0, "32-row tiles per wave");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     // block -> (row tile, token tile); the token tiles of one row tile share an XCD.
     // Row tiles run over the matrices of the set back to back.
@@ -151,7 +154,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
             u32x4 A[MI], Bv[NJ];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                A[i] = *(const u32x4*)(wt_base + swz<BK>(wr * (BR / 2) + 32 * i + m32, 2 * kk + h));
+                A[i] = *(const u32x4*)(wt_base + swz<BK>(wr * (BR / NWR) + 32 * i + m32, 2 * kk + h));
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
                 Bv[j] = *(const u32x4*)(xt_base + swz<BK>(wt * (BT / 2) + 32 * j + m32, 2 * kk + h));
@@ -171,7 +174,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
         for (int i = 0; i < MI; ++i) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const int o = r0 + wr * (BR / 2) + 32 * i + 8 * b + 4 * h;
+                const int o = r0 + wr * (BR / NWR) + 32 * i + 8 * b + 4 * h;
                 float* dst = y + (int64_t)t * N + o;
                 const f32x4 v = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2],
                                  acc[i][j][4 * b + 3]};
@@ -188,7 +191,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
 
 namespace {
 
-template <int BR, int BT, int BK, int NS>
+template <int BR, int BT, int BK, int NS, int NW = 4>
 hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
                        hipStream_t s) {
     GemmMats gm = {};
@@ -206,8 +209,8 @@ hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const GemmMatArg*
     const int nrt8 = (rt + 7) / 8 * 8;
     const unsigned blocks = (unsigned)(nrt8 * ntt);
     constexpr int lds = NS * (BR + BT) * BK * 2;
-    k_gemm<BR, BT, BK, NS><<<dim3(blocks), dim3(256), lds, s>>>((const uint16_t*)x, gm, (int)T,
-                                                               (int)d_in, ntt);
+    k_gemm<BR, BT, BK, NS, NW><<<dim3(blocks), dim3(64 * NW), lds, s>>>((const uint16_t*)x, gm,
+                                                                       (int)T, (int)d_in, ntt);
     return hipGetLastError();
 }
 
@@ -243,6 +246,7 @@ hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMat
         for (int i = 0; i < n; ++i) r += (mats[i].d_out + br - 1) / br;
         return r * ((T + bt - 1) / bt);
     };
+    if (blocks(256, 256) >= 200) return launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s);
     if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s);
     if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 4>(x, T, d_in, mats, n, s);
     if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 4>(x, T, d_in, mats, n, s);

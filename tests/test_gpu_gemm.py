@@ -2,8 +2,8 @@
 (the tiled matrix-core GEMM): bd_base_gemm against a binary64 product of the
 same bf16 inputs, over shapes with ragged token counts, row counts that are not
 multiples of the 256-row tile, K from one 64-column stage up, and a batch past
-one token tile, and every tile shape (the dispatch takes the largest of 128 x 256,
-128 x 128, 64 x 128 and 64 x 64 that yields about 200 blocks).  Accumulation is fp32
+one token tile, and every tile shape (the dispatch takes the largest of 256 x 256
+(8 waves), 128 x 256, 128 x 128, 64 x 128 and 64 x 64 that yields about 200 blocks).  Accumulation is fp32
 over exact bf16 products, so the bound is the fp32 one (max |err| <= 1e-4 * rms)."""
 import numpy as np
 import pytest
@@ -25,6 +25,8 @@ SHAPES = [  # (T, d_out, d_in)
     (512, 4096, 256),    # 64 x 128
     (256, 14336, 128),   # 128 x 128
     (2048, 4096, 128),   # 128 x 256
+    (512, 25600, 128),   # 256 x 256, 8 waves
+    (700, 25700, 192),   # 256 x 256 with ragged tokens and rows
     (40, 10240, 256),    # 17..64 tokens on a wide matrix: 64 x 64 tiles
 ]
 
