@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--load", action="store_true",
                     help="also time loading one user's packed deltas of the Llama-3.1-8B linear "
                          "stack from pinned host memory, against the dense bf16 weights (stderr)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="stack: first N layers only (0: all 32); for counter runs, not the headline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device 3 times (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters)")
@@ -132,7 +134,7 @@ class Stack:
     # matrices of a layer that read one activation tensor: (first, count)
     GROUPS = ((0, 3), (3, 1), (4, 2), (6, 1))
 
-    def __init__(self, dev):
+    def __init__(self, dev, layers=0):
         import numpy as np
         import torch
 
@@ -146,7 +148,9 @@ class Stack:
         self.ids = torch.from_numpy(self.ids_np).to(dev)
         self.p = B.params("matrix")
         self.active = sorted(set(int(u) for u in self.ids_np if 0 <= u < self.U))
-        mats = w.matrices
+        # (layers > 0: the first `layers` layers only, for counter runs; every layer has the
+        # same launches, so per-launch figures do not change)
+        mats = w.matrices[:7 * layers] if layers > 0 else w.matrices
         big = max(m.d_out * m.d_in for m in mats)
         wf = torch.empty(big, dtype=torch.bfloat16, device=dev)
         cws = B.workspace(max(B.bd_compress_workspace_bytes(self.p, m.d_out, m.d_in)
@@ -173,7 +177,7 @@ class Stack:
         torch.cuda.synchronize()
         assert B.bd_device_status(cws) == B.BD_OK
         del wf, cws
-        self.xs = [S.dev_x(w, g) for g in range(len(w.xgroups))]
+        self.xs = [S.dev_x(w, g) for g in range(4 * (len(mats) // 7))]
         self.batches = {}
         for d_in in sorted(set(w.xgroups)):
             self.batches[d_in] = B.workspace(
@@ -243,7 +247,7 @@ class Stack:
 def stack_leg(args, dev):
     import torch
 
-    S = Stack(dev)
+    S = Stack(dev, args.layers)
     B = S.B
     log(f"stack ready: {S.n_mats} matrices, {S.U} users' banks, {len(S.active)} active "
         f"({S.setup_s:.1f} s)")
@@ -277,7 +281,10 @@ def stack_leg(args, dev):
 
     ms_per_step = wall_us * 1e-3
     value = S.bytes_step / (ms_per_step * 1e-3) / 1e9
-    n_delta = n_gemm = 4 * S.n_layers  # grouped launches: q|k|v, o, gate|up, down
+    n_gemm = 4 * S.n_layers  # grouped launches: q|k|v, o, gate|up, down
+    # delta launches: one per 8 units of 512 columns of each group's d_in (down: 28 units
+    # in 4 launches of 7)
+    n_delta = S.n_layers * sum(-(-(-(-d // 512)) // 8) for d in (4096, 4096, 4096, 14336))
     delta_gbs = S.bytes_delta / (phases["delta"] * 1e-6) / 1e9
     gemm_tfs = S.flops_gemm / (phases["gemm"] * 1e-6) / 1e12
     rl_delta = {"bound": "hbm", "kernel": "k_delta8", "achieved": round(delta_gbs, 1),
@@ -306,6 +313,7 @@ def stack_leg(args, dev):
         "phases_us_per_step": {k: round(v, 1) for k, v in phases.items()},
         "phase_launches_per_step": {"prepare": len(S.batches), "encode": 4 * S.n_layers,
                                     "gemm": n_gemm, "delta": n_delta},
+        "delta_launches_per_layer": "q|k|v 1, o 1, gate|up 1, down 4 (7 units each)",
         "matrices_per_launch": "q|k|v, o, gate|up, down (grouped calls on one encoding)",
         "roofline": dominant,
         "roofline_secondary": other,
