@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import DEV, TOL_BF16, custom, gpu_bank, max_err_vs_rms, o_sdtype, oracle_bank
+from gpu_util import DEV, custom, gpu_bank, max_err_vs_rms, o_sdtype, oracle_bank, tol_delta
 from tenant_serving_amd import bitdelta as B
 from tenant_serving_amd import synth as S
 
@@ -50,7 +50,7 @@ def test_shared_encoding_equals_per_matrix_delta_apply(mode):
     _, _, yd = O.apply(S.host_x(mats[0][0], 0), wb_np, words, scs, p.mode, ids,
                        g=p.group_size, sdtype=o_sdtype(p))
     err, rms = max_err_vs_rms(y.cpu().numpy(), yd)
-    assert err <= TOL_BF16 * rms
+    assert err <= tol_delta(mode) * rms, (mode, err, rms)
 
 
 def test_product_on_another_modes_encoding_reports_batch_error():

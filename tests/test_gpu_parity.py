@@ -10,8 +10,9 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import (DEV, TOL_BF16, TOL_F32, custom, gpu_bank, max_err_vs_rms, o_sdtype,
-                      oracle_bank, rel_err_ok, scales_as_f64, to_np)
+from gpu_util import (DEV, TOL_BF16, TOL_F32, assert_delta_within_bound, custom, gpu_bank,
+                      max_err_vs_rms, o_sdtype,
+                      oracle_bank, rel_err_ok, scales_as_f64, to_np, tol_delta)
 from tenant_serving_amd import bitdelta as B
 from tenant_serving_amd import synth as S
 
@@ -158,7 +159,10 @@ def test_apply_parity(case):
     # the delta term alone: same bank, zero base weight
     y0 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
     err0, rms0 = max_err_vs_rms(y0.cpu().numpy(), yd)
-    assert err0 <= tol * rms0, (err0, rms0)
+    tol0 = TOL_F32 if dtype == S.F32 else tol_delta(mode)
+    assert err0 <= tol0 * rms0, (err0, rms0)
+    if dtype == S.BF16:
+        assert_delta_within_bound(y0.cpu().numpy(), yd, x, osc, p, ids)
     assert np.all(y0.cpu().numpy()[ids < 0] == 0)
 
 
@@ -183,7 +187,8 @@ def test_apply_parity_large_batch(mode):
     assert err <= TOL_BF16 * rms, (err, rms)
     y0 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
     err0, rms0 = max_err_vs_rms(y0.cpu().numpy(), yd)
-    assert err0 <= TOL_BF16 * rms0, (err0, rms0)
+    assert err0 <= tol_delta(mode) * rms0, (err0, rms0)
+    assert_delta_within_bound(y0.cpu().numpy(), yd, S.host_x(w, 0), osc, p, ids)
 
 
 @pytest.mark.parametrize("mode", ["matrix", "col"])
@@ -206,7 +211,8 @@ def test_apply_parity_single_wave_grouping(mode):
     assert err <= TOL_BF16 * rms, (err, rms)
     y0 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
     err0, rms0 = max_err_vs_rms(y0.cpu().numpy(), yd)
-    assert err0 <= TOL_BF16 * rms0, (err0, rms0)
+    assert err0 <= tol_delta(mode) * rms0, (err0, rms0)
+    assert_delta_within_bound(y0.cpu().numpy(), yd, S.host_x(w, 0), osc, p, ids)
 
 
 def test_apply_out_of_range_user_gets_base_and_status():

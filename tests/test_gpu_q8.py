@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import DEV, TOL_BF16, custom, gpu_bank, max_err_vs_rms, o_sdtype, oracle_bank, to_np
+from gpu_util import (DEV, TOL_BF16, assert_delta_within_bound, custom, gpu_bank, max_err_vs_rms,
+                      o_sdtype, oracle_bank, to_np, tol_delta)
 from tenant_serving_amd import bitdelta as B
 from tenant_serving_amd import synth as S
 
@@ -55,7 +56,8 @@ def test_apply_on_int8_base_matches_oracle(case):
     err, rms = max_err_vs_rms(y.float().cpu().numpy(), yr)
     assert err <= TOL_BF16 * rms, (err, rms)
     err0, rms0 = max_err_vs_rms(y0.cpu().numpy(), yd)
-    assert err0 <= TOL_BF16 * rms0, (err0, rms0)
+    assert err0 <= tol_delta(mode) * rms0, (err0, rms0)
+    assert_delta_within_bound(y0.cpu().numpy(), yd, S.host_x(w, 0), osc, p, ids)
     assert np.all(y0.cpu().numpy()[ids < 0] == 0)
 
 

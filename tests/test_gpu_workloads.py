@@ -1,17 +1,22 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration the
-benchmark uses (bd_apply on device-generated inputs), against the CPU oracle on
-sampled outputs: for sampled (user, matrix) pairs the oracle compresses the
-whole matrix from host-generated inputs and the packed signs must match bit
-for bit and the scales within 1e-6 relative; for sampled tokens and output
-rows the oracle computes y from its own banks and the GPU y must match within
-max|err| <= tol * rms (1e-4 fp32, 2e-2 bf16), also for the delta term alone
-(the same banks applied on a zero base weight)."""
+benchmark uses (bd_apply on device-generated inputs), against the CPU oracle:
+- compression: for sampled (user, matrix) pairs the oracle compresses the whole
+  matrix from host-generated inputs; the packed signs must match bit for bit and the
+  scales within 1e-6 relative;
+- apply: every token of the batch on sampled output rows (the first, the last and a
+  seeded sample), with the oracle's banks of every user in the batch restricted to
+  those rows (built from the oracle's own steps; the clip bounds and the MATRIX and
+  COL scales still read each user's whole matrix); y must match within
+  max|err| <= tol * rms (1e-4 fp32, 2e-2 bf16), and the delta term alone (the same
+  banks on a zero base weight) within 5e-3 rms (1e-2 for COL scales)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from gpu_util import DEV, TOL_BF16, TOL_F32, max_err_vs_rms, rel_err_ok, scales_as_f64, to_np
+from gpu_util import (DEV, TOL_BF16, TOL_F32, assert_delta_within_bound, max_err_vs_rms,
+                      oracle_rows_bank, rel_err_ok,
+                      scales_as_f64, to_np, tol_delta)
 from tenant_serving_amd import bitdelta as B
 from tenant_serving_amd import synth as S
 
@@ -56,8 +61,9 @@ def rows_of_scales(sc, p, mat, rows):
     return sc  # MATRIX (1 value) and COL (d_in values) do not depend on the row
 
 
-def check_matrix(w, m, ids, check_users, tokens, rows, wb_dev=None, x_dev=None, banks=None):
-    """Compress every user on the GPU, apply the batch, compare with the oracle."""
+def check_matrix(w, m, ids, check_users, rows, wb_dev=None, x_dev=None, banks=None):
+    """Compress every user on the GPU, apply the whole batch, compare with the oracle:
+    whole-matrix compression of `check_users`, and every token on the output rows `rows`."""
     mat = w.matrices[m]
     p = params_of(w, mat)
     if wb_dev is None:
@@ -69,39 +75,42 @@ def check_matrix(w, m, ids, check_users, tokens, rows, wb_dev=None, x_dev=None, 
     y = B.apply(x_dev, wb_dev, signs, scales, p, ids_dev, check=True)
     y0 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
     torch.cuda.synchronize()
+    got = y.float().cpu().numpy()[:, rows]
+    got0 = y0.cpu().numpy()[:, rows]
+    del y, y0
 
-    wb_np = S.host_wbase(w, m)
     # compress parity on the sampled users (whole matrices)
-    users = sorted(set(check_users) | set(int(ids[t]) for t in tokens if ids[t] >= 0))
-    ob = {}
-    for u in users:
+    wb_np = S.host_wbase(w, m)
+    for u in check_users:
         words, sc = oracle_user(w, m, u, wb_np, p)
-        ob[u] = (words, sc)
-        if u in check_users:
-            assert np.array_equal(to_np(signs[u]), words), f"signs differ: user {u} matrix {mat.name}"
-            assert rel_err_ok(scales_as_f64(to_np(scales[u]), p), scales_as_f64(sc, p)), \
-                f"scales differ: user {u} matrix {mat.name}"
-    # apply parity on sampled tokens x rows
-    tok_users = sorted(set(int(ids[t]) for t in tokens if ids[t] >= 0))
-    remap = {u: i for i, u in enumerate(tok_users)}
-    sub_ids = np.array([remap.get(int(ids[t]), -1) for t in tokens], dtype=np.int32)
-    x_np = S.host_x(w, mat.xgroup, tokens=tokens)
-    if tok_users:
-        words_bank = np.stack([ob[u][0][rows] for u in tok_users])
-        sc_bank = np.stack([rows_of_scales(ob[u][1], p, mat, rows) for u in tok_users])
+        assert np.array_equal(to_np(signs[u]), words), f"signs differ: user {u} matrix {mat.name}"
+        assert rel_err_ok(scales_as_f64(to_np(scales[u]), p), scales_as_f64(sc, p)), \
+            f"scales differ: user {u} matrix {mat.name}"
+    del wb_np
+    # apply parity: every token on the sampled rows, banks of every user in the batch
+    users = sorted(set(int(u) for u in ids if u >= 0))
+    remap = np.full(w.n_users, -1, dtype=np.int32)
+    remap[users] = np.arange(len(users), dtype=np.int32)
+    sub_ids = np.where(ids >= 0, remap[np.maximum(ids, 0)], -1).astype(np.int32)
+    if users:
+        words_bank, sc_bank = oracle_rows_bank(w, m, p, users, rows)
     else:
         words_bank = np.zeros((1, len(rows), mat.d_in // 64), dtype=np.uint64)
         sc_bank = np.zeros((1, 1), dtype=np.float32)
-    yr, yb, yd = O.apply(x_np, wb_np[rows], words_bank, sc_bank, p.mode, sub_ids,
-                         g=p.group_size, sdtype=o_sd(p))
+    x_np = S.host_x(w, mat.xgroup)
+    yr, yb, yd = O.apply(x_np, S.host_wbase(w, m, rows), words_bank, sc_bank,
+                         p.mode, sub_ids, g=p.group_size, sdtype=o_sd(p))
     tol = TOL_F32 if w.dtype == S.F32 else TOL_BF16
-    got = y.float().cpu().numpy()[np.ix_(tokens, rows)]
     err, rms = max_err_vs_rms(got, yr)
     assert err <= tol * rms, (mat.name, err, rms)
-    got0 = y0.cpu().numpy()[np.ix_(tokens, rows)]
     if np.any(yd != 0):
+        tol0 = TOL_F32 if w.dtype == S.F32 else tol_delta(p.mode)
         err0, rms0 = max_err_vs_rms(got0, yd)
-        assert err0 <= tol * rms0, (mat.name, "delta only", err0, rms0)
+        print(f"{mat.name}: {len(users)} users, {len(ids)} tokens x {len(rows)} rows, "
+              f"delta-only max|err|/rms = {err0 / rms0:.3e}")
+        assert err0 <= tol0 * rms0, (mat.name, "delta only", err0, rms0)
+        if w.dtype == S.BF16:
+            assert_delta_within_bound(got0, yd, x_np, sc_bank, p, sub_ids, mat.name)
     return signs, scales
 
 
@@ -122,23 +131,23 @@ def test_workload1_tiny_fp32_full():
     w = S.workload(1)
     ids = S.user_ids(w)
     mat = w.matrices[0]
-    check_matrix(w, 0, ids, [0], list(range(w.T)), list(range(mat.d_out)))
+    check_matrix(w, 0, ids, [0], list(range(mat.d_out)))
 
 
 @pytest.mark.timeout(600)
 def test_workload2_q_proj_16_users():
     w = S.workload(2)
     ids = S.user_ids(w)
-    check_matrix(w, 0, ids, [0, 7, 15], list(range(w.T)), pick_rows(4096, 192, 2))
+    check_matrix(w, 0, ids, [0, 7, 15], pick_rows(4096, 192, 2))
 
 
 @pytest.mark.timeout(900)
 def test_workload3_mlp_clipped_group_scales():
     w = S.workload(3)
     ids = S.user_ids(w)
-    tokens = pick_tokens(ids, 3, 3)
+    user = int(ids[pick_tokens(ids, 1, 3)[0]])
     for m in range(3):
-        check_matrix(w, m, ids, [int(ids[tokens[0]])], tokens, pick_rows(w.matrices[m].d_out, 96, 30 + m))
+        check_matrix(w, m, ids, [user], pick_rows(w.matrices[m].d_out, 96, 30 + m))
         torch.cuda.empty_cache()
 
 
@@ -146,22 +155,22 @@ def test_workload3_mlp_clipped_group_scales():
 def test_workload4_qwen_mlp_per_axis_mixed_batch():
     w = S.workload(4)
     ids = S.user_ids(w)
-    # one token of a prefill chunk, one decode token, one more at random
-    tokens = sorted({5, 8 * 128 + 3, pick_tokens(ids, 1, 4)[0]})
+    # the user of a prefill chunk and the user of a decode token
+    users = sorted({int(ids[5]), int(ids[8 * 128 + 3])})
     for m in range(3):
-        check_matrix(w, m, ids, [int(ids[5])], tokens, pick_rows(w.matrices[m].d_out, 64, 40 + m))
+        check_matrix(w, m, ids, users, pick_rows(w.matrices[m].d_out, 64, 40 + m))
         torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(1200)
 def test_workload5_llama8b_stack_128_users():
     """All 224 matrices' banks resident (about 112 GB), one decode step of 512
-    tokens through every matrix; sampled checks on layer 0 q_proj and layer 31
-    down_proj (compress of the first token's user, apply on sampled tokens)."""
+    tokens through every matrix; checks on layer 0 q_proj and layer 31 down_proj
+    (compress of a sampled token's user, apply of every token on sampled rows)."""
     w = S.workload(5)
     ids = S.user_ids(w)
     ids_dev = torch.from_numpy(ids).to(DEV)
-    tokens = pick_tokens(ids, 3, 5)
+    tokens = pick_tokens(ids, 1, 5)
     checked = {0: None, 223: None}
     banks, bases, xs = [], [], {}
     for m, mat in enumerate(w.matrices):
@@ -180,7 +189,7 @@ def test_workload5_llama8b_stack_128_users():
     for m in checked:
         mat = w.matrices[m]
         rows = pick_rows(mat.d_out, 48, 50 + m)
-        check_matrix(w, m, ids, [int(ids[tokens[0]])], tokens, rows, wb_dev=bases[m],
+        check_matrix(w, m, ids, [int(ids[tokens[0]])], rows, wb_dev=bases[m],
                      x_dev=xs[mat.xgroup], banks=banks[m])
         y_again = ys[m].cpu().numpy()
         y_ref = B.apply(xs[mat.xgroup], bases[m], banks[m][0], banks[m][1], params_of(w, mat),
