@@ -5,14 +5,14 @@
  *
  * The operations are those described on the pages
  *  [P1] "BitDelta (ZIP-7) - Per-User Personalization Without LoRA"
- *       (hanzoskills.com/bitdelta), "How BitDelta Works" steps 1-5 and
- *       "Safety Benefits / 1. Outlier Clipping";
+ *       (hanzoskills.com/bitdelta), "How BitDelta Works" steps 1-5,
+ *       "Safety Benefits / 1. Outlier Clipping" and "Production Serving";
  *  [P2] "BitDelta Guide: 1-Bit Delta Quantization for LLM Serving"
  *       (aifetchly blog), "1. Mathematical Formulation", "2. Optimal L2 Norm
  *       Initialization", "Systems Mechanics: Fused 1-Bit GEMM and
- *       Multi-Tenant Serving Runtimes" 1-2;
+ *       Multi-Tenant Serving Runtimes" 1-3;
  *  [P5] "Per-Axis Weight Deltas for Frequent Model Updates" (ai.info summary
- *       of arXiv 2512.19720), "Key Contributions" 1 and the implementation
+ *       of arXiv 2512.19720), "Key Contributions" 1 and 4 and the implementation
  *       details under "Methodology in Plain English".
  *
  * Conventions shared by every entry point
@@ -21,8 +21,8 @@
  *    X[T][d_in]; outputs Y[T][d_out].
  *  - Every pointer except the host-side `params` structs is a DEVICE pointer
  *    owned by the caller.  The library never allocates, frees or keeps device
- *    memory; scratch space is the caller's `workspace`, sized by the
- *    *_workspace_bytes queries.
+ *    memory (the one exception: the static scratch of bd_apply_noalloc); scratch
+ *    space is the caller's `workspace`, sized by the *_workspace_bytes queries.
  *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
  *    stream).  All work is enqueued on it; no entry point synchronises except
  *    bd_device_status.  Calls are re-entrant: no global mutable state.
@@ -212,6 +212,45 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
                    int64_t d_out, const uint64_t* signs_bank, const void* scales_bank,
                    const bd_compress_params* p, int32_t n_users, const int32_t* user_ids, void* y,
                    bd_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/* bd_apply on banks held in a resident pool of slots: the deltas of a bounded set of
+ * users stay in HBM while the rest wait in host memory and are swapped in per
+ * request ([P2] "Systems Mechanics" 3, dynamic hot-swapping: deltas cached in the
+ * GPU's spare memory or streamed from host memory; [P1] "Production Serving": the
+ * base model stays on the GPU, the deltas in CPU memory; [P5] "Key Contributions" 4:
+ * a user's packed delta of a module moves in one transfer).  A module's slot holds
+ * each of its matrices' signs and scales at fixed offsets, so one copy fills a slot
+ * and the banks of one matrix are strided through the pool.
+ *
+ *  signs_pool    : signs of slot 0 of this matrix; slot k's at signs_pool +
+ *                  k * signs_stride bytes ([d_out][d_in/64] uint64 each).
+ *  scales_pool   : scales of slot 0; slot k's at scales_pool + k * scales_stride
+ *                  bytes (bd_scales_count values of p->scale_dtype each).
+ *  signs_stride, scales_stride : bytes between slots, multiples of 16 and at least
+ *                  one slot's signs / scales; 0 = a dense bank ([n_slots][...]).
+ *  n_slots       : slots of the pool.
+ *  slot_of_user  : device int32[n_users], the slot of each user, or -1 for a user
+ *                  without one (not resident).
+ *  user_ids      : device int32[T] user ids as for bd_apply (-1: base model only).
+ *                  A token whose user has no slot, or whose id is outside
+ *                  [-1, n_users), gets the base product only and sets
+ *                  BD_ERR_USER_ID in the status word.
+ *  workspace     : >= bd_apply_paged_workspace_bytes(...) bytes, 256-byte aligned.
+ * The slot of every token's user is looked up once per call (one small launch); the
+ * call is then bd_apply over the slots, with every other argument, result and error
+ * as for bd_apply.  The pool, table and ids are only read: filling slots and the
+ * table (and not overwriting a slot that an earlier call on another stream still
+ * reads) is the caller's. */
+size_t bd_apply_paged_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t n_slots,
+                                      int64_t d_out, int64_t d_in, bd_dtype x_dtype,
+                                      bd_dtype y_dtype);
+bd_status bd_apply_paged(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                         const void* w_base, int64_t d_out, const uint64_t* signs_pool,
+                         const void* scales_pool, uint64_t signs_stride, uint64_t scales_stride,
+                         int32_t n_slots, const bd_compress_params* p,
+                         const int32_t* slot_of_user, int32_t n_users, const int32_t* user_ids,
+                         void* y, bd_dtype y_dtype, void* workspace, size_t ws_bytes,
+                         void* stream);
 
 /* bd_apply for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace

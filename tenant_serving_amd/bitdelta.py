@@ -84,6 +84,13 @@ def lib() -> ctypes.CDLL:
         L.bd_apply_noalloc.restype = ctypes.c_int
         L.bd_apply_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp, P, i32, vp, vp,
                                        ctypes.c_int, vp, vp]
+        L.bd_apply_paged_workspace_bytes.restype = sz
+        L.bd_apply_paged_workspace_bytes.argtypes = [P, i64, i32, i64, i64, ctypes.c_int,
+                                                     ctypes.c_int]
+        L.bd_apply_paged.restype = ctypes.c_int
+        L.bd_apply_paged.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp, ctypes.c_uint64,
+                                     ctypes.c_uint64, i32, P, vp, i32, vp, vp, ctypes.c_int, vp, sz,
+                                     vp]
         L.bd_device_status.restype = ctypes.c_int
         L.bd_device_status.argtypes = [vp, vp]
         L.bd_batch_workspace_bytes.restype = sz
@@ -290,6 +297,45 @@ def bd_apply_noalloc(x, w_base, signs_bank, scales_bank, p, n_users, user_ids, y
                                       _ptr(signs_bank), _ptr(scales_bank), ctypes.byref(p),
                                       int(n_users), _ptr(user_ids), _ptr(y), _dtype_code(y),
                                       _ptr(status), _stream(x, stream)))
+
+
+def bd_apply_paged_workspace_bytes(p, T: int, n_slots: int, d_out: int, d_in: int,
+                                   x_dtype: int, y_dtype: int) -> int:
+    return int(lib().bd_apply_paged_workspace_bytes(ctypes.byref(p), T, n_slots, d_out, d_in,
+                                                    x_dtype, y_dtype))
+
+
+def bd_apply_paged(x, w_base, signs_pool, scales_pool, signs_stride: int, scales_stride: int,
+                   n_slots: int, p, slot_of_user, user_ids, y, workspace, stream=None) -> int:
+    """bd_apply over banks in a pool of slots (include/bitdelta.h).  signs_pool and
+    scales_pool: uint8 views that start at slot 0's signs / scales of this matrix and
+    reach the last slot's; strides in bytes (0: dense [n_slots][...] banks of the bank
+    dtypes instead); slot_of_user: int32[n_users] device table."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    T, d_in = x.shape
+    dev = x.device
+    d_out = w_base.shape[0]
+    _dev(w_base, "w_base", (x.dtype,), (d_out, d_in), dev)
+    n_sc = bd_scales_count(p, d_out, d_in)
+    esz = 2 if p.scale_dtype == BD_F16 else 4
+    for t, name, stride, need in ((signs_pool, "signs_pool", signs_stride, d_out * d_in // 8),
+                                  (scales_pool, "scales_pool", scales_stride, n_sc * esz)):
+        _dev(t, name, None, None, dev)
+        span = (n_slots - 1) * (stride or need) + need if n_slots > 0 else 0
+        if _nbytes(t) < span:
+            raise ValueError(f"{name} holds {_nbytes(t)} bytes, {n_slots} slots need {span}")
+    _dev(slot_of_user, "slot_of_user", (torch.int32,), None, dev)
+    if slot_of_user.dim() != 1:
+        raise ValueError("slot_of_user must be one-dimensional")
+    _ids(user_ids, T, dev)
+    _dev(y, "y", (torch.float32, torch.bfloat16), (T, d_out), dev)
+    _dev(workspace, "workspace", None, None, dev)
+    return int(lib().bd_apply_paged(_ptr(x), _dtype_code(x), T, d_in, _ptr(w_base), d_out,
+                                    _ptr(signs_pool), _ptr(scales_pool), int(signs_stride),
+                                    int(scales_stride), int(n_slots), ctypes.byref(p),
+                                    _ptr(slot_of_user), slot_of_user.numel(), _ptr(user_ids),
+                                    _ptr(y), _dtype_code(y), _ptr(workspace), _nbytes(workspace),
+                                    _stream(x, stream)))
 
 
 def bd_device_status(workspace, stream=None) -> int:

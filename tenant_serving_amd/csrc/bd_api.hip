@@ -41,6 +41,24 @@ __global__ void k_copy_word(const uint32_t* src, uint32_t* dst) {
     if (threadIdx.x == 0) dst[0] = src ? src[0] : 0u;
 }
 
+// slot_ids[t] = the slot of token t's user: -1 stays -1 (base model only); an id outside
+// [0, n_users), or a user without a slot (table value outside [0, n_slots)), becomes
+// n_slots, which the apply reports as a bad user id (base product only).
+__global__ void k_map_slots(const int32_t* __restrict__ ids, int64_t T,
+                            const int32_t* __restrict__ slot_of_user, int32_t n_users,
+                            int32_t n_slots, int32_t* __restrict__ slot_ids) {
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t u = ids[t];
+        int32_t k = -1;
+        if (u != -1) {
+            k = (uint32_t)u < (uint32_t)n_users ? slot_of_user[u] : n_slots;
+            if ((uint32_t)k >= (uint32_t)n_slots) k = n_slots;
+        }
+        slot_ids[t] = k;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -347,15 +365,19 @@ bd_status bd_apply_q8(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, 
 }  // extern "C"
 
 // bd_apply on a workspace of ws_bytes (the caller's, or the no-allocation scratch).
+// sstride / cstride: bytes and scale elements from one user's bank to the next (0: dense).
 static bd_status apply_on(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
                           const void* w_base, int64_t d_out, const uint64_t* signs_bank,
                           const void* scales_bank, const bd_compress_params* p, int32_t n_users,
                           const int32_t* user_ids, void* y, bd_dtype y_dtype, void* workspace,
-                          size_t ws_bytes, void* stream) {
+                          size_t ws_bytes, void* stream, uint64_t sstride = 0,
+                          int64_t cstride = 0) {
     if (!p) return BD_ERR_INVALID_ARG;
     ApplyPlan pl;
     bd_status st = make_apply_plan(p, T, n_users, d_out, d_in, x_dtype, y_dtype, &pl);
     if (st != BD_OK) return st;
+    pl.delta.sstride = sstride;
+    pl.delta.cstride = cstride;
     if (!workspace || ws_bytes < pl.total || !aligned(workspace, kAlign)) return BD_ERR_WORKSPACE;
     if (T > 0) {
         if (!x || !w_base || !y || !user_ids) return BD_ERR_INVALID_ARG;
@@ -397,6 +419,52 @@ bd_status bd_apply(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, con
                    bd_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream) {
     return apply_on(x, x_dtype, T, d_in, w_base, d_out, signs_bank, scales_bank, p, n_users,
                     user_ids, y, y_dtype, workspace, ws_bytes, stream);
+}
+
+size_t bd_apply_paged_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t n_slots,
+                                      int64_t d_out, int64_t d_in, bd_dtype x_dtype,
+                                      bd_dtype y_dtype) {
+    const size_t w = bd_apply_workspace_bytes(p, T, n_slots, d_out, d_in, x_dtype, y_dtype);
+    if (w == 0 || T < 0) return 0;
+    return w + ((size_t)T * 4 + kAlign - 1) / kAlign * kAlign;
+}
+
+bd_status bd_apply_paged(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                         const void* w_base, int64_t d_out, const uint64_t* signs_pool,
+                         const void* scales_pool, uint64_t signs_stride, uint64_t scales_stride,
+                         int32_t n_slots, const bd_compress_params* p,
+                         const int32_t* slot_of_user, int32_t n_users, const int32_t* user_ids,
+                         void* y, bd_dtype y_dtype, void* workspace, size_t ws_bytes,
+                         void* stream) {
+    if (!p) return BD_ERR_INVALID_ARG;
+    const size_t need = bd_apply_paged_workspace_bytes(p, T, n_slots, d_out, d_in, x_dtype, y_dtype);
+    if (need == 0) {  // invalid sizes or parameters: the plain call names the error
+        ApplyPlan pl;
+        const bd_status st = make_apply_plan(p, T, n_slots, d_out, d_in, x_dtype, y_dtype, &pl);
+        return st != BD_OK ? st : BD_ERR_INVALID_ARG;
+    }
+    if (n_users < 0) return BD_ERR_INVALID_ARG;
+    const size_t esz = p->scale_dtype == BD_F16 ? 2 : 4;
+    const uint64_t sbytes = (uint64_t)d_out * (uint64_t)(d_in / 8);
+    const uint64_t cbytes = (uint64_t)bd_scales_count(p, d_out, d_in) * esz;
+    if ((signs_stride != 0 && (signs_stride < sbytes || signs_stride % 16 != 0)) ||
+        (scales_stride != 0 && (scales_stride < cbytes || scales_stride % 16 != 0)))
+        return BD_ERR_INVALID_ARG;
+    if (!workspace || ws_bytes < need || !aligned(workspace, kAlign)) return BD_ERR_WORKSPACE;
+    if (T > 0 && (!user_ids || (n_users > 0 && !slot_of_user) || !aligned(user_ids, 4) ||
+                  (slot_of_user && !aligned(slot_of_user, 4))))
+        return BD_ERR_INVALID_ARG;
+    const size_t w = need - ((size_t)T * 4 + kAlign - 1) / kAlign * kAlign;
+    int32_t* slot_ids = (int32_t*)((char*)workspace + w);
+    if (T > 0) {
+        hipLaunchKernelGGL(k_map_slots, dim3((unsigned)((T + 255) / 256 < 1024 ? (T + 255) / 256 : 1024)),
+                           dim3(256), 0, (hipStream_t)stream, user_ids, T, slot_of_user, n_users,
+                           n_slots, slot_ids);
+        if (hipGetLastError() != hipSuccess) return BD_ERR_DEVICE;
+    }
+    return apply_on(x, x_dtype, T, d_in, w_base, d_out, signs_pool, scales_pool, p, n_slots,
+                    slot_ids, y, y_dtype, workspace, w, stream, signs_stride,
+                    (int64_t)(scales_stride / esz));
 }
 
 bd_status bd_apply_noalloc(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,

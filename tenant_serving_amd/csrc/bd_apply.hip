@@ -311,16 +311,16 @@ k_base_f32(const float* __restrict__ x, const float* __restrict__ w, float* __re
 
 __global__ void __launch_bounds__(256)
 k_delta_f32(const float* __restrict__ x, const int32_t* __restrict__ ids, int U,
-            const uint64_t* __restrict__ signs, const void* __restrict__ scales, int sdtype,
-            int64_t per_user, int mode, int group, float* __restrict__ y, int64_t T, int64_t d_in,
-            int64_t d_out) {
+            const uint64_t* __restrict__ signs, uint64_t sstride, const void* __restrict__ scales,
+            int sdtype, int64_t cstride, int mode, int group, float* __restrict__ y, int64_t T,
+            int64_t d_in, int64_t d_out) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= T * d_out) return;
     const int64_t t = idx / d_out, o = idx % d_out;
     const int u = ids[t];
     if (u < 0 || u >= U) return;
-    const uint64_t* row = signs + ((int64_t)u * d_out + o) * (d_in / 64);
-    const void* su = (const char*)scales + (size_t)u * per_user * (sdtype == BD_F16 ? 2 : 4);
+    const uint64_t* row = (const uint64_t*)((const char*)signs + (uint64_t)u * sstride) + o * (d_in / 64);
+    const void* su = (const char*)scales + (size_t)u * cstride * (sdtype == BD_F16 ? 2 : 4);
     const float* xt = x + t * d_in;
     float total = 0.f, part = 0.f;
     for (int64_t k = 0; k < d_in; ++k) {
@@ -533,8 +533,9 @@ hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
     const int32_t* row_user = (const int32_t*)(batch + bp.off_user);
     if (bp.xdtype == BD_F32) {
         hipLaunchKernelGGL(k_delta_f32, dim3(grid_1d(bp.T * dp.d_out, 256, 1ll << 30)), dim3(256), 0,
-                           s, (const float*)x, row_user, bp.U, signs, scales, dp.sdtype, dp.per_user,
-                           dp.mode, dp.group, y, bp.T, bp.d_in, dp.d_out);
+                           s, (const float*)x, row_user, bp.U, signs,
+                           sign_stride(dp.sstride, dp.d_out, bp.d_in), scales, dp.sdtype,
+                           scale_stride(dp), dp.mode, dp.group, y, bp.T, bp.d_in, dp.d_out);
         return hipGetLastError();
     }
     return hipErrorInvalidValue;  // (unreachable: bf16 and fp32 are the only x dtypes)

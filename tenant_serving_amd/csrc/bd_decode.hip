@@ -243,7 +243,7 @@ template <int MODE>
 __global__ void __launch_bounds__(64 * kDecodeWaves)
 k_decode(const uint16_t* __restrict__ x, int T, int64_t d_in, int64_t dpad,
          const uint16_t* __restrict__ w, int64_t d_out, const uint64_t* __restrict__ signs,
-         const void* __restrict__ scales, int sdtype, int64_t per_user,
+         uint64_t sstride, const void* __restrict__ scales, int sdtype, int64_t per_user,
          const uint32_t* __restrict__ meta, const int32_t* __restrict__ perm,
          const int32_t* __restrict__ suser, const int4* __restrict__ seg,
          const uint16_t* __restrict__ xs, const uint8_t* __restrict__ x8,
@@ -363,7 +363,7 @@ k_decode(const uint16_t* __restrict__ x, int T, int64_t d_in, int64_t dpad,
             const bool ok = j < nseg && u < nunit;  // uniform
             const int usr = __builtin_amdgcn_readlane(utab, ok ? j : 0);
             const __amdgpu_buffer_rsrc_t br =
-                make_rsrc((const char*)signs + (uint64_t)(uint32_t)usr * user_bytes, user_bytes);
+                make_rsrc((const char*)signs + (uint64_t)(uint32_t)usr * sstride, user_bytes);
             const bool in = ok && (int64_t)u * 512 + 128 * g < d_in;
             return buf_load16(br, in ? brow + (uint32_t)(u * 64) : kOOB);
         };
@@ -589,8 +589,9 @@ template <int MODE>
 __global__ void __launch_bounds__(64 * kFusedWaves)
 k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int T, int U,
                int64_t d_in, int dpad, const uint16_t* __restrict__ w, int64_t d_out,
-               const uint64_t* __restrict__ signs, const void* __restrict__ scales, int sdtype,
-               int64_t per_user, void* __restrict__ y, int ydtype, uint32_t* __restrict__ status) {
+               const uint64_t* __restrict__ signs, uint64_t sstride, const void* __restrict__ scales,
+               int sdtype, int64_t per_user, void* __restrict__ y, int ydtype,
+               uint32_t* __restrict__ status) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -720,7 +721,7 @@ k_decode_fused(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
         const bool ok = lk < nuw && lj < nseg;  // uniform
         const int usr = __builtin_amdgcn_readlane(utab, ok ? lj : 0);
         const __amdgpu_buffer_rsrc_t br =
-            make_rsrc((const char*)signs + (uint64_t)(uint32_t)usr * user_bytes, user_bytes);
+            make_rsrc((const char*)signs + (uint64_t)(uint32_t)usr * sstride, user_bytes);
         const u32x4 v = buf_load16(br, ok ? (lk == 0 ? uoff[0] : uoff[1]) : kOOB);
         if (++lj == nsegR) {
             lj = 0;
@@ -915,8 +916,9 @@ template <int MODE, bool Q8>
 __global__ void __launch_bounds__(64 * kUnitWaves)
 k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int T, int U,
               int64_t d_in, const void* __restrict__ w, const float* __restrict__ wscale,
-              int64_t d_out, const uint64_t* __restrict__ signs, const void* __restrict__ scales,
-              int sdtype, int64_t per_user, void* __restrict__ y, int ydtype,
+              int64_t d_out, const uint64_t* __restrict__ signs, uint64_t sstride,
+              const void* __restrict__ scales, int sdtype, int64_t per_user, void* __restrict__ y,
+              int ydtype,
               uint32_t* __restrict__ status) {
     __shared__ f32x4 red[2 * kUnitWaves * 64];  // base then delta partial tiles, wave order
     __shared__ __attribute__((aligned(16))) char xlds[kUnitWaves * 16384];
@@ -998,7 +1000,7 @@ k_decode_unit(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, i
         const uint64_t msk = 0ull - (uint64_t)(i < nsegR);  // uniform: all ones for sign rows
         const int s = i - nsegR;
         const int usr = __builtin_amdgcn_readlane(utab, i < nseg ? i : 0);
-        const uint64_t sbase = (uint64_t)(uintptr_t)signs + (uint64_t)(uint32_t)usr * user_bytes;
+        const uint64_t sbase = (uint64_t)(uintptr_t)signs + (uint64_t)(uint32_t)usr * sstride;
         const uint64_t base = wbase + ((sbase - wbase) & msk);
         const uint64_t bytes = w_bytes + ((user_bytes - w_bytes) & msk);
         const uint32_t so = i < nseg ? soff : kOOB;
@@ -1236,7 +1238,7 @@ hipError_t launch_decode_prep(const DecodePlan& pl, int U, const DeltaPlan& dp, 
     gp = gp < 1 ? 1 : (gp > 1024 ? 1024 : gp);
     hipLaunchKernelGGL(k_decode_prep, dim3((unsigned)gp), dim3(256), 0, s, (const uint16_t*)x, ids,
                        (int)pl.T, U, pl.d_in, pl.dpad, dp.mode == BD_SCALE_COL ? 1 : 0, scales,
-                       dp.sdtype, dp.per_user, (uint32_t*)(ws + pl.off_meta),
+                       dp.sdtype, scale_stride(dp), (uint32_t*)(ws + pl.off_meta),
                        (int32_t*)(ws + pl.off_perm), (int32_t*)(ws + pl.off_suser),
                        (int4*)(ws + pl.off_seg), (uint16_t*)(ws + pl.off_xs),
                        (uint8_t*)(ws + pl.off_x8), (uint8_t*)(ws + pl.off_e8));
@@ -1249,8 +1251,9 @@ hipError_t launch_decode_main(const DecodePlan& pl, const DeltaPlan& dp, const v
     const dim3 grid((unsigned)((dp.d_out + 15) / 16));
 #define BD_DECODE(MODE)                                                                           \
     hipLaunchKernelGGL(k_decode<MODE>, grid, dim3(64 * kDecodeWaves), 0, s, (const uint16_t*)x,   \
-                       (int)pl.T, pl.d_in, pl.dpad, (const uint16_t*)wb, dp.d_out, signs, scales,  \
-                       dp.sdtype, dp.per_user, (const uint32_t*)(ws + pl.off_meta),                \
+                       (int)pl.T, pl.d_in, pl.dpad, (const uint16_t*)wb, dp.d_out, signs,          \
+                       sign_stride(dp.sstride, dp.d_out, pl.d_in), scales, dp.sdtype,              \
+                       scale_stride(dp), (const uint32_t*)(ws + pl.off_meta),                      \
                        (const int32_t*)(ws + pl.off_perm), (const int32_t*)(ws + pl.off_suser),    \
                        (const int4*)(ws + pl.off_seg), (const uint16_t*)(ws + pl.off_xs),          \
                        (const uint8_t*)(ws + pl.off_x8), (const uint8_t*)(ws + pl.off_e8), y,      \
@@ -1283,8 +1286,9 @@ hipError_t launch_decode_q8(int64_t T, int U, int64_t d_in, const DeltaPlan& dp,
     const dim3 grid((unsigned)((dp.d_out + 15) / 16));
 #define BD_UNITQ(MODE)                                                                        \
     k_decode_unit<MODE, true><<<grid, dim3(64 * kUnitWaves), 0, s>>>(                         \
-        (const uint16_t*)x, ids, (int)T, U, d_in, wq, wscale, dp.d_out, signs, scales,           \
-        dp.sdtype, dp.per_user, y, ydtype, (uint32_t*)ws)
+        (const uint16_t*)x, ids, (int)T, U, d_in, wq, wscale, dp.d_out, signs,                   \
+        sign_stride(dp.sstride, dp.d_out, d_in), scales, dp.sdtype, scale_stride(dp), y, ydtype,  \
+        (uint32_t*)ws)
     if (dp.mode == BD_SCALE_MATRIX) BD_UNITQ(BD_SCALE_MATRIX);
     else BD_UNITQ(BD_SCALE_ROW);
 #undef BD_UNITQ
@@ -1301,8 +1305,9 @@ hipError_t launch_decode_fused(int64_t T, int U, int64_t d_in, const DeltaPlan& 
     if (dpad <= 512 * kUnitWaves) {
 #define BD_UNIT(MODE)                                                                         \
     k_decode_unit<MODE, false><<<grid, dim3(64 * kUnitWaves), 0, s>>>(                        \
-        (const uint16_t*)x, ids, (int)T, U, d_in, wb, nullptr, dp.d_out, signs, scales,          \
-        dp.sdtype, dp.per_user, y, ydtype, (uint32_t*)ws)
+        (const uint16_t*)x, ids, (int)T, U, d_in, wb, nullptr, dp.d_out, signs,                  \
+        sign_stride(dp.sstride, dp.d_out, d_in), scales, dp.sdtype, scale_stride(dp), y, ydtype,  \
+        (uint32_t*)ws)
         if (dp.mode == BD_SCALE_MATRIX) BD_UNIT(BD_SCALE_MATRIX);
         else BD_UNIT(BD_SCALE_ROW);
 #undef BD_UNIT
@@ -1311,7 +1316,8 @@ hipError_t launch_decode_fused(int64_t T, int U, int64_t d_in, const DeltaPlan& 
 #define BD_FUSED(MODE)                                                                          \
     k_decode_fused<MODE><<<grid, dim3(64 * kFusedWaves), lds, s>>>(                             \
         (const uint16_t*)x, ids, (int)T, U, d_in, dpad, (const uint16_t*)wb, dp.d_out, signs,   \
-        scales, dp.sdtype, dp.per_user, y, ydtype, (uint32_t*)ws)
+        sign_stride(dp.sstride, dp.d_out, d_in), scales, dp.sdtype, scale_stride(dp), y, ydtype, \
+        (uint32_t*)ws)
     if (dp.mode == BD_SCALE_MATRIX) BD_FUSED(BD_SCALE_MATRIX);
     else BD_FUSED(BD_SCALE_ROW);
 #undef BD_FUSED

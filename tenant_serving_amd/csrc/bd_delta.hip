@@ -301,7 +301,9 @@ struct DeltaMats {
     const void* scales[kMaxMats];
     float* y[kMaxMats];
     int64_t d_out[kMaxMats];
-    int64_t per_user[kMaxMats];
+    int64_t per_user[kMaxMats];   // scales of one user
+    uint64_t sstride[kMaxMats];   // bytes from one user's (slot's) signs to the next
+    int64_t cstride[kMaxMats];    // scale elements from one user's scales to the next
     int rb_begin[kMaxMats + 1];
     int n;
 };
@@ -391,6 +393,8 @@ k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
     float* const y = pick_mat(dm.y, mi);
     const int64_t d_out = pick_mat(dm.d_out, mi);
     const int64_t per_user = pick_mat(dm.per_user, mi);
+    const uint64_t sstride = pick_mat(dm.sstride, mi);
+    const int64_t cstride = pick_mat(dm.cstride, mi);
     const int rbl = rb - pick_rb(dm.rb_begin, mi);
     const int64_t rw0 = (int64_t)rbl * (16 * kWaves * RT) + 16 * RT * wv;  // the wave's first row
     // (wave 0: a uniform branch, so the values around it stay scalar)
@@ -466,8 +470,8 @@ k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
     uint32_t ub_lo, ub_hi, sb_lo, sb_hi;
     {
         const uint64_t usr = n < nus ? (uint64_t)(uint32_t)smeta[32 + n] : 0ull;
-        const uint64_t ub = (uint64_t)(const char*)signs + usr * user_bytes;
-        const uint64_t sbp = (uint64_t)(const char*)scales + usr * sc_bytes;
+        const uint64_t ub = (uint64_t)(const char*)signs + usr * sstride;
+        const uint64_t sbp = (uint64_t)(const char*)scales + usr * (uint64_t)cstride * SB;
         ub_lo = (uint32_t)ub;
         ub_hi = (uint32_t)(ub >> 32);
         sb_lo = (uint32_t)sbp;
@@ -726,7 +730,7 @@ k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
                 if (tok[e] < 0) continue;
                 float f = 1.f;
                 if (MODE == BD_SCALE_MATRIX || MODE == BD_SCALE_ROW) {
-                    const size_t i = (size_t)tus[e] * per_user + (MODE == BD_SCALE_ROW ? (size_t)o : 0);
+                    const size_t i = (size_t)tus[e] * cstride + (MODE == BD_SCALE_ROW ? (size_t)o : 0);
                     f = -(SF16 ? f16_to_f32(((const uint16_t*)scales)[i]) : ((const float*)scales)[i]);
                 } else if (COL) {
                     f = -1.f;
@@ -851,7 +855,7 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         const int64_t d_out = pick_mat(dm.d_out, mi);
         const int64_t row0 = (int64_t)(cL - pick_rb(dm.rb_begin, mi)) * kChunkRows;
         const uint64_t base = (uint64_t)(uintptr_t)sg +
-                              (uint64_t)(ok ? usr : 0) * (uint64_t)d_out * bank_row +
+                              (uint64_t)(ok ? usr : 0) * pick_mat(dm.sstride, mi) +
                               (uint64_t)row0 * bank_row;
         const uint64_t rem = ok && row0 < d_out ? (uint64_t)(d_out - row0) * bank_row : 0ull;
         const int nrec = rem > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)rem;
@@ -944,7 +948,8 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
                         typedef const __attribute__((address_space(1))) uint16_t* gh;
                         typedef const __attribute__((address_space(1))) float* gf;
                         const void* sp = pick_mat(dm.scales, q);
-                        f = SF16 ? f16_to_f32(((gh)sp)[c_tuser]) : ((gf)sp)[c_tuser];
+                        const size_t i = (size_t)c_tuser * (size_t)pick_mat(dm.cstride, q);
+                        f = SF16 ? f16_to_f32(((gh)sp)[i]) : ((gf)sp)[i];
                     }
                 }
                 sF[G][n] = f;
@@ -1022,7 +1027,7 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         idout = pick_mat(dm.d_out, mi);
         irow0 = (int64_t)(c - pick_rb(dm.rb_begin, mi)) * kChunkRows;
         isc = pick_mat(dm.scales, mi);
-        ipu = pick_mat(dm.per_user, mi);
+        ipu = pick_mat(dm.cstride, mi);
         imi = mi;
         fresh = true;  // (ROW: its factors load in its first sweep)
 #pragma unroll
@@ -1209,7 +1214,7 @@ hipError_t launch_tile_encode(const BatchPlan& bp, const DeltaPlan& dp, char* ba
     const int32_t* tiles = (const int32_t*)(batch + bp.off_tiles);
 #define BD_ENC(G, C)                                                                           \
     hipLaunchKernelGGL((k_tile_encode<G, C>), ge, dim3(256), 0, s, (const uint16_t*)x, bp.T,   \
-                       (int)bp.U, bp.d_in, perm, suser, meta, tiles, scales, dp.sdtype, dp.per_user, tmeta, \
+                       (int)bp.U, bp.d_in, perm, suser, meta, tiles, scales, dp.sdtype, scale_stride(dp), tmeta, \
                        enc, meta)
     if (dp.mode == BD_SCALE_GROUP) BD_ENC(true, false);
     else if (dp.mode == BD_SCALE_COL) BD_ENC(false, true);
@@ -1256,6 +1261,8 @@ static hipError_t launch_delta8_set(const BatchPlan& bp, const DeltaPlan& dp, ch
         dm.per_user[i] = dp.mode == BD_SCALE_MATRIX ? 1
                          : dp.mode == BD_SCALE_ROW ? mats[i].d_out
                                                    : bp.d_in;
+        dm.sstride[i] = sign_stride(mats[i].sstride, mats[i].d_out, bp.d_in);
+        dm.cstride[i] = mats[i].cstride ? mats[i].cstride : dm.per_user[i];
         dm.rb_begin[i] = cb;
         cb += (int)((mats[i].d_out + kChunkRows - 1) / kChunkRows);
     }
@@ -1321,6 +1328,8 @@ hipError_t launch_delta6_set(const BatchPlan& bp, const DeltaPlan& dp, char* bat
                          : dp.mode == BD_SCALE_GROUP ? mats[i].d_out * (bp.d_in / dp.group)
                          : dp.mode == BD_SCALE_ROW ? mats[i].d_out
                                                    : bp.d_in;
+        dm.sstride[i] = sign_stride(mats[i].sstride, mats[i].d_out, bp.d_in);
+        dm.cstride[i] = mats[i].cstride ? mats[i].cstride : dm.per_user[i];
         dm.rb_begin[i] = rb;
         rb += (int)((mats[i].d_out + rows_rb - 1) / rows_rb);
     }
@@ -1358,7 +1367,7 @@ hipError_t launch_delta6_set(const BatchPlan& bp, const DeltaPlan& dp, char* bat
 hipError_t launch_delta6_encoded(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                                  const uint64_t* signs, const void* scales, float* y,
                                  hipStream_t s) {
-    const DeltaMatArg m = {signs, scales, y, dp.d_out};
+    const DeltaMatArg m = {signs, scales, y, dp.d_out, dp.sstride, dp.cstride};
     return launch_delta6_set(bp, dp, batch, &m, 1, s);
 }
 

@@ -88,11 +88,20 @@ struct BatchPlan {
     size_t total = 0;
 };
 
-// One matrix's delta application on a prepared batch.
+// One matrix's delta application on a prepared batch.  per_user: scales of one user;
+// sstride / cstride: bytes from one user's (slot's) signs to the next and scale
+// elements from one user's scales to the next, 0 for a dense bank (d_out d_in / 8 and
+// per_user).
 struct DeltaPlan {
     int64_t d_out = 0, per_user = 0;
     int mode = 0, group = 0, sdtype = 0;
+    uint64_t sstride = 0;
+    int64_t cstride = 0;
 };
+__host__ __device__ inline uint64_t sign_stride(uint64_t sstride, int64_t d_out, int64_t d_in) {
+    return sstride ? sstride : (uint64_t)d_out * (uint64_t)(d_in / 8);
+}
+inline int64_t scale_stride(const DeltaPlan& dp) { return dp.cstride ? dp.cstride : dp.per_user; }
 
 // One-pass path for decode batches of at most kDecodeMaxT bf16 tokens: the
 // prepared batch (sorted tokens, user segments) and the fp8 encoding of X.
@@ -154,6 +163,8 @@ struct DeltaMatArg {
     const void* scales;
     float* y;
     int64_t d_out;
+    uint64_t sstride = 0;  // as DeltaPlan's; 0: dense bank
+    int64_t cstride = 0;
 };
 hipError_t launch_delta6_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                              const DeltaMatArg* mats, int n, hipStream_t s);

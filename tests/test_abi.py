@@ -104,6 +104,36 @@ def test_apply_rejects_bad_arguments_synchronously():
     assert call(x=(1 << 12) + 2) == B.BD_ERR_INVALID_ARG
 
 
+def test_paged_apply_rejects_bad_arguments_synchronously():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    p = B.params("row", 128, 0.0, B.BD_F16)
+    d_out, d_in, T, K = 64, 128, 16, 3
+    sbytes, cbytes = d_out * d_in // 8, d_out * 2
+    need = B.bd_apply_paged_workspace_bytes(p, T, K, d_out, d_in, B.BD_BF16, B.BD_F32)
+    assert need >= B.bd_apply_workspace_bytes(p, T, K, d_out, d_in, B.BD_BF16, B.BD_F32) + T * 4
+    assert B.bd_apply_paged_workspace_bytes(p, T, K, d_out, 96, B.BD_BF16, B.BD_F32) == 0
+
+    def call(ss=4096, cs=4096, d_in=d_in, ws=1 << 12, ws_bytes=1 << 30, ids=1 << 12, table=1 << 12,
+             n_users=5, xd=B.BD_BF16):
+        return L.bd_apply_paged(vp(1 << 12), xd, T, d_in, vp(1 << 12), d_out, vp(1 << 12),
+                                vp(1 << 12), ss, cs, K, ctypes.byref(p), vp(table) if table else None,
+                                n_users, vp(ids) if ids else None, vp(1 << 12), B.BD_F32,
+                                vp(ws) if ws else None, ws_bytes, None)
+
+    assert call(d_in=96) == B.BD_ERR_SHAPE
+    assert call(xd=B.BD_F16) == B.BD_ERR_DTYPE
+    assert call(ss=sbytes - 16) == B.BD_ERR_INVALID_ARG   # a slot smaller than one bank
+    assert call(ss=sbytes + 8) == B.BD_ERR_INVALID_ARG    # not a multiple of 16
+    assert call(cs=cbytes - 2) == B.BD_ERR_INVALID_ARG
+    assert call(n_users=-1) == B.BD_ERR_INVALID_ARG
+    assert call(ws=0) == B.BD_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == B.BD_ERR_WORKSPACE
+    assert call(ids=0) == B.BD_ERR_INVALID_ARG
+    assert call(table=0) == B.BD_ERR_INVALID_ARG
+    assert call(table=(1 << 12) + 2) == B.BD_ERR_INVALID_ARG
+
+
 def _select_raw(d_out=64, d_in=128, dtype=B.BD_BF16, clip_k=0.0, wf=1 << 12, ws=1 << 16,
                 ws_bytes=1 << 30, errors=1 << 20, axis=1 << 20):
     # fake, never dereferenced device addresses: every case fails before any launch
