@@ -279,8 +279,8 @@ bd_status bd_apply_noalloc(const void* x, bd_dtype x_dtype, int64_t T, int64_t d
 
 /* ------------------------------------------------- INT8 base weights */
 
-/* INT8 base weights for the apply below ([P2] "Systems Mechanics": the 1-bit delta
- * on top of an INT8-quantized base).  The pages name no quantizer; this one is
+/* INT8 base weights for the apply below ([P2] "Production Engineering" 3, Quantized
+ * Base Model Compatibility: the 1-bit delta on top of an INT8-quantized base).  The pages name no quantizer; this one is
  * symmetric per output row: scales_out[o] = max_i |w[o][i]| / 127 and
  * q_out[o][i] = round-half-even(w[o][i] / scales_out[o]) clamped to [-127, 127],
  * both divisions in binary32 (a zero row gets scale 0 and codes 0).
@@ -291,11 +291,16 @@ bd_status bd_quantize_base(const void* w, bd_dtype w_dtype, int64_t d_out, int64
 
 /* bd_apply with the base weight given as INT8 rows (bd_quantize_base):
  *     y[t] = wscales (.) (X[t] . wq^T) + scale_u (.) (X[t] . S_u^T),
- * in one launch for decode batches: bf16 X, 1..16 tokens, MATRIX or ROW scales,
- * d_in <= 4096 (BD_ERR_UNSUPPORTED otherwise).  The base weight crosses HBM at one
- * byte per element; its codes are widened to bf16 exactly on chip.  Other
- * arguments, the workspace (bd_apply_workspace_bytes) and the status word as for
- * bd_apply. */
+ * bf16 X only (BD_ERR_UNSUPPORTED for fp32).  Decode batches (1..16 tokens, MATRIX or
+ * ROW scales, d_in <= 4096) take one launch; every other batch (any scale mode, up
+ * to 8192 tokens, d_in a multiple of 64) the prepared-batch path of bd_apply with the
+ * base product on the matrix cores from the codes.  The base weight crosses HBM at
+ * one byte per element; its codes are widened to bf16 exactly on chip and each row's
+ * sum is scaled once.  workspace: >= bd_apply_q8_workspace_bytes(...) bytes; other
+ * arguments and the status word as for bd_apply. */
+size_t bd_apply_q8_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t n_users,
+                                   int64_t d_out, int64_t d_in, bd_dtype x_dtype,
+                                   bd_dtype y_dtype);
 bd_status bd_apply_q8(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const int8_t* wq,
                       const float* wscales, int64_t d_out, const uint64_t* signs_bank,
                       const void* scales_bank, const bd_compress_params* p, int32_t n_users,

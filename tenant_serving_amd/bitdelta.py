@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.bd_compress.argtypes = [vp, vp, ctypes.c_int, i64, i64, P, vp, vp, vp, sz, vp]
         L.bd_quantize_base.restype = ctypes.c_int
         L.bd_quantize_base.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp]
+        L.bd_apply_q8_workspace_bytes.restype = sz
+        L.bd_apply_q8_workspace_bytes.argtypes = [P, i64, i32, i64, i64, ctypes.c_int,
+                                                  ctypes.c_int]
         L.bd_apply_q8.restype = ctypes.c_int
         L.bd_apply_q8.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, vp, vp, P, i32, vp, vp,
                                   ctypes.c_int, vp, sz, vp]
@@ -555,6 +558,12 @@ def quantize_base(w: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Ten
     return q, s
 
 
+def bd_apply_q8_workspace_bytes(p, T: int, n_users: int, d_out: int, d_in: int, x_dtype: int,
+                                y_dtype: int) -> int:
+    return int(lib().bd_apply_q8_workspace_bytes(ctypes.byref(p), T, n_users, d_out, d_in,
+                                                 x_dtype, y_dtype))
+
+
 def apply_q8(x, wq, wscales, signs_bank, scales_bank, p, user_ids, y_dtype=torch.float32,
              ws=None, stream=None, check: bool = False) -> torch.Tensor:
     T, d_in = x.shape
@@ -562,8 +571,8 @@ def apply_q8(x, wq, wscales, signs_bank, scales_bank, p, user_ids, y_dtype=torch
     U = signs_bank.shape[0]
     y = torch.empty((T, d_out), dtype=y_dtype, device=x.device)
     if ws is None:
-        ws = workspace(bd_apply_workspace_bytes(p, T, U, d_out, d_in, _dtype_code(x),
-                                                _dtype_code(y)), x.device)
+        ws = workspace(bd_apply_q8_workspace_bytes(p, T, U, d_out, d_in, _dtype_code(x),
+                                                   _dtype_code(y)), x.device)
     _check(bd_apply_q8(x, wq, wscales, signs_bank, scales_bank, p, U, user_ids, y, ws, stream),
            "bd_apply_q8")
     if check:

@@ -338,17 +338,29 @@ bd_status bd_quantize_base(const void* w, bd_dtype w_dtype, int64_t d_out, int64
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
+size_t bd_apply_q8_workspace_bytes(const bd_compress_params* p, int64_t T, int32_t n_users,
+                                   int64_t d_out, int64_t d_in, bd_dtype x_dtype,
+                                   bd_dtype y_dtype) {
+    if (!p) return 0;
+    ApplyPlan pl;
+    const bool dec = q8_path_supported(x_dtype, T, p->mode, d_in);
+    if (make_apply_plan(p, T, n_users, d_out, d_in, x_dtype, y_dtype, &pl, dec) != BD_OK) return 0;
+    return pl.total;
+}
+
 bd_status bd_apply_q8(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, const int8_t* wq,
                       const float* wscales, int64_t d_out, const uint64_t* signs_bank,
                       const void* scales_bank, const bd_compress_params* p, int32_t n_users,
                       const int32_t* user_ids, void* y, bd_dtype y_dtype, void* workspace,
                       size_t ws_bytes, void* stream) {
     if (!p) return BD_ERR_INVALID_ARG;
+    const bool dec = q8_path_supported(x_dtype, T, p->mode, d_in);
     ApplyPlan pl;
-    bd_status st = make_apply_plan(p, T, n_users, d_out, d_in, x_dtype, y_dtype, &pl);
+    bd_status st = make_apply_plan(p, T, n_users, d_out, d_in, x_dtype, y_dtype, &pl, dec);
     if (st != BD_OK) return st;
     if (T == 0) return BD_OK;
-    if (!q8_path_supported(x_dtype, T, p->mode, d_in)) return BD_ERR_UNSUPPORTED;
+    if (x_dtype != BD_BF16 || (!dec && !gemm_q8_supported(T, d_in, d_out)))
+        return BD_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < pl.total || !aligned(workspace, kAlign)) return BD_ERR_WORKSPACE;
     if (!x || !wq || !wscales || !y || !user_ids) return BD_ERR_INVALID_ARG;
     if (n_users > 0 && (!signs_bank || !scales_bank)) return BD_ERR_INVALID_ARG;
@@ -356,9 +368,20 @@ bd_status bd_apply_q8(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in, 
         !aligned(user_ids, 4) || (signs_bank && !aligned(signs_bank, 16)) ||
         (scales_bank && !aligned(scales_bank, 16)))
         return BD_ERR_INVALID_ARG;
-    hipError_t e = launch_decode_q8(T, n_users, d_in, pl.delta, x, user_ids, wq, wscales,
-                                    signs_bank, scales_bank, y, y_dtype, (char*)workspace,
-                                    (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    if (dec) {
+        hipError_t e = launch_decode_q8(T, n_users, d_in, pl.delta, x, user_ids, wq, wscales,
+                                        signs_bank, scales_bank, y, y_dtype, ws, s);
+        return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+    }
+    hipError_t e = launch_batch_prepare(pl.batch, x, user_ids, ws, s);
+    float* yacc = y_dtype == BD_F32 ? (float*)y : (float*)(ws + pl.off_yf);
+    if (e == hipSuccess) e = launch_gemm_q8(x, T, d_in, wq, wscales, d_out, yacc, s);
+    if (e == hipSuccess)
+        e = launch_delta(pl.batch, pl.delta, ws, x, signs_bank, scales_bank, yacc, s);
+    if (e == hipSuccess && y_dtype == BD_BF16)
+        e = launch_cast_bf16(yacc, (uint16_t*)y, T * d_out, s);
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 

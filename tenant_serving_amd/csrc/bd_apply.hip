@@ -445,7 +445,7 @@ bd_status make_delta_plan(const bd_compress_params* p, const BatchPlan& b, int64
 }
 
 bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int64_t d_out,
-                          int64_t d_in, int xdtype, int ydtype, ApplyPlan* pl) {
+                          int64_t d_in, int xdtype, int ydtype, ApplyPlan* pl, bool allow_decode) {
     if (!p || !pl) return BD_ERR_INVALID_ARG;
     if (ydtype != BD_F32 && ydtype != BD_BF16) return BD_ERR_DTYPE;
     ApplyPlan q;
@@ -454,8 +454,8 @@ bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int
     st = make_delta_plan(p, q.batch, d_out, &q.delta);
     if (st != BD_OK) return st;
     q.ydtype = ydtype;
-    q.decode = decode_path_supported(xdtype, T, p->mode);
-    q.fused = fused_path_supported(xdtype, T, p->mode, d_in);
+    q.decode = allow_decode && decode_path_supported(xdtype, T, p->mode);
+    q.fused = allow_decode && fused_path_supported(xdtype, T, p->mode, d_in);
     if (q.decode) {
         make_decode_plan(T, d_in, &q.dec);
         q.total = q.dec.total;

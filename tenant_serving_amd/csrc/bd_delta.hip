@@ -180,9 +180,10 @@ k_tile_encode(const uint16_t* __restrict__ x, int64_t T, int U, int64_t d_in,
     const int lane = threadIdx.x & 63;
     const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15, G = lane >> 4;
+    // (the tag also for a batch without tiles: no token with a valid user)
+    if (t == 0 && u == 0 && threadIdx.x == 0) meta_w[kEncTagWord] = enc_tag(GRP, COL);
     const int ntv = (int)meta_r[3];
     if (t >= ntv) return;  // uniform: no such tile in this batch
-    if (t == 0 && u == 0 && threadIdx.x == 0) meta_w[kEncTagWord] = enc_tag(GRP, COL);
     const int ts = tiles[t], tl = tiles[t + 1] - ts;  // start, length
     const int p = ts + m;
     const int tok0 = m < tl ? perm[p] : -1;

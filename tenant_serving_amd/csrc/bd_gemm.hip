@@ -39,6 +39,25 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Four int8 codes (one dword, low byte first) as two dwords of bf16 pairs: each code
+// sign-extended and converted to fp32, whose upper half is its bf16 value (exact:
+// |code| <= 128 needs 8 significant bits).  The sign extension is written with shifts:
+// with the signed bit-field-extract builtin this compiler folded the extract into an
+// unsigned byte conversion (v_cvt_f32_u32 with a sign-extended byte), which turns
+// negative codes into values near 2^32.
+__device__ __forceinline__ void widen_i8x4(uint32_t d, uint32_t& lo, uint32_t& hi) {
+    const float f0 = (float)((int)(d << 24) >> 24);
+    const float f1 = (float)((int)(d << 16) >> 24);
+    const float f2 = (float)((int)(d << 8) >> 24);
+    const float f3 = (float)((int)d >> 24);
+    lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+}
+
 // 16 bytes per lane from global memory straight into LDS at lds + 16 * lane.
 // (A plain device function: the host pass of the kernel template never sees the
 // LDS address-space cast.)
@@ -59,7 +78,11 @@ __device__ __forceinline__ uint32_t swz(int r, int c) {
 
 // Kernel templates live outside the anonymous namespace: the host compiler does
 // not emit the launch stubs of internal-linkage kernel templates.
-template <int BR, int BT, int BK, int NS, int NW>
+// Q8: W holds int8 codes with one scale per row (the INT8 base): each lane loads 16
+// codes of a row into registers, widens them to bf16 and writes the two chunks to their
+// swizzled LDS slots (NS = 2: the next stage's codes are loaded during this stage's
+// products and written after them); the epilogue multiplies each row by its scale.
+template <int BR, int BT, int BK, int NS, int NW, bool Q8>
 __global__ void __launch_bounds__(64 * NW)
 k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt) {
     // NW waves: NW / 2 along the rows, 2 along the tokens
@@ -72,6 +95,8 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
     static_assert(kWBytes % (1024 * NW) == 0 && kXBytes % (1024 * NW) == 0,
                   "whole copy instructions per wave");
     static_assert(MI >= 1 && BR % (32 * NWR) == 0, "32-row tiles per wave");
+    static_assert(!Q8 || (NS == 2 && (BR * BK) % (1024 * NW) == 0), "INT8 codes: two stages");
+    constexpr int kQInst = Q8 ? BR * BK / (1024 * NW) : 1;  // 16-code loads per lane and stage
     extern __shared__ __attribute__((aligned(16))) char smem[];
     // block -> (row tile, token tile); the token tiles of one row tile share an XCD.
     // Row tiles run over the matrices of the set back to back.
@@ -86,6 +111,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
     const uint16_t* const w = mi == 0 ? gm.w[0] : mi == 1 ? gm.w[1] : mi == 2 ? gm.w[2] : gm.w[3];
     float* const y = mi == 0 ? gm.y[0] : mi == 1 ? gm.y[1] : mi == 2 ? gm.y[2] : gm.y[3];
     const int N = mi == 0 ? gm.N[0] : mi == 1 ? gm.N[1] : mi == 2 ? gm.N[2] : gm.N[3];
+    const float* const wsc = mi == 0 ? gm.s[0] : mi == 1 ? gm.s[1] : mi == 2 ? gm.s[2] : gm.s[3];
     const int rt = rtg - (mi == 0 ? gm.rt_begin[0] : mi == 1 ? gm.rt_begin[1]
                           : mi == 2 ? gm.rt_begin[2] : gm.rt_begin[3]);
     const int r0 = rt * BR, t0 = tt * BT;
@@ -94,7 +120,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wv >> 1, wt = wv & 1;
 
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(w, (uint64_t)N * K * 2);
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(w, (uint64_t)N * K * (Q8 ? 1 : 2));
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint64_t)T * K * 2);
 
     // Loader: copy instruction i of a tile fills LDS bytes [1024 i, +1024): lane l
@@ -113,15 +139,48 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
         const int c = (lane % CPR) ^ ((r / (16 / CPR)) % CPR);
         xsrc[j] = t0 + r < T ? (uint32_t)(((int64_t)(t0 + r) * K + 8 * c) * 2) : kOOB;
     }
+    // Q8 loader: load j of lane l covers codes [16 c, 16 c + 16) of row r (g = 64 (wv
+    // kQInst + j) + l, r = g / (BK / 16), c = g % (BK / 16)), bf16 chunks 2 c and 2 c + 1
+    uint32_t qsrc[kQInst], qdst[kQInst];
+    u32x4 qreg[kQInst];
+#pragma unroll
+    for (int j = 0; j < kQInst; ++j) {
+        const int g = (wv * kQInst + j) * 64 + lane;
+        const int r = g / (BK / 16), c = g % (BK / 16);
+        qsrc[j] = Q8 && r0 + r < N ? (uint32_t)((int64_t)(r0 + r) * K + 16 * c) : kOOB;
+        qdst[j] = (uint32_t)(r * 4096 + c);  // (row, code group), unpacked at the store
+    }
     const int nk = K / BK;
+    auto qload = [&](int s) {  // stage s's codes into registers (zeros past K)
+#pragma unroll
+        for (int j = 0; j < kQInst; ++j)
+            qreg[j] = buf_load16(wrs, (s < nk && qsrc[j] != kOOB) ? qsrc[j] + (uint32_t)s * BK : kOOB);
+    };
+    auto qstore = [&](int s) {  // the codes of stage s, widened, into ring slot s % NS
+        char* base = smem + (s % NS) * kStageBytes;
+#pragma unroll
+        for (int j = 0; j < kQInst; ++j) {
+            const int r = (int)(qdst[j] >> 12), c = (int)(qdst[j] & 4095u);
+            uint32_t v[8];
+            widen_i8x4(qreg[j].x, v[0], v[1]);
+            widen_i8x4(qreg[j].y, v[2], v[3]);
+            widen_i8x4(qreg[j].z, v[4], v[5]);
+            widen_i8x4(qreg[j].w, v[6], v[7]);
+            const u32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+            *(u32x4*)(base + swz<BK>(r, 2 * c)) = a;
+            *(u32x4*)(base + swz<BK>(r, 2 * c + 1)) = b;
+        }
+    };
     auto issue = [&](int s) {  // stage s into ring slot s % NS (zeros past K)
         char* base = smem + (s % NS) * kStageBytes;
         const bool ok = s < nk;
         const uint32_t kb = (uint32_t)s * BK * 2;
+        if (!Q8) {
 #pragma unroll
-        for (int j = 0; j < kWInst; ++j)
-            copy16_to_lds(wrs, base + (wv * kWInst + j) * 1024,
-                          (ok && wsrc[j] != kOOB) ? wsrc[j] + kb : kOOB);
+            for (int j = 0; j < kWInst; ++j)
+                copy16_to_lds(wrs, base + (wv * kWInst + j) * 1024,
+                              (ok && wsrc[j] != kOOB) ? wsrc[j] + kb : kOOB);
+        }
 #pragma unroll
         for (int j = 0; j < kXInst; ++j)
             copy16_to_lds(xrs, base + kWBytes + (wv * kXInst + j) * 1024,
@@ -138,15 +197,22 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
 
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(s);
+    if (Q8) {
+        qload(0);
+        qstore(0);
+    }
 
     const int m32 = lane & 31, h = lane >> 5;
     for (int s = 0; s < nk; ++s) {
         // this wave's copies of stage s are done (NS - 2 younger stages in flight); the
         // barrier makes every wave's copies visible and frees the slot of stage s - 1
+        // (Q8: also this wave's LDS writes of the stage's codes)
         constexpr int kAhead = (kWInst + kXInst) * (NS - 2);
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (kAhead & 0xF) | (((kAhead >> 4) & 3) << 14));
+        __builtin_amdgcn_s_waitcnt((Q8 ? 0x0070 : 0x0F70) | (kAhead & 0xF) |
+                                   (((kAhead >> 4) & 3) << 14));
         __builtin_amdgcn_s_barrier();  // no fence: the explicit wait above covers the copies
         issue(s + NS - 1);
+        if (Q8) qload(s + 1);
         const char* wt_base = smem + (s % NS) * kStageBytes;
         const char* xt_base = wt_base + kWBytes;
 #pragma unroll
@@ -163,6 +229,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(A[i], Bv[j], acc[i][j]);
         }
+        if (Q8 && s + 1 < nk) qstore(s + 1);  // slot of stage s - 1: free since the barrier
     }
 
     // D lane layout (32 x 32): column m32, register 4b + e holds row 8b + 4h + e
@@ -176,8 +243,12 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
             for (int b = 0; b < 4; ++b) {
                 const int o = r0 + wr * (BR / NWR) + 32 * i + 8 * b + 4 * h;
                 float* dst = y + (int64_t)t * N + o;
-                const f32x4 v = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2],
-                                 acc[i][j][4 * b + 3]};
+                f32x4 v = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2],
+                           acc[i][j][4 * b + 3]};
+                if (Q8) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] *= o + e < N ? wsc[o + e] : 0.f;
+                }
                 if (o + 3 < N && (N & 3) == 0) {
                     *(f32x4*)dst = v;
                 } else {
@@ -191,14 +262,15 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
 
 namespace {
 
-template <int BR, int BT, int BK, int NS, int NW = 4>
+template <int BR, int BT, int BK, int NS, int NW = 4, bool Q8 = false>
 hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
-                       hipStream_t s) {
+                       hipStream_t s, const float* const* wscales = nullptr) {
     GemmMats gm = {};
     gm.n = n;
     int rt = 0;
     for (int i = 0; i < n; ++i) {
         gm.w[i] = (const uint16_t*)mats[i].w;
+        gm.s[i] = wscales ? wscales[i] : nullptr;
         gm.y[i] = mats[i].y;
         gm.N[i] = (int)mats[i].d_out;
         gm.rt_begin[i] = rt;
@@ -209,8 +281,8 @@ hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const GemmMatArg*
     const int nrt8 = (rt + 7) / 8 * 8;
     const unsigned blocks = (unsigned)(nrt8 * ntt);
     constexpr int lds = NS * (BR + BT) * BK * 2;
-    k_gemm<BR, BT, BK, NS, NW><<<dim3(blocks), dim3(64 * NW), lds, s>>>((const uint16_t*)x, gm,
-                                                                       (int)T, (int)d_in, ntt);
+    k_gemm<BR, BT, BK, NS, NW, Q8><<<dim3(blocks), dim3(64 * NW), lds, s>>>(
+        (const uint16_t*)x, gm, (int)T, (int)d_in, ntt);
     return hipGetLastError();
 }
 
@@ -257,6 +329,25 @@ hipError_t launch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb, i
                        float* y, hipStream_t s) {
     const GemmMatArg m = {wb, y, d_out};
     return launch_gemm_set(x, T, d_in, &m, 1, s);
+}
+
+bool gemm_q8_supported(int64_t T, int64_t d_in, int64_t d_out) {
+    return T >= 1 && d_in % kGemmK == 0 && T * d_in * 2 < ((int64_t)1 << 31) &&
+           d_out * d_in < ((int64_t)1 << 31) && d_out < ((int64_t)1 << 30);
+}
+
+// The tile choice of launch_gemm_set, with two LDS stages throughout.
+hipError_t launch_gemm_q8(const void* x, int64_t T, int64_t d_in, const int8_t* wq,
+                          const float* wscale, int64_t d_out, float* y, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const GemmMatArg m = {wq, y, d_out};
+    const float* sc[1] = {wscale};
+    auto blocks = [&](int64_t br, int64_t bt) { return ((d_out + br - 1) / br) * ((T + bt - 1) / bt); };
+    if (blocks(256, 256) >= 200) return launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, &m, 1, s, sc);
+    if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, &m, 1, s, sc);
+    if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 2, 4, true>(x, T, d_in, &m, 1, s, sc);
+    if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 2, 4, true>(x, T, d_in, &m, 1, s, sc);
+    return launch_tile<64, 64, 64, 2, 4, true>(x, T, d_in, &m, 1, s, sc);
 }
 
 }  // namespace bd

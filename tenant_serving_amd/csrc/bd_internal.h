@@ -130,8 +130,10 @@ bd_status check_params(const bd_compress_params* p, int64_t d_out, int64_t d_in,
 bd_status make_batch_plan(int64_t T, int32_t U, int64_t d_in, int xdtype, BatchPlan* plan);
 bd_status make_delta_plan(const bd_compress_params* p, const BatchPlan& b, int64_t d_out,
                           DeltaPlan* plan);
+// allow_decode = false: the prepared-batch plan even where the decode path applies.
 bd_status make_apply_plan(const bd_compress_params* p, int64_t T, int32_t U, int64_t d_out,
-                          int64_t d_in, int xdtype, int ydtype, ApplyPlan* plan);
+                          int64_t d_in, int xdtype, int ydtype, ApplyPlan* plan,
+                          bool allow_decode = true);
 hipError_t launch_batch_prepare(const BatchPlan& pl, const void* x, const int32_t* ids,
                                 char* batch, hipStream_t s);
 hipError_t launch_base_gemm(const void* x, int xdtype, int64_t T, int64_t d_in, const void* wb,
@@ -186,7 +188,8 @@ struct GemmMatArg {
     int64_t d_out;
 };
 struct GemmMats {
-    const uint16_t* w[kMaxMats];
+    const uint16_t* w[kMaxMats];  // bf16 rows, or int8 rows for the INT8-base product
+    const float* s[kMaxMats];     // INT8 base: the rows' scales
     float* y[kMaxMats];
     int N[kMaxMats];
     int rt_begin[kMaxMats + 1];
@@ -194,6 +197,11 @@ struct GemmMats {
 };
 hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
                            hipStream_t s);
+// Y = s (.) (X Wq^T) for an INT8 base weight (per-row symmetric codes wq, row scales
+// wscale): the same tiles, the codes widened to bf16 on their way into LDS (exact).
+bool gemm_q8_supported(int64_t T, int64_t d_in, int64_t d_out);
+hipError_t launch_gemm_q8(const void* x, int64_t T, int64_t d_in, const int8_t* wq,
+                          const float* wscale, int64_t d_out, float* y, hipStream_t s);
 
 bool decode_path_supported(int xdtype, int64_t T, int mode);
 void make_decode_plan(int64_t T, int64_t d_in, DecodePlan* plan);

@@ -169,10 +169,14 @@ def test_int8_base_entry_points_reject_bad_arguments_synchronously():
         return int(L.bd_apply_q8(1 << 12, xdt, T, d_in, wq, 1 << 12, 64, 1 << 12, 1 << 12,
                                  ctypes.byref(p), 2, 1 << 12, 1 << 12, B.BD_F32, ws, ws_bytes, None))
 
-    assert q8(B.params("group", 128)) == B.BD_ERR_UNSUPPORTED
-    assert q8(B.params("matrix"), T=17) == B.BD_ERR_UNSUPPORTED
-    assert q8(B.params("matrix"), d_in=4608) == B.BD_ERR_UNSUPPORTED
+    assert q8(B.params("group", 64)) == B.BD_ERR_UNSUPPORTED   # bf16 GROUP needs g >= 128
+    assert q8(B.params("matrix"), T=9000) == B.BD_ERR_UNSUPPORTED
     assert q8(B.params("matrix"), xdt=B.BD_F32) == B.BD_ERR_UNSUPPORTED
+    p = B.params("row", 128, 0.0, B.BD_F16)
+    dec = B.bd_apply_q8_workspace_bytes(p, 4, 2, 64, 512, B.BD_BF16, B.BD_F32)
+    gen = B.bd_apply_q8_workspace_bytes(p, 4, 2, 64, 4608, B.BD_BF16, B.BD_F32)  # past decode
+    assert dec > 0 and gen >= B.bd_batch_workspace_bytes(4, 2, 4608, B.BD_BF16)
+    assert q8(p, d_in=4608, ws_bytes=gen - 1) == B.BD_ERR_WORKSPACE
     assert q8(B.params("matrix"), d_in=100) == B.BD_ERR_SHAPE
     assert q8(B.params("matrix"), ws=0) == B.BD_ERR_WORKSPACE
     assert q8(B.params("matrix"), wq=0) == B.BD_ERR_INVALID_ARG

@@ -231,6 +231,24 @@ def test_apply_out_of_range_user_gets_base_and_status():
     assert not torch.equal(y[0], base[0])
 
 
+@pytest.mark.parametrize("mode", ["matrix", "group"])
+def test_apply_without_valid_users_is_the_base_product(mode):
+    """A many-token batch whose ids are all -1 has no tile of delta products: y is the
+    base product and the status word stays clear."""
+    w = custom(72, 1024, S.BF16, n_users=2, T=40, cid=1420)
+    p = B.params(mode)
+    wb_dev = S.dev_wbase(w, 0)
+    signs, scales = gpu_bank(w, 0, wb_dev, p, range(2))
+    ids = np.full(40, -1, np.int32)
+    y = B.apply(S.dev_x(w, 0), wb_dev, signs, scales, p, torch.from_numpy(ids).to(DEV), check=True)
+    wb = S.host_wbase(w, 0)
+    words, osc = oracle_bank(w, 0, wb, p, range(2))
+    _, yb, yd = O.apply(S.host_x(w, 0), wb, words, osc, p.mode, ids)
+    assert np.all(yd == 0)
+    err, rms = max_err_vs_rms(y.cpu().numpy(), yb)
+    assert err <= 1e-5 * rms, (err, rms)
+
+
 def test_apply_empty_batch_is_a_noop():
     w = custom(64, 512, S.BF16, n_users=2, T=0, cid=1401)
     p = B.params("matrix")

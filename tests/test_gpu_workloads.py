@@ -195,3 +195,48 @@ def test_workload5_llama8b_stack_128_users():
         y_ref = B.apply(xs[mat.xgroup], bases[m], banks[m][0], banks[m][1], params_of(w, mat),
                         ids_dev).cpu().numpy()
         assert np.array_equal(y_again, y_ref)  # the stack step equals the per-matrix check
+
+
+def check_matrix_q8(w, m, ids, rows):
+    """bd_apply_q8 over every user's GPU bank and the GPU-quantized base, every token on
+    the rows `rows`, against the oracle's apply on its own INT8 rows and banks."""
+    mat = w.matrices[m]
+    p = params_of(w, mat)
+    wb_dev = S.dev_wbase(w, m)
+    x_dev = S.dev_x(w, mat.xgroup)
+    signs, scales = compress_all(w, m, wb_dev, p)
+    q, s = B.quantize_base(wb_dev)
+    del wb_dev
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    y = B.apply_q8(x_dev, q, s, signs, scales, p, ids_dev, check=True)
+    y0 = B.apply_q8(x_dev, torch.zeros_like(q), s, signs, scales, p, ids_dev, check=True)
+    torch.cuda.synchronize()
+    got, got0 = y.cpu().numpy()[:, rows], y0.cpu().numpy()[:, rows]
+    del y, y0, signs, scales, q
+    users = sorted(set(int(u) for u in ids if u >= 0))
+    remap = np.full(w.n_users, -1, dtype=np.int32)
+    remap[users] = np.arange(len(users), dtype=np.int32)
+    sub_ids = np.where(ids >= 0, remap[np.maximum(ids, 0)], -1).astype(np.int32)
+    words_bank, sc_bank = oracle_rows_bank(w, m, p, users, rows)
+    oq, os_ = O.quantize_rows(S.host_wbase(w, m, rows), dtype=O.BF16)
+    x_np = S.host_x(w, mat.xgroup)
+    yr, yb, yd = O.apply_q8(x_np, oq, os_, words_bank, sc_bank, p.mode, sub_ids, g=p.group_size,
+                            sdtype=o_sd(p))
+    err, rms = max_err_vs_rms(got, yr)
+    assert err <= TOL_BF16 * rms, (mat.name, err, rms)
+    err0, rms0 = max_err_vs_rms(got0, yd)
+    print(f"INT8 base {mat.name}: {len(users)} users, {len(ids)} tokens x {len(rows)} rows, "
+          f"max|err|/rms {err / rms:.3e}, delta-only {err0 / rms0:.3e}")
+    assert err0 <= tol_delta(p.mode) * rms0, (mat.name, "delta only", err0, rms0)
+    assert_delta_within_bound(got0, yd, x_np, sc_bank, p, sub_ids, mat.name)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid,m", [(3, 2), (4, 2), (5, 4)])
+def test_int8_base_at_workload_shapes(cid, m):
+    """The INT8 base under the 1-bit deltas at the workloads' sizes: the clipped MLP's
+    down_proj (GROUP, 64 users, 256 tokens), Qwen's down_proj (COL, 1144 mixed tokens)
+    and the Llama stack's layer 0 gate_proj (MATRIX, 512 Zipf tokens, 128 users)."""
+    w = S.workload(cid)
+    check_matrix_q8(w, m, S.user_ids(w), pick_rows(w.matrices[m].d_out, 48, 60 + cid))
+    torch.cuda.empty_cache()
