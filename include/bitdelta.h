@@ -198,7 +198,10 @@ bd_status bd_reconstruct(const uint64_t* signs, const void* scales, const bd_com
  *                the fp32 result).
  *  workspace   : >= bd_apply_workspace_bytes(...) bytes, 256-byte aligned.
  * Accumulation is fp32.  T == 0 is a no-op.  bf16 inputs: T <= 8192 tokens
- * per call and GROUP group_size >= 128 (BD_ERR_UNSUPPORTED otherwise).
+ * per call (BD_ERR_UNSUPPORTED otherwise).  The matrix-core delta products scale
+ * whole 128-column products: bf16 GROUP scales with groups of 8..64 columns take a
+ * plain kernel instead (one thread per token and row summing each group in fp32;
+ * correct at any size, several times slower than groups of 128 or more).
  * bf16 batches of 1..16 tokens with MATRIX, ROW or COL scales take the decode path:
  * for MATRIX or ROW scales and d_in <= 5120 one launch that writes only y and the
  * status word (the workspace is NOT left prepared for bd_decode_apply; callers
@@ -334,7 +337,10 @@ bd_status bd_base_gemm(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
  * bf16 inputs the call is bd_batch_encode followed by bd_delta_apply_encoded:
  * it first writes this x (times the column scales, for COL) into `batch` as
  * tiles of 16 user-sorted tokens encoded as fp6 e2m3 operands, so calls on one
- * batch must not overlap; the grouping itself is left unchanged. */
+ * batch must not overlap; the grouping itself is left unchanged.  (bf16 GROUP
+ * scales with groups under 128 columns: the plain kernel of bd_apply, no encoding;
+ * bd_batch_encode and bd_delta_apply_encoded(_n) return BD_ERR_UNSUPPORTED for
+ * them.) */
 bd_status bd_delta_apply(void* batch, size_t batch_bytes, const void* x, bd_dtype x_dtype,
                          int64_t T, int64_t d_in, int32_t n_users, int64_t d_out,
                          const uint64_t* signs_bank, const void* scales_bank,

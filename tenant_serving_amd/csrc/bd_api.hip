@@ -223,6 +223,8 @@ bd_status bd_delta_apply(void* batch, size_t batch_bytes, const void* x, bd_dtyp
 bd_status bd_batch_encode(void* batch, size_t batch_bytes, const void* x, bd_dtype x_dtype,
                           int64_t T, int64_t d_in, int32_t n_users, const void* scales_bank,
                           const bd_compress_params* p, void* stream) {
+    // the shared encoding feeds the matrix-core products: groups of 128 columns or more
+    if (p && p->mode == BD_SCALE_GROUP && p->group_size < 128) return BD_ERR_UNSUPPORTED;
     if (x_dtype != BD_BF16) return BD_ERR_DTYPE;
     BatchPlan bp;
     DeltaPlan dp;
@@ -244,6 +246,8 @@ bd_status bd_delta_apply_encoded(void* batch, size_t batch_bytes, bd_dtype x_dty
                                  int64_t d_in, int32_t n_users, int64_t d_out,
                                  const uint64_t* signs_bank, const void* scales_bank,
                                  const bd_compress_params* p, float* y, void* stream) {
+    // the shared encoding feeds the matrix-core products: groups of 128 columns or more
+    if (p && p->mode == BD_SCALE_GROUP && p->group_size < 128) return BD_ERR_UNSUPPORTED;
     if (x_dtype != BD_BF16) return BD_ERR_DTYPE;
     BatchPlan bp;
     DeltaPlan dp;
@@ -301,6 +305,8 @@ bd_status bd_delta_apply_encoded_n(void* batch, size_t batch_bytes, bd_dtype x_d
                                    const int64_t* d_outs, const uint64_t* const* signs_banks,
                                    const void* const* scales_banks, const bd_compress_params* p,
                                    float* const* ys, void* stream) {
+    // the shared encoding feeds the matrix-core products: groups of 128 columns or more
+    if (p && p->mode == BD_SCALE_GROUP && p->group_size < 128) return BD_ERR_UNSUPPORTED;
     if (x_dtype != BD_BF16) return BD_ERR_DTYPE;
     if (n_mats < 1 || n_mats > kMaxMats || !d_outs || !signs_banks || !scales_banks || !ys)
         return BD_ERR_INVALID_ARG;

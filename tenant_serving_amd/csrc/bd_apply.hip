@@ -339,6 +339,55 @@ k_delta_f32(const float* __restrict__ x, const int32_t* __restrict__ ids, int U,
     y[idx] += total;
 }
 
+// GROUP scales with groups of fewer than 128 columns on bf16 tokens (the matrix-core
+// products cover 128 columns per group scale): one block per (sorted position, 256
+// rows), one thread per row; the token's row of X comes through LDS in chunks of
+// kSmallGroupChunk columns, each thread sums its signed values per group in fp32 and
+// adds group sum * group scale.  Each (token, row) has one thread: a plain add into Y.
+constexpr int kSmallGroupChunk = 4096;
+__global__ void __launch_bounds__(256)
+k_delta_small_group(const uint16_t* __restrict__ x, int64_t T, int64_t d_in,
+                    const int32_t* __restrict__ perm, const int32_t* __restrict__ suser,
+                    const uint32_t* __restrict__ meta, int U, const uint64_t* __restrict__ signs,
+                    uint64_t sstride, const void* __restrict__ scales, int sdtype, int64_t cstride,
+                    int group, float* __restrict__ y, int64_t d_out) {
+    __shared__ float xs[kSmallGroupChunk];
+    const int64_t p = blockIdx.y;
+    if (p >= (int64_t)meta[2]) return;  // uniform: past the tokens with a valid user
+    const int tok = perm[p], u = suser[p];
+    if (tok < 0 || tok >= T || u < 0 || u >= U) return;  // uniform
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = o < d_out;
+    const int64_t wpr = d_in / 64;
+    const uint64_t* srow =
+        (const uint64_t*)((const char*)signs + (uint64_t)u * sstride) + (live ? o : 0) * wpr;
+    const void* su = (const char*)scales + (size_t)u * cstride * (sdtype == BD_F16 ? 2 : 4);
+    const int64_t gpr = d_in / group;
+    float total = 0.f;
+    for (int64_t c0 = 0; c0 < d_in; c0 += kSmallGroupChunk) {
+        const int64_t n = d_in - c0 < kSmallGroupChunk ? d_in - c0 : kSmallGroupChunk;
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < n; i += 256)
+            xs[i] = __uint_as_float((uint32_t)x[(int64_t)tok * d_in + c0 + i] << 16);
+        __syncthreads();
+        if (!live) continue;
+        for (int64_t w = 0; w < n / 64; ++w) {
+            const uint64_t bits = srow[c0 / 64 + w];
+            float part = 0.f;
+            for (int k = 0; k < 64; ++k) {
+                const float v = xs[64 * w + k];
+                part += (bits >> k) & 1ull ? v : -v;
+                if (((k + 1) & (group - 1)) == 0) {
+                    const int64_t gi = (c0 + 64 * w + k) / group;
+                    total = fmaf(part, load_scale(su, sdtype, o * gpr + gi), total);
+                    part = 0.f;
+                }
+            }
+        }
+    }
+    if (live) y[(int64_t)tok * d_out + o] += total;
+}
+
 __global__ void k_check_ids(const int32_t* __restrict__ ids, int64_t T, int U, uint32_t* meta) {
     bool bad = false;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T;
@@ -374,8 +423,7 @@ bd_status check_params(const bd_compress_params* p, int64_t d_out, int64_t d_in,
         const int g = p->group_size;
         if (g < 8 || g > kSegCols || (g & (g - 1)) != 0) return BD_ERR_UNSUPPORTED;
         if (d_in % g != 0) return BD_ERR_SHAPE;
-        // the MFMA path keeps each step inside one 128-column block
-        if (xdtype == BD_BF16 && g < 128) return BD_ERR_UNSUPPORTED;
+        (void)xdtype;  // bf16 groups under 128 columns: k_delta_small_group
     }
     return BD_OK;
 }
@@ -529,6 +577,16 @@ hipError_t launch_delta(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                         const void* x, const uint64_t* signs, const void* scales, float* y,
                         hipStream_t s) {
     if (bp.T == 0) return hipSuccess;
+    if (bp.xdtype == BD_BF16 && dp.mode == BD_SCALE_GROUP && dp.group < 128) {
+        const dim3 g((unsigned)((dp.d_out + 255) / 256), (unsigned)bp.T);
+        hipLaunchKernelGGL(k_delta_small_group, g, dim3(256), 0, s, (const uint16_t*)x, bp.T,
+                           bp.d_in, (const int32_t*)(batch + bp.off_perm),
+                           (const int32_t*)(batch + bp.off_user),
+                           (const uint32_t*)(batch + bp.off_meta), bp.U, signs,
+                           sign_stride(dp.sstride, dp.d_out, bp.d_in), scales, dp.sdtype,
+                           scale_stride(dp), dp.group, y, dp.d_out);
+        return hipGetLastError();
+    }
     if (bp.xdtype == BD_BF16) return launch_delta6(bp, dp, batch, x, signs, scales, y, s);
     const int32_t* row_user = (const int32_t*)(batch + bp.off_user);
     if (bp.xdtype == BD_F32) {

@@ -96,7 +96,8 @@ def test_apply_rejects_bad_arguments_synchronously():
     assert call(yd=B.BD_F16) == B.BD_ERR_DTYPE
     assert call(T=-1) == B.BD_ERR_INVALID_ARG
     assert call(U=-2) == B.BD_ERR_INVALID_ARG
-    assert call(p=B.params("group", 64)) == B.BD_ERR_UNSUPPORTED  # bf16 MFMA path needs g >= 128
+    assert call(p=B.params("group", 1024)) == B.BD_ERR_UNSUPPORTED  # groups of 8..512 columns
+    assert call(p=B.params("group", 48)) == B.BD_ERR_UNSUPPORTED    # powers of two
     assert call(T=9000) == B.BD_ERR_UNSUPPORTED
     assert call(ws=0) == B.BD_ERR_WORKSPACE
     assert call(ws_bytes=16) == B.BD_ERR_WORKSPACE
@@ -169,7 +170,7 @@ def test_int8_base_entry_points_reject_bad_arguments_synchronously():
         return int(L.bd_apply_q8(1 << 12, xdt, T, d_in, wq, 1 << 12, 64, 1 << 12, 1 << 12,
                                  ctypes.byref(p), 2, 1 << 12, 1 << 12, B.BD_F32, ws, ws_bytes, None))
 
-    assert q8(B.params("group", 64)) == B.BD_ERR_UNSUPPORTED   # bf16 GROUP needs g >= 128
+    assert q8(B.params("group", 256), d_in=384) == B.BD_ERR_SHAPE  # groups divide d_in
     assert q8(B.params("matrix"), T=9000) == B.BD_ERR_UNSUPPORTED
     assert q8(B.params("matrix"), xdt=B.BD_F32) == B.BD_ERR_UNSUPPORTED
     p = B.params("row", 128, 0.0, B.BD_F16)

@@ -249,6 +249,38 @@ def test_apply_without_valid_users_is_the_base_product(mode):
     assert err <= 1e-5 * rms, (err, rms)
 
 
+@pytest.mark.parametrize("g,T,sd", [(32, 40, B.BD_F32), (64, 9, B.BD_F16), (16, 100, B.BD_F32)])
+def test_apply_small_groups(g, T, sd):
+    """bf16 GROUP scales with groups under 128 columns (the plain per-row kernel): y and
+    the delta term against the oracle; the delta term is fp32 sums of exact bf16
+    products, so it is held to 1e-5 rms.  Also under the INT8 base."""
+    U = 4
+    ids = np.random.default_rng(g + T).integers(-1, U, T).astype(np.int32)
+    w = custom(136, 1152, S.BF16, n_users=U, T=T, b=5e-3, cid=1440 + g)
+    p = B.params("group", g, 0.0, sd)
+    wb_dev = S.dev_wbase(w, 0)
+    x_dev = S.dev_x(w, 0)
+    signs, scales = gpu_bank(w, 0, wb_dev, p, range(U))
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    y = B.apply(x_dev, wb_dev, signs, scales, p, ids_dev, check=True)
+    y0 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
+    wb = S.host_wbase(w, 0)
+    words, osc = oracle_bank(w, 0, wb, p, range(U))
+    assert np.array_equal(to_np(signs), words)
+    x = S.host_x(w, 0)
+    yr, _, yd = O.apply(x, wb, words, osc, p.mode, ids, g=g, sdtype=o_sdtype(p))
+    err, rms = max_err_vs_rms(y.cpu().numpy(), yr)
+    assert err <= TOL_BF16 * rms, (err, rms)
+    err0, rms0 = max_err_vs_rms(y0.cpu().numpy(), yd)
+    assert err0 <= 1e-5 * rms0, (err0, rms0)
+    q, qs = B.quantize_base(wb_dev)
+    y8 = B.apply_q8(x_dev, q, qs, signs, scales, p, ids_dev, check=True)
+    oq, os_ = O.quantize_rows(wb, dtype=O.BF16)
+    y8r, _, _ = O.apply_q8(x, oq, os_, words, osc, p.mode, ids, g=g, sdtype=o_sdtype(p))
+    err8, rms8 = max_err_vs_rms(y8.cpu().numpy(), y8r)
+    assert err8 <= TOL_BF16 * rms8, (err8, rms8)
+
+
 def test_apply_empty_batch_is_a_noop():
     w = custom(64, 512, S.BF16, n_users=2, T=0, cid=1401)
     p = B.params("matrix")

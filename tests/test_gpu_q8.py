@@ -103,12 +103,12 @@ def test_tiled_int8_product_over_tile_shapes(case):
 
 
 def test_apply_q8_rejects_what_it_does_not_serve():
-    p = B.params("group", 64)  # the bf16 delta products take groups of 128 or more
-    x = torch.zeros((4, 512), dtype=torch.bfloat16, device=DEV)
+    p = B.params("matrix")
+    x = torch.zeros((4, 512), dtype=torch.float32, device=DEV)  # fp32 activations
     q = torch.zeros((64, 512), dtype=torch.int8, device=DEV)
     s = torch.ones(64, dtype=torch.float32, device=DEV)
     signs = torch.zeros((1, 64, 8), dtype=torch.int64, device=DEV)
-    sc = torch.zeros((1, 64 * 8), dtype=torch.float32, device=DEV)
+    sc = torch.zeros((1, 1), dtype=torch.float32, device=DEV)
     ids = torch.zeros(4, dtype=torch.int32, device=DEV)
     y = torch.empty((4, 64), dtype=torch.float32, device=DEV)
     ws = B.workspace(1 << 20, DEV)
