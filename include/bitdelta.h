@@ -286,7 +286,8 @@ bd_status bd_apply_noalloc(const void* x, bd_dtype x_dtype, int64_t T, int64_t d
  * Base Model Compatibility: the 1-bit delta on top of an INT8-quantized base).  The pages name no quantizer; this one is
  * symmetric per output row: scales_out[o] = max_i |w[o][i]| / 127 and
  * q_out[o][i] = round-half-even(w[o][i] / scales_out[o]) clamped to [-127, 127],
- * both divisions in binary32 (a zero row gets scale 0 and codes 0).
+ * both divisions in binary32 (a zero row gets scale 0 and codes 0; a row holding a
+ * NaN or Inf weight gets scale NaN and codes 0, so that its outputs are NaN).
  *  w          : [d_out][d_in] of w_dtype (BD_F32 or BD_BF16).
  *  q_out      : [d_out][d_in] int8.   scales_out : [d_out] fp32. */
 bd_status bd_quantize_base(const void* w, bd_dtype w_dtype, int64_t d_out, int64_t d_in,

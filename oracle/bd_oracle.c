@@ -395,11 +395,15 @@ void orc_quantize_rows(const void* w, int dtype, int64_t d_out, int64_t d_in, in
                        float* s) {
     for (int64_t o = 0; o < d_out; ++o) {
         float m = 0.0f;
+        int finite = 1;
         for (int64_t i = 0; i < d_in; ++i) {
             float a = fabsf(o_load(w, dtype, o * d_in + i));
+            if (!isfinite(a)) finite = 0;
             if (a > m) m = a;
         }
-        float so = m / 127.0f;
+        /* a row holding a NaN or Inf weight has no INT8 codes: scale NaN, codes 0, so
+         * that its outputs are NaN rather than finite and wrong */
+        float so = finite ? m / 127.0f : NAN;
         s[o] = so;
         for (int64_t i = 0; i < d_in; ++i) {
             float v = so > 0.0f ? o_load(w, dtype, o * d_in + i) / so : 0.0f;

@@ -88,14 +88,21 @@ k_quantize_rows(const WT* __restrict__ w, int64_t d_in, int8_t* __restrict__ q,
     const int64_t o = blockIdx.x;
     const WT* row = w + o * d_in;
     float m = 0.f;
-    for (int64_t i = threadIdx.x; i < d_in; i += 256) m = fmaxf(m, fabsf(load_w(row, i)));
+    bool bad = false;
+    for (int64_t i = threadIdx.x; i < d_in; i += 256) {
+        const float a = fabsf(load_w(row, i));
+        bad |= !(a <= 3.402823466e38f);  // NaN or Inf
+        m = fmaxf(m, a);
+    }
     sh[threadIdx.x] = m;
-    __syncthreads();
+    const bool anybad = __syncthreads_or((int)bad) != 0;
     for (int k = 128; k > 0; k >>= 1) {
         if ((int)threadIdx.x < k) sh[threadIdx.x] = fmaxf(sh[threadIdx.x], sh[threadIdx.x + k]);
         __syncthreads();
     }
-    const float so = sh[0] / 127.0f;
+    // a row holding a NaN or Inf weight has no INT8 codes: scale NaN and codes 0, so
+    // that its outputs are NaN rather than finite and wrong
+    const float so = anybad ? __builtin_nanf("") : sh[0] / 127.0f;
     if (threadIdx.x == 0) s[o] = so;
     for (int64_t i = threadIdx.x; i < d_in; i += 256) {
         float r = so > 0.f ? rintf(load_w(row, i) / so) : 0.f;

@@ -31,6 +31,20 @@ def test_quantize_base_matches_oracle(dtype):
     assert np.array_equal(to_np(s), os_)
 
 
+def test_quantize_base_marks_rows_with_non_finite_weights():
+    w = custom(40, 512, S.F32, cid=2310)
+    wb = S.host_wbase(w, 0).copy()
+    wb[3, 17] = np.nan
+    wb[11, 0] = np.inf
+    wb[30, 511] = -np.inf
+    q, s = B.quantize_base(torch.from_numpy(wb).to(DEV))
+    torch.cuda.synchronize()
+    oq, os_ = O.quantize_rows(wb, dtype=O.F32)
+    assert np.array_equal(to_np(q), oq)
+    assert np.array_equal(to_np(s), os_, equal_nan=True)
+    assert np.isnan(os_[[3, 11, 30]]).all()
+
+
 CASES = [
     # (mode, scale dtype, d_out, d_in, ids, n_users, y dtype)
     ("matrix", B.BD_F32, 200, 1024, np.random.default_rng(1).permutation(16).astype(np.int32), 16, torch.float32),

@@ -352,6 +352,24 @@ def test_row_quantizer_matches_numpy_and_its_bounds():
     assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-6) + 1e-30)  # half a step per element
 
 
+def test_row_quantizer_marks_rows_with_non_finite_weights():
+    """A row holding a NaN or an Inf has no INT8 codes: scale NaN, codes 0 (so its base
+    outputs are NaN); the other rows are quantized as without it."""
+    rng = np.random.default_rng(23)
+    w = rng.normal(0, 0.02, (6, 128)).astype(np.float32)
+    clean_q, clean_s = O.quantize_rows(w)
+    w[1, 5] = np.nan
+    w[4, 100] = -np.inf
+    q, s = O.quantize_rows(w)
+    assert np.isnan(s[1]) and np.isnan(s[4]) and np.all(q[[1, 4]] == 0)
+    keep = [0, 2, 3, 5]
+    assert np.array_equal(q[keep], clean_q[keep]) and np.array_equal(s[keep], clean_s[keep])
+    words = np.zeros((1, 6, 2), np.uint64)
+    _, yb, _ = O.apply_q8(np.ones((1, 128), np.float32), q, s, words, np.zeros((1, 1), np.float32),
+                          O.MATRIX, np.array([-1], np.int32))
+    assert np.all(np.isnan(yb[0, [1, 4]])) and np.all(np.isfinite(yb[0, keep]))
+
+
 def test_apply_on_int8_base_reduces_to_numpy_matmul():
     rng = np.random.default_rng(19)
     T, d_out, d_in, U = 5, 24, 128, 3
