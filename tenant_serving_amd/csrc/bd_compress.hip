@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(kCompressThreads)
 k_compress(const WT* __restrict__ wf, const WT* __restrict__ wb, int64_t d_out, int64_t d_in,
            int64_t rows_per_block, int group, int sdtype, uint64_t* __restrict__ signs,
            void* __restrict__ scales, const Stats* __restrict__ st, double* __restrict__ part,
-           uint32_t* __restrict__ status) {
+           uint32_t* __restrict__ flags) {
     __shared__ double sh[kCompressThreads / 64];
     constexpr bool kCol = (PASS == 2 && MODE == BD_SCALE_COL) || PASS == 3;
     __shared__ double colsh[kCol ? kCompressThreads / 64 : 1][kCol ? kSegCols : 1];
@@ -218,7 +218,12 @@ k_compress(const WT* __restrict__ wf, const WT* __restrict__ wb, int64_t d_out, 
         }
     }
 
-    if (PASS >= 2 && __ballot(bad) != 0ull && lane == 0) atomicOr(status, ST_NONFINITE);
+    // this block's non-finite flag (the call's status word is set from all of them by the
+    // launch that finishes the scales, so nothing has to clear it first)
+    if (PASS >= 2) {
+        const int anybad = __syncthreads_or((int)bad);
+        if (threadIdx.x == 0) flags[blockIdx.y * gridDim.x + blockIdx.x] = anybad ? 1u : 0u;
+    }
     if (PASS < 2 || PASS == 3 || MODE == BD_SCALE_MATRIX) {
         const double tot = block_sum(acc, sh);
         if (threadIdx.x == 0) part[rc * n_seg + seg] = tot;
@@ -267,10 +272,29 @@ __device__ __forceinline__ void store_scale(void* scales, int sdtype, int64_t i,
     else ((float*)scales)[i] = (float)v;
 }
 
-// Scale finalisation for MATRIX (one block), ROW (thread per row), COL (thread per column).
+// The call's status word from the packing pass's block flags (one block of 256 threads;
+// every thread must call it).
+__device__ __forceinline__ void status_from_flags(const uint32_t* __restrict__ flags,
+                                                  int64_t n_flags, uint32_t* __restrict__ status) {
+    uint32_t any = 0u;
+    for (int64_t i = threadIdx.x; i < n_flags; i += 256) any |= flags[i];
+    const int bad = __syncthreads_or((int)any);
+    if (threadIdx.x == 0) status[0] = bad ? ST_NONFINITE : 0u;
+}
+
+// GROUP scales are final after the packing pass: the status word only.
+__global__ void __launch_bounds__(256)
+k_status_finalize(const uint32_t* __restrict__ flags, int64_t n_flags, uint32_t* __restrict__ status) {
+    status_from_flags(flags, n_flags, status);
+}
+
+// Scale finalisation for MATRIX (one block), ROW (thread per row), COL (thread per column);
+// block 0 also sets the status word.
 __global__ void __launch_bounds__(256)
 k_scales_finalize(int mode, const double* __restrict__ part, int64_t n_seg, int64_t n_rchunk,
-                  int64_t d_out, int64_t d_in, int sdtype, void* __restrict__ scales) {
+                  int64_t d_out, int64_t d_in, int sdtype, void* __restrict__ scales,
+                  const uint32_t* __restrict__ flags, uint32_t* __restrict__ status) {
+    if (blockIdx.x == 0) status_from_flags(flags, n_seg * n_rchunk, status);
     if (mode == BD_SCALE_MATRIX) {
         __shared__ double sh[256];
         const int64_t n_part = n_seg * n_rchunk;
@@ -331,7 +355,9 @@ k_axis_sums(const double* __restrict__ part, int64_t n_seg, int64_t n_rchunk, in
 __global__ void __launch_bounds__(256)
 k_axis_finalize(const double* __restrict__ part, int64_t n_blocks, const double* __restrict__ rsq,
                 const double* __restrict__ csq, int64_t d_out, int64_t d_in,
-                double* __restrict__ errors, int32_t* __restrict__ axis) {
+                double* __restrict__ errors, int32_t* __restrict__ axis,
+                const uint32_t* __restrict__ flags, uint32_t* __restrict__ status) {
+    status_from_flags(flags, n_blocks, status);
     __shared__ double sh[3][256];
     double a = 0.0, b = 0.0, c = 0.0;
 #pragma unroll 8
@@ -374,24 +400,24 @@ hipError_t launch_typed(const CompressPlan& pl, const WT* wf, const WT* wb, uint
     double* psum = (double*)(ws + pl.off_part_sum);
     double* pm2 = (double*)(ws + pl.off_part_m2);
     double* pabs = (double*)(ws + pl.off_part_abs);
+    uint32_t* flags = (uint32_t*)(ws + pl.off_flags);
     const dim3 grid((unsigned)pl.n_seg, (unsigned)pl.n_rchunk), block(kCompressThreads);
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, status, (int64_t)(kAlign / 4));
     if (pl.clip) {
         hipLaunchKernelGGL((k_compress<WT, HB, 0, 0, false>), grid, block, 0, s, wf, wb, pl.d_out,
                            pl.d_in, pl.rows_per_block, pl.group, pl.sdtype, signs, scales, st, psum,
-                           status);
+                           flags);
         hipLaunchKernelGGL(k_stats_finalize<0>, dim3(1), dim3(256), 0, s, psum, pl.n_blocks, pl.n,
                            pl.clip_k, st);
         hipLaunchKernelGGL((k_compress<WT, HB, 1, 0, false>), grid, block, 0, s, wf, wb, pl.d_out,
                            pl.d_in, pl.rows_per_block, pl.group, pl.sdtype, signs, scales, st, pm2,
-                           status);
+                           flags);
         hipLaunchKernelGGL(k_stats_finalize<1>, dim3(1), dim3(256), 0, s, pm2, pl.n_blocks, pl.n,
                            pl.clip_k, st);
     }
 #define BD_PACK(MODE, CL)                                                                          \
     hipLaunchKernelGGL((k_compress<WT, HB, 2, MODE, CL>), grid, block, 0, s, wf, wb, pl.d_out,    \
                        pl.d_in, pl.rows_per_block, pl.group, pl.sdtype, signs, scales, st, pabs,  \
-                       status)
+                       flags)
     switch (pl.mode) {
         case BD_SCALE_MATRIX: if (pl.clip) BD_PACK(BD_SCALE_MATRIX, true); else BD_PACK(BD_SCALE_MATRIX, false); break;
         case BD_SCALE_GROUP: if (pl.clip) BD_PACK(BD_SCALE_GROUP, true); else BD_PACK(BD_SCALE_GROUP, false); break;
@@ -403,7 +429,9 @@ hipError_t launch_typed(const CompressPlan& pl, const WT* wf, const WT* wb, uint
         int64_t nthreads = pl.mode == BD_SCALE_MATRIX ? 256 : (pl.mode == BD_SCALE_ROW ? pl.d_out : pl.d_in);
         unsigned nb = pl.mode == BD_SCALE_MATRIX ? 1u : (unsigned)((nthreads + 255) / 256);
         hipLaunchKernelGGL(k_scales_finalize, dim3(nb), dim3(256), 0, s, pl.mode, pabs, pl.n_seg,
-                           pl.n_rchunk, pl.d_out, pl.d_in, pl.sdtype, scales);
+                           pl.n_rchunk, pl.d_out, pl.d_in, pl.sdtype, scales, flags, status);
+    } else {
+        hipLaunchKernelGGL(k_status_finalize, dim3(1), dim3(256), 0, s, flags, pl.n_blocks, status);
     }
     return hipGetLastError();
 }
@@ -419,32 +447,32 @@ hipError_t launch_axis_typed(const AxisPlan& ap, const WT* wf, const WT* wb, dou
     double* part = (double*)(ws + ap.off_part);
     double* rsq = (double*)(ws + ap.off_rsq);
     double* csq = (double*)(ws + ap.off_csq);
+    uint32_t* flags = (uint32_t*)(ws + pl.off_flags);
     const dim3 grid((unsigned)pl.n_seg, (unsigned)pl.n_rchunk), block(kCompressThreads);
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, status, (int64_t)(kAlign / 4));
     if (pl.clip) {
         hipLaunchKernelGGL((k_compress<WT, HB, 0, 0, false>), grid, block, 0, s, wf, wb, pl.d_out,
                            pl.d_in, pl.rows_per_block, 0, BD_F32, nullptr, nullptr, st, psum,
-                           status);
+                           flags);
         hipLaunchKernelGGL(k_stats_finalize<0>, dim3(1), dim3(256), 0, s, psum, pl.n_blocks, pl.n,
                            pl.clip_k, st);
         hipLaunchKernelGGL((k_compress<WT, HB, 1, 0, false>), grid, block, 0, s, wf, wb, pl.d_out,
                            pl.d_in, pl.rows_per_block, 0, BD_F32, nullptr, nullptr, st, pm2,
-                           status);
+                           flags);
         hipLaunchKernelGGL(k_stats_finalize<1>, dim3(1), dim3(256), 0, s, pm2, pl.n_blocks, pl.n,
                            pl.clip_k, st);
         hipLaunchKernelGGL((k_compress<WT, HB, 3, BD_SCALE_COL, true>), grid, block, 0, s, wf, wb,
                            pl.d_out, pl.d_in, pl.rows_per_block, 0, BD_F32, nullptr, nullptr, st,
-                           part, status);
+                           part, flags);
     } else {
         hipLaunchKernelGGL((k_compress<WT, HB, 3, BD_SCALE_COL, false>), grid, block, 0, s, wf, wb,
                            pl.d_out, pl.d_in, pl.rows_per_block, 0, BD_F32, nullptr, nullptr, st,
-                           part, status);
+                           part, flags);
     }
     const int64_t nmax = pl.d_out > pl.d_in ? pl.d_out : pl.d_in;
     hipLaunchKernelGGL(k_axis_sums, dim3((unsigned)((nmax + 255) / 256)), dim3(256), 0, s, part,
                        pl.n_seg, pl.n_rchunk, pl.n_blocks, pl.d_out, pl.d_in, rsq, csq);
     hipLaunchKernelGGL(k_axis_finalize, dim3(1), dim3(256), 0, s, part, pl.n_blocks, rsq, csq,
-                       pl.d_out, pl.d_in, errors, axis);
+                       pl.d_out, pl.d_in, errors, axis, flags, status);
     return hipGetLastError();
 }
 
@@ -469,6 +497,8 @@ bd_status make_axis_plan(float clip_k, int64_t d_out, int64_t d_in, AxisPlan* ap
     off += align_up(sizeof(double) * (size_t)d_out);
     q.off_csq = off;
     off += align_up(sizeof(double) * (size_t)d_in);
+    q.c.off_flags = off;  // (after ours: the compress layout's flags would overlap them)
+    off += align_up(sizeof(uint32_t) * (size_t)q.c.n_blocks);
     q.total = off;
     *ap = q;
     return BD_OK;
@@ -534,6 +564,8 @@ bd_status make_compress_plan(const bd_compress_params* p, int64_t d_out, int64_t
     if (q.mode == BD_SCALE_ROW) nabs = (size_t)(d_out * q.n_seg);
     if (q.mode == BD_SCALE_COL) nabs = (size_t)(q.n_rchunk * d_in);
     off += align_up(sizeof(double) * nabs);
+    q.off_flags = off;
+    off += align_up(sizeof(uint32_t) * (size_t)q.n_blocks);
     q.total = off;
     *pl = q;
     return BD_OK;

@@ -34,7 +34,8 @@ struct CompressPlan {
     bool clip = false;
     double clip_k = 0.0;
     // workspace offsets (bytes)
-    size_t off_status = 0, off_stats = 0, off_part_sum = 0, off_part_m2 = 0, off_part_abs = 0;
+    size_t off_status = 0, off_stats = 0, off_part_sum = 0, off_part_m2 = 0, off_part_abs = 0,
+           off_flags = 0;  // one non-finite flag per block of the packing pass
     size_t total = 0;
 };
 
