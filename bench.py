@@ -186,16 +186,29 @@ class Stack:
         torch.cuda.synchronize()
         self.setup_s = time.perf_counter() - t0
 
-        # algorithmic bytes (each byte the math must touch once, summed per matrix apply)
+        self.mats = mats
+        self._account()
+        self.n_mats = len(mats)
+        self.n_layers = len(mats) // 7
+
+    def _account(self):
+        """Algorithmic bytes (each byte the math must touch once, summed per matrix
+        apply) and base GEMM flops of one step on the current batch."""
         na, T = len(self.active), self.T
         self.bytes_step = self.bytes_delta = self.flops_gemm = 0
-        for m in mats:
+        for m in self.mats:
             self.bytes_step += (m.d_out * m.d_in * 2 + na * (m.d_out * m.d_in // 8 + 4)
                                 + T * m.d_in * 2 + T * m.d_out * 4 + 4 * T)
             self.bytes_delta += na * (m.d_out * m.d_in // 8 + 4) + T * m.d_out * 4
             self.flops_gemm += 2 * T * m.d_out * m.d_in
-        self.n_mats = len(mats)
-        self.n_layers = len(mats) // 7
+
+    def set_ids(self, ids_np):
+        """Another batch of the same size over the same resident banks."""
+        import torch
+        self.ids_np = ids_np
+        self.ids = torch.from_numpy(ids_np).to(self.ids.device)
+        self.active = sorted(set(int(u) for u in ids_np if 0 <= u < self.U))
+        self._account()
 
     # one phase at a time (graphs of one kind of launch, for per-kernel timing)
     def prepare(self):
@@ -299,11 +312,29 @@ def stack_leg(args, dev):
                "flops_per_launch": S.flops_gemm // n_gemm,
                "avg_launch_us": round(phases["gemm"] / n_gemm, 3)}
     dominant, other = (rl_delta, rl_gemm) if phases["delta"] >= phases["gemm"] else (rl_gemm, rl_delta)
+
+    # the same step on a batch with the mean number of distinct users: Zipf seed 0 draws
+    # 83 distinct users of 128, the lightest of seeds 0..39 (mean 91.9); seed 3 draws 92
+    from tenant_serving_amd import synth as SY
+    ids0 = S.ids_np
+    S.set_ids(SY.user_ids(SY.workload(5, seed=3)))
+    g3 = capture(S.step, K)
+    g3.replay()
+    wall3, _ = replay_timed(g3, K)
+    del g3
+    mean_batch = {"user_ids": "Zipf(1.1), seed 3", "active_users": len(S.active),
+                  "ms_per_step": round(wall3 * 1e-3, 4),
+                  "achieved_GBs": round(S.bytes_step / (wall3 * 1e-6) / 1e9, 1),
+                  "tokens_per_s": round(S.T / (wall3 * 1e-6), 1)}
+    S.set_ids(ids0)
+    log(f"stack step, seed-3 batch ({mean_batch['active_users']} users): {wall3 / 1e3:.3f} ms")
     out = {
         "value": round(value, 1), "ms_per_step": round(ms_per_step, 4),
         "config": {"workload": S.w.name, "layers": S.n_layers, "matrices": S.n_mats,
                    "n_users": S.U, "active_users": len(S.active), "tokens": S.T,
-                   "scale": "matrix fp32", "y_dtype": "fp32", "user_ids": "Zipf(1.1), seed 0",
+                   "scale": "matrix fp32", "y_dtype": "fp32",
+                   "user_ids": "Zipf(1.1), seed 0 (83 distinct users: the lightest of seeds "
+                               "0..39, whose mean is 91.9; step_mean_batch: seed 3, 92 users)",
                    "banks": "bd_compress of seeded synthetic fine-tunes (Laplace b=5e-4)",
                    "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(S.T / (ms_per_step * 1e-3), 1),
@@ -320,8 +351,117 @@ def stack_leg(args, dev):
         "base_gemm": {"TFLOPs": round(gemm_tfs, 1), "frac_of_bf16_peak": round(gemm_tfs / BF16_PEAK_TFLOPS, 4),
                       "flops_per_step": S.flops_gemm},
         "setup_s": round(S.setup_s, 1),
+        "step_mean_batch": mean_batch,
     }
     return out, S
+
+
+# ---------------------------------------------------------------- INT8 base and paging legs
+def int8_leg(S, dev, K):
+    """The same decode step with the base weights as INT8 rows (bd_quantize_base): one
+    bd_apply_q8 per matrix (each: prepare, tiled INT8-code GEMM, encode, delta), K steps
+    in one HIP graph.  Algorithmic bytes as the bf16 step's with one byte per base
+    weight and a scale per row."""
+    import torch
+    B = S.B
+    qs = [B.quantize_base(wb) for wb in S.wb]
+    torch.cuda.synchronize()
+    ws = {}
+    for m in range(S.n_mats):
+        d_out, d_in = S.wb[m].shape
+        ws.setdefault((d_out, d_in), B.workspace(B.bd_apply_q8_workspace_bytes(
+            S.p, S.T, S.U, d_out, d_in, B.BD_BF16, B.BD_F32), dev))
+
+    def step():
+        for l in range(S.n_layers):
+            for gi, (first, cnt) in enumerate(S.GROUPS):
+                x = S.xs[4 * l + gi]
+                for m in range(7 * l + first, 7 * l + first + cnt):
+                    q, sc = qs[m]
+                    assert B.bd_apply_q8(x, q, sc, S.signs[m], S.scales[m], S.p, S.U, S.ids,
+                                         S.y[m], ws[tuple(S.wb[m].shape)]) == B.BD_OK
+
+    step()
+    torch.cuda.synchronize()
+    for w_ in ws.values():
+        assert B.bd_device_status(w_) == B.BD_OK
+    g = capture(step, K)
+    g.replay()
+    wall_us, ev_us = replay_timed(g, K)
+    del g
+    nbytes = 0
+    for m in range(S.n_mats):
+        d_out, d_in = S.wb[m].shape
+        nbytes += (d_out * d_in + 4 * d_out + len(S.active) * (d_out * d_in // 8 + 4)
+                   + S.T * d_in * 2 + S.T * d_out * 4 + 4 * S.T)
+    gbs = nbytes / (wall_us * 1e-6) / 1e9
+    return {"ms_per_step": round(wall_us * 1e-3, 4), "gpu_step_us_events": round(ev_us, 1),
+            "algorithmic_bytes_per_step": nbytes, "achieved_GBs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "calls": f"{S.n_mats} bd_apply_q8 (one per matrix, ungrouped)",
+            "base": "per-row symmetric INT8 codes + fp32 row scales (bd_quantize_base)"}
+
+
+def paged_leg(S, dev, n_slots=96, reps=5):
+    """Layer 0's seven matrices served from a pool of n_slots device slots (BankPager):
+    every one of the 128 users' packed layer-0 module in pinned host memory, the pool
+    warmed with this step's users; then a step of another Zipf batch (seed 1), whose
+    users not resident are loaded first (one host-to-device copy per module, least
+    recently used slots evicted).  Times the cold step (loads + 7 bd_apply_paged) and
+    the same batch again (all resident), wall clock around each."""
+    import torch
+
+    from tenant_serving_amd import synth as SY
+    from tenant_serving_amd.pager import BankPager
+    B = S.B
+    shapes = [tuple(S.wb[m].shape) for m in range(7)]
+    pager = BankPager(shapes, [1] * 7, torch.float32, n_slots, S.U, dev)
+    t0 = time.perf_counter()
+    for u in range(S.U):
+        pager.pack(u, [S.signs[m][u] for m in range(7)], [S.scales[m][u] for m in range(7)])
+    pack_s = time.perf_counter() - t0
+    ids_b = SY.user_ids(SY.workload(5, seed=1))
+    ids_b_dev = torch.from_numpy(ids_b).to(dev)
+    ws = {}
+    for m in range(7):
+        d_out, d_in = shapes[m]
+        ws[m] = B.workspace(B.bd_apply_paged_workspace_bytes(S.p, S.T, n_slots, d_out, d_in,
+                                                             B.BD_BF16, B.BD_F32), dev)
+    xs = [S.xs[0]] * 3 + [S.xs[1]] + [S.xs[2]] * 2 + [S.xs[3]]
+
+    def layer(ids_dev):
+        for m in range(7):
+            pager.apply(m, xs[m], S.wb[m], S.p, ids_dev, y=S.y[m], ws=ws[m])
+
+    cold, warm, misses = [], [], []
+    for r in range(reps):
+        pager.ensure(S.ids_np)  # this step's users resident (batch A)
+        layer(S.ids)
+        torch.cuda.synchronize()
+        before = pager.loads
+        t1 = time.perf_counter()
+        pager.ensure(ids_b)
+        layer(ids_b_dev)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        layer(ids_b_dev)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        cold.append(t2 - t1)
+        warm.append(t3 - t2)
+        misses.append(pager.loads - before)
+    for m in range(7):
+        assert B.bd_device_status(ws[m]) == B.BD_OK
+    users_b = len(set(int(u) for u in ids_b if u >= 0))
+    loaded = misses[-1] * pager.slot_bytes
+    cold_ms, warm_ms = 1e3 * min(cold), 1e3 * min(warm)
+    return {"module": "layer 0: q, k, v, o, gate, up, down", "slot_bytes": pager.slot_bytes,
+            "slots": n_slots, "users_in_host_store": S.U, "host_store_pack_s": round(pack_s, 2),
+            "cold_batch_users": users_b, "misses_per_cold_step": misses[-1],
+            "cold_step_ms": round(cold_ms, 3), "warm_step_ms": round(warm_ms, 3),
+            "load_GBs_effective": round(loaded / max(1e-9, (cold_ms - warm_ms) * 1e-3) / 1e9, 1),
+            "timing": "wall clock, min over reps; cold = ensure (misses copied from pinned "
+                      "host memory) + 7 applies; warm = the 7 applies again"}
 
 
 # ---------------------------------------------------------------- q_proj decode leg
@@ -562,6 +702,12 @@ def main():
     cpu_sample = None
     if not args.no_cpu_baseline:
         cpu_sample = (S.ids_np, S.active, S.bytes_step)
+    if not args.no_legs:
+        log("INT8 base step")
+        out["int8_base_step"] = int8_leg(S, dev, max(1, args.steps // 2))
+        torch.cuda.empty_cache()
+        log("paged banks (layer 0)")
+        out["paged_layer0"] = paged_leg(S, dev)
     del S
     torch.cuda.empty_cache()
 
