@@ -806,26 +806,35 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         neff += __popcll(__ballot(k < ntl && tpre[k] < tot));
     }
     neff = uni(neff);
-    // the first item (linear index k C + c) whose first sweep is at or after sweep w
-    auto locate = [&](int64_t w) -> int64_t {
+    // Sweep w of the launch (sweeps in the order tile rank k, chunk c, user j of the tile;
+    // tile k's sweeps start at tpre[k] C) -> (k, c, j).  Each block takes an equal share of
+    // the sweeps, so an item (tile, chunk) may be split between two blocks at a user: each
+    // then adds only its own users' tokens.
+    auto locate = [&](int64_t w, int& kk, int& cc, int& jj) __attribute__((always_inline)) {
         int cnt = 0;
         for (int b = 0; b < neff; b += 64) {
-            const int k = b + lane;
-            cnt += __popcll(__ballot(k < neff && (int64_t)tpre[k] * C <= w));
+            const int q = b + lane;
+            cnt += __popcll(__ballot(q < neff && (int64_t)tpre[q] * C <= w));
         }
-        const int k = uni(cnt) - 1;  // (>= 0: tpre[0] = 0)
-        if (k < 0 || k >= neff) return (int64_t)neff * C;
-        const int64_t rem = w - (int64_t)sload(tpre, k) * C;
-        int nu = sload(tpre, k + 1) - sload(tpre, k);
-        nu = nu < 1 ? 1 : nu;
-        const int64_t c = (rem + nu - 1) / nu;
-        const int64_t i = (int64_t)k * C + c;
-        return i < (int64_t)neff * C ? i : (int64_t)neff * C;
+        const int q = uni(cnt) - 1;  // (>= 0: tpre[0] = 0)
+        kk = q;
+        cc = jj = 0;
+        if (q < 0 || q >= neff) return;
+        const int64_t rem = w - (int64_t)sload(tpre, q) * C;
+        int nq = sload(tpre, q + 1) - sload(tpre, q);
+        nq = nq < 1 ? 1 : nq;
+        cc = (int)(rem / nq);
+        jj = (int)(rem % nq);
     };
     const int64_t Wt = (int64_t)tot * C;
-    const int64_t i0 = uni64(locate(Wt * (int64_t)blockIdx.x / gridDim.x));
-    const int64_t i1 = uni64(locate(Wt * ((int64_t)blockIdx.x + 1) / gridDim.x));
-    if (i0 >= i1) return;  // uniform: no items
+    const int64_t w0 = Wt * (int64_t)blockIdx.x / gridDim.x;
+    const int64_t w1 = Wt * ((int64_t)blockIdx.x + 1) / gridDim.x;
+    if (w0 >= w1) return;  // uniform: no sweeps
+    int sk0, sc0, sj0;
+    locate(w0, sk0, sc0, sj0);
+    sk0 = uni(sk0);
+    sc0 = uni(sc0);
+    sj0 = uni(sj0);
 
     const int u = u0 + wv;
     const bool uact = u < units;  // uniform
@@ -837,8 +846,8 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
 #define BD_VOFF(r) (lane_off + (uint32_t)(r) * rstride)
 
     // ---- loading side: item (kL, cL), user jL; scalar state, one descriptor per sweep
-    int kL = (int)(i0 / C), cL = (int)(i0 % C), jL = 0;
-    int64_t leftL = i1 - i0;  // items the loader has not finished
+    int kL = sk0, cL = sc0, jL = sj0;
+    int64_t leftL = w1 - w0;  // sweeps the loader has not issued
     int tileL = sload(torder, kL), nuL = 1;
     {
         const int nu = sload(tpre, kL + 1) - sload(tpre, kL);
@@ -860,10 +869,11 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
                               (uint64_t)row0 * bank_row;
         const uint64_t rem = ok && row0 < d_out ? (uint64_t)(d_out - row0) * bank_row : 0ull;
         const int nrec = rem > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)rem;
-        if (live && ++jL == nuL) {  // next item
-            jL = 0;
-            if (--leftL > 0) {
-                if (++cL == C) {
+        if (live) {
+            --leftL;
+            if (++jL == nuL) {  // next item
+                jL = 0;
+                if (leftL > 0 && ++cL == C) {
                     cL = 0;
                     ++kL;
                     tileL = sload(torder, kL);
@@ -898,9 +908,10 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
     asm volatile("s_mov_b32 %0, 0xCCCCCCCC" : "=s"(k1));
     asm volatile("s_mov_b32 %0, 0x88888888" : "=s"(k2));
     asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(k3));
-    int k = (int)(i0 / C), c = (int)(i0 % C);
-    int64_t left = i1 - i0;
-    int tile = -1, nu = 1, j = 0, ci = 0;  // ci: items done (LDS buffer parity)
+    int k = sk0, c = sc0;
+    int64_t left = w1 - w0;  // sweeps not yet done
+    int tile = -1, nu = 1, j = sj0, ja = sj0, ci = 0;  // ja: the item's first user here;
+                                                     // ci: items done (LDS buffer parity)
     // a new tile (its loads are the youngest: their first use waits for every load in
     // flight; once or twice per block)
     auto tile_setup = [&](int t, int nut) __attribute__((always_inline)) {
@@ -1070,7 +1081,9 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         }
         pend = false;
     };
-    auto item_end = [&]() __attribute__((always_inline)) {
+    // (users [jb, je) of the item's tile were done here: the sums of the other users'
+    // tokens are another block's)
+    auto item_end = [&](int jb, int je) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) part[ci & 1][r][wv][lane] = acc[r];
         // this wave's partial writes have landed in LDS; then a bare barrier (a fence
@@ -1079,6 +1092,18 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         asm volatile("s_barrier" ::: "memory");
 #pragma unroll
         for (int e = 0; e < 4; ++e) ptk[e] = ltok(e);  // (every lane active)
+        if (jb > 0 || je < nu) {  // uniform: part of the item's users
+            int q_e[4] = {-1, -1, -1, -1};
+            for (int q = 0; q < nu; ++q) {
+                const int uq = __shfl(trow, 32 + q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (lusr(e) == uq) q_e[e] = q;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (q_e[e] < jb || q_e[e] >= je) ptk[e] = -1;
+        }
         if constexpr (MODE == BD_SCALE_MATRIX) {
             const f32x4 f4 = *(const f32x4*)&sF[imi][4 * G];
 #pragma unroll
@@ -1166,19 +1191,22 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
                 fresh = false;
             }
         }
-        if (left > 0 && ++j == nu) {  // uniform: the item is complete
-            j = 0;
-            item_end();
-            if (--left > 0) {
-                if (++c == C) {
-                    c = 0;
-                    ++k;
-                    tile = sload(torder, k);
-                    const int q = sload(tpre, k + 1) - sload(tpre, k);
-                    nu = q < 1 ? 1 : (q > 16 ? 16 : q);
-                    tile_setup(tile, nu);
+        if (left > 0) {  // uniform
+            --left;
+            if (++j == nu || left == 0) {  // the item, or this block's part of it, is done
+                item_end(ja, j);
+                j = ja = 0;
+                if (left > 0) {
+                    if (++c == C) {
+                        c = 0;
+                        ++k;
+                        tile = sload(torder, k);
+                        const int q = sload(tpre, k + 1) - sload(tpre, k);
+                        nu = q < 1 ? 1 : (q > 16 ? 16 : q);
+                        tile_setup(tile, nu);
+                    }
+                    item_start();
                 }
-                item_start();
             }
         }
     };
