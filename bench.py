@@ -183,6 +183,11 @@ class Stack:
             self.batches[d_in] = B.workspace(
                 B.bd_batch_workspace_bytes(self.T, self.U, d_in, B.BD_BF16), dev)
         self.first_x = {d: next(x for x in self.xs if x.shape[1] == d) for d in self.batches}
+        # the grouped base GEMMs' K-split partial products (one workspace for every group)
+        need = max(B.bd_base_gemm_n_workspace_bytes(
+            B.BD_BF16, self.T, mats[7 * l + f].d_in, [mats[7 * l + f + i].d_out for i in range(c)])
+            for l in range(len(mats) // 7) for f, c in self.GROUPS) if len(mats) >= 7 else 0
+        self.gemm_ws = B.workspace(need, dev) if need > 0 else None
         torch.cuda.synchronize()
         self.setup_s = time.perf_counter() - t0
 
@@ -229,7 +234,8 @@ class Stack:
 
     def _gemm(self, x, ms):
         B = self.B
-        assert B.bd_base_gemm_n(x, [self.wb[m] for m in ms], [self.y[m] for m in ms]) == B.BD_OK
+        assert B.bd_base_gemm_n(x, [self.wb[m] for m in ms], [self.y[m] for m in ms],
+                                workspace=self.gemm_ws) == B.BD_OK
 
     def _delta(self, x, bt, ms):
         B = self.B

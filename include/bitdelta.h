@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BD_ABI_VERSION 2
+#define BD_ABI_VERSION 3
 
 typedef enum {
     BD_OK = 0,
@@ -384,10 +384,18 @@ bd_status bd_delta_apply_encoded(void* batch, size_t batch_bytes, bd_dtype x_dty
  *                bd_delta_apply_encoded with d_out = d_outs[i].
  *  ys          : host array of n_mats device pointers, fp32 [T][d_outs[i]] each.
  * bd_base_gemm_n falls back to one launch per matrix for batches the tiled GEMM
- * does not take (T <= 64, fp32). */
+ * does not take (T <= 64, fp32).  Where the largest tile would leave most of the
+ * chip idle (few rows and tokens: q|k|v, o or down at 512 tokens) and `workspace` is
+ * given, K is split into 2, 4 or 8 ordered parts whose partial products go to the
+ * workspace and are summed by a second launch in part order, so y repeats bit for
+ * bit; workspace NULL (or bd_base_gemm_n_workspace_bytes == 0): no split.
+ *  workspace   : >= bd_base_gemm_n_workspace_bytes(...) bytes, 256-byte aligned,
+ *                or NULL. */
+size_t bd_base_gemm_n_workspace_bytes(bd_dtype x_dtype, int64_t T, int64_t d_in, int32_t n_mats,
+                                      const int64_t* d_outs);
 bd_status bd_base_gemm_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
                          int32_t n_mats, const void* const* w_bases, const int64_t* d_outs,
-                         float* const* ys, void* stream);
+                         float* const* ys, void* workspace, size_t ws_bytes, void* stream);
 bd_status bd_delta_apply_encoded_n(void* batch, size_t batch_bytes, bd_dtype x_dtype, int64_t T,
                                    int64_t d_in, int32_t n_users, int32_t n_mats,
                                    const int64_t* d_outs, const uint64_t* const* signs_banks,

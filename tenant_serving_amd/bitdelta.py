@@ -110,8 +110,10 @@ def lib() -> ctypes.CDLL:
         L.bd_delta_apply_encoded.restype = ctypes.c_int
         L.bd_delta_apply_encoded.argtypes = [vp, sz, ctypes.c_int, i64, i64, i32, i64, vp, vp, P,
                                              vp, vp]
+        L.bd_base_gemm_n_workspace_bytes.restype = sz
+        L.bd_base_gemm_n_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32, vp]
         L.bd_base_gemm_n.restype = ctypes.c_int
-        L.bd_base_gemm_n.argtypes = [vp, ctypes.c_int, i64, i64, i32, vp, vp, vp, vp]
+        L.bd_base_gemm_n.argtypes = [vp, ctypes.c_int, i64, i64, i32, vp, vp, vp, vp, sz, vp]
         L.bd_delta_apply_encoded_n.restype = ctypes.c_int
         L.bd_delta_apply_encoded_n.argtypes = [vp, sz, ctypes.c_int, i64, i64, i32, i32, vp, vp,
                                                vp, P, vp, vp]
@@ -417,8 +419,14 @@ def _ptr_array(ts):
     return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
 
 
-def bd_base_gemm_n(x, w_bases, ys, stream=None) -> int:
-    """Base products of up to 4 matrices that read x, in one launch."""
+def bd_base_gemm_n_workspace_bytes(x_dtype: int, T: int, d_in: int, d_outs) -> int:
+    arr = (ctypes.c_int64 * len(d_outs))(*[int(d) for d in d_outs])
+    return int(lib().bd_base_gemm_n_workspace_bytes(x_dtype, T, d_in, len(d_outs), arr))
+
+
+def bd_base_gemm_n(x, w_bases, ys, workspace=None, stream=None) -> int:
+    """Base products of up to 4 matrices that read x, in one launch (K split in ordered
+    parts through `workspace` where that fills the chip better; None: no split)."""
     _dev(x, "x", (torch.float32, torch.bfloat16))
     T, d_in = x.shape
     if not 1 <= len(w_bases) <= 4 or len(ys) != len(w_bases):
@@ -426,9 +434,11 @@ def bd_base_gemm_n(x, w_bases, ys, stream=None) -> int:
     for w, y in zip(w_bases, ys):
         _dev(w, "w_base", (x.dtype,), (w.shape[0], d_in), x.device)
         _dev(y, "y", (torch.float32,), (T, w.shape[0]), x.device)
+    _dev(workspace, "workspace", None, None, x.device, optional=True)
     d_outs = (ctypes.c_int64 * len(ys))(*[w.shape[0] for w in w_bases])
     return int(lib().bd_base_gemm_n(_ptr(x), _dtype_code(x), T, d_in, len(ys),
-                                    _ptr_array(w_bases), d_outs, _ptr_array(ys),
+                                    _ptr_array(w_bases), d_outs, _ptr_array(ys), _ptr(workspace),
+                                    0 if workspace is None else _nbytes(workspace),
                                     _stream(x, stream)))
 
 

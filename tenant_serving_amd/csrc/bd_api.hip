@@ -267,9 +267,19 @@ bd_status bd_delta_apply_encoded(void* batch, size_t batch_bytes, bd_dtype x_dty
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
+size_t bd_base_gemm_n_workspace_bytes(bd_dtype x_dtype, int64_t T, int64_t d_in, int32_t n_mats,
+                                      const int64_t* d_outs) {
+    if (x_dtype != BD_BF16 || T <= 0 || n_mats < 1 || n_mats > kMaxMats || !d_outs || d_in <= 0 ||
+        d_in % 64 != 0)
+        return 0;
+    for (int i = 0; i < n_mats; ++i)
+        if (!gemm_path_supported(T, d_in, d_outs[i])) return 0;
+    return gemm_split_bytes(T, d_in, d_outs, n_mats);
+}
+
 bd_status bd_base_gemm_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
                          int32_t n_mats, const void* const* w_bases, const int64_t* d_outs,
-                         float* const* ys, void* stream) {
+                         float* const* ys, void* workspace, size_t ws_bytes, void* stream) {
     if (!valid_wdtype(x_dtype)) return BD_ERR_DTYPE;
     if (T < 0 || n_mats < 1 || n_mats > kMaxMats || !w_bases || !d_outs || !ys)
         return BD_ERR_INVALID_ARG;
@@ -292,7 +302,13 @@ bd_status bd_base_gemm_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_i
     if (tiled) {
         GemmMatArg m[kMaxMats];
         for (int i = 0; i < n_mats; ++i) m[i] = GemmMatArg{w_bases[i], ys[i], d_outs[i]};
-        e = launch_gemm_set(x, T, d_in, m, n_mats, s);
+        const size_t need = gemm_split_bytes(T, d_in, d_outs, n_mats);
+        if (need > 0 && workspace) {
+            if (ws_bytes < need || !aligned(workspace, kAlign)) return BD_ERR_WORKSPACE;
+            e = launch_gemm_set_split(x, T, d_in, m, n_mats, (char*)workspace, s);
+        } else {
+            e = launch_gemm_set(x, T, d_in, m, n_mats, s);
+        }
     } else {
         for (int i = 0; i < n_mats && e == hipSuccess; ++i)
             e = launch_base_gemm(x, x_dtype, T, d_in, w_bases[i], d_outs[i], ys[i], s);

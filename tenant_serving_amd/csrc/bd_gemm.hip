@@ -84,7 +84,7 @@ __device__ __forceinline__ uint32_t swz(int r, int c) {
 // products and written after them); the epilogue multiplies each row by its scale.
 template <int BR, int BT, int BK, int NS, int NW, bool Q8>
 __global__ void __launch_bounds__(64 * NW)
-k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt) {
+k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt, int S, int kps) {
     // NW waves: NW / 2 along the rows, 2 along the tokens
     constexpr int NWR = NW / 2;
     constexpr int MI = BR / NWR / 32, NJ = BT / 64;  // 32 x 32 tiles per wave
@@ -98,9 +98,13 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
     static_assert(!Q8 || (NS == 2 && (BR * BK) % (1024 * NW) == 0), "INT8 codes: two stages");
     constexpr int kQInst = Q8 ? BR * BK / (1024 * NW) : 1;  // 16-code loads per lane and stage
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    // block -> (row tile, token tile); the token tiles of one row tile share an XCD.
-    // Row tiles run over the matrices of the set back to back.
-    const int id = blockIdx.x;
+    // block -> (K part, row tile, token tile); the token tiles of one row tile share an
+    // XCD.  Row tiles run over the matrices of the set back to back.  S > 1: K part sp
+    // covers columns [sp kps, (sp + 1) kps) and writes its partial tile to part.
+    const int per = (int)(gridDim.x / (unsigned)S);
+    const int sp = (int)blockIdx.x / per;
+    const int id = (int)blockIdx.x - sp * per;
+    const int kbeg = sp * kps;
     const int q = id >> 3;
     const int tt = q % ntt;
     const int rtg = (q / ntt) * 8 + (id & 7);
@@ -109,7 +113,9 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
 #pragma unroll
     for (int j = 1; j < kMaxMats; ++j) mi += (j < gm.n && rtg >= gm.rt_begin[j]) ? 1 : 0;
     const uint16_t* const w = mi == 0 ? gm.w[0] : mi == 1 ? gm.w[1] : mi == 2 ? gm.w[2] : gm.w[3];
-    float* const y = mi == 0 ? gm.y[0] : mi == 1 ? gm.y[1] : mi == 2 ? gm.y[2] : gm.y[3];
+    float* const y = S > 1 ? (mi == 0 ? gm.part[0] : mi == 1 ? gm.part[1] : mi == 2 ? gm.part[2] : gm.part[3]) +
+                                 (int64_t)sp * T * (mi == 0 ? gm.N[0] : mi == 1 ? gm.N[1] : mi == 2 ? gm.N[2] : gm.N[3])
+                           : (mi == 0 ? gm.y[0] : mi == 1 ? gm.y[1] : mi == 2 ? gm.y[2] : gm.y[3]);
     const int N = mi == 0 ? gm.N[0] : mi == 1 ? gm.N[1] : mi == 2 ? gm.N[2] : gm.N[3];
     const float* const wsc = mi == 0 ? gm.s[0] : mi == 1 ? gm.s[1] : mi == 2 ? gm.s[2] : gm.s[3];
     const int rt = rtg - (mi == 0 ? gm.rt_begin[0] : mi == 1 ? gm.rt_begin[1]
@@ -150,11 +156,11 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
         qsrc[j] = Q8 && r0 + r < N ? (uint32_t)((int64_t)(r0 + r) * K + 16 * c) : kOOB;
         qdst[j] = (uint32_t)(r * 4096 + c);  // (row, code group), unpacked at the store
     }
-    const int nk = K / BK;
+    const int nk = kps / BK;  // stages of this block's K part
     auto qload = [&](int s) {  // stage s's codes into registers (zeros past K)
 #pragma unroll
         for (int j = 0; j < kQInst; ++j)
-            qreg[j] = buf_load16(wrs, (s < nk && qsrc[j] != kOOB) ? qsrc[j] + (uint32_t)s * BK : kOOB);
+            qreg[j] = buf_load16(wrs, (s < nk && qsrc[j] != kOOB) ? qsrc[j] + (uint32_t)(kbeg + s * BK) : kOOB);
     };
     auto qstore = [&](int s) {  // the codes of stage s, widened, into ring slot s % NS
         char* base = smem + (s % NS) * kStageBytes;
@@ -174,7 +180,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt)
     auto issue = [&](int s) {  // stage s into ring slot s % NS (zeros past K)
         char* base = smem + (s % NS) * kStageBytes;
         const bool ok = s < nk;
-        const uint32_t kb = (uint32_t)s * BK * 2;
+        const uint32_t kb = (uint32_t)(kbeg + s * BK) * 2;
         if (!Q8) {
 #pragma unroll
             for (int j = 0; j < kWInst; ++j)
@@ -264,13 +270,15 @@ namespace {
 
 template <int BR, int BT, int BK, int NS, int NW = 4, bool Q8 = false>
 hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
-                       hipStream_t s, const float* const* wscales = nullptr) {
+                       hipStream_t s, const float* const* wscales = nullptr, int S = 1,
+                       float* const* parts = nullptr) {
     GemmMats gm = {};
     gm.n = n;
     int rt = 0;
     for (int i = 0; i < n; ++i) {
         gm.w[i] = (const uint16_t*)mats[i].w;
         gm.s[i] = wscales ? wscales[i] : nullptr;
+        gm.part[i] = parts ? parts[i] : nullptr;
         gm.y[i] = mats[i].y;
         gm.N[i] = (int)mats[i].d_out;
         gm.rt_begin[i] = rt;
@@ -279,14 +287,82 @@ hipError_t launch_tile(const void* x, int64_t T, int64_t d_in, const GemmMatArg*
     for (int i = n; i <= kMaxMats; ++i) gm.rt_begin[i] = rt;
     const int ntt = (int)((T + BT - 1) / BT);
     const int nrt8 = (rt + 7) / 8 * 8;
-    const unsigned blocks = (unsigned)(nrt8 * ntt);
+    const unsigned blocks = (unsigned)(nrt8 * ntt * S);
     constexpr int lds = NS * (BR + BT) * BK * 2;
     k_gemm<BR, BT, BK, NS, NW, Q8><<<dim3(blocks), dim3(64 * NW), lds, s>>>(
-        (const uint16_t*)x, gm, (int)T, (int)d_in, ntt);
+        (const uint16_t*)x, gm, (int)T, (int)d_in, ntt, S, (int)(d_in / S));
     return hipGetLastError();
 }
 
+// y = the sum of the S partial products, in split order (grid.y: the matrix).
+__global__ void __launch_bounds__(256)
+k_split_reduce(const GemmMats gm, int64_t T, int S) {
+    const int mi = (int)blockIdx.y;
+    const int64_t n4 = T * (int64_t)gm.N[mi] / 4;  // (N % 4 == 0 on this path)
+    const f32x4* part = (const f32x4*)gm.part[mi];
+    f32x4* y = (f32x4*)gm.y[mi];
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        f32x4 v = part[i];
+        for (int q = 1; q < S; ++q) v += part[(int64_t)q * n4 + i];
+        y[i] = v;
+    }
+}
+
+// K parts for the 256 x 256 tile: S in {2, 4, 8} when the grid would otherwise stay under
+// 200 blocks, each part at least 1024 columns (16 stages), the split grid 192..320 blocks.
+int choose_split(int64_t T, int64_t d_in, const int64_t* d_outs, int n) {
+    if (T <= kGemmMinT) return 1;
+    int64_t b = 0;
+    for (int i = 0; i < n; ++i) {
+        if (d_outs[i] % 4 != 0) return 1;
+        b += (d_outs[i] + 255) / 256;
+    }
+    b *= (T + 255) / 256;
+    if (b >= 200) return 1;
+    for (int S = 8; S >= 2; S /= 2)
+        if (d_in % (64 * S) == 0 && d_in / S >= 1024 && b * S >= 192 && b * S <= 320) return S;
+    return 1;
+}
+
 }  // namespace
+
+size_t gemm_split_bytes(int64_t T, int64_t d_in, const int64_t* d_outs, int n) {
+    const int S = choose_split(T, d_in, d_outs, n);
+    if (S == 1) return 0;
+    size_t b = 0;
+    for (int i = 0; i < n; ++i) b += ((size_t)S * T * d_outs[i] * 4 + kAlign - 1) / kAlign * kAlign;
+    return b;
+}
+
+hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats,
+                                 int n, char* ws, hipStream_t s) {
+    if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
+    int64_t d_outs[kMaxMats];
+    for (int i = 0; i < n; ++i) d_outs[i] = mats[i].d_out;
+    const int S = choose_split(T, d_in, d_outs, n);
+    if (S == 1 || !ws) return launch_gemm_set(x, T, d_in, mats, n, s);
+    float* parts[kMaxMats];
+    size_t off = 0;
+    int64_t nmax = 0;
+    for (int i = 0; i < n; ++i) {
+        parts[i] = (float*)(ws + off);
+        off += ((size_t)S * T * d_outs[i] * 4 + kAlign - 1) / kAlign * kAlign;
+        nmax = d_outs[i] > nmax ? d_outs[i] : nmax;
+    }
+    hipError_t e = launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
+    if (e != hipSuccess) return e;
+    GemmMats gm = {};
+    gm.n = n;
+    for (int i = 0; i < n; ++i) {
+        gm.part[i] = parts[i];
+        gm.y[i] = mats[i].y;
+        gm.N[i] = (int)d_outs[i];
+    }
+    const int64_t n4 = T * nmax / 4;
+    const unsigned gx = (unsigned)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048);
+    hipLaunchKernelGGL(k_split_reduce, dim3(gx, (unsigned)n), dim3(256), 0, s, gm, T, S);
+    return hipGetLastError();
+}
 
 // 17..64 tokens on a wide matrix: one 64-token tile per 64 rows copies the tokens once
 // per 64 rows (the streaming kernel re-reads them from L2 for every 16 rows), and at

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert "bd_compress" in names and "bd_apply" in names and "bd_reconstruct" in names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
-    assert lib.bd_abi_version() == 2
+    assert lib.bd_abi_version() == 3
 
 
 def test_status_strings():

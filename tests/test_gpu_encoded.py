@@ -108,3 +108,37 @@ def test_grouped_calls_equal_per_matrix_calls():
     assert B.bd_device_status(bt) == B.BD_OK
     for y, yr in zip(ys, ref):
         assert torch.equal(y, yr)
+
+
+@pytest.mark.parametrize("d_outs,d_in,T", [((4096, 1024, 1024), 4096, 512),  # q|k|v: 4 parts
+                                           ((4096,), 14336, 512),              # down: 8 parts
+                                           ((1028, 1028, 1024), 8192, 300)])   # ragged rows, T
+def test_grouped_gemm_with_k_split(d_outs, d_in, T):
+    """bd_base_gemm_n with K split in ordered parts (workspace given): against the
+    oracle's base term on sampled rows of every matrix (exact bf16 products, fp32 sums:
+    1e-5 rms), against the unsplit launch within fp32 summation order, and bit for bit
+    from one call to the next."""
+    need = B.bd_base_gemm_n_workspace_bytes(B.BD_BF16, T, d_in, d_outs)
+    assert need > 0
+    ws_ = [custom(d, d_in, S.BF16, T=T, cid=2750 + i) for i, d in enumerate(d_outs)]
+    wbs = [S.dev_wbase(w, 0) for w in ws_]
+    x = S.dev_x(ws_[0], 0)
+    ws = B.workspace(need, DEV)
+    ys = [torch.empty(T, d, device=DEV) for d in d_outs]
+    assert B.bd_base_gemm_n(x, wbs, ys, workspace=ws) == B.BD_OK
+    ys2 = [torch.empty(T, d, device=DEV) for d in d_outs]
+    assert B.bd_base_gemm_n(x, wbs, ys2, workspace=ws) == B.BD_OK
+    yn = [torch.empty(T, d, device=DEV) for d in d_outs]
+    assert B.bd_base_gemm_n(x, wbs, yn) == B.BD_OK  # no workspace: no split
+    torch.cuda.synchronize()
+    x_np = S.host_x(ws_[0], 0)
+    ids = np.full(T, -1, np.int32)
+    for i, d in enumerate(d_outs):
+        assert torch.equal(ys[i], ys2[i])
+        rows = sorted({0, d - 1} | set(np.random.default_rng(d).choice(d, 40, replace=False).tolist()))
+        _, yb, _ = O.apply(x_np, S.host_wbase(ws_[i], 0, rows), np.zeros((1, len(rows), d_in // 64), np.uint64),
+                           np.zeros((1, 1), np.float32), O.MATRIX, ids)
+        err, rms = max_err_vs_rms(ys[i].cpu().numpy()[:, rows], yb)
+        assert err <= 1e-5 * rms, (i, err, rms)
+        err, rms = max_err_vs_rms(ys[i].cpu().numpy(), yn[i].cpu().numpy().astype(np.float64))
+        assert err <= 1e-5 * rms, (i, err, rms)
