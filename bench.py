@@ -364,37 +364,44 @@ def stack_leg(args, dev):
 
 # ---------------------------------------------------------------- INT8 base and paging legs
 def int8_leg(S, dev, K):
-    """The same decode step with the base weights as INT8 rows (bd_quantize_base): one
-    bd_apply_q8 per matrix (each: prepare, tiled INT8-code GEMM, encode, delta), K steps
-    in one HIP graph.  Algorithmic bytes as the bf16 step's with one byte per base
-    weight and a scale per row."""
+    """The same step with the base weights as INT8 rows (bd_quantize_base), grouped as
+    the bf16 step is: prepare once per width, then per group of matrices that read the
+    same activations one encode, one bd_base_gemm_q8_n (the codes widened on chip, K
+    split where the bf16 GEMM splits) and one bd_delta_apply_encoded_n; K steps in one
+    HIP graph.  Algorithmic bytes as the bf16 step's with one byte per base weight and
+    a scale per row."""
     import torch
     B = S.B
     qs = [B.quantize_base(wb) for wb in S.wb]
     torch.cuda.synchronize()
-    ws = {}
-    for m in range(S.n_mats):
-        d_out, d_in = S.wb[m].shape
-        ws.setdefault((d_out, d_in), B.workspace(B.bd_apply_q8_workspace_bytes(
-            S.p, S.T, S.U, d_out, d_in, B.BD_BF16, B.BD_F32), dev))
 
     def step():
-        for l in range(S.n_layers):
-            for gi, (first, cnt) in enumerate(S.GROUPS):
-                x = S.xs[4 * l + gi]
-                for m in range(7 * l + first, 7 * l + first + cnt):
-                    q, sc = qs[m]
-                    assert B.bd_apply_q8(x, q, sc, S.signs[m], S.scales[m], S.p, S.U, S.ids,
-                                         S.y[m], ws[tuple(S.wb[m].shape)]) == B.BD_OK
+        S.prepare()
+        for x, bt, ms in S._groups():
+            assert B.bd_batch_encode(bt, x, S.U, None, S.p) == B.BD_OK
+            assert B.bd_base_gemm_q8_n(x, [qs[m][0] for m in ms], [qs[m][1] for m in ms],
+                                       [S.y[m] for m in ms], workspace=S.gemm_ws) == B.BD_OK
+            S._delta(x, bt, ms)
 
     step()
     torch.cuda.synchronize()
-    for w_ in ws.values():
-        assert B.bd_device_status(w_) == B.BD_OK
+    for bt in S.batches.values():
+        assert B.bd_device_status(bt) == B.BD_OK
     g = capture(step, K)
     g.replay()
     wall_us, ev_us = replay_timed(g, K)
     del g
+
+    def gemm_all():
+        for x, _, ms in S._groups():
+            assert B.bd_base_gemm_q8_n(x, [qs[m][0] for m in ms], [qs[m][1] for m in ms],
+                                       [S.y[m] for m in ms], workspace=S.gemm_ws) == B.BD_OK
+
+    gp = capture(gemm_all, K)
+    gp.replay()
+    _, gemm_us = replay_timed(gp, K)
+    del gp
+    del qs
     nbytes = 0
     for m in range(S.n_mats):
         d_out, d_in = S.wb[m].shape
@@ -402,9 +409,12 @@ def int8_leg(S, dev, K):
                    + S.T * d_in * 2 + S.T * d_out * 4 + 4 * S.T)
     gbs = nbytes / (wall_us * 1e-6) / 1e9
     return {"ms_per_step": round(wall_us * 1e-3, 4), "gpu_step_us_events": round(ev_us, 1),
+            "gemm_phase_us": round(gemm_us, 1),
+            "gemm_TFLOPs": round(S.flops_gemm / (gemm_us * 1e-6) / 1e12, 1),
             "algorithmic_bytes_per_step": nbytes, "achieved_GBs": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "calls": f"{S.n_mats} bd_apply_q8 (one per matrix, ungrouped)",
+            "calls": "per width one bd_batch_prepare; per group bd_batch_encode, "
+                     "bd_base_gemm_q8_n, bd_delta_apply_encoded_n",
             "base": "per-row symmetric INT8 codes + fp32 row scales (bd_quantize_base)"}
 
 

@@ -402,6 +402,25 @@ bd_status bd_delta_apply_encoded_n(void* batch, size_t batch_bytes, bd_dtype x_d
                                    const void* const* scales_banks, const bd_compress_params* p,
                                    float* const* ys, void* stream);
 
+/* bd_base_gemm_n on INT8 base weights (bd_quantize_base; [P2] "Production
+ * Engineering" 3): ys[i][t] = wscales[i] (.) (X[t] . wqs[i]^T) for up to 4 matrices
+ * that read the same bf16 activations, so that an INT8-based stack groups its
+ * matrices as the bf16 one does.  Same tiles as bd_apply_q8's base product (the
+ * codes widened to bf16 exactly on chip, each row's sum scaled once), K split as in
+ * bd_base_gemm_n: the workspace is sized by bd_base_gemm_n_workspace_bytes with
+ * x_dtype BD_BF16 and these shapes, NULL for no split.
+ *  x       : bf16 [T][d_in], 1 <= T, d_in a multiple of 64.
+ *  wqs     : host array of n_mats device pointers, int8 [d_outs[i]][d_in] each.
+ *  wscales : host array of n_mats device pointers, fp32 [d_outs[i]] each.
+ *  ys      : host array of n_mats device pointers, fp32 [T][d_outs[i]] each.
+ * Errors: BD_ERR_DTYPE (x not bf16), BD_ERR_SHAPE, BD_ERR_UNSUPPORTED (32-bit offsets
+ * exceeded), BD_ERR_INVALID_ARG (null or misaligned pointer), BD_ERR_WORKSPACE;
+ * nothing is launched on an error. */
+bd_status bd_base_gemm_q8_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                            int32_t n_mats, const int8_t* const* wqs,
+                            const float* const* wscales, const int64_t* d_outs,
+                            float* const* ys, void* workspace, size_t ws_bytes, void* stream);
+
 /* The two launches of bd_apply's one-pass path for decode batches: bf16 x and
  * w_base, 1 <= T <= 16, MATRIX, ROW or COL scales (BD_ERR_UNSUPPORTED for any
  * other batch).  Same formula as bd_apply ([P2] "Systems Mechanics" 1-2).

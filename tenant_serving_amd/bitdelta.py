@@ -114,6 +114,9 @@ def lib() -> ctypes.CDLL:
         L.bd_base_gemm_n_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32, vp]
         L.bd_base_gemm_n.restype = ctypes.c_int
         L.bd_base_gemm_n.argtypes = [vp, ctypes.c_int, i64, i64, i32, vp, vp, vp, vp, sz, vp]
+        L.bd_base_gemm_q8_n.restype = ctypes.c_int
+        L.bd_base_gemm_q8_n.argtypes = [vp, ctypes.c_int, i64, i64, i32, vp, vp, vp, vp, vp, sz,
+                                        vp]
         L.bd_delta_apply_encoded_n.restype = ctypes.c_int
         L.bd_delta_apply_encoded_n.argtypes = [vp, sz, ctypes.c_int, i64, i64, i32, i32, vp, vp,
                                                vp, P, vp, vp]
@@ -440,6 +443,25 @@ def bd_base_gemm_n(x, w_bases, ys, workspace=None, stream=None) -> int:
                                     _ptr_array(w_bases), d_outs, _ptr_array(ys), _ptr(workspace),
                                     0 if workspace is None else _nbytes(workspace),
                                     _stream(x, stream)))
+
+
+def bd_base_gemm_q8_n(x, wqs, wscales, ys, workspace=None, stream=None) -> int:
+    """bd_base_gemm_n on INT8 base rows (quantize_base): up to 4 matrices that read x, in
+    one launch; `workspace` as for bd_base_gemm_n (sized by its query, None: no split)."""
+    _dev(x, "x", (torch.bfloat16,))
+    T, d_in = x.shape
+    if not 1 <= len(wqs) <= 4 or len(ys) != len(wqs) or len(wscales) != len(wqs):
+        raise ValueError("1..4 matrices, one scale vector and one output each")
+    for w, sc, y in zip(wqs, wscales, ys):
+        _dev(w, "wq", (torch.int8,), (w.shape[0], d_in), x.device)
+        _dev(sc, "wscales", (torch.float32,), (w.shape[0],), x.device)
+        _dev(y, "y", (torch.float32,), (T, w.shape[0]), x.device)
+    _dev(workspace, "workspace", None, None, x.device, optional=True)
+    d_outs = (ctypes.c_int64 * len(ys))(*[w.shape[0] for w in wqs])
+    return int(lib().bd_base_gemm_q8_n(_ptr(x), _dtype_code(x), T, d_in, len(ys), _ptr_array(wqs),
+                                       _ptr_array(wscales), d_outs, _ptr_array(ys), _ptr(workspace),
+                                       0 if workspace is None else _nbytes(workspace),
+                                       _stream(x, stream)))
 
 
 def bd_delta_apply_encoded_n(batch, T, d_in, n_users, signs_banks, scales_banks, p, ys,

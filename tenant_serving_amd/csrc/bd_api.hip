@@ -316,6 +316,39 @@ bd_status bd_base_gemm_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_i
     return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
 }
 
+bd_status bd_base_gemm_q8_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t d_in,
+                            int32_t n_mats, const int8_t* const* wqs,
+                            const float* const* wscales, const int64_t* d_outs,
+                            float* const* ys, void* workspace, size_t ws_bytes, void* stream) {
+    if (x_dtype != BD_BF16) return BD_ERR_DTYPE;
+    if (T < 0 || n_mats < 1 || n_mats > kMaxMats || !wqs || !wscales || !d_outs || !ys)
+        return BD_ERR_INVALID_ARG;
+    if (d_in <= 0 || d_in % 64 != 0) return BD_ERR_SHAPE;
+    for (int i = 0; i < n_mats; ++i) {
+        if (d_outs[i] <= 0) return BD_ERR_SHAPE;
+        if (T > 0 && !gemm_q8_supported(T, d_in, d_outs[i])) return BD_ERR_UNSUPPORTED;
+    }
+    if (T == 0) return BD_OK;
+    if (!x || !aligned(x, 16)) return BD_ERR_INVALID_ARG;
+    for (int i = 0; i < n_mats; ++i)
+        if (!wqs[i] || !wscales[i] || !ys[i] || !aligned(wqs[i], 16) || !aligned(wscales[i], 4) ||
+            !aligned(ys[i], 16))
+            return BD_ERR_INVALID_ARG;
+    GemmMatArg m[kMaxMats];
+    for (int i = 0; i < n_mats; ++i) m[i] = GemmMatArg{wqs[i], ys[i], d_outs[i]};
+    // split exactly where bd_base_gemm_n_workspace_bytes (bf16 shapes) asks for room
+    const size_t need = bd_base_gemm_n_workspace_bytes(BD_BF16, T, d_in, n_mats, d_outs);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (need > 0 && workspace) {
+        if (ws_bytes < need || !aligned(workspace, kAlign)) return BD_ERR_WORKSPACE;
+        e = launch_gemm_set_split(x, T, d_in, m, n_mats, (char*)workspace, s, wscales);
+    } else {
+        e = launch_gemm_set(x, T, d_in, m, n_mats, s, wscales);
+    }
+    return e == hipSuccess ? BD_OK : BD_ERR_DEVICE;
+}
+
 bd_status bd_delta_apply_encoded_n(void* batch, size_t batch_bytes, bd_dtype x_dtype, int64_t T,
                                    int64_t d_in, int32_t n_users, int32_t n_mats,
                                    const int64_t* d_outs, const uint64_t* const* signs_banks,

@@ -335,12 +335,12 @@ size_t gemm_split_bytes(int64_t T, int64_t d_in, const int64_t* d_outs, int n) {
 }
 
 hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats,
-                                 int n, char* ws, hipStream_t s) {
+                                 int n, char* ws, hipStream_t s, const float* const* wscales) {
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
     int64_t d_outs[kMaxMats];
     for (int i = 0; i < n; ++i) d_outs[i] = mats[i].d_out;
     const int S = choose_split(T, d_in, d_outs, n);
-    if (S == 1 || !ws) return launch_gemm_set(x, T, d_in, mats, n, s);
+    if (S == 1 || !ws) return launch_gemm_set(x, T, d_in, mats, n, s, wscales);
     float* parts[kMaxMats];
     size_t off = 0;
     int64_t nmax = 0;
@@ -349,7 +349,9 @@ hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const G
         off += ((size_t)S * T * d_outs[i] * 4 + kAlign - 1) / kAlign * kAlign;
         nmax = d_outs[i] > nmax ? d_outs[i] : nmax;
     }
-    hipError_t e = launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
+    hipError_t e = wscales
+        ? launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, wscales, S, parts)
+        : launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
     if (e != hipSuccess) return e;
     GemmMats gm = {};
     gm.n = n;
@@ -385,15 +387,25 @@ bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out) {
 
 // The largest tile that still yields enough blocks to cover the chip: 128 rows x 256
 // tokens (most reuse per copied byte), 128 x 128, 64 x 128, else 64 x 64 (small
-// matrices and batches, where idle CUs cost more than the extra copies).
+// matrices and batches, where idle CUs cost more than the extra copies).  INT8 codes
+// (wscales set): the same choice with two LDS stages throughout.
 hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
-                           hipStream_t s) {
+                           hipStream_t s, const float* const* wscales) {
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
+    if (T == 0) return hipSuccess;
     auto blocks = [&](int64_t br, int64_t bt) {
         int64_t r = 0;
         for (int i = 0; i < n; ++i) r += (mats[i].d_out + br - 1) / br;
         return r * ((T + bt - 1) / bt);
     };
+    if (wscales) {
+        const float* const* sc = wscales;
+        if (blocks(256, 256) >= 200) return launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, sc);
+        if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+        if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+        if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+        return launch_tile<64, 64, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+    }
     if (blocks(256, 256) >= 200) return launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s);
     if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s);
     if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 4>(x, T, d_in, mats, n, s);
@@ -412,18 +424,11 @@ bool gemm_q8_supported(int64_t T, int64_t d_in, int64_t d_out) {
            d_out * d_in < ((int64_t)1 << 31) && d_out < ((int64_t)1 << 30);
 }
 
-// The tile choice of launch_gemm_set, with two LDS stages throughout.
 hipError_t launch_gemm_q8(const void* x, int64_t T, int64_t d_in, const int8_t* wq,
                           const float* wscale, int64_t d_out, float* y, hipStream_t s) {
-    if (T == 0) return hipSuccess;
     const GemmMatArg m = {wq, y, d_out};
     const float* sc[1] = {wscale};
-    auto blocks = [&](int64_t br, int64_t bt) { return ((d_out + br - 1) / br) * ((T + bt - 1) / bt); };
-    if (blocks(256, 256) >= 200) return launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, &m, 1, s, sc);
-    if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, &m, 1, s, sc);
-    if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 2, 4, true>(x, T, d_in, &m, 1, s, sc);
-    if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 2, 4, true>(x, T, d_in, &m, 1, s, sc);
-    return launch_tile<64, 64, 64, 2, 4, true>(x, T, d_in, &m, 1, s, sc);
+    return launch_gemm_set(x, T, d_in, &m, 1, s, sc);
 }
 
 }  // namespace bd

@@ -197,14 +197,16 @@ struct GemmMats {
     int rt_begin[kMaxMats + 1];
     int n;
 };
+// wscales (one per matrix, or null): the matrices hold INT8 codes with these row scales.
 hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
-                           hipStream_t s);
+                           hipStream_t s, const float* const* wscales = nullptr);
 // The same with K split in S ordered parts where the large tiles would leave the chip
 // idle: the partial products go to `ws` and a second launch sums them in split order
 // (deterministic).  gemm_split_bytes: the workspace that split needs, 0 for no split.
 size_t gemm_split_bytes(int64_t T, int64_t d_in, const int64_t* d_outs, int n);
 hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats,
-                                 int n, char* ws, hipStream_t s);
+                                 int n, char* ws, hipStream_t s,
+                                 const float* const* wscales = nullptr);
 // Y = s (.) (X Wq^T) for an INT8 base weight (per-row symmetric codes wq, row scales
 // wscale): the same tiles, the codes widened to bf16 on their way into LDS (exact).
 bool gemm_q8_supported(int64_t T, int64_t d_in, int64_t d_out);

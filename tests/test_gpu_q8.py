@@ -116,6 +116,67 @@ def test_tiled_int8_product_over_tile_shapes(case):
     assert err <= 1e-5 * rms, (err, rms)  # exact products, fp32 sums of d_in terms
 
 
+GROUPED_Q8_CASES = [
+    ((4096, 1024, 1024), 4096, 512),   # q|k|v of the 8B layer: K split in 4
+    ((4096,), 14336, 512),             # down: K split in 8
+    ((1028, 1028, 1024), 8192, 300),   # ragged rows and tokens, split
+    ((14336, 14336), 4096, 512),       # gate|up: no split
+    ((512, 640), 1024, 40),            # small batch: the small tiles
+]
+
+
+@pytest.mark.parametrize("d_outs,d_in,T", GROUPED_Q8_CASES,
+                         ids=lambda c: str(c) if not isinstance(c, tuple) else "x".join(map(str, c)))
+def test_grouped_int8_gemm(d_outs, d_in, T):
+    """bd_base_gemm_q8_n (INT8 rows of up to 4 matrices on one launch, K split through
+    the workspace where bd_base_gemm_n would split): every token of sampled rows of every
+    matrix against the oracle's base term on the oracle's INT8 rows (exact products,
+    fp32 sums: 1e-5 rms), against the unsplit call within fp32 summation order, and bit
+    for bit from one call to the next."""
+    mats = [custom(d, d_in, S.BF16, T=T, cid=2900 + i) for i, d in enumerate(d_outs)]
+    qs = [B.quantize_base(S.dev_wbase(w, 0)) for w in mats]
+    x = S.dev_x(mats[0], 0)
+    need = B.bd_base_gemm_n_workspace_bytes(B.BD_BF16, T, d_in, d_outs)
+    ws = B.workspace(need, DEV) if need > 0 else None
+    ys = [torch.empty(T, d, device=DEV) for d in d_outs]
+    ys2 = [torch.empty(T, d, device=DEV) for d in d_outs]
+    yn = [torch.empty(T, d, device=DEV) for d in d_outs]
+    wq, wsc = [q for q, _ in qs], [sc for _, sc in qs]
+    assert B.bd_base_gemm_q8_n(x, wq, wsc, ys, workspace=ws) == B.BD_OK
+    assert B.bd_base_gemm_q8_n(x, wq, wsc, ys2, workspace=ws) == B.BD_OK
+    assert B.bd_base_gemm_q8_n(x, wq, wsc, yn) == B.BD_OK  # no workspace: no split
+    torch.cuda.synchronize()
+    x_np = S.host_x(mats[0], 0)
+    ids = np.full(T, -1, np.int32)
+    for i, d in enumerate(d_outs):
+        assert torch.equal(ys[i], ys2[i])
+        rows = sorted({0, d - 1} | set(np.random.default_rng(d + i).choice(d, 40, replace=False).tolist()))
+        oq, os_ = O.quantize_rows(S.host_wbase(mats[i], 0, rows), dtype=O.BF16)
+        _, yb, _ = O.apply_q8(x_np, oq, os_, np.zeros((1, len(rows), d_in // 64), np.uint64),
+                              np.zeros((1, 1), np.float32), O.MATRIX, ids)
+        err, rms = max_err_vs_rms(ys[i].cpu().numpy()[:, rows], yb)
+        assert err <= 1e-5 * rms, (i, err, rms)
+        err, rms = max_err_vs_rms(ys[i].cpu().numpy(), yn[i].cpu().numpy().astype(np.float64))
+        assert err <= 1e-5 * rms, (i, err, rms)
+
+
+def test_grouped_int8_gemm_rejections():
+    x = torch.zeros((128, 512), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((64, 512), dtype=torch.int8, device=DEV)
+    s = torch.ones(64, dtype=torch.float32, device=DEV)
+    y = torch.empty((128, 64), dtype=torch.float32, device=DEV)
+    lib, c = B.lib(), __import__("ctypes")
+    d = (c.c_int64 * 1)(64)
+    P = (c.c_void_p * 1)
+    args = lambda xd, din, wq, sc, yy: (x.data_ptr(), xd, 128, din, 1, wq, sc, d, yy, None, 0, None)
+    ok = (P(q.data_ptr()), P(s.data_ptr()), P(y.data_ptr()))
+    assert lib.bd_base_gemm_q8_n(*args(B.BD_F32, 512, *ok)) == B.BD_ERR_DTYPE
+    assert lib.bd_base_gemm_q8_n(*args(B.BD_BF16, 500, *ok)) == B.BD_ERR_SHAPE
+    assert lib.bd_base_gemm_q8_n(*args(B.BD_BF16, 512, P(None), ok[1], ok[2])) == B.BD_ERR_INVALID_ARG
+    assert lib.bd_base_gemm_q8_n(*args(B.BD_BF16, 512, ok[0], P(s.data_ptr() + 2), ok[2])) == \
+        B.BD_ERR_INVALID_ARG
+
+
 def test_apply_q8_rejects_what_it_does_not_serve():
     p = B.params("matrix")
     x = torch.zeros((4, 512), dtype=torch.float32, device=DEV)  # fp32 activations
