@@ -798,40 +798,64 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
     }
     const int ntl = sload(meta, 3);
     const int C = dm.rb_begin[kMaxMats];  // chunks of the matrix set
+    // tpre of the first 64 ranks in registers (lane = rank; one load for batches of up to
+    // 63 tiles), the rest read where needed
+    const int tp_l = lane <= ntl ? tpre[lane] : 0x7FFFFFFF;
     const int tot = sload(tpre, ntl);     // sweeps of one chunk over all tiles
+    auto tpre_at = [&](int q) __attribute__((always_inline)) {
+        return q < 64 ? __builtin_amdgcn_readlane(tp_l, q) : sload(tpre, q);
+    };
     // ranks with users: torder lists them first and tpre rises over them
-    int neff = 0;
-    for (int b = 0; b < ntl; b += 64) {
+    int neff = __popcll(__ballot(lane < ntl && tp_l < tot));
+    for (int b = 64; b < ntl; b += 64) {
         const int k = b + lane;
         neff += __popcll(__ballot(k < ntl && tpre[k] < tot));
     }
     neff = uni(neff);
-    // Sweep w of the launch (sweeps in the order tile rank k, chunk c, user j of the tile;
-    // tile k's sweeps start at tpre[k] C) -> (k, c, j).  Each block takes an equal share of
-    // the sweeps, so an item (tile, chunk) may be split between two blocks at a user: each
-    // then adds only its own users' tokens.
-    auto locate = [&](int64_t w, int& kk, int& cc, int& jj) __attribute__((always_inline)) {
-        int cnt = 0;
-        for (int b = 0; b < neff; b += 64) {
-            const int q = b + lane;
-            cnt += __popcll(__ballot(q < neff && (int64_t)tpre[q] * C <= w));
-        }
-        const int q = uni(cnt) - 1;  // (>= 0: tpre[0] = 0)
-        kk = q;
+    // The blocks split the launch's cost evenly: kCostSweep units per sweep and kCostEnd
+    // per item end (the item's partial sums meet in LDS behind a barrier of the block's
+    // waves and go to y: measured at a quarter to a third of a sweep), so a block of one-user
+    // tiles, whose every sweep ends an item, takes fewer sweeps.  Sweeps run in the order
+    // tile rank k, chunk c, user j of the tile; rank k starts at cost
+    // C (kCostSweep tpre[k] + kCostEnd k) and each of its items costs
+    // kCostSweep nu + kCostEnd (the last user's sweep carries the end).  locate: the sweep
+    // whose cost range holds position w, as (k, c, j) and as a sweep index (tile k's
+    // sweeps start at tpre[k] C); the end of the cost range gives the number of sweeps.
+    // A block boundary may fall inside an item, at a user: each side then adds only its
+    // own users' tokens.
+    constexpr int kCostSweep = 8, kCostEnd = 2;
+    const int64_t Wc = (int64_t)C * ((int64_t)kCostSweep * tot + (int64_t)kCostEnd * neff);
+    auto locate = [&](int64_t w, int& kk, int& cc, int& jj) __attribute__((always_inline)) -> int64_t {
+        kk = neff;
         cc = jj = 0;
-        if (q < 0 || q >= neff) return;
-        const int64_t rem = w - (int64_t)sload(tpre, q) * C;
-        int nq = sload(tpre, q + 1) - sload(tpre, q);
+        if (w >= Wc) return (int64_t)tot * C;  // (uniform)
+        auto start = [&](int t, int q) { return (int64_t)C * ((int64_t)kCostSweep * t + (int64_t)kCostEnd * q); };
+        int cnt = __popcll(__ballot(lane < neff && start(tp_l, lane) <= w));
+        for (int b = 64; b < neff; b += 64) {
+            const int q = b + lane;
+            cnt += __popcll(__ballot(q < neff && start(tpre[q], q) <= w));
+        }
+        const int q = uni(cnt) - 1;  // (>= 0: rank 0 starts at 0)
+        const int t0q = tpre_at(q);
+        int nq = tpre_at(q + 1) - t0q;
         nq = nq < 1 ? 1 : nq;
-        cc = (int)(rem / nq);
-        jj = (int)(rem % nq);
+        const int64_t rem = w - start(t0q, q);
+        const int64_t isz = (int64_t)kCostSweep * nq + kCostEnd;
+        kk = q;
+        cc = (int)(rem / isz);
+        const int r2 = (int)(rem - (int64_t)cc * isz) / kCostSweep;
+        jj = r2 < nq - 1 ? r2 : nq - 1;
+        return (int64_t)t0q * C + (int64_t)cc * nq + jj;
     };
-    const int64_t Wt = (int64_t)tot * C;
-    const int64_t w0 = Wt * (int64_t)blockIdx.x / gridDim.x;
-    const int64_t w1 = Wt * ((int64_t)blockIdx.x + 1) / gridDim.x;
-    if (w0 >= w1) return;  // uniform: no sweeps
-    int sk0, sc0, sj0;
-    locate(w0, sk0, sc0, sj0);
+    // share of block b: the workgroups of a launch go round-robin over the 8 XCDs (b on
+    // XCD b % 8), so each XCD takes a contiguous run of shares and a tile's encoded
+    // operands and split items stay within fewer L2s
+    const int64_t nb = gridDim.x, bx = blockIdx.x;
+    const int64_t sh = nb % 8 == 0 ? (bx % 8) * (nb / 8) + bx / 8 : bx;
+    int sk0, sc0, sj0, ek, ec, ej;
+    const int64_t s0 = locate(Wc * sh / nb, sk0, sc0, sj0);
+    const int64_t s1 = locate(Wc * (sh + 1) / nb, ek, ec, ej);
+    if (s1 <= s0) return;  // uniform: no sweeps
     sk0 = uni(sk0);
     sc0 = uni(sc0);
     sj0 = uni(sj0);
@@ -847,7 +871,7 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
 
     // ---- loading side: item (kL, cL), user jL; scalar state, one descriptor per sweep
     int kL = sk0, cL = sc0, jL = sj0;
-    int64_t leftL = w1 - w0;  // sweeps the loader has not issued
+    int64_t leftL = s1 - s0;  // sweeps the loader has not issued
     int tileL = sload(torder, kL), nuL = 1;
     {
         const int nu = sload(tpre, kL + 1) - sload(tpre, kL);
@@ -909,12 +933,21 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
     asm volatile("s_mov_b32 %0, 0x88888888" : "=s"(k2));
     asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(k3));
     int k = sk0, c = sc0;
-    int64_t left = w1 - w0;  // sweeps not yet done
+    int64_t left = s1 - s0;  // sweeps not yet done
     int tile = -1, nu = 1, j = sj0, ja = sj0, ci = 0;  // ja: the item's first user here;
                                                      // ci: items done (LDS buffer parity)
-    // a new tile (its loads are the youngest: their first use waits for every load in
-    // flight; once or twice per block)
-    auto tile_setup = [&](int t, int nut) __attribute__((always_inline)) {
+    // A new tile in two parts.  tile_load issues the tile's loads: its meta (waited for:
+    // the checks and the user of each token need it), the encoded operands and (MATRIX,
+    // wave 0) the scale of each token's user in each matrix.  tile_finish uses them.  The
+    // first tile's loads go out before the ring's, so its products wait only for them;
+    // later tiles' loads are the youngest (their first use waits for every load in
+    // flight; once or twice per block).
+    uint64_t cdw = 0;
+    int tv = -1;       // lane l: word l of the tile's meta
+    bool tdead_n = true;
+    uint32_t tfraw = 0;  // MATRIX: the scale of token lane % 16's user in matrix lane / 16
+    bool tfok = false;
+    auto tile_load = [&](int t, int nut) __attribute__((always_inline)) {
         const bool tok_ok = (uint32_t)t < (uint32_t)ntl;
         const int tt = tok_ok ? t : 0;
         const int v = tmeta[(size_t)tt * kTileMetaInts + lane];
@@ -929,8 +962,8 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
             hi[p] = i32x6{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y};
             lo[p] = i32x6{(int)c1.z, (int)c1.w, (int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w};
         }
-        const uint64_t cdw = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                              er, 12 * 1024 + 16 * lane, 0, 0));
+        cdw = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                               er, 12 * 1024 + 16 * lane, 0, 0));
         // the tile's tokens, their users and its user list must fit this call's T and
         // n_users, and its user count the plan's (a batch prepared for other sizes): a
         // tile that does not is flagged and adds nothing
@@ -939,6 +972,37 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
                          : lane < 48 ? (lane - 32 < nut && (v < 0 || v >= U))
                                      : lane == 48 && v != nut;
         const bool dead = !tok_ok || __ballot(bad) != 0ull;  // uniform
+        tv = v;
+        tdead_n = dead;
+        if constexpr (MODE == BD_SCALE_MATRIX) {
+            // lane: matrix G, token n (raw bits: converted in tile_finish, so that nothing
+            // here waits for the load; a lane with no token reads entry 0 of matrix 0)
+            const int c_tuser = __shfl(v, 16 + n);
+            const bool ok = G < dm.n && c_tuser >= 0 && !dead;
+            typedef const __attribute__((address_space(1))) uint16_t* gh;
+            typedef const __attribute__((address_space(1))) uint32_t* gw;
+            // (pick_mat takes a uniform index: the lane's matrix is selected from the four)
+            const void* const sp0 = pick_mat(dm.scales, 0);
+            const void* sp = sp0;
+            int64_t cs = pick_mat(dm.cstride, 0);
+#pragma unroll
+            for (int q = 1; q < kMaxMats; ++q) {
+                const void* const spq = pick_mat(dm.scales, q);
+                const int64_t csq = pick_mat(dm.cstride, q);
+                if (G == q) {
+                    sp = spq;
+                    cs = csq;
+                }
+            }
+            if (!ok) sp = sp0;
+            const size_t i = ok ? (size_t)c_tuser * (size_t)cs : 0;
+            tfraw = SF16 ? (uint32_t)((gh)sp)[i] : ((gw)sp)[i];
+            tfok = ok;
+        }
+    };
+    auto tile_finish = [&](int nut) __attribute__((always_inline)) {
+        const int v = tv;
+        const bool dead = tdead_n;
         if (dead && threadIdx.x == 0) atomicOr(meta, ST_ENCODING);
         trow = v;
         tdead = dead;
@@ -947,25 +1011,11 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         for (int q = 0; q < nut; ++q)
             if (__shfl(v, 32 + q) == c_tuser) jt = q;
         if constexpr (MODE == BD_SCALE_MATRIX) {
-            // the scale of each token's user in each matrix of the launch (wave 0, lane:
-            // matrix lane / 16, token lane % 16; 0 for no token), after every wave is done
-            // with the last tile's
+            // the scales into LDS (wave 0), after every wave is done with the last tile's
             __builtin_amdgcn_s_waitcnt(0xC07F);
             asm volatile("s_barrier" ::: "memory");
-            if (wv == 0) {
-                float f = 0.f;
-#pragma unroll
-                for (int q = 0; q < kMaxMats; ++q) {
-                    if (q < dm.n && G == q && c_tuser >= 0 && !dead) {
-                        typedef const __attribute__((address_space(1))) uint16_t* gh;
-                        typedef const __attribute__((address_space(1))) float* gf;
-                        const void* sp = pick_mat(dm.scales, q);
-                        const size_t i = (size_t)c_tuser * (size_t)pick_mat(dm.cstride, q);
-                        f = SF16 ? f16_to_f32(((gh)sp)[i]) : ((gf)sp)[i];
-                    }
-                }
-                sF[G][n] = f;
-            }
+            if (wv == 0)
+                sF[G][n] = !tfok ? 0.f : SF16 ? f16_to_f32((uint16_t)tfraw) : __uint_as_float(tfraw);
             __builtin_amdgcn_s_waitcnt(0xC07F);
             asm volatile("s_barrier" ::: "memory");
         }
@@ -1119,7 +1169,14 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         if constexpr (MODE == BD_SCALE_ROW && RPW > 1) reduce_prev();
     };
 
-    // the ring: the first two sweeps, then the first tile and item
+    // the first tile's loads, the ring (the first two sweeps), then the first tile and item
+    tile = sload(torder, k);
+    {
+        const int q = tpre_at(k + 1) - tpre_at(k);
+        nu = q < 1 ? 1 : (q > 16 ? 16 : q);
+    }
+    tile_load(tile, nu);
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 ring[D];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1128,12 +1185,7 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         for (int r = 0; r < RT; ++r) ring[h * RT + r] = buf_load16(br, BD_VOFF(r));
     }
     __builtin_amdgcn_sched_barrier(0);
-    tile = sload(torder, k);
-    {
-        const int q = sload(tpre, k + 1) - sload(tpre, k);
-        nu = q < 1 ? 1 : (q > 16 ? 16 : q);
-    }
-    tile_setup(tile, nu);
+    tile_finish(nu);
     item_start();
 
     // one sweep (user j of the item) from ring half H; its slots reload with the sweep
@@ -1201,9 +1253,10 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
                         c = 0;
                         ++k;
                         tile = sload(torder, k);
-                        const int q = sload(tpre, k + 1) - sload(tpre, k);
+                        const int q = tpre_at(k + 1) - tpre_at(k);
                         nu = q < 1 ? 1 : (q > 16 ? 16 : q);
-                        tile_setup(tile, nu);
+                        tile_load(tile, nu);
+                        tile_finish(nu);
                     }
                     item_start();
                 }
