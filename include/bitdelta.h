@@ -421,7 +421,8 @@ bd_status bd_base_gemm_q8_n(const void* x, bd_dtype x_dtype, int64_t T, int64_t 
                             const float* const* wscales, const int64_t* d_outs,
                             float* const* ys, void* workspace, size_t ws_bytes, void* stream);
 
-/* The two launches of bd_apply's one-pass path for decode batches: bf16 x and
+/* The two-launch form of bd_apply's decode path (what bd_apply runs for COL scales
+ * and rows wider than 5120 columns), callable on its own: bf16 x and
  * w_base, 1 <= T <= 16, MATRIX, ROW or COL scales (BD_ERR_UNSUPPORTED for any
  * other batch).  Same formula as bd_apply ([P2] "Systems Mechanics" 1-2).
  *
