@@ -1055,7 +1055,15 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
     // (the lane's tokens 4 G .. 4 G + 3 and their users, from the tile's meta)
     auto ltok = [&](int e) __attribute__((always_inline)) { return tdead ? -1 : __shfl(trow, 4 * G + e); };
     auto lusr = [&](int e) __attribute__((always_inline)) { return __shfl(trow, 16 + 4 * G + e); };
-    float fs[4] = {1.f, 1.f, 1.f, 1.f};
+    // ROW: the factors of the wave's row tiles of the item (RPF of them, loaded in the
+    // item's first sweep and used when its sums are added, an item later); with more than
+    // two row tiles per wave the further ones load at the item's end instead
+    constexpr int RPF = MODE == BD_SCALE_ROW && RPW == 2 ? 2 : 1;
+    float fs[RPF][4];
+#pragma unroll
+    for (int t = 0; t < RPF; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fs[t][e] = 1.f;
     bool fresh = false;
     int imi = 0;
     const void* isc = nullptr;
@@ -1112,13 +1120,13 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
             if (r < RT) {  // uniform
                 f32x4 v = part[pci & 1][r][0][lane];
                 for (int q = 1; q < W; ++q) v += part[pci & 1][r][q][lane];
-                // (ROW: the wave's further row tiles load their factors here, before the
-                // next item changes the item state)
+                // (ROW with more than two row tiles per wave: the further ones load their
+                // factors here, before the next item changes the item state)
                 float f[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     f[e] = MODE == BD_SCALE_MATRIX ? pfm[e]
-                           : MODE == BD_SCALE_ROW ? (t > 0 ? factor(r, e) : fs[e]) : 1.f;
+                           : MODE == BD_SCALE_ROW ? (t < RPF ? fs[t < RPF ? t : 0][e] : factor(r, e)) : 1.f;
                     if (SF16 && MODE == BD_SCALE_ROW) f[e] = f16_to_f32((uint16_t)__builtin_bit_cast(uint32_t, f[e]));
                 }
                 const int64_t o = prow0 + 16 * (int64_t)r + n;
@@ -1165,8 +1173,8 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         pci = ci;
         pend = true;
         ++ci;
-        // ROW with several row tiles per wave: their factors follow the item state
-        if constexpr (MODE == BD_SCALE_ROW && RPW > 1) reduce_prev();
+        // ROW with more than two row tiles per wave: their factors follow the item state
+        if constexpr (MODE == BD_SCALE_ROW && RPW > RPF) reduce_prev();
     };
 
     // the first tile's loads, the ring (the first two sweeps), then the first tile and item
@@ -1234,11 +1242,14 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
             acc[r + 1] = b;
             if (r == 0 && fresh) {  // uniform: the item's first sweep
                 if (pend) reduce_prev();  // the previous item's sums
-                // ROW: this item's factors of the wave's first row tile (used when its sums
-                // are added, an item later)
+                // ROW: this item's factors of the wave's row tiles (used when its sums are
+                // added, an item later)
                 if constexpr (MODE == BD_SCALE_ROW) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) fs[e] = factor(wv, e);
+                    for (int t = 0; t < RPF; ++t)
+                        if (wv + t * W < RT)  // uniform
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) fs[t][e] = factor(wv + t * W, e);
                 }
                 fresh = false;
             }
