@@ -349,8 +349,9 @@ __device__ __forceinline__ int pick_rb(const int (&a)[kMaxMats + 1], int m) {
     return (int)(uint32_t)s_sel64<3>(m, (uint64_t)(uint32_t)a[3], v);
 }
 
+// (two waves per SIMD: at most 256 registers each, so that two blocks share a CU)
 template <int MODE, bool SF16, int RT>
-__global__ void __launch_bounds__(64 * kWaves)
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
 k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
          const int32_t* __restrict__ torder, const char* __restrict__ enc,
          uint32_t* __restrict__ meta, int64_t d_in, int nunit, int T, int U) {
@@ -654,6 +655,9 @@ k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
                 for (int t = 0; t < RT; ++t) {
                     const u32x4 b0 = bx[t][0], b1 = bx[t][1], b2 = bx[t][2], b3 = bx[t][3];
                     if (GRP) {
+                      // (GROUP: the empty slots past the end skip their products; without
+                      // this branch the group-scale path needs more than 256 registers)
+                      if (cs < S) {
                         // this lane's row, unit h, row tile t: the window of lane group t + RT h
                         const u32x4 swv = wring[r / 2];
                         const int src = 4 * (n + 16 * (t + RT * h));
@@ -688,6 +692,7 @@ k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
     }
                         BD_G(0, b0, sv.x) BD_G(1, b1, sv.y) BD_G(2, b2, sv.z) BD_G(3, b3, sv.w)
 #undef BD_G
+                      }
                     } else {
                         // MATRIX, ROW and COL: the scale is applied per token at the end
                         acc[t] = mfma_f6f4<0>(hi[0], b0, acc[t], sh);
