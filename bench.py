@@ -67,6 +67,10 @@ def parse():
     return ap.parse_args()
 
 
+def _fail(what):
+    raise RuntimeError(f"{what} call failed")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -191,6 +195,7 @@ class Stack:
         torch.cuda.synchronize()
         self.setup_s = time.perf_counter() - t0
 
+        self.side = torch.cuda.Stream(dev)  # (default priority)
         self.mats = mats
         self._account()
         self.n_mats = len(mats)
@@ -254,13 +259,26 @@ class Stack:
         for x, bt, ms in self._groups():
             self._delta(x, bt, ms)
 
+    def forked(self, encode, gemm, delta):
+        """One group's launches: the encoding and the base product read the same
+        activations and write different buffers, so the encoding runs on a second
+        stream beside the GEMM (both after the previous group's delta products, which
+        read the batch's last encoding); the delta products wait for both."""
+        import torch
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            encode()
+        gemm()
+        main.wait_stream(self.side)
+        delta()
+
     def step(self):
         B = self.B
         self.prepare()
         for x, bt, ms in self._groups():
-            assert B.bd_batch_encode(bt, x, self.U, None, self.p) == B.BD_OK
-            self._gemm(x, ms)
-            self._delta(x, bt, ms)
+            self.forked(lambda: B.bd_batch_encode(bt, x, self.U, None, self.p) == B.BD_OK or _fail("encode"),
+                        lambda: self._gemm(x, ms), lambda: self._delta(x, bt, ms))
 
 
 def stack_leg(args, dev):
@@ -301,9 +319,9 @@ def stack_leg(args, dev):
     ms_per_step = wall_us * 1e-3
     value = S.bytes_step / (ms_per_step * 1e-3) / 1e9
     n_gemm = 4 * S.n_layers  # grouped launches: q|k|v, o, gate|up, down
-    # delta launches: one per 8 units of 512 columns of each group's d_in (down: 28 units
-    # in 4 launches of 7)
-    n_delta = S.n_layers * sum(-(-(-(-d // 512)) // 8) for d in (4096, 4096, 4096, 14336))
+    # delta launches: one per group of matrices (down's 28 units of 512 columns are taken
+    # 7 at a time inside its launch)
+    n_delta = 4 * S.n_layers
     delta_gbs = S.bytes_delta / (phases["delta"] * 1e-6) / 1e9
     gemm_tfs = S.flops_gemm / (phases["gemm"] * 1e-6) / 1e12
     rl_delta = {"bound": "hbm", "kernel": "k_delta8", "achieved": round(delta_gbs, 1),
@@ -350,7 +368,7 @@ def stack_leg(args, dev):
         "phases_us_per_step": {k: round(v, 1) for k, v in phases.items()},
         "phase_launches_per_step": {"prepare": len(S.batches), "encode": 4 * S.n_layers,
                                     "gemm": n_gemm, "delta": n_delta},
-        "delta_launches_per_layer": "q|k|v 1, o 1, gate|up 1, down 4 (7 units each)",
+        "delta_launches_per_layer": "q|k|v 1, o 1, gate|up 1, down 1 (28 units, 7 at a time)",
         "matrices_per_launch": "q|k|v, o, gate|up, down (grouped calls on one encoding)",
         "roofline": dominant,
         "roofline_secondary": other,
@@ -375,13 +393,15 @@ def int8_leg(S, dev, K):
     qs = [B.quantize_base(wb) for wb in S.wb]
     torch.cuda.synchronize()
 
+    def gemm_q8(x, ms):
+        assert B.bd_base_gemm_q8_n(x, [qs[m][0] for m in ms], [qs[m][1] for m in ms],
+                                   [S.y[m] for m in ms], workspace=S.gemm_ws) == B.BD_OK
+
     def step():
         S.prepare()
         for x, bt, ms in S._groups():
-            assert B.bd_batch_encode(bt, x, S.U, None, S.p) == B.BD_OK
-            assert B.bd_base_gemm_q8_n(x, [qs[m][0] for m in ms], [qs[m][1] for m in ms],
-                                       [S.y[m] for m in ms], workspace=S.gemm_ws) == B.BD_OK
-            S._delta(x, bt, ms)
+            S.forked(lambda: B.bd_batch_encode(bt, x, S.U, None, S.p) == B.BD_OK or _fail("encode"),
+                     lambda: gemm_q8(x, ms), lambda: S._delta(x, bt, ms))
 
     step()
     torch.cuda.synchronize()

@@ -749,10 +749,13 @@ k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
 }
 
 // ------------------------------------------------ delta products, persistent
-// The products of one launch's units [u0, u0 + W) for MATRIX, ROW and COL scales.
+// The products of all units of d_in for MATRIX, ROW and COL scales, W units (one per
+// wave) at a time: rows wider than W units are taken in groups of W, the block running
+// its share of the items once per group (the sweep ring runs on from one group to the
+// next, so no group waits for a new launch's start).
 // Work item = (tile rank k, chunk c): 128 output rows (8 row tiles) of the matrix set
 // for the 16 tokens of tile torder[k]; its cost is one sweep per user of the tile.
-// One block per CU, W waves, wave w on unit u0 + w; the block takes the items whose
+// One block per CU, W waves, wave w on unit g W + w in group g; the block takes the items whose
 // first sweep falls in its equal share of all sweeps (tpre: sweeps of the ranks before
 // k), tile-major, so it keeps one tile's operands for many chunks.  A wave loads its
 // unit's encoded tokens when its tile changes (13 KB into registers: fp6 hi / lo of
@@ -765,7 +768,7 @@ k_delta6(const DeltaMats dm, int bsh, const int32_t* __restrict__ tmeta,
 // barrier per item); wave w sums row tiles w, w + W, ... over the units in unit order,
 // scales them per token (MATRIX / ROW: the scale of the token's user; COL: in the
 // tokens) and adds them to y, one no-return atomic per element.  Every y element gets
-// its addends (the base product, then one per launch) in a fixed order: the result
+// its addends (the base product, then one per group) in a fixed order: the result
 // repeats bit for bit.
 constexpr int kRT8 = 8;                // row tiles of a chunk: one sweep
 constexpr int kChunkRows = 16 * kRT8;  // rows of a chunk
@@ -784,10 +787,10 @@ __global__ void __launch_bounds__(64 * kMaxW8)
 k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
          const int32_t* __restrict__ torder, const int32_t* __restrict__ tpre,
          const char* __restrict__ enc, uint32_t* __restrict__ meta, int64_t d_in, int nunit,
-         int u0, int units, int T, int U) {
+         int ngrp, int units, int T, int U) {
     // dm.rb_begin: first chunk of each matrix; RPW: row tiles each wave sums per item
-    // (at least ceil(8 / W)); units: the units of d_in (every launch has W waves; a wave whose
-    // unit is past them adds zeros)
+    // (at least ceil(8 / W)); units: the units of d_in, taken W at a time in ngrp groups
+    // (wave w of group g on unit g W + w; a wave whose unit is past them adds zeros)
     static_assert(MODE != BD_SCALE_GROUP, "GROUP scales take k_delta6");
     constexpr bool COL = MODE == BD_SCALE_COL;
     constexpr int RT = kRT8, D = 2 * RT;  // ring: two sweeps
@@ -865,23 +868,30 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
     sc0 = uni(sc0);
     sj0 = uni(sj0);
 
-    const int u = u0 + wv;
-    const bool uact = u < units;  // uniform
+    // The block runs its share once per group of units; the sweep ring runs on across the
+    // groups (the loader's unit is in each sweep's descriptor).  A y element gets one add
+    // per group, from the same lane of the same wave and in group order (same-address
+    // atomics of one thread are applied in program order), as from one launch per group.
+    int u = wv;
+    bool uact = u < units;  // uniform
+    const int64_t nsw = s1 - s0;  // sweeps of the share, per group
     const uint32_t bank_row = (uint32_t)(d_in / 8);
-    // a wave's 16 lanes of B column n read 16 bytes of row n at its unit's 64; row tile r
-    // of a chunk 16 r rows further (the chunk's first row is in the descriptor)
-    const uint32_t lane_off = (uint32_t)n * bank_row + 64u * (uint32_t)(uact ? u : 0) + 16u * (uint32_t)G;
+    // a wave's 16 lanes of B column n read 16 bytes of row n at its unit's 64 (the unit's
+    // column offset is in the descriptor); row tile r of a chunk 16 r rows further
+    const uint32_t lane_off = (uint32_t)n * bank_row + 16u * (uint32_t)G;
     const uint32_t rstride = 16u * bank_row;
 #define BD_VOFF(r) (lane_off + (uint32_t)(r) * rstride)
 
     // ---- loading side: item (kL, cL), user jL; scalar state, one descriptor per sweep
-    int kL = sk0, cL = sc0, jL = sj0;
-    int64_t leftL = s1 - s0;  // sweeps the loader has not issued
-    int tileL = sload(torder, kL), nuL = 1;
+    int kL = sk0, cL = sc0, jL = sj0, gL = 0;
+    int64_t leftL = nsw;  // sweeps of its group the loader has not issued
+    const int tile0 = sload(torder, sk0);
+    int nu0 = 1;
     {
-        const int nu = sload(tpre, kL + 1) - sload(tpre, kL);
-        nuL = nu < 1 ? 1 : (nu > 16 ? 16 : nu);
+        const int q = sload(tpre, sk0 + 1) - sload(tpre, sk0);
+        nu0 = q < 1 ? 1 : (q > 16 ? 16 : q);
     }
+    int tileL = tile0, nuL = nu0;
     auto lsweep = [&]() __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
         const bool live = leftL > 0;
         int mi = 0;
@@ -889,14 +899,16 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
         for (int q = 1; q < kMaxMats; ++q) mi += (q < dm.n && cL >= dm.rb_begin[q]) ? 1 : 0;
         const int usr = live && (uint32_t)tileL < (uint32_t)ntl
                             ? sload(tmeta, (int64_t)tileL * kTileMetaInts + 32 + jL) : -1;
-        const bool ok = uact && (uint32_t)usr < (uint32_t)U;
+        const int uL = gL * W + wv;
+        const bool ok = uL < units && (uint32_t)usr < (uint32_t)U;
         const uint64_t* sg = pick_mat(dm.signs, mi);
         const int64_t d_out = pick_mat(dm.d_out, mi);
         const int64_t row0 = (int64_t)(cL - pick_rb(dm.rb_begin, mi)) * kChunkRows;
+        const uint64_t ucol = ok ? 64ull * (uint64_t)uL : 0ull;  // (< bank_row)
         const uint64_t base = (uint64_t)(uintptr_t)sg +
                               (uint64_t)(ok ? usr : 0) * pick_mat(dm.sstride, mi) +
-                              (uint64_t)row0 * bank_row;
-        const uint64_t rem = ok && row0 < d_out ? (uint64_t)(d_out - row0) * bank_row : 0ull;
+                              (uint64_t)row0 * bank_row + ucol;
+        const uint64_t rem = ok && row0 < d_out ? (uint64_t)(d_out - row0) * bank_row - ucol : 0ull;
         const int nrec = rem > 0x7FFFFFFFull ? 0x7FFFFFFF : (int)rem;
         if (live) {
             --leftL;
@@ -909,6 +921,15 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
                     const int nu = sload(tpre, kL + 1) - sload(tpre, kL);
                     nuL = nu < 1 ? 1 : (nu > 16 ? 16 : nu);
                 }
+            }
+            if (leftL == 0 && gL + 1 < ngrp) {  // the share again, for the next group
+                ++gL;
+                kL = sk0;
+                cL = sc0;
+                jL = sj0;
+                leftL = nsw;
+                tileL = tile0;
+                nuL = nu0;
             }
         }
         return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, 0x00020000);
@@ -937,8 +958,8 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
     asm volatile("s_mov_b32 %0, 0xCCCCCCCC" : "=s"(k1));
     asm volatile("s_mov_b32 %0, 0x88888888" : "=s"(k2));
     asm volatile("s_mov_b32 %0, 0x22222222" : "=s"(k3));
-    int k = sk0, c = sc0;
-    int64_t left = s1 - s0;  // sweeps not yet done
+    int k = sk0, c = sc0, grp = 0;
+    int64_t left = nsw;  // sweeps of the group not yet done
     int tile = -1, nu = 1, j = sj0, ja = sj0, ci = 0;  // ja: the item's first user here;
                                                      // ci: items done (LDS buffer parity)
     // A new tile in two parts.  tile_load issues the tile's loads: its meta (waited for:
@@ -1183,11 +1204,8 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
     };
 
     // the first tile's loads, the ring (the first two sweeps), then the first tile and item
-    tile = sload(torder, k);
-    {
-        const int q = tpre_at(k + 1) - tpre_at(k);
-        nu = q < 1 ? 1 : (q > 16 ? 16 : q);
-    }
+    tile = tile0;
+    nu = nu0;
     tile_load(tile, nu);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 ring[D];
@@ -1264,13 +1282,28 @@ k_delta8(const DeltaMats dm, const int32_t* __restrict__ tmeta,
             if (++j == nu || left == 0) {  // the item, or this block's part of it, is done
                 item_end(ja, j);
                 j = ja = 0;
-                if (left > 0) {
-                    if (++c == C) {
+                const bool regroup = left == 0 && grp + 1 < ngrp;  // uniform: the share
+                if (left > 0 || regroup) {                          // again, next units
+                    bool newtile = regroup;
+                    if (regroup) {
+                        ++grp;
+                        u = grp * W + wv;
+                        uact = u < units;
+                        left = nsw;
+                        k = sk0;
+                        c = sc0;
+                        j = ja = sj0;
+                        tile = tile0;
+                        nu = nu0;
+                    } else if (++c == C) {
                         c = 0;
                         ++k;
                         tile = sload(torder, k);
                         const int q = tpre_at(k + 1) - tpre_at(k);
                         nu = q < 1 ? 1 : (q > 16 ? 16 : q);
+                        newtile = true;
+                    }
+                    if (newtile) {
                         tile_load(tile, nu);
                         tile_finish(nu);
                     }
@@ -1335,8 +1368,8 @@ static int device_cus() {
     return cus[dev];
 }
 
-// Non-GROUP modes: persistent launches (k_delta8), the units of d_in split into
-// ceil(units / 8) launches of equal width, in unit order.
+// Non-GROUP modes: one persistent launch (k_delta8), the units of d_in split into
+// ceil(units / 8) groups of equal width, taken in unit order.
 static hipError_t launch_delta8_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                                     const DeltaMatArg* mats, int n, hipStream_t s) {
     uint32_t* meta = (uint32_t*)(batch + bp.off_meta);
@@ -1367,11 +1400,11 @@ static hipError_t launch_delta8_set(const BatchPlan& bp, const DeltaPlan& dp, ch
     for (int i = n; i <= kMaxMats; ++i) dm.rb_begin[i] = cb;
     const dim3 gd((unsigned)device_cus());
     const bool f16 = dp.sdtype == BD_F16;
-    for (int l = 0; l < nl; ++l) {
-        const int u0 = l * W;  // (the last launch may hold fewer units: its extra waves add 0)
+    {
+        // one launch: nl groups of W units (the last may hold fewer: its extra waves add 0)
 #define BD_D8(MODE, F16, RPW)                                                                  \
     hipLaunchKernelGGL((k_delta8<MODE, F16, RPW>), gd, dim3(64 * W), 0, s, dm, tmeta, torder,  \
-                       tpre, enc, meta, bp.d_in, nunit, u0, units, (int)bp.T, (int)bp.U)
+                       tpre, enc, meta, bp.d_in, nunit, nl, units, (int)bp.T, (int)bp.U)
 #define BD_D8W(MODE, F16)                                      \
     do {                                                       \
         if (W == kMaxW8) BD_D8(MODE, F16, 1);                  \
