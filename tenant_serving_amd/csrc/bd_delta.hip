@@ -1429,10 +1429,25 @@ static hipError_t launch_delta8_set(const BatchPlan& bp, const DeltaPlan& dp, ch
     return hipSuccess;
 }
 
+// MATRIX / ROW / COL take the persistent kernel (k_delta8) for batches of many users with a
+// few tokens each, when its groups of units are at least 7 wide; otherwise the per-tile
+// kernel k_delta6.  Measured on one MI355X: the persistent kernel takes the 32-layer stack's
+// delta phase (512 tokens, 128 users' banks) in 20.0 ms against 24.6; on the Qwen3-14B MLP
+// batch (1144 tokens, 32 users, 8 prefill chunks of 128 tokens: a user's chunk fills 8
+// tiles, which k_delta6 runs side by side, one tile per block) k_delta6 takes the step from
+// 2054 to 1866 us; with fewer than 7 waves (rows of 5120 columns: two groups of 5 units) the
+// persistent kernel's two-sweep ring keeps too few bytes in flight per CU.  The host knows
+// only the batch's size and user count: the mean tokens per user decides.
+static bool delta8_fits(const BatchPlan& bp) {
+    const int64_t units = (bp.d_in + 511) / 512;
+    const int64_t nl = (units + kMaxW8 - 1) / kMaxW8;
+    return (units + nl - 1) / nl >= 7 && bp.T < 16 * (int64_t)bp.U;
+}
+
 hipError_t launch_delta6_set(const BatchPlan& bp, const DeltaPlan& dp, char* batch,
                              const DeltaMatArg* mats, int n, hipStream_t s) {
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
-    if (dp.mode != BD_SCALE_GROUP) return launch_delta8_set(bp, dp, batch, mats, n, s);
+    if (dp.mode != BD_SCALE_GROUP && delta8_fits(bp)) return launch_delta8_set(bp, dp, batch, mats, n, s);
     uint32_t* meta = (uint32_t*)(batch + bp.off_meta);
     const int32_t* tmeta = (const int32_t*)(batch + bp.off_tmeta);
     const int32_t* torder = (const int32_t*)(batch + bp.off_torder);

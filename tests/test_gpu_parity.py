@@ -191,6 +191,45 @@ def test_apply_parity_large_batch(mode):
     assert_delta_within_bound(y0.cpu().numpy(), yd, S.host_x(w, 0), osc, p, ids)
 
 
+# MATRIX / ROW / COL batches take one of two delta kernels: the persistent one for
+# batches of few tokens per user (fewer than 16 on average) on rows whose groups of
+# 512-column units are at least 7 wide, the per-tile one otherwise.  Each route and mode:
+# (name, d_in, tokens per user (users 0..), unassigned tokens)
+ROUTE_CASES = [
+    ("persistent", 4096, (20, 1, 3, 0, 2, 5, 1, 4), 3),           # 36 tokens, 8 users
+    ("persistent_two_groups", 7168, (20, 1, 3, 0, 2, 5, 1, 4), 3),  # 14 units: 2 groups of 7
+    ("per_tile", 4096, (40, 9), 2),                                  # 49 tokens, 2 users
+]
+
+
+@pytest.mark.parametrize("mode", ["matrix", "row", "col"])
+@pytest.mark.parametrize("route", ROUTE_CASES, ids=lambda c: c[0])
+def test_apply_parity_delta_routes(route, mode):
+    _, d_in, users, extra = route
+    ids = _ids_mixed(T_users=users, extra_none=extra, seed=21)
+    T, U = len(ids), len(users)
+    d_out = 200  # a ragged 128-row chunk
+    w = custom(d_out, d_in, S.BF16, n_users=U, T=T, b=5e-3, cid=1370 + d_in // 512)
+    p = B.params(mode, 128, 0.0, B.BD_F32 if mode == "matrix" else B.BD_F16)
+    wb_dev = S.dev_wbase(w, 0)
+    x_dev = S.dev_x(w, 0)
+    signs, scales = gpu_bank(w, 0, wb_dev, p, range(U))
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    y = B.apply(x_dev, wb_dev, signs, scales, p, ids_dev, check=True)
+    wb = S.host_wbase(w, 0)
+    words, osc = oracle_bank(w, 0, wb, p, range(U))
+    yr, yb, yd = O.apply(S.host_x(w, 0), wb, words, osc, p.mode, ids, g=128, sdtype=o_sdtype(p))
+    err, rms = max_err_vs_rms(y.cpu().numpy(), yr)
+    assert err <= TOL_BF16 * rms, (err, rms)
+    y0 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
+    err0, rms0 = max_err_vs_rms(y0.cpu().numpy(), yd)
+    assert err0 <= tol_delta(mode) * rms0, (err0, rms0)
+    assert_delta_within_bound(y0.cpu().numpy(), yd, S.host_x(w, 0), osc, p, ids)
+    assert np.all(y0.cpu().numpy()[ids < 0] == 0)
+    y1 = B.apply(x_dev, torch.zeros_like(wb_dev), signs, scales, p, ids_dev, check=True)
+    assert torch.equal(y0, y1)  # repeat calls agree bit for bit
+
+
 @pytest.mark.parametrize("mode", ["matrix", "col"])
 def test_apply_parity_single_wave_grouping(mode):
     # T <= 64 takes the one-wave grouping kernel; a 40-token user spans two items
