@@ -837,11 +837,13 @@ def cpu_baseline(ids_np, active, bytes_step, rows=64, seconds=12.0, max_calls=20
 
 
 def workloads_leg(reps=10):
-    """One layer step of workloads 3 and 4 through the prepared-batch calls: per
-    distinct input width one bd_batch_prepare (the grouping and tile packing of the
-    batch), then per matrix bd_base_gemm and bd_delta_apply.  Random banks (the time
-    does not depend on the bit values; parity at these sizes is tested separately).
-    The step is captured `reps` times in a HIP graph and replayed."""
+    """One layer step of workloads 3 and 4 through the prepared-batch calls, grouped as
+    the stack's step is: per distinct input width one bd_batch_prepare (the grouping and
+    tile packing of the batch), then per activation tensor one bd_batch_encode, one
+    bd_base_gemm_n and one bd_delta_apply_encoded_n over the matrices that read it
+    (gate|up; down alone).  Random banks (the time does not depend on the bit values;
+    parity at these sizes is tested separately).  The step is captured `reps` times in a
+    HIP graph and replayed."""
     import torch
 
     from tenant_serving_amd import bitdelta as B
@@ -857,7 +859,7 @@ def workloads_leg(reps=10):
         nact = len(set(int(u) for u in ids_np if 0 <= u < U))
         gen = torch.Generator(device=dev)
         gen.manual_seed(1000 + wid)
-        xs, batches, mats = {}, {}, []
+        xs, batches, groups = {}, {}, {}
         tot_bytes = tot_flops = 0
         for m in w.matrices:
             p = B.params(m.mode, w.group_size, w.clip_k,
@@ -873,17 +875,30 @@ def workloads_leg(reps=10):
                 batches[m.d_in] = (xs[m.xgroup], B.workspace(
                     B.bd_batch_workspace_bytes(T, U, m.d_in, B.BD_BF16), dev))
             y = torch.empty(T, m.d_out, device=dev)
-            mats.append((xs[m.xgroup], p, wb, signs, scales, y, batches[m.d_in][1]))
+            # matrices that read one activation tensor share its encoding (COL scales are
+            # folded into the encoded tokens: a COL matrix keeps an encoding of its own)
+            key = (m.xgroup, len(groups)) if m.mode == S.COL else (m.xgroup, -1)
+            groups.setdefault(key, (xs[m.xgroup], p, batches[m.d_in][1], []))[3].append(
+                (wb, signs, scales, y))
             tot_bytes += (m.d_out * m.d_in * 2 + nact * (m.d_out * m.d_in // 8 + scales.element_size() * n_sc)
                           + T * m.d_in * 2 + T * m.d_out * 4 + 4 * T)
             tot_flops += 2 * T * m.d_out * m.d_in
+        need = max(B.bd_base_gemm_n_workspace_bytes(B.BD_BF16, T, x.shape[1],
+                                                    [wb.shape[0] for wb, _, _, _ in ms])
+                   for x, _, _, ms in groups.values())
+        gws = B.workspace(need, dev) if need > 0 else None
 
         def step():
             for x, bt in batches.values():
                 assert B.bd_batch_prepare(x, ids, U, bt) == B.BD_OK
-            for x, p, wb, signs, scales, y, bt in mats:
-                assert B.bd_base_gemm(x, wb, y) == B.BD_OK
-                assert B.bd_delta_apply(bt, x, U, signs, scales, p, y) == B.BD_OK
+            for x, p, bt, ms in groups.values():
+                col = ms[0][2] if p.mode == B.BD_SCALE_COL else None
+                assert B.bd_batch_encode(bt, x, U, col, p) == B.BD_OK
+                assert B.bd_base_gemm_n(x, [m[0] for m in ms], [m[3] for m in ms],
+                                        workspace=gws) == B.BD_OK
+                assert B.bd_delta_apply_encoded_n(bt, T, x.shape[1], U, [m[1] for m in ms],
+                                                  [m[2] for m in ms], p,
+                                                  [m[3] for m in ms]) == B.BD_OK
 
         step()
         torch.cuda.synchronize()
@@ -909,12 +924,12 @@ def workloads_leg(reps=10):
                     "active_users": nact, "us_per_step": round(us, 1),
                     "algorithmic_bytes": tot_bytes, "achieved_GBs": round(tot_bytes / us / 1e3, 1),
                     "frac_of_hbm_peak": round(tot_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                    "base_TFLOPs": round(tot_flops / us / 1e6, 1)})
-        del mats, xs, batches, g
+                    "base_TFLOPs": round(tot_flops / us / 1e6, 1),
+                    "calls": "per width bd_batch_prepare; per activation tensor bd_batch_encode, "
+                             "bd_base_gemm_n, bd_delta_apply_encoded_n"})
+        del groups, xs, batches, g, gws
         torch.cuda.empty_cache()
     return out
-
-
 
 
 LLAMA8B_LINEARS = ((4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096),  # q k v o
