@@ -67,10 +67,6 @@ def parse():
     return ap.parse_args()
 
 
-def _fail(what):
-    raise RuntimeError(f"{what} call failed")
-
-
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -195,7 +191,6 @@ class Stack:
         torch.cuda.synchronize()
         self.setup_s = time.perf_counter() - t0
 
-        self.side = torch.cuda.Stream(dev)  # (default priority)
         self.mats = mats
         self._account()
         self.n_mats = len(mats)
@@ -259,26 +254,13 @@ class Stack:
         for x, bt, ms in self._groups():
             self._delta(x, bt, ms)
 
-    def forked(self, encode, gemm, delta):
-        """One group's launches: the encoding and the base product read the same
-        activations and write different buffers, so the encoding runs on a second
-        stream beside the GEMM (both after the previous group's delta products, which
-        read the batch's last encoding); the delta products wait for both."""
-        import torch
-        main = torch.cuda.current_stream()
-        self.side.wait_stream(main)
-        with torch.cuda.stream(self.side):
-            encode()
-        gemm()
-        main.wait_stream(self.side)
-        delta()
-
     def step(self):
         B = self.B
         self.prepare()
         for x, bt, ms in self._groups():
-            self.forked(lambda: B.bd_batch_encode(bt, x, self.U, None, self.p) == B.BD_OK or _fail("encode"),
-                        lambda: self._gemm(x, ms), lambda: self._delta(x, bt, ms))
+            assert B.bd_batch_encode(bt, x, self.U, None, self.p) == B.BD_OK
+            self._gemm(x, ms)
+            self._delta(x, bt, ms)
 
 
 def stack_leg(args, dev):
@@ -400,8 +382,9 @@ def int8_leg(S, dev, K):
     def step():
         S.prepare()
         for x, bt, ms in S._groups():
-            S.forked(lambda: B.bd_batch_encode(bt, x, S.U, None, S.p) == B.BD_OK or _fail("encode"),
-                     lambda: gemm_q8(x, ms), lambda: S._delta(x, bt, ms))
+            assert B.bd_batch_encode(bt, x, S.U, None, S.p) == B.BD_OK
+            gemm_q8(x, ms)
+            S._delta(x, bt, ms)
 
     step()
     torch.cuda.synchronize()

@@ -324,10 +324,51 @@ int choose_split(int64_t T, int64_t d_in, const int64_t* d_outs, int n) {
     return 1;
 }
 
+// The bf16 product's tile and K split.  Measured at 512 tokens on one MI355X (one matrix
+// per launch, HIP events; split times include the sum of the parts): 6144 x 4096 (q|k|v)
+// 42 us on 128 x 128 tiles unsplit against 48 on 256 x 256 in 4 parts; 4096 x 4096 (o)
+// 28 us on 64 x 64 tiles (two blocks per CU) against 31 on 64 x 128; 4096 x 14336 (down)
+// 76 us on 128 x 256 in 4 parts against 82 on 256 x 256 in 8; 28672 x 4096 (gate|up) 123 us
+// on 256 x 256 unsplit, the best.  Order: 256 x 256 when it fills the chip; 128 x 128 when
+// its grid is one block per CU (192..256); with a workspace, 128 x 256 in 2..8 parts of at
+// least 2048 columns (grid 192..320), then 256 x 256 in parts (choose_split); otherwise
+// the largest unsplit tile that still fills the chip.
+enum { kT256x256, kT128x256, kT128x128, kT64x128, kT64x64 };
+struct GemmPlan {
+    int tile, S;
+};
+GemmPlan plan_bf16(int64_t T, int64_t d_in, const int64_t* d_outs, int n, bool split_ok) {
+    auto blocks = [&](int64_t br, int64_t bt) {
+        int64_t r = 0;
+        for (int i = 0; i < n; ++i) r += (d_outs[i] + br - 1) / br;
+        return r * ((T + bt - 1) / bt);
+    };
+    bool n4 = true;
+    for (int i = 0; i < n; ++i) n4 = n4 && d_outs[i] % 4 == 0;  // (the parts' sum reads f32x4)
+    if (blocks(256, 256) >= 200) return {kT256x256, 1};
+    const int64_t b128 = blocks(128, 128);
+    if (b128 >= 192 && b128 <= 256) return {kT128x128, 1};
+    if (split_ok && n4 && T > kGemmMinT) {
+        const int64_t b = blocks(128, 256);
+        for (int S = 2; S <= 8; S *= 2)
+            if (d_in % (64 * S) == 0 && d_in / S >= 2048 && b * S >= 192 && b * S <= 320) return {kT128x256, S};
+        const int S = choose_split(T, d_in, d_outs, n);
+        if (S > 1) return {kT256x256, S};
+    }
+    if (blocks(128, 256) >= 200) return {kT128x256, 1};
+    if (b128 >= 200) return {kT128x128, 1};
+    if (blocks(64, 64) >= 400) return {kT64x64, 1};
+    if (blocks(64, 128) >= 200) return {kT64x128, 1};
+    return {kT64x64, 1};
+}
+
 }  // namespace
 
 size_t gemm_split_bytes(int64_t T, int64_t d_in, const int64_t* d_outs, int n) {
-    const int S = choose_split(T, d_in, d_outs, n);
+    // room for the bf16 plan's parts and for the INT8 product's (256 x 256 in choose_split's
+    // parts), which sizes its workspace with the same query
+    const int Sb = plan_bf16(T, d_in, d_outs, n, true).S, Sq = choose_split(T, d_in, d_outs, n);
+    const int S = Sb > Sq ? Sb : Sq;
     if (S == 1) return 0;
     size_t b = 0;
     for (int i = 0; i < n; ++i) b += ((size_t)S * T * d_outs[i] * 4 + kAlign - 1) / kAlign * kAlign;
@@ -339,7 +380,9 @@ hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const G
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
     int64_t d_outs[kMaxMats];
     for (int i = 0; i < n; ++i) d_outs[i] = mats[i].d_out;
-    const int S = choose_split(T, d_in, d_outs, n);
+    const GemmPlan pl = wscales ? GemmPlan{kT256x256, choose_split(T, d_in, d_outs, n)}
+                                : plan_bf16(T, d_in, d_outs, n, ws != nullptr);
+    const int S = pl.S;
     if (S == 1 || !ws) return launch_gemm_set(x, T, d_in, mats, n, s, wscales);
     float* parts[kMaxMats];
     size_t off = 0;
@@ -349,9 +392,9 @@ hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const G
         off += ((size_t)S * T * d_outs[i] * 4 + kAlign - 1) / kAlign * kAlign;
         nmax = d_outs[i] > nmax ? d_outs[i] : nmax;
     }
-    hipError_t e = wscales
-        ? launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, wscales, S, parts)
-        : launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
+    hipError_t e = wscales ? launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, wscales, S, parts)
+                   : pl.tile == kT128x256 ? launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s, nullptr, S, parts)
+                                          : launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
     if (e != hipSuccess) return e;
     GemmMats gm = {};
     gm.n = n;
@@ -385,10 +428,10 @@ bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out) {
            d_out * d_in * 2 < ((int64_t)1 << 31) && d_out < ((int64_t)1 << 30);
 }
 
-// The largest tile that still yields enough blocks to cover the chip: 128 rows x 256
-// tokens (most reuse per copied byte), 128 x 128, 64 x 128, else 64 x 64 (small
-// matrices and batches, where idle CUs cost more than the extra copies).  INT8 codes
-// (wscales set): the same choice with two LDS stages throughout.
+// Without K parts: bf16 takes plan_bf16's unsplit tile (the largest that still covers the
+// chip; small matrices and batches take small tiles, where idle CUs cost more than the extra
+// copies).  INT8 codes (wscales set): 256 x 256, 128 x 256, 128 x 128, 64 x 128, else
+// 64 x 64, each when it gives 200 blocks, with two LDS stages throughout.
 hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
                            hipStream_t s, const float* const* wscales) {
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
@@ -406,11 +449,15 @@ hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMat
         if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
         return launch_tile<64, 64, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
     }
-    if (blocks(256, 256) >= 200) return launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s);
-    if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s);
-    if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 4>(x, T, d_in, mats, n, s);
-    if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 4>(x, T, d_in, mats, n, s);
-    return launch_tile<64, 64, 64, 4>(x, T, d_in, mats, n, s);
+    int64_t d_outs[kMaxMats];
+    for (int i = 0; i < n; ++i) d_outs[i] = mats[i].d_out;
+    switch (plan_bf16(T, d_in, d_outs, n, false).tile) {
+        case kT256x256: return launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s);
+        case kT128x256: return launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s);
+        case kT128x128: return launch_tile<128, 128, 64, 4>(x, T, d_in, mats, n, s);
+        case kT64x128: return launch_tile<64, 128, 64, 4>(x, T, d_in, mats, n, s);
+        default: return launch_tile<64, 64, 64, 4>(x, T, d_in, mats, n, s);
+    }
 }
 
 hipError_t launch_gemm(const void* x, int64_t T, int64_t d_in, const void* wb, int64_t d_out,

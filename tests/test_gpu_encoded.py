@@ -110,14 +110,16 @@ def test_grouped_calls_equal_per_matrix_calls():
         assert torch.equal(y, yr)
 
 
-@pytest.mark.parametrize("d_outs,d_in,T", [((4096, 1024, 1024), 4096, 512),  # q|k|v: 4 parts
-                                           ((4096,), 14336, 512),              # down: 8 parts
-                                           ((1028, 1028, 1024), 8192, 300)])   # ragged rows, T
+@pytest.mark.parametrize("d_outs,d_in,T", [((4096, 1024, 1024), 4096, 512),  # q|k|v: 128 x 128, whole K
+                                           ((4096,), 14336, 512),              # down: 128 x 256, 4 parts
+                                           ((1028, 1028, 1024), 8192, 300),    # ragged rows, T: 128 x 256, 4 parts
+                                           ((14336, 14336), 4096, 256)])       # gate|up at 256 tokens: 256 x 256, 2 parts
 def test_grouped_gemm_with_k_split(d_outs, d_in, T):
-    """bd_base_gemm_n with K split in ordered parts (workspace given): against the
+    """bd_base_gemm_n with a workspace (K split in ordered parts where the plan splits;
+    the workspace query also leaves room for the INT8 product's parts): against the
     oracle's base term on sampled rows of every matrix (exact bf16 products, fp32 sums:
-    1e-5 rms), against the unsplit launch within fp32 summation order, and bit for bit
-    from one call to the next."""
+    1e-5 rms), against the launch without a workspace within the sum of both bounds, and
+    bit for bit from one call to the next."""
     need = B.bd_base_gemm_n_workspace_bytes(B.BD_BF16, T, d_in, d_outs)
     assert need > 0
     ws_ = [custom(d, d_in, S.BF16, T=T, cid=2750 + i) for i, d in enumerate(d_outs)]
@@ -140,5 +142,7 @@ def test_grouped_gemm_with_k_split(d_outs, d_in, T):
                            np.zeros((1, 1), np.float32), O.MATRIX, ids)
         err, rms = max_err_vs_rms(ys[i].cpu().numpy()[:, rows], yb)
         assert err <= 1e-5 * rms, (i, err, rms)
+        # two fp32 summation orders (K parts, tile shape), each within 1e-5 rms of the
+        # binary64 product: their difference within the sum of the two bounds
         err, rms = max_err_vs_rms(ys[i].cpu().numpy(), yn[i].cpu().numpy().astype(np.float64))
-        assert err <= 1e-5 * rms, (i, err, rms)
+        assert err <= 2e-5 * rms, (i, err, rms)
