@@ -324,7 +324,7 @@ int choose_split(int64_t T, int64_t d_in, const int64_t* d_outs, int n) {
     return 1;
 }
 
-// The bf16 product's tile and K split.  Measured at 512 tokens on one MI355X (one matrix
+// The product's tile and K split (bf16 and INT8 bases alike).  Measured at 512 tokens on one MI355X (one matrix
 // per launch, HIP events; split times include the sum of the parts): 6144 x 4096 (q|k|v)
 // 42 us on 128 x 128 tiles unsplit against 48 on 256 x 256 in 4 parts; 4096 x 4096 (o)
 // 28 us on 64 x 64 tiles (two blocks per CU) against 31 on 64 x 128; 4096 x 14336 (down)
@@ -337,7 +337,7 @@ enum { kT256x256, kT128x256, kT128x128, kT64x128, kT64x64 };
 struct GemmPlan {
     int tile, S;
 };
-GemmPlan plan_bf16(int64_t T, int64_t d_in, const int64_t* d_outs, int n, bool split_ok) {
+GemmPlan plan_gemm(int64_t T, int64_t d_in, const int64_t* d_outs, int n, bool split_ok) {
     auto blocks = [&](int64_t br, int64_t bt) {
         int64_t r = 0;
         for (int i = 0; i < n; ++i) r += (d_outs[i] + br - 1) / br;
@@ -365,10 +365,7 @@ GemmPlan plan_bf16(int64_t T, int64_t d_in, const int64_t* d_outs, int n, bool s
 }  // namespace
 
 size_t gemm_split_bytes(int64_t T, int64_t d_in, const int64_t* d_outs, int n) {
-    // room for the bf16 plan's parts and for the INT8 product's (256 x 256 in choose_split's
-    // parts), which sizes its workspace with the same query
-    const int Sb = plan_bf16(T, d_in, d_outs, n, true).S, Sq = choose_split(T, d_in, d_outs, n);
-    const int S = Sb > Sq ? Sb : Sq;
+    const int S = plan_gemm(T, d_in, d_outs, n, true).S;  // (the INT8 product's too)
     if (S == 1) return 0;
     size_t b = 0;
     for (int i = 0; i < n; ++i) b += ((size_t)S * T * d_outs[i] * 4 + kAlign - 1) / kAlign * kAlign;
@@ -380,8 +377,7 @@ hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const G
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
     int64_t d_outs[kMaxMats];
     for (int i = 0; i < n; ++i) d_outs[i] = mats[i].d_out;
-    const GemmPlan pl = wscales ? GemmPlan{kT256x256, choose_split(T, d_in, d_outs, n)}
-                                : plan_bf16(T, d_in, d_outs, n, ws != nullptr);
+    const GemmPlan pl = plan_gemm(T, d_in, d_outs, n, ws != nullptr);
     const int S = pl.S;
     if (S == 1 || !ws) return launch_gemm_set(x, T, d_in, mats, n, s, wscales);
     float* parts[kMaxMats];
@@ -392,9 +388,13 @@ hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const G
         off += ((size_t)S * T * d_outs[i] * 4 + kAlign - 1) / kAlign * kAlign;
         nmax = d_outs[i] > nmax ? d_outs[i] : nmax;
     }
-    hipError_t e = wscales ? launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, wscales, S, parts)
-                   : pl.tile == kT128x256 ? launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s, nullptr, S, parts)
-                                          : launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
+    hipError_t e;
+    if (wscales)
+        e = pl.tile == kT128x256 ? launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, mats, n, s, wscales, S, parts)
+                                 : launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, wscales, S, parts);
+    else
+        e = pl.tile == kT128x256 ? launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s, nullptr, S, parts)
+                                 : launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
     if (e != hipSuccess) return e;
     GemmMats gm = {};
     gm.n = n;
@@ -428,30 +428,27 @@ bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out) {
            d_out * d_in * 2 < ((int64_t)1 << 31) && d_out < ((int64_t)1 << 30);
 }
 
-// Without K parts: bf16 takes plan_bf16's unsplit tile (the largest that still covers the
-// chip; small matrices and batches take small tiles, where idle CUs cost more than the extra
-// copies).  INT8 codes (wscales set): 256 x 256, 128 x 256, 128 x 128, 64 x 128, else
-// 64 x 64, each when it gives 200 blocks, with two LDS stages throughout.
+// Without K parts: plan_gemm's unsplit tile (the largest that still covers the chip; small
+// matrices and batches take small tiles, where idle CUs cost more than the extra copies).
+// INT8 codes (wscales set): the same tiles with two LDS stages throughout.
 hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
                            hipStream_t s, const float* const* wscales) {
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
     if (T == 0) return hipSuccess;
-    auto blocks = [&](int64_t br, int64_t bt) {
-        int64_t r = 0;
-        for (int i = 0; i < n; ++i) r += (mats[i].d_out + br - 1) / br;
-        return r * ((T + bt - 1) / bt);
-    };
-    if (wscales) {
-        const float* const* sc = wscales;
-        if (blocks(256, 256) >= 200) return launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, sc);
-        if (blocks(128, 256) >= 200) return launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
-        if (blocks(128, 128) >= 200) return launch_tile<128, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
-        if (blocks(64, 128) >= 200) return launch_tile<64, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
-        return launch_tile<64, 64, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
-    }
     int64_t d_outs[kMaxMats];
     for (int i = 0; i < n; ++i) d_outs[i] = mats[i].d_out;
-    switch (plan_bf16(T, d_in, d_outs, n, false).tile) {
+    const int tile = plan_gemm(T, d_in, d_outs, n, false).tile;
+    if (wscales) {
+        const float* const* sc = wscales;
+        switch (tile) {
+            case kT256x256: return launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, sc);
+            case kT128x256: return launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+            case kT128x128: return launch_tile<128, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+            case kT64x128: return launch_tile<64, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+            default: return launch_tile<64, 64, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+        }
+    }
+    switch (tile) {
         case kT256x256: return launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s);
         case kT128x256: return launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s);
         case kT128x128: return launch_tile<128, 128, 64, 4>(x, T, d_in, mats, n, s);

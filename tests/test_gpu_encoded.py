@@ -110,18 +110,18 @@ def test_grouped_calls_equal_per_matrix_calls():
         assert torch.equal(y, yr)
 
 
-@pytest.mark.parametrize("d_outs,d_in,T", [((4096, 1024, 1024), 4096, 512),  # q|k|v: 128 x 128, whole K
-                                           ((4096,), 14336, 512),              # down: 128 x 256, 4 parts
-                                           ((1028, 1028, 1024), 8192, 300),    # ragged rows, T: 128 x 256, 4 parts
-                                           ((14336, 14336), 4096, 256)])       # gate|up at 256 tokens: 256 x 256, 2 parts
-def test_grouped_gemm_with_k_split(d_outs, d_in, T):
-    """bd_base_gemm_n with a workspace (K split in ordered parts where the plan splits;
-    the workspace query also leaves room for the INT8 product's parts): against the
-    oracle's base term on sampled rows of every matrix (exact bf16 products, fp32 sums:
-    1e-5 rms), against the launch without a workspace within the sum of both bounds, and
-    bit for bit from one call to the next."""
+@pytest.mark.parametrize("d_outs,d_in,T,split", [
+    ((4096, 1024, 1024), 4096, 512, False),  # q|k|v: 128 x 128, whole K
+    ((4096,), 14336, 512, True),             # down: 128 x 256, 4 parts
+    ((1028, 1028, 1024), 8192, 300, True),   # ragged rows, T: 128 x 256, 4 parts
+    ((14336, 14336), 4096, 256, True)])      # gate|up at 256 tokens: 256 x 256, 2 parts
+def test_grouped_gemm_with_k_split(d_outs, d_in, T, split):
+    """bd_base_gemm_n with a workspace (K split in ordered parts where the plan splits):
+    against the oracle's base term on sampled rows of every matrix (exact bf16 products,
+    fp32 sums: 1e-5 rms), against the launch without a workspace within the sum of both
+    bounds, and bit for bit from one call to the next."""
     need = B.bd_base_gemm_n_workspace_bytes(B.BD_BF16, T, d_in, d_outs)
-    assert need > 0
+    assert (need > 0) == split
     ws_ = [custom(d, d_in, S.BF16, T=T, cid=2750 + i) for i, d in enumerate(d_outs)]
     wbs = [S.dev_wbase(w, 0) for w in ws_]
     x = S.dev_x(ws_[0], 0)
