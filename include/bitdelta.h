@@ -376,7 +376,8 @@ bd_status bd_delta_apply_encoded(void* batch, size_t batch_bytes, bd_dtype x_dty
 /* Grouped forms for matrices that read the same activations (q, k and v; gate and
  * up), up to 4 per call: one launch each instead of one per matrix, so small
  * matrices (k and v) share the grid with large ones.  Results equal, bit for bit,
- * n_mats calls of bd_base_gemm / bd_delta_apply_encoded with the same arguments.
+ * n_mats calls of bd_base_gemm / bd_delta_apply_encoded with the same arguments
+ * (bd_base_gemm_n without a workspace: with one, K may be split, below).
  *  n_mats      : 1..4.
  *  d_outs      : host int64[n_mats], the output rows of each matrix.
  *  w_bases     : host array of n_mats device pointers, [d_outs[i]][d_in] each.
@@ -384,11 +385,11 @@ bd_status bd_delta_apply_encoded(void* batch, size_t batch_bytes, bd_dtype x_dty
  *                bd_delta_apply_encoded with d_out = d_outs[i].
  *  ys          : host array of n_mats device pointers, fp32 [T][d_outs[i]] each.
  * bd_base_gemm_n falls back to one launch per matrix for batches the tiled GEMM
- * does not take (T <= 64, fp32).  Where the largest tile would leave most of the
- * chip idle (few rows and tokens: q|k|v, o or down at 512 tokens) and `workspace` is
- * given, K is split into 2, 4 or 8 ordered parts whose partial products go to the
- * workspace and are summed by a second launch in part order, so y repeats bit for
- * bit; workspace NULL (or bd_base_gemm_n_workspace_bytes == 0): no split.
+ * does not take (T <= 64, fp32).  Where no tile gives the chip a full grid with K
+ * whole (few rows and tokens: down_proj at 512 tokens) and `workspace` is given, K
+ * is split into 2, 4 or 8 ordered parts whose partial products go to the workspace
+ * and are summed by a second launch in part order, so y repeats bit for bit;
+ * workspace NULL (or bd_base_gemm_n_workspace_bytes == 0): no split.
  *  workspace   : >= bd_base_gemm_n_workspace_bytes(...) bytes, 256-byte aligned,
  *                or NULL. */
 size_t bd_base_gemm_n_workspace_bytes(bd_dtype x_dtype, int64_t T, int64_t d_in, int32_t n_mats,
