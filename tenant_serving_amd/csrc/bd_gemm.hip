@@ -329,10 +329,12 @@ int choose_split(int64_t T, int64_t d_in, const int64_t* d_outs, int n) {
 // 42 us on 128 x 128 tiles unsplit against 48 on 256 x 256 in 4 parts; 4096 x 4096 (o)
 // 28 us on 64 x 64 tiles (two blocks per CU) against 31 on 64 x 128; 4096 x 14336 (down)
 // 76 us on 128 x 256 in 4 parts against 82 on 256 x 256 in 8; 28672 x 4096 (gate|up) 123 us
-// on 256 x 256 unsplit, the best.  Order: 256 x 256 when it fills the chip; 128 x 128 when
+// on 256 x 256 unsplit, the best; at 256 tokens 4096 x 14336 (the clipped MLP's down) 46 us
+// on 128 x 128 in 4 parts against 73 on 64 x 64 (4096 x 4096 in 2 parts of 2048 columns
+// does not pay: 32 us against 28).  Order: 256 x 256 when it fills the chip; 128 x 128 when
 // its grid is one block per CU (192..256); with a workspace, 128 x 256 in 2..8 parts of at
-// least 2048 columns (grid 192..320), then 256 x 256 in parts (choose_split); otherwise
-// the largest unsplit tile that still fills the chip.
+// least 2048 columns (grid 192..320), 128 x 128 in parts of at least 3072 columns, then
+// 256 x 256 in parts (choose_split); otherwise the largest unsplit tile that fills the chip.
 enum { kT256x256, kT128x256, kT128x128, kT64x128, kT64x64 };
 struct GemmPlan {
     int tile, S;
@@ -352,6 +354,8 @@ GemmPlan plan_gemm(int64_t T, int64_t d_in, const int64_t* d_outs, int n, bool s
         const int64_t b = blocks(128, 256);
         for (int S = 2; S <= 8; S *= 2)
             if (d_in % (64 * S) == 0 && d_in / S >= 2048 && b * S >= 192 && b * S <= 320) return {kT128x256, S};
+        for (int S = 2; S <= 8; S *= 2)
+            if (d_in % (64 * S) == 0 && d_in / S >= 3072 && b128 * S >= 192 && b128 * S <= 320) return {kT128x128, S};
         const int S = choose_split(T, d_in, d_outs, n);
         if (S > 1) return {kT256x256, S};
     }
@@ -391,10 +395,12 @@ hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const G
     hipError_t e;
     if (wscales)
         e = pl.tile == kT128x256 ? launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, mats, n, s, wscales, S, parts)
-                                 : launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, wscales, S, parts);
+            : pl.tile == kT128x128 ? launch_tile<128, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, wscales, S, parts)
+                                   : launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, wscales, S, parts);
     else
         e = pl.tile == kT128x256 ? launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s, nullptr, S, parts)
-                                 : launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
+            : pl.tile == kT128x128 ? launch_tile<128, 128, 64, 4>(x, T, d_in, mats, n, s, nullptr, S, parts)
+                                   : launch_tile<256, 256, 64, 2, 8>(x, T, d_in, mats, n, s, nullptr, S, parts);
     if (e != hipSuccess) return e;
     GemmMats gm = {};
     gm.n = n;

@@ -114,7 +114,8 @@ def test_grouped_calls_equal_per_matrix_calls():
     ((4096, 1024, 1024), 4096, 512, False),  # q|k|v: 128 x 128, whole K
     ((4096,), 14336, 512, True),             # down: 128 x 256, 4 parts
     ((1028, 1028, 1024), 8192, 300, True),   # ragged rows, T: 128 x 256, 4 parts
-    ((14336, 14336), 4096, 256, True)])      # gate|up at 256 tokens: 256 x 256, 2 parts
+    ((14336, 14336), 4096, 256, True),       # gate|up at 256 tokens: 256 x 256, 2 parts
+    ((4096,), 14336, 256, True)])            # down at 256 tokens: 128 x 128, 4 parts
 def test_grouped_gemm_with_k_split(d_outs, d_in, T, split):
     """bd_base_gemm_n with a workspace (K split in ordered parts where the plan splits):
     against the oracle's base term on sampled rows of every matrix (exact bf16 products,
