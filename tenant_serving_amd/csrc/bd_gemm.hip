@@ -17,6 +17,8 @@
 // row tile hit the XCD's L2.
 #include "bd_internal.h"
 
+#include <type_traits>
+
 namespace bd {
 namespace {
 
@@ -79,9 +81,11 @@ __device__ __forceinline__ uint32_t swz(int r, int c) {
 // Kernel templates live outside the anonymous namespace: the host compiler does
 // not emit the launch stubs of internal-linkage kernel templates.
 // Q8: W holds int8 codes with one scale per row (the INT8 base): each lane loads 16
-// codes of a row into registers, widens them to bf16 and writes the two chunks to their
-// swizzled LDS slots (NS = 2: the next stage's codes are loaded during this stage's
-// products and written after them); the epilogue multiplies each row by its scale.
+// codes of a row into registers two stages ahead (two register sets, alternating), widens
+// them to bf16 and writes the two chunks to their swizzled LDS slots after the products of
+// the stage before; the epilogue multiplies each row by its scale.  Each stage's code
+// loads go out before its token copies: vector loads complete in order, so waiting for
+// the codes leaves the younger token copies in flight and the ring keeps its depth.
 template <int BR, int BT, int BK, int NS, int NW, bool Q8>
 __global__ void __launch_bounds__(64 * NW)
 k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt, int S, int kps) {
@@ -95,7 +99,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt,
     static_assert(kWBytes % (1024 * NW) == 0 && kXBytes % (1024 * NW) == 0,
                   "whole copy instructions per wave");
     static_assert(MI >= 1 && BR % (32 * NWR) == 0, "32-row tiles per wave");
-    static_assert(!Q8 || (NS == 2 && (BR * BK) % (1024 * NW) == 0), "INT8 codes: two stages");
+    static_assert(!Q8 || (BR * BK) % (1024 * NW) == 0, "INT8 codes: whole loads per wave");
     constexpr int kQInst = Q8 ? BR * BK / (1024 * NW) : 1;  // 16-code loads per lane and stage
     extern __shared__ __attribute__((aligned(16))) char smem[];
     // block -> (K part, row tile, token tile); the token tiles of one row tile share an
@@ -148,7 +152,7 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt,
     // Q8 loader: load j of lane l covers codes [16 c, 16 c + 16) of row r (g = 64 (wv
     // kQInst + j) + l, r = g / (BK / 16), c = g % (BK / 16)), bf16 chunks 2 c and 2 c + 1
     uint32_t qsrc[kQInst], qdst[kQInst];
-    u32x4 qreg[kQInst];
+    u32x4 qreg[2][kQInst];  // stage s's codes in set s % 2
 #pragma unroll
     for (int j = 0; j < kQInst; ++j) {
         const int g = (wv * kQInst + j) * 64 + lane;
@@ -157,21 +161,23 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt,
         qdst[j] = (uint32_t)(r * 4096 + c);  // (row, code group), unpacked at the store
     }
     const int nk = kps / BK;  // stages of this block's K part
-    auto qload = [&](int s) {  // stage s's codes into registers (zeros past K)
+    auto qload = [&](int s, auto pc) {  // stage s's codes into set pc (zeros past K)
+        constexpr int P = decltype(pc)::value;
 #pragma unroll
         for (int j = 0; j < kQInst; ++j)
-            qreg[j] = buf_load16(wrs, (s < nk && qsrc[j] != kOOB) ? qsrc[j] + (uint32_t)(kbeg + s * BK) : kOOB);
+            qreg[P][j] = buf_load16(wrs, (s < nk && qsrc[j] != kOOB) ? qsrc[j] + (uint32_t)(kbeg + s * BK) : kOOB);
     };
-    auto qstore = [&](int s) {  // the codes of stage s, widened, into ring slot s % NS
+    auto qstore = [&](int s, auto pc) {  // the codes of stage s (set pc), widened, into ring slot s % NS
+        constexpr int P = decltype(pc)::value;
         char* base = smem + (s % NS) * kStageBytes;
 #pragma unroll
         for (int j = 0; j < kQInst; ++j) {
             const int r = (int)(qdst[j] >> 12), c = (int)(qdst[j] & 4095u);
             uint32_t v[8];
-            widen_i8x4(qreg[j].x, v[0], v[1]);
-            widen_i8x4(qreg[j].y, v[2], v[3]);
-            widen_i8x4(qreg[j].z, v[4], v[5]);
-            widen_i8x4(qreg[j].w, v[6], v[7]);
+            widen_i8x4(qreg[P][j].x, v[0], v[1]);
+            widen_i8x4(qreg[P][j].y, v[2], v[3]);
+            widen_i8x4(qreg[P][j].z, v[4], v[5]);
+            widen_i8x4(qreg[P][j].w, v[6], v[7]);
             const u32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
             *(u32x4*)(base + swz<BK>(r, 2 * c)) = a;
             *(u32x4*)(base + swz<BK>(r, 2 * c + 1)) = b;
@@ -201,24 +207,31 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt,
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if constexpr (Q8) {
+        qload(0, P0());
+        qload(1, P1());
+    }
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(s);
-    if (Q8) {
-        qload(0);
-        qstore(0);
-    }
+    if constexpr (Q8) qstore(0, P0());
 
     const int m32 = lane & 31, h = lane >> 5;
-    for (int s = 0; s < nk; ++s) {
-        // this wave's copies of stage s are done (NS - 2 younger stages in flight); the
-        // barrier makes every wave's copies visible and frees the slot of stage s - 1
+    // stage s (parity pc: Q8 loads stage s + 2's codes into set pc and stores stage s + 1's
+    // from the other set)
+    auto stage = [&](int s, auto pc) {
+        constexpr int P = decltype(pc)::value;
+        // this wave's copies of stage s are done (NS - 2 younger stages in flight, each one
+        // stage's token copies (bf16: and W copies; Q8: and the codes of a later stage));
+        // the barrier makes every wave's copies visible and frees the slot of stage s - 1
         // (Q8: also this wave's LDS writes of the stage's codes)
-        constexpr int kAhead = (kWInst + kXInst) * (NS - 2);
+        constexpr int kAhead = ((Q8 ? kQInst : kWInst) + kXInst) * (NS - 2);
         __builtin_amdgcn_s_waitcnt((Q8 ? 0x0070 : 0x0F70) | (kAhead & 0xF) |
                                    (((kAhead >> 4) & 3) << 14));
         __builtin_amdgcn_s_barrier();  // no fence: the explicit wait above covers the copies
+        if constexpr (Q8) qload(s + 2, pc);  // (set P: stage s's codes were stored before)
         issue(s + NS - 1);
-        if (Q8) qload(s + 1);
         const char* wt_base = smem + (s % NS) * kStageBytes;
         const char* xt_base = wt_base + kWBytes;
 #pragma unroll
@@ -235,7 +248,13 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt,
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(A[i], Bv[j], acc[i][j]);
         }
-        if (Q8 && s + 1 < nk) qstore(s + 1);  // slot of stage s - 1: free since the barrier
+        if constexpr (Q8) {
+            if (s + 1 < nk) qstore(s + 1, std::integral_constant<int, 1 - P>());  // slot of stage s - 1: free
+        }
+    };
+    for (int s = 0; s < nk; s += 2) {
+        stage(s, P0());
+        if (s + 1 < nk) stage(s + 1, P1());  // (uniform)
     }
 
     // D lane layout (32 x 32): column m32, register 4b + e holds row 8b + 4h + e
@@ -394,8 +413,8 @@ hipError_t launch_gemm_set_split(const void* x, int64_t T, int64_t d_in, const G
     }
     hipError_t e;
     if (wscales)
-        e = pl.tile == kT128x256 ? launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, mats, n, s, wscales, S, parts)
-            : pl.tile == kT128x128 ? launch_tile<128, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, wscales, S, parts)
+        e = pl.tile == kT128x256 ? launch_tile<128, 256, 64, 3, 4, true>(x, T, d_in, mats, n, s, wscales, S, parts)
+            : pl.tile == kT128x128 ? launch_tile<128, 128, 64, 4, 4, true>(x, T, d_in, mats, n, s, wscales, S, parts)
                                    : launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, wscales, S, parts);
     else
         e = pl.tile == kT128x256 ? launch_tile<128, 256, 64, 3>(x, T, d_in, mats, n, s, nullptr, S, parts)
@@ -436,7 +455,7 @@ bool gemm_path_supported(int64_t T, int64_t d_in, int64_t d_out) {
 
 // Without K parts: plan_gemm's unsplit tile (the largest that still covers the chip; small
 // matrices and batches take small tiles, where idle CUs cost more than the extra copies).
-// INT8 codes (wscales set): the same tiles with two LDS stages throughout.
+// INT8 codes (wscales set): the same tiles and LDS rings.
 hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMatArg* mats, int n,
                            hipStream_t s, const float* const* wscales) {
     if (n < 1 || n > kMaxMats) return hipErrorInvalidValue;
@@ -448,10 +467,10 @@ hipError_t launch_gemm_set(const void* x, int64_t T, int64_t d_in, const GemmMat
         const float* const* sc = wscales;
         switch (tile) {
             case kT256x256: return launch_tile<256, 256, 64, 2, 8, true>(x, T, d_in, mats, n, s, sc);
-            case kT128x256: return launch_tile<128, 256, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
-            case kT128x128: return launch_tile<128, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
-            case kT64x128: return launch_tile<64, 128, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
-            default: return launch_tile<64, 64, 64, 2, 4, true>(x, T, d_in, mats, n, s, sc);
+            case kT128x256: return launch_tile<128, 256, 64, 3, 4, true>(x, T, d_in, mats, n, s, sc);
+            case kT128x128: return launch_tile<128, 128, 64, 4, 4, true>(x, T, d_in, mats, n, s, sc);
+            case kT64x128: return launch_tile<64, 128, 64, 4, 4, true>(x, T, d_in, mats, n, s, sc);
+            default: return launch_tile<64, 64, 64, 4, 4, true>(x, T, d_in, mats, n, s, sc);
         }
     }
     switch (tile) {
