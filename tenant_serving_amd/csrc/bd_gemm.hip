@@ -209,12 +209,17 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt,
 
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    if constexpr (Q8) {
-        qload(0, P0());
-        qload(1, P1());
-    }
+    // The prologue issues in the loop's order, as if by stages t = -max(NS - 1, 2) .. -1
+    // (stage t: stage t + 2's codes, then stage t + NS - 1's copies), so that the wait at the
+    // top of every stage counts the same younger loads as in the loop.
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(s);
+    for (int t = -(NS - 1 > 2 ? NS - 1 : 2); t < 0; ++t) {
+        if constexpr (Q8) {
+            if (t + 2 == 0) qload(0, P0());
+            if (t + 2 == 1) qload(1, P1());
+        }
+        if (t + NS - 1 >= 0) issue(t + NS - 1);
+    }
     if constexpr (Q8) qstore(0, P0());
 
     const int m32 = lane & 31, h = lane >> 5;
