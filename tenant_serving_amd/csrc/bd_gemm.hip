@@ -241,6 +241,8 @@ k_gemm(const uint16_t* __restrict__ x, const GemmMats gm, int T, int K, int ntt,
         const char* xt_base = wt_base + kWBytes;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {  // 16 columns per step: lane half h takes chunk 2kk + h
+            // the compiler's interleaving of LDS reads with the products (scheduling only)
+            __builtin_amdgcn_iglp_opt(0);
             u32x4 A[MI], Bv[NJ];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
